@@ -1,0 +1,292 @@
+/*
+ * Plain CPU oracle.  TEST INFRASTRUCTURE ONLY: see oracle.h for the sources
+ * followed, the precision rules and who may load this code.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off oracle.c -lm
+ * (no fast-math: the fp32 divisions below must be correctly rounded and the
+ * fp64 sums must be evaluated as written).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_LOG2E 1.4426950408889634073599246810018921 /* log2(e) */
+
+/* ---- number formats --------------------------------------------------- */
+
+/* OCP e4m3fn: sign, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent
+ * field 0 is the subnormal range m * 2^-9; S.1111.111 is NaN; there are no
+ * infinities.  0x7E = 1.75 * 2^8 = 448 is the largest finite value, the
+ * maximum the storage section of the fp8-kv-cache page divides by. */
+double orc_e4m3_value(uint8_t code) {
+  int sign = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+/* Round-to-nearest-even onto the e4m3 grid after saturating at 448.
+ * In the binade [2^e, 2^(e+1)) (e >= -6) the grid spacing is 2^(e-3); below
+ * 2^-6 the subnormals keep the spacing 2^-9.  a / spacing is the integer
+ * significand (8 + m, or m for subnormals), so rounding it half-to-even is
+ * rounding the code half-to-even. */
+uint8_t orc_e4m3_encode(float y) {
+  double a = fabs((double)y);
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  int ex, e;
+  double spacing, r;
+  if (a > 448.0) a = 448.0;
+  if (a == 0.0) return sign;
+  frexp(a, &ex); /* a = f * 2^ex, f in [0.5, 1) */
+  e = ex - 1;    /* a in [2^e, 2^(e+1)) */
+  if (e < -6) e = -6;
+  spacing = ldexp(1.0, e - 3);
+  r = rint(a / spacing) * spacing; /* default rounding mode: half to even */
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) /* subnormal: exponent field 0, m = r / 2^-9 */
+    return (uint8_t)(sign | (uint8_t)ldexp(r, 9));
+  frexp(r, &ex);
+  /* r = (8 + m) * 2^(ex-4), exponent field E = ex + 6 */
+  return (uint8_t)(sign | ((ex + 6) << 3) | ((int)ldexp(r, 4 - ex) - 8));
+}
+
+/* bf16: 8 significant bits, the exponent range of fp32, subnormals below
+ * 2^-126 with spacing 2^-133.  Same grid argument as above. */
+uint16_t orc_bf16_round(double x) {
+  double a = fabs(x);
+  uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  int ex, e;
+  double r;
+  float f;
+  uint32_t u;
+  if (a == 0.0) return sign;
+  frexp(a, &ex);
+  e = ex - 1;
+  if (e < -126) e = -126;
+  r = rint(ldexp(a, 7 - e));
+  r = ldexp(r, e - 7);
+  f = (float)r; /* exact: r has at most 8 significant bits (inf on overflow) */
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)((u >> 16) & 0x7FFF));
+}
+
+double orc_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+void orc_e4m3_encode_array(const float* y, uint8_t* codes, size_t n) {
+  size_t i;
+  for (i = 0; i < n; ++i) codes[i] = orc_e4m3_encode(y[i]);
+}
+
+void orc_bf16_round_array_f32(const float* x, uint16_t* bits, size_t n) {
+  size_t i;
+  for (i = 0; i < n; ++i) bits[i] = orc_bf16_round((double)x[i]);
+}
+
+/* ---- append: per-(token, KV head) row quantisation -------------------- */
+
+/* Storage section of the fp8-kv-cache page: one fp32 scale per row,
+ * amax(|row|) / 448 over the head dimension, codes in e4m3. */
+void orc_quantize_rows(const float* x, int64_t n_rows, int d, uint8_t* codes,
+                       float* scales) {
+  int64_t r;
+  int j;
+  for (r = 0; r < n_rows; ++r) {
+    const float* row = x + r * d;
+    float amax = 0.0f, scale;
+    for (j = 0; j < d; ++j) {
+      float a = fabsf(row[j]);
+      if (a > amax) amax = a;
+    }
+    scale = amax / 448.0f; /* fp32 division, correctly rounded */
+    scales[r] = scale;
+    for (j = 0; j < d; ++j) {
+      float y;
+      if (scale == 0.0f) {
+        codes[r * d + j] = 0x00;
+        continue;
+      }
+      y = row[j] / scale; /* fp32 division, correctly rounded */
+      codes[r * d + j] = orc_e4m3_encode(y);
+    }
+  }
+}
+
+/* ---- attention -------------------------------------------------------- */
+
+typedef struct {
+  int mode, d, n_keys;
+  const uint8_t *k8, *v8;
+  const uint16_t *k16, *v16;
+  const float *ks, *vs;
+} kv_view;
+
+static double k_elem(const kv_view* kv, int t, int j) {
+  if (kv->mode == ORC_K8V8) return orc_e4m3_value(kv->k8[(size_t)t * kv->d + j]);
+  return orc_bf16_value(kv->k16[(size_t)t * kv->d + j]);
+}
+
+static double v_elem(const kv_view* kv, int t, int j) {
+  if (kv->mode == ORC_BF16) return orc_bf16_value(kv->v16[(size_t)t * kv->d + j]);
+  return orc_e4m3_value(kv->v8[(size_t)t * kv->d + j]);
+}
+
+static double k_scale(const kv_view* kv, int t) {
+  return kv->mode == ORC_K8V8 ? (double)kv->ks[t] : 1.0;
+}
+
+static double v_scale(const kv_view* kv, int t) {
+  return kv->mode == ORC_BF16 ? 1.0 : (double)kv->vs[t];
+}
+
+/* Score in log2 units: (q . K_t) * k_scale_t * sm_scale * log2(e).
+ * The K scale sits outside the dot product (CDNA 3 section of the hardware
+ * notes; "Math" section of the fp8-kv-cache page). */
+static double score(const kv_view* kv, const double* qv, int t, double c) {
+  double dot = 0.0;
+  int j;
+  for (j = 0; j < kv->d; ++j) dot += qv[j] * k_elem(kv, t, j);
+  return dot * k_scale(kv, t) * c;
+}
+
+/* P with the V scale folded in, rounded to bf16 when round_p is set. */
+static double p_folded(const kv_view* kv, double p, int t, int round_p) {
+  double w = p * v_scale(kv, t);
+  return round_p ? orc_bf16_value(orc_bf16_round(w)) : w;
+}
+
+static int clamp_valid(int nv, int n_keys) {
+  if (nv < 0) return 0;
+  return nv > n_keys ? n_keys : nv;
+}
+
+void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
+                     int n_keys, const uint8_t* k8, const uint16_t* k16,
+                     const float* ks, const uint8_t* v8, const uint16_t* v16,
+                     const float* vs, const int32_t* n_valid, float sm_scale,
+                     int round_p, double* out) {
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
+  double c = (double)sm_scale * ORC_LOG2E;
+  double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  int r, t, j;
+  for (r = 0; r < n_rows; ++r) {
+    int nv = clamp_valid(n_valid[r], n_keys);
+    double smax = -INFINITY, m, l = 0.0;
+    double* o = out + (size_t)r * d;
+    for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q[(size_t)r * d + j]);
+    if (nv == 0) { /* no visible key: the row outputs 0 */
+      for (j = 0; j < d; ++j) o[j] = 0.0;
+      continue;
+    }
+    /* pass 1: scores and their maximum */
+    for (t = 0; t < nv; ++t) {
+      s[t] = score(&kv, qv, t, c);
+      if (s[t] > smax) smax = s[t];
+    }
+    m = ceil(smax);
+    /* pass 2: probabilities, normaliser, P.V */
+    for (j = 0; j < d; ++j) acc[j] = 0.0;
+    for (t = 0; t < nv; ++t) {
+      double p = exp2(s[t] - m);
+      double w = p_folded(&kv, p, t, round_p);
+      l += p;
+      for (j = 0; j < d; ++j) acc[j] += w * v_elem(&kv, t, j);
+    }
+    for (j = 0; j < d; ++j) o[j] = acc[j] / l;
+  }
+  free(qv);
+  free(s);
+  free(acc);
+}
+
+void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
+                            int n_keys, const uint8_t* k8, const uint16_t* k16,
+                            const float* ks, const uint8_t* v8,
+                            const uint16_t* v16, const float* vs,
+                            const int32_t* n_valid, float sm_scale,
+                            int round_p, int tile, int split,
+                            double* part_acc, double* part_l, double* part_m,
+                            double* out) {
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
+  double c = (double)sm_scale * ORC_LOG2E;
+  int n_splits = n_keys > 0 ? (n_keys + split - 1) / split : 0;
+  double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* s = (double*)malloc(sizeof(double) * (size_t)tile);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  double* sacc = (double*)malloc(sizeof(double) * (size_t)(n_splits > 0 ? n_splits : 1) * d);
+  double* sl = (double*)malloc(sizeof(double) * (size_t)(n_splits > 0 ? n_splits : 1));
+  double* sm = (double*)malloc(sizeof(double) * (size_t)(n_splits > 0 ? n_splits : 1));
+  int r, sp, t0, t, j;
+  for (r = 0; r < n_rows; ++r) {
+    int nv = clamp_valid(n_valid[r], n_keys);
+    double mstar = -INFINITY, lsum = 0.0;
+    for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q[(size_t)r * d + j]);
+    for (sp = 0; sp < n_splits; ++sp) {
+      int k_lo = sp * split;
+      int k_hi = k_lo + split < n_keys ? k_lo + split : n_keys;
+      double m = -INFINITY, l = 0.0;
+      for (j = 0; j < d; ++j) acc[j] = 0.0;
+      for (t0 = k_lo; t0 < k_hi; t0 += tile) {
+        int t1 = t0 + tile < k_hi ? t0 + tile : k_hi;
+        double tmax = -INFINITY, m_new, alpha;
+        /* scores of the visible keys of this tile */
+        for (t = t0; t < t1; ++t) {
+          if (t >= nv) break;
+          s[t - t0] = score(&kv, qv, t, c);
+          if (s[t - t0] > tmax) tmax = s[t - t0];
+        }
+        if (tmax == -INFINITY) continue; /* fully masked tile: keep state */
+        m_new = ceil(tmax) > m ? ceil(tmax) : m;
+        alpha = (m == -INFINITY) ? 0.0 : exp2(m - m_new); /* power of two */
+        l *= alpha;
+        for (j = 0; j < d; ++j) acc[j] *= alpha;
+        for (t = t0; t < t1 && t < nv; ++t) {
+          double p = exp2(s[t - t0] - m_new);
+          double w = p_folded(&kv, p, t, round_p);
+          l += p;
+          for (j = 0; j < d; ++j) acc[j] += w * v_elem(&kv, t, j);
+        }
+        m = m_new;
+      }
+      sm[sp] = m;
+      sl[sp] = l;
+      memcpy(sacc + (size_t)sp * d, acc, sizeof(double) * (size_t)d);
+      if (part_acc)
+        memcpy(part_acc + ((size_t)sp * n_rows + r) * d, acc, sizeof(double) * (size_t)d);
+      if (part_l) part_l[(size_t)sp * n_rows + r] = l;
+      if (part_m) part_m[(size_t)sp * n_rows + r] = m;
+      if (m > mstar) mstar = m;
+    }
+    /* merge: weights 2^(M_s - M*), zero for a split with no visible key */
+    for (j = 0; j < d; ++j) acc[j] = 0.0;
+    for (sp = 0; sp < n_splits; ++sp) {
+      double w;
+      if (sm[sp] == -INFINITY) continue;
+      w = exp2(sm[sp] - mstar);
+      lsum += w * sl[sp];
+      for (j = 0; j < d; ++j) acc[j] += w * sacc[(size_t)sp * d + j];
+    }
+    for (j = 0; j < d; ++j)
+      out[(size_t)r * d + j] = lsum > 0.0 ? acc[j] / lsum : 0.0;
+  }
+  free(qv);
+  free(s);
+  free(acc);
+  free(sacc);
+  free(sl);
+  free(sm);
+}

@@ -1,0 +1,125 @@
+/*
+ * Plain CPU oracle for attention over an e4m3 KV cache with one fp32 scale
+ * per (token, KV head).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file and oracle.c are the slow, obviously
+ * correct statement of what the GPU library computes.  Only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark may load it.  The
+ * GPU library never links, includes or calls it, and it shares no code,
+ * header, table or constant with the GPU library.
+ *
+ * Sources (page titles as published):
+ *   [SKILL]  "kadirnar/kernel-agent/fp8-kv-cache", sections "Storage" and
+ *            "Math": e4m3 codes plus one fp32 scale per (token, KV head),
+ *            scale = amax over the head dimension / 448, written once at
+ *            append; scores (q . codes) * k_scale * sm_scale with the products
+ *            exact in fp32; the V scale folded into P, which is rounded to
+ *            bf16 before the P.V product.
+ *   [FA]     "03 . 8n - FA-style tiled prefill attention", section 2.1
+ *            (online softmax) and section 3.1 (GQA slicing: query head h
+ *            reads KV head h/gqa; causal mask kv <= q position; a row with no
+ *            valid key outputs 0).
+ *   [HW]     "FP8 KV attention: hardware paths and tile preparation", section
+ *            "AMD CDNA 3" (a per-row scale moves outside the dot product).
+ *   OCP 8-bit floating point specification (E4M3, bias 7, no infinities,
+ *   S.1111.111 is NaN, largest finite 448): the pages only fix the 448.
+ *
+ * Precision: every sum, product, exponential and quotient of the attention is
+ * carried in fp64.  The pages fix three narrower roundings and those are kept
+ * exactly: the fp32 scale (a correctly rounded fp32 division amax / 448), the
+ * e4m3 code (fp32 division x / scale, then round-to-nearest-even with
+ * saturation at 448) and the bf16 rounding of P (after the V scale is
+ * folded in).
+ *
+ * Reading of the pages where they are silent: P is rounded relative to an
+ * integer log2-domain reference M = ceil(max_t s_t) where s_t is the score in
+ * log2 units.  Any other integer reference gives the same output because
+ * scaling by a power of two commutes with bf16 rounding; a running maximum
+ * that changes from tile to tile therefore leaves the rounding unchanged.
+ */
+#ifndef FP8KV_ORACLE_H
+#define FP8KV_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_K8V8 = 0, ORC_K16V8 = 1, ORC_BF16 = 2 };
+
+/* Value of an OCP e4m3fn code (NaN for 0x7F / 0xFF). */
+double orc_e4m3_value(uint8_t code);
+
+/* Round-to-nearest-even e4m3 code of y after clamping |y| to 448.
+ * The sign is kept, so a negative value that rounds to zero gives 0x80. */
+uint8_t orc_e4m3_encode(float y);
+
+/* Round-to-nearest-even bf16 of a finite double; returns the bf16 bit
+ * pattern.  Used for bf16 cache storage and for P. */
+uint16_t orc_bf16_round(double x);
+
+/* Value of a bf16 bit pattern. */
+double orc_bf16_value(uint16_t bits);
+
+/* Array helpers over the scalar functions above (n elements). */
+void orc_e4m3_encode_array(const float* y, uint8_t* codes, size_t n);
+void orc_bf16_round_array_f32(const float* x, uint16_t* bits, size_t n);
+
+/* Quantise n_rows rows of d fp32 values each: per row
+ * amax = max |x|, scale = fp32(amax / 448), code = e4m3(fp32(x / scale)).
+ * A row whose scale is 0 gets all-zero codes. */
+void orc_quantize_rows(const float* x, int64_t n_rows, int d,
+                       uint8_t* codes, float* scales);
+
+/*
+ * Attention of n_rows query rows against one KV head's keys.
+ *
+ *   q      bf16 bits [n_rows][d]
+ *   k8/ks  K8V8: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
+ *   k16    K16V8 and BF16: bf16 bits [n_keys][d]
+ *   v8/vs  K8V8 and K16V8: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
+ *   v16    BF16: bf16 bits [n_keys][d]
+ *   n_valid[r]  keys 0 .. n_valid[r]-1 are visible to row r
+ *   round_p     1: P rounded to bf16 (the method); 0: unrounded (for pins)
+ *   out    fp64 [n_rows][d]
+ *
+ * Per row (two-pass form):
+ *   s_t  = (sum_d q_d * K_td) * ks_t * sm_scale * log2(e)
+ *   M    = ceil(max_t s_t)
+ *   p_t  = 2^(s_t - M),   l = sum_t p_t
+ *   P_t  = bf16(p_t * vs_t)
+ *   o_d  = (sum_t P_t * V_td) / l,  and o = 0 when no key is visible.
+ */
+void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
+                     int n_keys, const uint8_t* k8, const uint16_t* k16,
+                     const float* ks, const uint8_t* v8, const uint16_t* v16,
+                     const float* vs, const int32_t* n_valid, float sm_scale,
+                     int round_p, double* out);
+
+/*
+ * The same attention in the online form of the FA page, section 2.1: keys
+ * are consumed in tiles of `tile` keys, grouped into splits of `split` keys;
+ * each split carries (M, l, acc) across its tiles and writes an unnormalised
+ * partial; the partials are merged with power-of-two weights.  Used to pin
+ * the two-pass form (they must agree to rounding order) and as the reference
+ * for the partial/merge entry points.
+ *
+ *   part_acc [n_splits][n_rows][d], part_l / part_m [n_splits][n_rows]
+ *   (may be NULL when only `out` is wanted); part_m is -inf for a split
+ *   with no visible key.
+ */
+void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
+                            int n_keys, const uint8_t* k8, const uint16_t* k16,
+                            const float* ks, const uint8_t* v8,
+                            const uint16_t* v16, const float* vs,
+                            const int32_t* n_valid, float sm_scale,
+                            int round_p, int tile, int split,
+                            double* part_acc, double* part_l, double* part_m,
+                            double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
