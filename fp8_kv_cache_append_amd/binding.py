@@ -1,0 +1,211 @@
+"""Python binding of the fp8kv C ABI (include/fp8kv.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every computation runs in the HIP kernels of libfp8kv.so.  There
+is no fallback: if the library is missing or the call fails, an exception is
+raised.  Function names and argument order follow the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfp8kv.so")
+
+MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2}
+
+FP8KV_OK = 0
+FP8KV_ERR_INVALID = -1
+FP8KV_ERR_WORKSPACE = -2
+FP8KV_ERR_LAUNCH = -3
+FP8KV_ERR_UNSUPPORTED = -4
+
+# Every symbol include/fp8kv.h declares.
+EXPORTS = ("fp8kv_append", "fp8kv_decode_plan", "fp8kv_decode_workspace_bytes",
+           "fp8kv_decode_partial", "fp8kv_decode_merge", "fp8kv_decode",
+           "fp8kv_prefill", "fp8kv_strerror")
+
+
+class Fp8kvError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {strerror(status)} ({status})")
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of struct fp8kv_cache."""
+    _fields_ = [("mode", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfp8kv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "fp8_kv_cache_append_amd/build.py (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        C = ctypes.POINTER(CacheDesc)
+        sig = {
+            "fp8kv_append": (ctypes.c_int, [C, P, P, P, P, I32, P]),
+            "fp8kv_decode_plan": (ctypes.c_int, [C, I32, I32, I32, ctypes.POINTER(I32),
+                                                 ctypes.POINTER(I32)]),
+            "fp8kv_decode_workspace_bytes": (ctypes.c_size_t, [C, I32, I32, I32]),
+            "fp8kv_decode_partial": (ctypes.c_int, [C, P, I32, P, I32, I32, F, I32, I32,
+                                                    P, P, P]),
+            "fp8kv_decode_merge": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
+            "fp8kv_decode": (ctypes.c_int, [C, P, I32, P, I32, I32, F, P, P,
+                                            ctypes.c_size_t, P]),
+            "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, F, P, P]),
+            "fp8kv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().fp8kv_strerror(int(status)).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != FP8KV_OK:
+        raise Fp8kvError(status, call)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return t  # a raw integer address, passed through
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to fp8kv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+@dataclass
+class KVCache:
+    """A paged cache in device memory plus its C descriptor.
+
+    k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
+    k_scale, v_scale: float32 [num_blocks, block_size, Hkv] or None;
+    block_table: int32 [batch, max_blocks_per_seq].
+    """
+    mode: str
+    k: torch.Tensor
+    v: torch.Tensor
+    k_scale: torch.Tensor | None
+    v_scale: torch.Tensor | None
+    block_table: torch.Tensor
+
+    @classmethod
+    def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
+                 head_dim: int, block_table, device="cuda") -> "KVCache":
+        shape = (num_blocks, block_size, num_kv_heads, head_dim)
+        kd = torch.uint8 if mode == "K8V8" else torch.bfloat16
+        vd = torch.bfloat16 if mode == "BF16" else torch.uint8
+        k = torch.zeros(shape, dtype=kd, device=device)
+        v = torch.zeros(shape, dtype=vd, device=device)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if mode == "K8V8" else None
+        vs = torch.zeros(shape[:3], dtype=torch.float32, device=device) if mode != "BF16" else None
+        bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        return cls(mode, k, v, ks, vs, bt)
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.k.shape[3])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[2])
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(MODES[self.mode], int(self.k.shape[0]), int(self.k.shape[1]),
+                         int(self.k.shape[2]), int(self.k.shape[3]),
+                         int(self.block_table.shape[1]), _ptr(self.k), _ptr(self.v),
+                         _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table))
+
+
+def fp8kv_append(cache: KVCache, k_new, v_new, seq_idx, pos, stream=None) -> None:
+    """Quantise and store n_tok new tokens (k_new, v_new: fp32 [n_tok, Hkv, D])."""
+    d = cache.desc()
+    _check(lib().fp8kv_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(seq_idx),
+                              _ptr(pos), int(k_new.shape[0]), _stream(stream)), "fp8kv_append")
+
+
+def fp8kv_decode_plan(cache: KVCache, batch: int, gqa_group: int, max_seq_len: int):
+    """(chunk_tokens, n_splits) of the split-KV decode."""
+    d = cache.desc()
+    chunk, splits = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().fp8kv_decode_plan(ctypes.byref(d), batch, gqa_group, max_seq_len,
+                                   ctypes.byref(chunk), ctypes.byref(splits)),
+           "fp8kv_decode_plan")
+    return chunk.value, splits.value
+
+
+def fp8kv_decode_workspace_bytes(cache: KVCache, batch: int, gqa_group: int,
+                                 max_seq_len: int) -> int:
+    d = cache.desc()
+    return int(lib().fp8kv_decode_workspace_bytes(ctypes.byref(d), batch, gqa_group,
+                                                  max_seq_len))
+
+
+def fp8kv_decode_partial(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
+                         sm_scale: float, chunk_tokens: int, n_splits: int, part_acc,
+                         part_ml, stream=None) -> None:
+    d = cache.desc()
+    _check(lib().fp8kv_decode_partial(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
+                                      int(seq_lens.shape[0]), max_seq_len, sm_scale,
+                                      chunk_tokens, n_splits, _ptr(part_acc), _ptr(part_ml),
+                                      _stream(stream)), "fp8kv_decode_partial")
+
+
+def fp8kv_decode_merge(batch: int, num_kv_heads: int, gqa_group: int, head_dim: int,
+                       n_splits: int, part_acc, part_ml, out, stream=None) -> None:
+    _check(lib().fp8kv_decode_merge(batch, num_kv_heads, gqa_group, head_dim, n_splits,
+                                    _ptr(part_acc), _ptr(part_ml), _ptr(out),
+                                    _stream(stream)), "fp8kv_decode_merge")
+
+
+def fp8kv_decode(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
+                 sm_scale: float, out, workspace, stream=None) -> None:
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8kv_decode(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
+                              int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "fp8kv_decode")
+
+
+def fp8kv_prefill(cache: KVCache, q, gqa_group: int, cu_q, q_pos0, seq_lens,
+                  max_q_len: int, sm_scale: float, out, stream=None) -> None:
+    d = cache.desc()
+    _check(lib().fp8kv_prefill(ctypes.byref(d), _ptr(q), gqa_group, _ptr(cu_q), _ptr(q_pos0),
+                               _ptr(seq_lens), int(seq_lens.shape[0]), max_q_len, sm_scale,
+                               _ptr(out), _stream(stream)), "fp8kv_prefill")
+
+
+def fp8kv_strerror(status: int) -> str:
+    return strerror(status)

@@ -1,0 +1,59 @@
+// Device-side helpers shared by the fp8kv kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8kv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+enum { kK8V8 = 0, kK16V8 = 1, kBF16 = 2 };
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Two e4m3 codes (bytes 2*HI and 2*HI+1 of w) -> two bf16 (low half from the
+// lower byte).  Every e4m3 value, subnormals included, is exact in bf16; the
+// scale operand 1.0 leaves the value unchanged.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Same, with the half chosen by a value the caller's unrolled loop makes
+// constant (the instruction encodes the half as an immediate).
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  return hi ? e4m3x2_to_bf16x2<true>(w) : e4m3x2_to_bf16x2<false>(w);
+}
+
+// Two fp32 -> two bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte select over {src0 (selector values 4..7), src1 (values 0..3)}.
+__device__ __forceinline__ uint32_t byte_perm(uint32_t src0, uint32_t src1, uint32_t sel) {
+  return __builtin_amdgcn_perm(src0, src1, sel);
+}
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds row/column
+// l % 16 and the eight k-slots 8*(l/16) .. 8*(l/16)+7 of A and B; the result
+// rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace fp8kv

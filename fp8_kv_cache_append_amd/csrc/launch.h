@@ -1,0 +1,43 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8kv {
+
+struct CacheView {
+  int mode;   // kK8V8 / kK16V8 / kBF16
+  int bs;     // tokens per block (multiple of 16)
+  int hkv;    // KV heads
+  int d;      // head_dim, 64 or 128
+  int mbps;   // block-table row length
+  void* k;
+  void* v;
+  float* ks;
+  float* vs;
+  const int32_t* table;
+};
+
+hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
+                         const int32_t* seq_idx, const int32_t* pos, int n_tok,
+                         hipStream_t stream);
+
+// Split kernel: one work-group per (sequence, KV head, split).  c_scale is
+// sm_scale * log2(e) rounded to fp32.
+hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int group,
+                                 const int32_t* seq_lens, int batch, float c_scale,
+                                 int chunk, int n_splits, float* part_acc,
+                                 float* part_ml, hipStream_t stream);
+
+hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,
+                               const float* part_acc, const float* part_ml, float* out,
+                               hipStream_t stream);
+
+hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
+                          const int32_t* cu_q, const int32_t* q_pos0,
+                          const int32_t* seq_lens, int batch, int max_q_len,
+                          float c_scale, float* out, hipStream_t stream);
+
+}  // namespace fp8kv

@@ -120,15 +120,16 @@ def kv_sequence(w: Workload, b: int, n: int | None = None):
 def block_layout(w: Workload, capacity: int | None = None):
     """Block size, block table [batch, max_blocks] int32 and block count.
 
-    Contiguous: one block of ``capacity`` (default max_len) tokens per
-    sequence and block_table[b] = [b].  Paged: ceil(len_b / block_size)
+    Contiguous: one block of ``capacity`` (default max_len, rounded up to a
+    multiple of 16) tokens per sequence and block_table[b] = [b].  Paged: ceil(len_b / block_size)
     blocks per sequence, numbered 0..n-1 in order or by a seeded random
     permutation; unused table entries are -1.
     """
     if w.block_size == 0:
         cap = w.max_len if capacity is None else int(capacity)
+        cap = max(16, -(-cap // 16) * 16)  # block sizes are multiples of 16
         table = np.arange(w.batch, dtype=np.int32).reshape(w.batch, 1)
-        return max(cap, 1), table, w.batch
+        return cap, table, w.batch
     bs = w.block_size
     cap = w.lens if capacity is None else np.maximum(w.lens, capacity)
     per = (np.asarray(cap, np.int64) + bs - 1) // bs

@@ -1,0 +1,197 @@
+/*
+ * fp8kv: attention over an FP8 (OCP e4m3fn) KV cache on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named as "device" is HIP device memory; the
+ * caller owns every buffer.  The library allocates no device memory, keeps
+ * no state between calls apart from a per-device architecture check, and
+ * never synchronises: each call validates its arguments on the host, enqueues
+ * its kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ * returns.  Calls are HIP-graph capturable (no allocation, no memset).
+ *
+ * Status codes: FP8KV_OK (0) or a negative fp8kv_status.  INVALID,
+ * WORKSPACE and UNSUPPORTED mean nothing was enqueued.  LAUNCH means the HIP
+ * runtime reported a launch failure; the error has been read (and so
+ * cleared) before returning, so it does not leak into later calls on the
+ * stream.
+ *
+ * Device-side preconditions that are NOT checked (reading device memory
+ * would need a synchronisation): every `pos`, `seq_idx`, `seq_lens` entry is
+ * in range for the cache and block table, the block-table entries a sequence
+ * uses are valid block ids, and inputs are finite.
+ *
+ * Sources (page titles as published):
+ *   [SKILL] "kadirnar/kernel-agent/fp8-kv-cache": sections "Storage"
+ *           (e4m3 + one fp32 scale per (token, KV head), amax/448, written
+ *           once at append), "Math" (K scale folded into the scores, V scale
+ *           folded into P rounded to bf16) and "Speed" (split the cache over
+ *           programs; fp32 partials merged by a second kernel).
+ *   [HW]    "FP8 KV attention: hardware paths and tile preparation":
+ *           "Operating model" (reconstruct only the active tile, online
+ *           softmax tile by tile), "NVIDIA Hopper" path 3 (K16/V8, the
+ *           no-K-transform control), "Collect the profiler evidence" (dtype
+ *           controls including K16/V16).
+ *   [FA]    "03 . 8n - FA-style tiled prefill attention": sections 2.1
+ *           (online softmax), 3.1 (64-token query tiles, GQA slicing,
+ *           positions are data, causal mask) and 3.2/3.3 (a row with no
+ *           visible key outputs 0; a fully masked tile keeps the state).
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache element formats ([SKILL] Storage; [HW] Hopper path 3 and the dtype
+ * controls).
+ *   FP8KV_K8V8   K and V: uint8 e4m3 codes + fp32 scale per (token, KV head)
+ *   FP8KV_K16V8  K: bf16; V: e4m3 codes + fp32 scale
+ *   FP8KV_BF16   K and V: bf16 (no scales) */
+typedef enum { FP8KV_K8V8 = 0, FP8KV_K16V8 = 1, FP8KV_BF16 = 2 } fp8kv_mode;
+
+typedef enum {
+  FP8KV_OK = 0,
+  FP8KV_ERR_INVALID = -1,     /* bad argument: null pointer, shape, alignment */
+  FP8KV_ERR_WORKSPACE = -2,   /* workspace smaller than the size query says  */
+  FP8KV_ERR_LAUNCH = -3,      /* the HIP runtime rejected a launch           */
+  FP8KV_ERR_UNSUPPORTED = -4  /* device is not gfx950, or head_dim/G unsupported */
+} fp8kv_status;
+
+/*
+ * Paged KV cache descriptor (all pointers device memory, owned by the
+ * caller).  Layout, token-major within a block:
+ *   k, v            [num_blocks][block_size][num_kv_heads][head_dim]
+ *                   K8V8: uint8 codes for both; K16V8: k bf16, v uint8;
+ *                   BF16: bf16 for both
+ *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 only
+ *                   (NULL otherwise)
+ *   v_scale         same shape, K8V8 and K16V8 (NULL for BF16)
+ *   block_table     int32 [batch][max_blocks_per_seq]; token t of sequence b
+ *                   is slot t % block_size of block
+ *                   block_table[b * max_blocks_per_seq + t / block_size]
+ * A contiguous cache [B][T][Hkv][D] is block_size = T with block_table[b] = b.
+ * Requirements: head_dim 64 or 128; block_size a multiple of 16; k, v 16-byte
+ * aligned; k_scale, v_scale, block_table 4-byte aligned.
+ */
+typedef struct fp8kv_cache {
+  int32_t mode;                /* fp8kv_mode */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  const int32_t* block_table;
+} fp8kv_cache;
+
+/*
+ * Append (quantise and store) n_tok new tokens, all KV heads.  [SKILL]
+ * Storage: per (token, KV head) row of head_dim values
+ *   amax = max |x|,  scale = fp32(amax / 448) (correctly rounded),
+ *   code = e4m3 round-to-nearest-even of fp32(x / scale), saturated at 448,
+ *   a row whose scale is 0 stores all-zero codes.
+ * K16V8 stores K as bf16 (round-to-nearest-even); BF16 stores K and V as bf16.
+ *   k_new, v_new   device fp32 [n_tok][num_kv_heads][head_dim]
+ *   seq_idx, pos   device int32 [n_tok]: token i goes to sequence seq_idx[i]
+ *                  at position pos[i]
+ * Each (token, head) row is written exactly once per call; two tokens of one
+ * call must not target the same slot.  n_tok == 0 is a no-op.
+ */
+int fp8kv_append(const fp8kv_cache* cache, const float* k_new,
+                 const float* v_new, const int32_t* seq_idx,
+                 const int32_t* pos, int32_t n_tok, void* stream);
+
+/*
+ * Split plan for decode: keys of each (sequence, KV head) are cut into
+ * splits of *chunk_tokens keys (a multiple of 64); *n_splits =
+ * ceil(max_seq_len / chunk_tokens).  Chosen so that the split kernel has
+ * enough work-groups for 256 compute units ([SKILL] Speed).
+ */
+int fp8kv_decode_plan(const fp8kv_cache* cache, int32_t batch,
+                      int32_t gqa_group, int32_t max_seq_len,
+                      int32_t* chunk_tokens, int32_t* n_splits);
+
+/* Bytes of workspace fp8kv_decode needs: the partials of the plan above,
+ * batch * num_kv_heads * n_splits * gqa_group * (head_dim + 2) * 4. */
+size_t fp8kv_decode_workspace_bytes(const fp8kv_cache* cache, int32_t batch,
+                                    int32_t gqa_group, int32_t max_seq_len);
+
+/*
+ * Split-KV decode, first kernel.  For every (sequence b, KV head h, split s)
+ * the keys t in [s*chunk, min((s+1)*chunk, seq_lens[b])) are attended by the
+ * gqa_group query heads h*G .. h*G+G-1 ([FA] 3.1 GQA slicing) and the
+ * unnormalised partial is written:
+ *   score     s_t = (q . K_t) * k_scale_t * sm_scale * log2(e)   (log2 units)
+ *   M         integer reference, >= every s_t of the split (the running
+ *             maximum rounded up to an integer, updated tile by tile)
+ *   part_l    sum_t 2^(s_t - M)
+ *   part_acc  sum_t bf16(2^(s_t - M) * v_scale_t) * V_t
+ * ([SKILL] Math; [FA] 2.1).  A split with no key gets M = -inf and l = 0.
+ *   q            device bf16 [batch][num_kv_heads * gqa_group][head_dim]
+ *   seq_lens     device int32 [batch], 0 <= seq_lens[b] <= max_seq_len
+ *   part_acc     device fp32 [batch][num_kv_heads][n_splits][G][head_dim]
+ *   part_ml      device fp32 [batch][num_kv_heads][n_splits][G][2] = (M, l)
+ * chunk_tokens must be a positive multiple of 256; n_splits >=
+ * ceil(max_seq_len / chunk_tokens).  gqa_group in 1..16.
+ */
+int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q,
+                         int32_t gqa_group, const int32_t* seq_lens,
+                         int32_t batch, int32_t max_seq_len, float sm_scale,
+                         int32_t chunk_tokens, int32_t n_splits,
+                         float* part_acc, float* part_ml, void* stream);
+
+/*
+ * Split-KV decode, second kernel ([SKILL] Speed): merge the fp32 partials of
+ * every (sequence, query head):
+ *   M* = max_s M_s,  w_s = 2^(M_s - M*) (0 for an empty split),
+ *   out = sum_s w_s acc_s / sum_s w_s l_s,  out = 0 when every split is empty.
+ *   out   device fp32 [batch][num_kv_heads * gqa_group][head_dim]
+ */
+int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
+                       int32_t head_dim, int32_t n_splits,
+                       const float* part_acc, const float* part_ml, float* out,
+                       void* stream);
+
+/*
+ * Decode attention: fp8kv_decode_partial with the plan of fp8kv_decode_plan
+ * (partials in `workspace`), then fp8kv_decode_merge.  One query token per
+ * sequence; seq_lens counts the keys it attends (the appended token
+ * included).  out: device fp32 [batch][num_kv_heads * gqa_group][head_dim].
+ */
+int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q,
+                 int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
+                 int32_t max_seq_len, float sm_scale, float* out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal prefill attention ([FA] 3.1): queries of sequence b are rows
+ * cu_q[b] .. cu_q[b+1]-1 of q; query i of the sequence sits at position
+ * q_pos0[b] + i and attends the cached keys t <= q_pos0[b] + i with
+ * t < seq_lens[b].  The keys must already be in the cache (fp8kv_append).
+ * Per row the result equals decode attention over its visible keys; a row
+ * with no visible key outputs 0.
+ *   q        device bf16 [total_q][num_kv_heads * gqa_group][head_dim]
+ *   cu_q     device int32 [batch + 1], cu_q[0] = 0, non-decreasing
+ *   q_pos0, seq_lens  device int32 [batch]
+ *   max_q_len  >= every cu_q[b+1] - cu_q[b]
+ *   out      device fp32 [total_q][num_kv_heads * gqa_group][head_dim]
+ */
+int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q,
+                  int32_t gqa_group, const int32_t* cu_q,
+                  const int32_t* q_pos0, const int32_t* seq_lens,
+                  int32_t batch, int32_t max_q_len, float sm_scale,
+                  float* out, void* stream);
+
+/* Static description of a status code. */
+const char* fp8kv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP8KV_H */

@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.orc_attend_rows.restype = None
         L.orc_attend_rows.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
-            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P]
+            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P]
         L.orc_attend_rows_online.restype = None
         L.orc_attend_rows_online.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
@@ -154,24 +154,28 @@ def _head_view(store: dict, h: int) -> dict:
 
 
 def attend_rows(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
-                round_p: bool = True) -> np.ndarray:
+                round_p: bool = True, bounds: bool = False):
     """Two-pass attention of query rows q_bits [R, D] against one KV head.
 
     kv holds the stores of that head ([T, D] and [T]); n_valid[r] keys are
-    visible to row r.  Returns fp64 [R, D].
+    visible to row r.  Returns fp64 [R, D]; with bounds=True returns
+    (out, lo, hi) where [lo, hi] holds every output reachable by rounding an
+    ambiguous P (one within fp32 noise of a bf16 midpoint) either way.
     """
     q_bits = _c(q_bits, np.uint16)
     r, d = q_bits.shape
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
     out = np.empty((r, d), dtype=np.float64)
+    lo = np.empty((r, d), dtype=np.float64) if bounds else None
+    hi = np.empty((r, d), dtype=np.float64) if bounds else None
     lib().orc_attend_rows(
         MODES[mode], d, r, _ptr(q_bits), n_keys,
         _ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("k16"), np.uint16)),
         _ptr(_c(kv.get("ks"), np.float32)), _ptr(_c(kv.get("v8"), np.uint8)),
         _ptr(_c(kv.get("v16"), np.uint16)), _ptr(_c(kv.get("vs"), np.float32)),
-        _ptr(n_valid), float(sm_scale), int(bool(round_p)), _ptr(out))
-    return out
+        _ptr(n_valid), float(sm_scale), int(bool(round_p)), _ptr(out), _ptr(lo), _ptr(hi))
+    return (out, lo, hi) if bounds else out
 
 
 def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
@@ -207,19 +211,21 @@ def _n_keys(kv: dict) -> int:
 
 
 def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
-           pairs=None, round_p: bool = True) -> np.ndarray:
+           pairs=None, round_p: bool = True, bounds: bool = False):
     """Decode attention from the fp32 K/V of each sequence.
 
     q_bits  bf16 bits [B, Hq, D]
     k_seqs  list of B fp32 arrays [len_b, Hkv, D] (v_seqs alike)
     pairs   optional iterable of (b, kv_head) to compute; other rows are NaN
-    Returns fp64 [B, Hq, D].  The oracle quantises each sequence itself.
+    Returns fp64 [B, Hq, D] (with bounds=True: (out, lo, hi), see
+    attend_rows).  The oracle quantises each sequence itself.
     """
     q_bits = np.asarray(q_bits, dtype=np.uint16)
     b_n, hq, d = q_bits.shape
     out = np.full((b_n, hq, d), np.nan)
+    lo, hi = out.copy(), out.copy()
     if b_n == 0:
-        return out
+        return (out, lo, hi) if bounds else out
     hkv = k_seqs[0].shape[1] if len(k_seqs) else 1
     g = hq // hkv
     if pairs is None:
@@ -232,26 +238,32 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
         store = store_rows(mode, k_seqs[b], v_seqs[b])
         for h in heads:
             rows = q_bits[b, h * g:(h + 1) * g]
-            out[b, h * g:(h + 1) * g] = attend_rows(
-                mode, rows, _head_view(store, h), n, sm_scale, round_p)
-    return out
+            sl = slice(h * g, (h + 1) * g)
+            res = attend_rows(mode, rows, _head_view(store, h), n, sm_scale, round_p, bounds)
+            if bounds:
+                out[b, sl], lo[b, sl], hi[b, sl] = res
+            else:
+                out[b, sl] = res
+    return (out, lo, hi) if bounds else out
 
 
 def prefill(mode: str, q_bits, k, v, q_pos0: int, sm_scale: float,
-            rows=None, round_p: bool = True) -> np.ndarray:
+            rows=None, round_p: bool = True, bounds: bool = False):
     """Causal prefill of one sequence.
 
     q_bits  bf16 bits [Lq, Hq, D]; query i sits at position q_pos0 + i
     k, v    fp32 [Lkv, Hkv, D], every key of the sequence (positions 0..Lkv-1)
     rows    optional query indices to compute; other rows are NaN
     Key t is visible to query i when t <= q_pos0 + i (FA page, section 3.1).
-    Returns fp64 [Lq, Hq, D].
+    Returns fp64 [Lq, Hq, D] (with bounds=True: (out, lo, hi), see
+    attend_rows).
     """
     q_bits = np.asarray(q_bits, dtype=np.uint16)
     lq, hq, d = q_bits.shape
     lkv, hkv = k.shape[0], k.shape[1]
     g = hq // hkv
     out = np.full((lq, hq, d), np.nan)
+    lo, hi = out.copy(), out.copy()
     if rows is None:
         rows = np.arange(lq)
     rows = np.asarray(rows, dtype=np.int64)
@@ -260,9 +272,12 @@ def prefill(mode: str, q_bits, k, v, q_pos0: int, sm_scale: float,
     for hk in range(hkv):
         view = _head_view(store, hk)
         for hh in range(hk * g, (hk + 1) * g):
-            out[rows, hh] = attend_rows(mode, q_bits[rows, hh], view, n_valid,
-                                        sm_scale, round_p)
-    return out
+            res = attend_rows(mode, q_bits[rows, hh], view, n_valid, sm_scale, round_p, bounds)
+            if bounds:
+                out[rows, hh], lo[rows, hh], hi[rows, hh] = res
+            else:
+                out[rows, hh] = res
+    return (out, lo, hi) if bounds else out
 
 
 # ---------------------------------------------------------------- metrics

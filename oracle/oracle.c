@@ -172,16 +172,32 @@ static int clamp_valid(int nv, int n_keys) {
   return nv > n_keys ? n_keys : nv;
 }
 
+/* Bound on |fp32 score - exact score| in log2 units for any summation order
+ * of the d exact products (the classic (n-1)u sum|x_i| bound, doubled, plus
+ * the roundings of the two scale products), as a relative window on
+ * p = 2^(s - M) with 2^-20 added for an fp32 exp2 within a few ulp. */
+static double p_window(const kv_view* kv, const double* qv, int t, double c) {
+  double sabs = 0.0;
+  int j;
+  for (j = 0; j < kv->d; ++j) sabs += fabs(qv[j] * k_elem(kv, t, j));
+  sabs *= fabs(k_scale(kv, t) * c);
+  return 0.6931471805599453 * 2.0 * (double)(kv->d + 4) * ldexp(1.0, -24) * sabs +
+         ldexp(1.0, -20);
+}
+
 void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
                      int n_keys, const uint8_t* k8, const uint16_t* k16,
                      const float* ks, const uint8_t* v8, const uint16_t* v16,
                      const float* vs, const int32_t* n_valid, float sm_scale,
-                     int round_p, double* out) {
+                     int round_p, double* out, double* out_lo, double* out_hi) {
   kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
   double c = (double)sm_scale * ORC_LOG2E;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
   double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  double* alo = (double*)malloc(sizeof(double) * (size_t)d);
+  double* ahi = (double*)malloc(sizeof(double) * (size_t)d);
+  int bounds = out_lo != NULL && out_hi != NULL;
   int r, t, j;
   for (r = 0; r < n_rows; ++r) {
     int nv = clamp_valid(n_valid[r], n_keys);
@@ -190,6 +206,8 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
     for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q[(size_t)r * d + j]);
     if (nv == 0) { /* no visible key: the row outputs 0 */
       for (j = 0; j < d; ++j) o[j] = 0.0;
+      if (bounds)
+        for (j = 0; j < d; ++j) out_lo[(size_t)r * d + j] = out_hi[(size_t)r * d + j] = 0.0;
       continue;
     }
     /* pass 1: scores and their maximum */
@@ -199,18 +217,37 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
     }
     m = ceil(smax);
     /* pass 2: probabilities, normaliser, P.V */
-    for (j = 0; j < d; ++j) acc[j] = 0.0;
+    for (j = 0; j < d; ++j) acc[j] = alo[j] = ahi[j] = 0.0;
     for (t = 0; t < nv; ++t) {
       double p = exp2(s[t] - m);
       double w = p_folded(&kv, p, t, round_p);
       l += p;
       for (j = 0; j < d; ++j) acc[j] += w * v_elem(&kv, t, j);
+      if (bounds) {
+        /* Both bf16 neighbours are valid roundings when p * v_scale lies
+         * within fp32 noise of a rounding midpoint. */
+        double win = round_p ? p_window(&kv, qv, t, c) : 0.0;
+        double wa = round_p ? p_folded(&kv, p * (1.0 - win), t, 1) : w;
+        double wb = round_p ? p_folded(&kv, p * (1.0 + win), t, 1) : w;
+        for (j = 0; j < d; ++j) {
+          double va = wa * v_elem(&kv, t, j), vb = wb * v_elem(&kv, t, j);
+          alo[j] += va < vb ? va : vb;
+          ahi[j] += va < vb ? vb : va;
+        }
+      }
     }
     for (j = 0; j < d; ++j) o[j] = acc[j] / l;
+    if (bounds)
+      for (j = 0; j < d; ++j) {
+        out_lo[(size_t)r * d + j] = alo[j] / l;
+        out_hi[(size_t)r * d + j] = ahi[j] / l;
+      }
   }
   free(qv);
   free(s);
   free(acc);
+  free(alo);
+  free(ahi);
 }
 
 void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,

@@ -84,6 +84,13 @@ void orc_quantize_rows(const float* x, int64_t n_rows, int d,
  *   n_valid[r]  keys 0 .. n_valid[r]-1 are visible to row r
  *   round_p     1: P rounded to bf16 (the method); 0: unrounded (for pins)
  *   out    fp64 [n_rows][d]
+ *   out_lo, out_hi  optional (both NULL or both set): the smallest and
+ *          largest output reachable when every P whose value p * v_scale
+ *          lies within fp32 rounding noise of a bf16 rounding midpoint is
+ *          rounded either way.  Both roundings are correct results of the
+ *          method for such a P (the scores themselves are only defined to
+ *          fp32 accuracy), so a GPU result is valid when it lies in
+ *          [out_lo, out_hi] up to its fp32 accumulation error.
  *
  * Per row (two-pass form):
  *   s_t  = (sum_d q_d * K_td) * ks_t * sm_scale * log2(e)
@@ -96,7 +103,7 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
                      int n_keys, const uint8_t* k8, const uint16_t* k16,
                      const float* ks, const uint8_t* v8, const uint16_t* v16,
                      const float* vs, const int32_t* n_valid, float sm_scale,
-                     int round_p, double* out);
+                     int round_p, double* out, double* out_lo, double* out_hi);
 
 /*
  * The same attention in the online form of the FA page, section 2.1: keys

@@ -1,0 +1,148 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-side validation rejects bad arguments before any
+launch.  Every call here returns on the host before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp8_kv_cache_append_amd import binding
+from fp8_kv_cache_append_amd.binding import CacheDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8kv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libfp8kv.so not built")
+
+FAKE = 0x10000  # aligned host-side stand-in; never dereferenced by these calls
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(fp8kv_[a-z_]+)\s*\(", text))
+
+
+def test_header_declares_binding_exports():
+    assert _declared() == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(fp8kv_\w+)$", out, flags=re.M))
+    assert _declared() <= exported
+
+
+def test_strerror():
+    assert binding.strerror(0) == "ok"
+    assert "invalid" in binding.strerror(-1)
+    assert "workspace" in binding.strerror(-2)
+    assert "unknown" in binding.strerror(7)
+
+
+def _desc(**kw):
+    base = dict(mode=0, num_blocks=4, block_size=16, num_kv_heads=2, head_dim=128,
+                max_blocks_per_seq=4, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
+                block_table=FAKE)
+    base.update(kw)
+    return CacheDesc(**base)
+
+
+BAD_CACHES = [
+    (dict(mode=3), -1),
+    (dict(head_dim=96), -4),
+    (dict(block_size=8), -1),
+    (dict(block_size=0), -1),
+    (dict(num_kv_heads=0), -1),
+    (dict(k=None), -1),
+    (dict(k=FAKE + 4), -1),          # codes must be 16-byte aligned
+    (dict(k_scale=None), -1),        # K8V8 needs both scales
+    (dict(mode=1), -1),              # K16V8 must not carry a K scale
+    (dict(mode=2, k_scale=None), -1),  # BF16 must not carry a V scale
+    (dict(block_table=FAKE + 2), -1),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_CACHES)
+def test_append_rejects_bad_cache(kw, status):
+    d = _desc(**kw)
+    r = binding.lib().fp8kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert r == status
+
+
+def test_append_rejects_bad_arguments():
+    lib = binding.lib()
+    d = _desc()
+    assert lib.fp8kv_append(None, FAKE, FAKE, FAKE, FAKE, 1, None) == -1
+    assert lib.fp8kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1, None) == -1
+    assert lib.fp8kv_append(ctypes.byref(d), None, FAKE, FAKE, FAKE, 1, None) == -1
+    assert lib.fp8kv_append(ctypes.byref(d), FAKE + 4, FAKE, FAKE, FAKE, 1, None) == -1
+    # zero tokens is a no-op that succeeds without a device
+    assert lib.fp8kv_append(ctypes.byref(d), None, None, None, None, 0, None) == 0
+
+
+def _plan(d, b, g, t):
+    c, s = ctypes.c_int32(), ctypes.c_int32()
+    r = binding.lib().fp8kv_decode_plan(ctypes.byref(d), b, g, t, ctypes.byref(c),
+                                        ctypes.byref(s))
+    return r, c.value, s.value
+
+
+def test_decode_plan():
+    # contiguous B16 x 2 KV heads x 2048 tokens
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    assert _plan(d, 16, 8, 2048) == (0, 256, 8)
+    # paged B64 x 8 KV heads up to 32768 tokens: longer splits, bounded grid
+    d = _desc(num_blocks=70000, block_size=16, num_kv_heads=8, max_blocks_per_seq=2048)
+    r, c, s = _plan(d, 64, 4, 32768)
+    assert r == 0 and c == 1024 and s == 32
+    assert _plan(d, 64, 17, 32768)[0] == -4
+    assert _plan(d, 64, 0, 32768)[0] == -1
+    assert _plan(d, 64, 4, 32768 + 1)[0] == -1   # beyond the block table
+    assert _plan(d, 0, 4, 0) == (0, 256, 0)
+
+
+def test_workspace_bytes():
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    n = binding.lib().fp8kv_decode_workspace_bytes(ctypes.byref(d), 16, 8, 2048)
+    assert n == 16 * 2 * 8 * 8 * (128 + 2) * 4
+    bad = _desc(head_dim=96)
+    assert binding.lib().fp8kv_decode_workspace_bytes(ctypes.byref(bad), 16, 8, 2048) == 0
+
+
+def test_decode_rejects_bad_arguments():
+    lib = binding.lib()
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    # workspace too small
+    assert lib.fp8kv_decode(ctypes.byref(d), FAKE, 8, FAKE, 16, 2048, 0.1, FAKE,
+                            FAKE, 16, None) == -2
+    assert lib.fp8kv_decode(ctypes.byref(d), FAKE, 8, FAKE, 16, 2048, 0.1, FAKE,
+                            None, 10 ** 9, None) == -2
+    # chunk not a multiple of 64, too few splits, misaligned partials
+    args = (ctypes.byref(d), FAKE, 8, FAKE, 16, 2048, 0.1)
+    assert lib.fp8kv_decode_partial(*args, 100, 32, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_partial(*args, 256, 7, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_partial(*args, 256, 8, FAKE + 4, FAKE, None) == -1
+    # merge shape checks
+    assert lib.fp8kv_decode_merge(4, 2, 17, 128, 4, FAKE, FAKE, FAKE, None) == -4
+    assert lib.fp8kv_decode_merge(4, 2, 8, 96, 4, FAKE, FAKE, FAKE, None) == -4
+    assert lib.fp8kv_decode_merge(4, 2, 8, 128, 4, None, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_merge(0, 2, 8, 128, 4, None, None, None, None) == 0
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = binding.lib()
+    d = _desc()
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 17, FAKE, FAKE, FAKE, 1, 64, 0.1,
+                             FAKE, None) == -4
+    assert lib.fp8kv_prefill(ctypes.byref(d), None, 8, FAKE, FAKE, FAKE, 1, 64, 0.1,
+                             FAKE, None) == -1
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 0, 64, 0.1,
+                             FAKE, None) == 0

@@ -1,0 +1,106 @@
+"""GPU parity of the causal tiled prefill (fp8kv_prefill) against the oracle.
+
+The keys are appended through fp8kv_append first (the store-then-attend path
+the FA page's parity test drives), then every query row is compared with the
+oracle's attention over its visible keys t <= q_pos0 + i.  Same gate as the
+decode tests (see test_gpu_decode.py): contract relative L2 and max abs, the
+latter measured outside the interval of valid bf16 roundings of P.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_kv_cache_append_amd import binding, synth
+from gpu_util import append_seq, check_layout, make_cache, q_tensor
+from test_gpu_decode import _gate
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_prefill(cache, q_bits, n_q, q_pos0, seq_lens, group, sm_scale):
+    n_q = np.asarray(n_q, np.int32)
+    cu = np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32)
+    seq_lens = np.asarray(seq_lens, np.int32)
+    q_pos0 = np.asarray(q_pos0, np.int32)
+    assert q_bits.shape[0] == cu[-1]
+    assert np.all(q_pos0 + n_q <= seq_lens) and np.all(q_pos0 >= 0)
+    check_layout(cache.block_table.cpu().numpy(), int(cache.k.shape[1]), seq_lens)
+    out = torch.full(q_bits.shape, float("nan"), dtype=torch.float32, device="cuda")
+    binding.fp8kv_prefill(cache, q_tensor(q_bits), group, torch.from_numpy(cu).cuda(),
+                          torch.from_numpy(q_pos0).cuda(), torch.from_numpy(seq_lens).cuda(),
+                          int(n_q.max()), sm_scale, out)
+    return out.cpu().numpy(), cu
+
+
+def _case(mode, hq, hkv, d, n_q, q_pos0, seq_lens, bs, seed, rows=None):
+    seq_lens = np.asarray(seq_lens, np.int32)
+    w = synth.Workload("t", len(seq_lens), hq, hkv, d, seq_lens, "outliers", block_size=bs,
+                       shuffle_blocks=bs > 0, seed=seed)
+    cache = make_cache(mode, w)
+    seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
+    for b, (k, v) in enumerate(seqs):
+        append_seq(cache, b, k, v)
+    total = int(np.sum(n_q))
+    q_bits = synth.q_bf16_bits(seed, (total, hq, d))
+    got, cu = gpu_prefill(cache, q_bits, n_q, q_pos0, seq_lens, hq // hkv, w.sm_scale)
+    refs = []
+    for b in range(w.batch):
+        qb = q_bits[cu[b]:cu[b + 1]]
+        r = None if rows is None else rows
+        refs.append(oracle.prefill(mode, qb, seqs[b][0], seqs[b][1], int(q_pos0[b]),
+                                   w.sm_scale, rows=r, bounds=True))
+    ref = np.concatenate([x[0] for x in refs])
+    lo = np.concatenate([x[1] for x in refs])
+    hi = np.concatenate([x[2] for x in refs])
+    return got, ref, lo, hi
+
+
+CASES = [
+    # hq, hkv, d, n_q per seq, q_pos0 per seq, seq_lens, block size
+    (4, 2, 64, [100], [0], [100], 16),
+    (28, 4, 128, [200], [0], [200], 0),
+    (8, 1, 128, [70], [130], [200], 32),                  # chunked prefill after 130 cached
+    (16, 2, 128, [1, 64, 65, 130], [0, 10, 0, 3], [1, 74, 65, 133], 16),
+    (2, 2, 64, [129], [0], [129], 64),                      # MHA
+    (16, 1, 64, [90], [5], [95], 0),                        # GQA 16
+]
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"hq{c[0]}_hkv{c[1]}_d{c[2]}_n{sum(c[3])}")
+def test_prefill_small(mode, case):
+    hq, hkv, d, n_q, q_pos0, lens, bs = case
+    got, ref, lo, hi = _case(mode, hq, hkv, d, n_q, q_pos0, lens, bs, seed=hq + d)
+    _gate(got, ref, lo, hi, (mode, case))
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "BF16"])
+def test_prefill_config5_sampled_rows(mode):
+    """Full configuration 5 (2048 tokens, 28/4 heads, D 128) on the GPU; the
+    oracle checks sampled query rows, all heads: tile edges, the diagonal
+    ends and random rows."""
+    w = synth.prefill_workload()
+    n = int(w.lens[0])
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2046, 2047],
+                                     rng.integers(0, n, 24)]))
+    got, ref, lo, hi = _case(mode, w.q_heads, w.kv_heads, w.head_dim, [n], [0], [n], 0,
+                             seed=w.seed, rows=rows)
+    _gate(got[rows], ref[rows], lo[rows], hi[rows], ("config5", mode))
+    assert not np.any(np.isnan(got))
+
+
+def test_prefill_repeat_bitwise_identical():
+    """Standalone repeated-run harness (FA page, section 4): LDS double
+    buffering must give identical bits run after run."""
+    w = synth.prefill_workload(tokens=512)
+    n = int(w.lens[0])
+    cache = make_cache("K8V8", w)
+    k, v = synth.kv_sequence(w, 0)
+    append_seq(cache, 0, k, v)
+    q_bits = synth.q_bf16_bits(w.seed, (n, w.q_heads, w.head_dim))
+    first, _ = gpu_prefill(cache, q_bits, [n], [0], [n], w.group, w.sm_scale)
+    for _ in range(100):
+        again, _ = gpu_prefill(cache, q_bits, [n], [0], [n], w.group, w.sm_scale)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))

@@ -332,3 +332,71 @@ def test_fp8_error_is_reported_in_expected_range():
     e16 = oracle.fp8_kv_error(q_bits, ks, vs, sm, "K16V8")
     assert 0.005 < e8 < 0.2 and 0.001 < e16 < e8
     assert oracle.fp8_kv_error(q_bits, ks, vs, sm, "BF16") == 0.0
+
+
+# ------------------------------------------------------------ rounding bounds
+
+def _fp32_attention(mode, q_bits, k, v, sm):
+    """An independent fp32 computation of the method (numpy fp32 BLAS dot
+    products, fp32 scale products and exp2, torch bf16 rounding of P): the
+    kind of result a GPU produces."""
+    import torch
+    store = oracle.store_rows(mode, k, v)
+    b_k = (oracle.e4m3_value(store["k8"]) if mode == "K8V8"
+           else oracle.bf16_value(store["k16"])).astype(np.float32)
+    b_v = (oracle.bf16_value(store["v16"]) if mode == "BF16"
+           else oracle.e4m3_value(store["v8"])).astype(np.float64)
+    ks = store["ks"] if mode == "K8V8" else np.ones(k.shape[:2], np.float32)
+    vs = store["vs"] if mode != "BF16" else np.ones(k.shape[:2], np.float32)
+    q = oracle.bf16_value(q_bits).astype(np.float32)
+    hq, hkv = q.shape[0], k.shape[1]
+    g = hq // hkv
+    c = np.float32(np.float32(sm) * np.float32(1.4426950408889634))
+    out = np.zeros(q.shape)
+    for h in range(hq):
+        kh = h // g
+        s = (b_k[:, kh] @ q[h]).astype(np.float32)             # fp32 BLAS dot
+        s = (s * ks[:, kh]).astype(np.float32) * c
+        m = np.float32(np.ceil(s.max()))
+        p = np.exp2((s - m).astype(np.float32)).astype(np.float32)
+        w = (p * vs[:, kh]).astype(np.float32)
+        pt = torch.from_numpy(w).to(torch.bfloat16).to(torch.float64).numpy()
+        out[h] = (pt[:, None] * b_v[:, kh]).sum(0) / p.astype(np.float64).sum()
+    return out
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+def test_rounding_bounds_contain_an_fp32_computation(mode):
+    """[lo, hi] holds every output reachable by rounding an ambiguous P either
+    way, so an independent fp32 computation must land inside it (up to the
+    smooth fp32 change of p, ~1e-6).  The explicit tie case is
+    test_rounding_bounds_at_a_bf16_midpoint."""
+    q_bits, ks, vs = _inputs(31, b=6, hq=16, hkv=2, d=128, t=40)
+    sm = float(np.float32(1 / math.sqrt(128)))
+    out, lo, hi = oracle.decode(mode, q_bits, ks, vs, sm, bounds=True)
+    assert np.all(lo <= out) and np.all(out <= hi)
+    # the window is the worst-case fp32 summation bound: a few 1e-3 at most
+    assert oracle.rel_l2(hi, lo) < 5e-3
+    assert np.count_nonzero(hi > lo) > 0.1 * hi.size   # ambiguous P do occur
+    for b in range(q_bits.shape[0]):
+        o32 = _fp32_attention(mode, q_bits[b], ks[b], vs[b], sm)
+        slack = 2e-6 * (np.abs(out[b]) + 0.1)
+        assert np.all(o32 >= lo[b] - slack) and np.all(o32 <= hi[b] + slack)
+
+
+def test_rounding_bounds_collapse_without_rounding():
+    q_bits, ks, vs = _inputs(32, b=1, hq=4, hkv=1, d=32, t=20)
+    out, lo, hi = oracle.decode("K8V8", q_bits, ks, vs, 0.2, round_p=False, bounds=True)
+    assert np.array_equal(lo, out) and np.array_equal(hi, out)
+
+
+def test_rounding_bounds_at_a_bf16_midpoint():
+    """v_scale = 1 + 2^-8 is the midpoint between bf16 1 and 1 + 2^-7; with
+    p = 1 both roundings are valid, so the bounds span V and V (1 + 2^-7)."""
+    k = np.zeros((1, 1, 64), np.float32)
+    v = np.zeros((1, 1, 64), np.float32)
+    v[0, 0, 0] = 449.75                      # amax / 448 = 1 + 2^-8 exactly
+    q_bits = oracle.bf16_round_f32(np.zeros((1, 1, 64), np.float32))  # s = 0, p = 1
+    out, lo, hi = oracle.decode("K16V8", q_bits, [k], [v], 0.1, bounds=True)
+    assert out[0, 0, 0] == 448.0             # ties to even: P = 1
+    assert lo[0, 0, 0] == 448.0 and hi[0, 0, 0] == 448.0 * (1 + 2 ** -7)
