@@ -1,0 +1,375 @@
+"""Benchmark: KV-cache GB/s (% of 8 TB/s) and us per decode step, K8V8 vs
+K16V8 vs BF16, on one MI355X.
+
+Step: one decode step of batch 16, 16 query / 2 KV heads (GQA 8), head_dim
+128, 2048 cached keys per sequence (e4m3 K/V, N(0,1) with 2 % x10 outliers):
+  fp8kv_append (one new token per sequence, written at position 2047)
+  fp8kv_decode_partial (split kernel) + fp8kv_decode_merge (merge kernel).
+The headline value is K8V8 KV bytes per step / time per step, HBM-cold: the
+step rotates over 64 copies of the cache (> 1 GB, larger than the 256 MB
+Infinity Cache), so no copy is cache-resident when it is read.  All steps of
+one rotation are captured in a HIP graph (no host launch cost inside the
+timed region).  Per-kernel durations come from HIP event pairs around each
+kernel of one more rotation, launched on the same stream right behind the
+timed replays (see DecodeBench.run).
+
+Extra fields: the K16V8 and BF16 controls (same protocol), the L2/MALL-warm
+rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
+the roofline of the split kernel and the CPU oracle as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+ROW_BYTES = {"K8V8": lambda d: 2 * d + 8, "K16V8": lambda d: 3 * d + 4, "BF16": lambda d: 4 * d}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_k8v8_b16_t2048_traffic.json")
+KERNEL_SOURCES = ["fp8_kv_cache_append_amd/csrc/decode.hip",
+                  "fp8_kv_cache_append_amd/csrc/device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class DecodeBench:
+    """Rotating copies of one decode workload plus the graph of one rotation."""
+
+    def __init__(self, mode: str, w, copies: int, warm: bool = False):
+        import torch
+        from fp8_kv_cache_append_amd import binding, synth
+        from fp8_kv_cache_append_amd.binding import KVCache
+
+        self.torch, self.binding = torch, binding
+        self.mode, self.w, self.copies, self.warm = mode, w, copies, warm
+        dev = "cuda"
+        n = int(w.lens[0])
+        bs, table, n_blocks = synth.block_layout(w)
+        base = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+        last_k, last_v = [], []
+        for b in range(w.batch):
+            k, v = synth.kv_sequence(w, b)
+            binding.fp8kv_append(base, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                                 torch.full((n,), b, dtype=torch.int32, device=dev),
+                                 torch.arange(n, dtype=torch.int32, device=dev))
+            last_k.append(k[-1])
+            last_v.append(v[-1])
+        n_copies = 1 if warm else copies
+        self.caches = [base] + [KVCache(mode, base.k.clone(), base.v.clone(),
+                                        None if base.k_scale is None else base.k_scale.clone(),
+                                        None if base.v_scale is None else base.v_scale.clone(),
+                                        base.block_table) for _ in range(n_copies - 1)]
+        # the new token of each sequence, appended at its last position
+        self.k_new = torch.from_numpy(np.stack(last_k)).to(dev)
+        self.v_new = torch.from_numpy(np.stack(last_v)).to(dev)
+        self.seq_idx = torch.arange(w.batch, dtype=torch.int32, device=dev)
+        self.pos = torch.full((w.batch,), n - 1, dtype=torch.int32, device=dev)
+        q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
+        self.q = torch.from_numpy(q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
+        self.max_len = n
+        self.chunk, self.splits = binding.fp8kv_decode_plan(base, w.batch, w.group, n)
+        g, d = w.group, w.head_dim
+        self.pacc = torch.empty((w.batch, w.kv_heads, self.splits, g, d), device=dev)
+        self.pml = torch.empty((w.batch, w.kv_heads, self.splits, g, 2), device=dev)
+        self.out = torch.empty((w.batch, w.q_heads, d), device=dev)
+        self.kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](d)
+        self.graph = None
+
+    def split(self, i: int):
+        w = self.w
+        self.binding.fp8kv_decode_partial(self.caches[i % len(self.caches)], self.q, w.group,
+                                          self.lens, self.max_len, w.sm_scale, self.chunk,
+                                          self.splits, self.pacc, self.pml)
+
+    def step(self, i: int, ev=None):
+        b, w = self.binding, self.w
+        c = self.caches[i % len(self.caches)]
+        if ev: ev[0].record()
+        b.fp8kv_append(c, self.k_new, self.v_new, self.seq_idx, self.pos)
+        if ev: ev[1].record()
+        b.fp8kv_decode_partial(c, self.q, w.group, self.lens, self.max_len, w.sm_scale,
+                               self.chunk, self.splits, self.pacc, self.pml)
+        if ev: ev[2].record()
+        b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
+                             self.pacc, self.pml, self.out)
+        if ev: ev[3].record()
+
+    def capture(self):
+        torch = self.torch
+        self.step(0)  # eager call first: the library's one-time device check
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(self.copies):
+                self.step(i)
+        torch.cuda.synchronize()
+        self.split_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.split_graph):
+            for i in range(self.copies):
+                self.split(i)
+        torch.cuda.synchronize()
+
+    def split_avg_ms(self, replays: int) -> float:
+        """Average duration of one split-kernel launch: the split kernel alone
+        over the rotation, back to back in a graph, between two events."""
+        torch = self.torch
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        self.split_graph.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(replays):
+            self.split_graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (replays * self.copies)
+
+    def run(self, replays: int, kernel_events: bool = False):
+        """Replay the rotation `replays` times between two events (ms).
+
+        With kernel_events, one more rotation is then launched eagerly with an
+        event pair around every kernel on the launch stream.  It is enqueued
+        while the GPU is still busy with the replays, so no host launch gap
+        falls inside a pair: each pair brackets exactly one kernel."""
+        torch = self.torch
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(replays):
+            self.graph.replay()
+        t1.record()
+        ev = None
+        if kernel_events:
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                  for _ in range(self.copies)]
+            for i in range(self.copies):
+                self.step(i, ev[i])
+        torch.cuda.synchronize()
+        self.events = ev
+        return t0.elapsed_time(t1)  # ms
+
+    def kernel_ms(self):
+        """Mean per-launch durations (ms) of append, split and merge."""
+        ev = self.events
+        app = [ev[i][0].elapsed_time(ev[i][1]) for i in range(self.copies)]
+        spl = [ev[i][1].elapsed_time(ev[i][2]) for i in range(self.copies)]
+        mrg = [ev[i][2].elapsed_time(ev[i][3]) for i in range(self.copies)]
+        return float(np.mean(app)), float(np.mean(spl)), float(np.mean(mrg))
+
+
+def bench_decode(mode, w, steps, warmup, copies):
+    bench = DecodeBench(mode, w, copies)
+    bench.capture()
+    reps = max(1, math.ceil(steps / copies))
+    bench.run(max(1, math.ceil(warmup / copies)))
+    ms = bench.run(reps, kernel_events=True)
+    n_steps = reps * copies
+    app, spl, mrg = bench.kernel_ms()
+    split_avg = bench.split_avg_ms(reps)
+    step_ms = ms / n_steps
+    res = {"ms_per_step": step_ms, "steps": n_steps, "kv_bytes": bench.kv_bytes,
+           "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
+           "kernel_us_event_pairs": {"append": app * 1e3, "split": spl * 1e3,
+                                     "merge": mrg * 1e3},
+           "split_us": split_avg * 1e3,
+           "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
+    res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
+    return res, bench
+
+
+def bench_warm(mode, w, steps, copies):
+    """The same graph of steps on one copy of the cache: L2/MALL-warm,
+    labelled as such (it can exceed the HBM rate)."""
+    bench = DecodeBench(mode, w, copies, warm=True)
+    bench.capture()
+    bench.run(2)
+    reps = max(1, math.ceil(steps / copies))
+    ms = bench.run(reps)
+    step_ms = ms / (reps * copies)
+    return {"ms_per_step": step_ms, "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
+            "split_us": bench.split_avg_ms(reps) * 1e3}
+
+
+def bench_prefill(reps=20):
+    import torch
+    from fp8_kv_cache_append_amd import binding, synth
+    from fp8_kv_cache_append_amd.binding import KVCache
+
+    w = synth.prefill_workload()
+    n = int(w.lens[0])
+    bs, table, n_blocks = synth.block_layout(w)
+    cache = KVCache.allocate("K8V8", n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda")
+    k, v = synth.kv_sequence(w, 0)
+    binding.fp8kv_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                         torch.zeros(n, dtype=torch.int32, device="cuda"),
+                         torch.arange(n, dtype=torch.int32, device="cuda"))
+    q_bits = synth.q_bf16_bits(w.seed, (n, w.q_heads, w.head_dim))
+    q = torch.from_numpy(q_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    out = torch.empty((n, w.q_heads, w.head_dim), device="cuda")
+
+    def call():
+        binding.fp8kv_prefill(cache, q, w.group, cu, pos0, lens, n, w.sm_scale, out)
+
+    for _ in range(5):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    flops = 4.0 * w.q_heads * w.head_dim * (n * (n + 1) / 2)
+    return {"workload": w.name, "us": us, "tflops": flops / (us * 1e-6) / 1e12,
+            "pct_mfma_peak": 100.0 * flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "algorithmic_gflop": flops / 1e9}
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    """The oracle as it stands, single-threaded, on whole decode steps of the
+    same workload: quantise the new tokens, then attend every (sequence, KV
+    head).  The cache is quantised once beforehand (not timed)."""
+    import oracle
+    from fp8_kv_cache_append_amd import synth
+
+    g, n = w.group, int(w.lens[0])
+    q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
+    stores, news = [], []
+    for b in range(w.batch):
+        k, v = synth.kv_sequence(w, b)
+        stores.append(oracle.store_rows("K8V8", k, v))
+        news.append((k[-1:], v[-1:]))
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(w.batch):
+            oracle.store_rows("K8V8", *news[b])
+            for h in range(w.kv_heads):
+                view = {key: np.ascontiguousarray(a[:, h]) for key, a in stores[b].items()}
+                oracle.attend_rows("K8V8", q_bits[b, h * g:(h + 1) * g], view, n, w.sm_scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES["K8V8"](w.head_dim)
+    return {"value": kv_bytes * steps / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full decode steps of the benchmark workload "
+                      f"(16 seqs x 2 KV heads x {n} keys, K8V8), {el:.1f} s single-threaded",
+            "ms_per_step": el / steps * 1e3}
+
+
+def traffic_for(kernel_hash: str, split_launches_bytes_hint=None):
+    """HBM bytes per split-kernel launch from the committed counter summary,
+    or None when it is missing or was taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=6400)
+    ap.add_argument("--warmup", type=int, default=640)
+    ap.add_argument("--copies", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="K8V8 decode only (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box here has one, and the decode path "
+              "has no cross-GPU step (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_kv_cache_append_amd import binding, synth
+
+    binding.lib()
+    torch.cuda.set_device(0)
+    w = synth.decode_workload(2)
+    head, hb = bench_decode("K8V8", w, args.steps, args.warmup, args.copies)
+    split_us = head["split_us"]
+    achieved = head["kv_bytes"] / (split_us * 1e-6) / 1e9
+    khash = kernel_source_hash()
+    traffic = traffic_for(khash)
+    extras = {}
+    if not args.no_extras:
+        for mode in ("K16V8", "BF16"):
+            r, _ = bench_decode(mode, w, args.steps, args.warmup, args.copies)
+            extras[mode] = r
+        extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
+        extras["prefill"] = bench_prefill()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+
+    rec = {
+        "metric": "KV-cache GB/s (% of 8 TB/s) and us/decode step, K8/V8 vs K16/V8 vs BF16",
+        "value": head["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_b16_hq16_hkv2_d128_t2048_k8v8_hbm_cold",
+                   "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "head_dim": w.head_dim, "cached_tokens": int(w.lens[0]),
+                   "kv_format": "e4m3 + fp32 scale per (token, KV head)",
+                   "cache_state": f"HBM-cold, rotating {args.copies} copies",
+                   "step": "append 1 token/seq + split kernel + merge kernel",
+                   "split_plan": head["split_plan"]},
+        "us_per_step": head["ms_per_step"] * 1e3,
+        "pct_roofline": head["pct_roofline"],
+        "split_us": head["split_us"],
+        "kernel_us_event_pairs": head["kernel_us_event_pairs"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "decode_partial_kernel<K8V8,128>",
+                     "bytes_per_launch": head["kv_bytes"],
+                     "kernel_source_hash": khash},
+        "cpu_baseline": cpu,
+    }
+    if extras:
+        keys = ("ms_per_step", "kv_gbs", "pct_roofline", "split_us", "kernel_us_event_pairs")
+        rec["modes"] = {"K8V8": {k: head[k] for k in keys}}
+        for mode in ("K16V8", "BF16"):
+            rec["modes"][mode] = {k: extras[mode][k] for k in keys}
+        rec["speedup_vs_bf16"] = extras["BF16"]["ms_per_step"] / head["ms_per_step"]
+        rec["speedup_vs_k16v8"] = extras["K16V8"]["ms_per_step"] / head["ms_per_step"]
+        rec["warm_l2_mall"] = extras["K8V8_warm"]
+        rec["prefill"] = extras["prefill"]
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,13 +61,94 @@ constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-rob
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kMaxGroup = 16; // query heads per KV head (one MFMA column block)
 
+// Raw (still compressed) K/V of one 64-token tile in the registers of one
+// lane, plus the scales of the lane's own token (token t0 + lane).
+template <int MODE, int D>
+struct TileRegs {
+  static constexpr bool K8 = (MODE == kK8V8);
+  static constexpr bool V8 = (MODE != kBF16);
+  static constexpr int KP = D / 64;                      // 16-element pieces
+  static constexpr int KRAW = K8 ? KP : 2 * KP;          // 16-byte K loads per sub-block
+  static constexpr int DPR = D / 16;
+  static constexpr int VW = V8 ? DPR / 4 : DPR / 2;      // dwords of V per token
+  u32x4_t k[4][KRAW];
+  uint32_t v[2][8][VW];
+  float ks, vs;
+};
+
+// Issue the loads of the tile starting at token t0.  Tokens at or past t_end
+// are not read (their registers are zero).  tab holds, in lane e, the block
+// id of block t_begin / bs + e of the sequence; it is indexed with a
+// wave-uniform lane, so every block id is a scalar.
+template <int MODE, int D>
+__device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a, int t0,
+                                          int t_end, int tab, int e_base, int h, int g4, int c,
+                                          int lane) {
+  using T = TileRegs<MODE, D>;
+  int blk[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+    blk[kb] = __builtin_amdgcn_readlane(tab, min((t0 + 16 * kb) / a.bs - e_base, 63));
+  auto row_of = [&](int kb, int t) -> int64_t {
+    return ((int64_t)blk[kb] * a.bs + t % a.bs) * a.hkv + h;
+  };
+  {  // scales of token t0 + lane
+    const int t = t0 + lane;
+    const int kb = lane >> 4;
+    const int64_t rr = ((int64_t)(kb == 0 ? blk[0] : kb == 1 ? blk[1] : kb == 2 ? blk[2] : blk[3]) *
+                            a.bs + t % a.bs) * a.hkv + h;
+    r.ks = (T::K8 && t < t_end) ? a.ks[rr] : 0.0f;
+    r.vs = (T::V8 && t < t_end) ? a.vs[rr] : 0.0f;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {  // K: lane (g4, c) reads token 16*kb + c
+    const int t = t0 + 16 * kb + c;
+    const bool ok = t < t_end;
+    const int64_t rr = row_of(kb, t);
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p) {
+      if (T::K8) {
+        const uint8_t* src = static_cast<const uint8_t*>(a.k) + rr * D + 64 * p + 16 * g4;
+        r.k[kb][p] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+      } else {
+        const uint16_t* src = static_cast<const uint16_t*>(a.k) + rr * D + 64 * p + 16 * g4;
+        r.k[kb][2 * p] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+        r.k[kb][2 * p + 1] =
+            ok ? *reinterpret_cast<const u32x4_t*>(src + 8) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {  // V: k-slot j of chunk kp -> token 32kp + 16(j/4) + 4g4 + j%4
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kb = 2 * kp + (j >> 2);
+      const int t = t0 + 16 * kb + 4 * g4 + (j & 3);
+      const bool ok = t < t_end;
+      const int64_t rr = row_of(kb, t);
+      const uint8_t* src = static_cast<const uint8_t*>(a.v) + (rr * D + T::DPR * c) * (T::V8 ? 1 : 2);
+      if constexpr (T::VW == 4) {
+        const u32x4_t w = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.v[kp][j][e] = w[e];
+      } else if constexpr (T::VW == 2) {
+        const u32x2_t w = ok ? *reinterpret_cast<const u32x2_t*>(src) : u32x2_t{0u, 0u};
+        r.v[kp][j][0] = w[0];
+        r.v[kp][j][1] = w[1];
+      } else {
+        r.v[kp][j][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+      }
+    }
+  }
+}
+
 template <int MODE, int D>
 __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
-  constexpr int KP = D / 64;         // 16-element pieces of a lane's d-set
+  using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
-  constexpr int DPR = D / 16;        // d values per V^T row group (MFMAs per PV chunk)
-  constexpr bool kK8 = (MODE == kK8V8);
-  constexpr bool kV8 = (MODE != kBF16);
+  constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
+  constexpr bool kK8 = T::K8;
+  constexpr bool kV8 = T::V8;
 
   __shared__ float s_scale[kWaves][2][kTile];
   __shared__ float s_m[kWaves][kMaxGroup];
@@ -84,10 +165,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int bh = wg / a.n_splits;  // b * hkv + h
   const int h = bh % a.hkv;
   const int b = bh / a.hkv;
-  const int len = a.seq_lens[b];
-  const int t_begin = split * a.chunk;
-  const int t_end = min(len, t_begin + a.chunk);
   const int G = a.group;
+  const int t_begin = split * a.chunk;
+
+  // First round trip, all independent: the sequence length, the block ids
+  // of this split (lane e: block t_begin / bs + e, index kept inside the
+  // table row; ids past the sequence are never used) and Q.
+  const int len = a.seq_lens[b];
+  const int e_base = t_begin / a.bs;
+  const int tab = a.table[(int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1)];
+  u32x4_t qb[KC];  // Q^T as the B operand of QK: lane (g4, c) holds head c's d-set
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+      qb[kc] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  const int t_end = min(len, t_begin + a.chunk);
 
   float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
   float* pml = a.part_ml + ((int64_t)bh * a.n_splits + split) * G * 2;
@@ -99,103 +196,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     return;
   }
 
-  // Q^T as the B operand of QK: lane (g4, c) holds head c's d-set.
-  u32x4_t qb[KC];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + c) * D;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
-      if (c < G)
-        qb[kc] = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      else
-        qb[kc] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
   float l_run = 0.0f;       // this lane's share of the normaliser of head c
   f32x4_t acc[DPR];
 #pragma unroll
   for (int j = 0; j < DPR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t tab_row = (int64_t)b * a.mbps;
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  // Double buffer: the loads of tile i + kWaves are in flight while tile i
+  // is computed.
+  T cur, nxt;
+  if (wave < n_tiles)
+    load_tile<MODE, D>(cur, a, t_begin + wave * kTile, t_end, tab, e_base, h, g4, c, lane);
 
   for (int tile = wave; tile < n_tiles; tile += kWaves) {
     const int t0 = t_begin + tile * kTile;
-    // Block of each 16-token sub-block (bs is a multiple of 16, so a
-    // sub-block never straddles two blocks).  Tokens past t_end load the
-    // last valid token instead and are masked below.
-    int blk[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int tb = min(t0 + 16 * kb, t_end - 1);
-      blk[kb] = a.table[tab_row + tb / a.bs];
-    }
-    auto row_of = [&](int kb, int t) -> int64_t {
-      const int tc = min(t, t_end - 1);
-      return ((int64_t)blk[kb] * a.bs + tc % a.bs) * a.hkv + h;
-    };
+    const bool more = tile + kWaves < n_tiles;
+    if (more)
+      load_tile<MODE, D>(nxt, a, t0 + kWaves * kTile, t_end, tab, e_base, h, g4, c, lane);
 
-    // --- per-token scales of the tile -> LDS (lane l: token t0 + l)
-    if (kK8 || kV8) {
-      const int64_t r = row_of(lane >> 4, t0 + lane);
-      if (kK8) s_scale[wave][0][lane] = a.ks[r];
-      if (kV8) s_scale[wave][1][lane] = a.vs[r];
-    }
-
-    // --- K tile loads: lane (g4, r = c) reads token 16*kb + c
-    u32x4_t kraw[4][kK8 ? KP : 2 * KP];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int64_t r = row_of(kb, t0 + 16 * kb + c);
-#pragma unroll
-      for (int p = 0; p < KP; ++p) {
-        if (kK8) {
-          const uint8_t* src = static_cast<const uint8_t*>(a.k) + r * D + 64 * p + 16 * g4;
-          kraw[kb][p] = *reinterpret_cast<const u32x4_t*>(src);
-        } else {
-          const uint16_t* src = static_cast<const uint16_t*>(a.k) + r * D + 64 * p + 16 * g4;
-          kraw[kb][2 * p] = *reinterpret_cast<const u32x4_t*>(src);
-          kraw[kb][2 * p + 1] = *reinterpret_cast<const u32x4_t*>(src + 8);
-        }
-      }
-    }
-
-    // --- V tile loads: lane (g4, r = c), chunk kp, k-slot j -> token
-    //     32*kp + 16*(j/4) + 4*g4 + (j%4); DPR contiguous elements at d = DPR*c
-    constexpr int VW = kV8 ? DPR / 4 : DPR / 2;  // dwords per token
-    uint32_t vraw[2][8][VW];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kb = 2 * kp + (j >> 2);
-        const int64_t r = row_of(kb, t0 + 16 * kb + 4 * g4 + (j & 3));
-        if (kV8) {
-          const uint8_t* src = static_cast<const uint8_t*>(a.v) + r * D + DPR * c;
-          if constexpr (VW == 2) {
-            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
-            vraw[kp][j][0] = w[0];
-            vraw[kp][j][VW - 1] = w[1];
-          } else {
-            vraw[kp][j][0] = *reinterpret_cast<const uint32_t*>(src);
-          }
-        } else {
-          const uint16_t* src = static_cast<const uint16_t*>(a.v) + r * D + DPR * c;
-          if constexpr (VW == 4) {
-            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
-#pragma unroll
-            for (int e = 0; e < VW; ++e) vraw[kp][j][e] = w[e];
-          } else {
-            const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
-            vraw[kp][j][0] = w[0];
-            vraw[kp][j][VW - 1] = w[1];
-          }
-        }
-      }
-    }
+    // --- per-token scales of the tile -> LDS, then the four each lane needs.
+    // The wave writes and reads its own slice; LDS operations of one wave
+    // complete in order, and the previous tile's reads precede these writes
+    // in program order.
+    if (kK8) s_scale[wave][0][lane] = cur.ks;
+    if (kV8) s_scale[wave][1][lane] = cur.vs;
+    __builtin_amdgcn_wave_barrier();
 
     // --- QK on the matrix cores
     f32x4_t sacc[4];
@@ -206,12 +232,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       for (int kc = 0; kc < KC; ++kc) {
         u32x4_t av;
         if (kK8) {
-          const u32x4_t w = kraw[kb][kc >> 1];
+          const u32x4_t w = cur.k[kb][kc >> 1];
           const uint32_t lo = w[2 * (kc & 1)], hi = w[2 * (kc & 1) + 1];
-          av = u32x4_t{e4m3x2_to_bf16x2(lo, false), e4m3x2_to_bf16x2(lo, true),
-                       e4m3x2_to_bf16x2(hi, false), e4m3x2_to_bf16x2(hi, true)};
+          av = u32x4_t{e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                       e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi)};
         } else {
-          av = kraw[kb][kc];
+          av = cur.k[kb][kc];
         }
         s = mfma_16x16x32_bf16(av, qb[kc], s);
       }
@@ -219,33 +245,29 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     }
 
     // --- scores in log2 units, K scale folded in after the product
-    float ksc[4][4], vsc[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int base = 16 * kb + 4 * g4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ksc[kb][i] = kK8 ? s_scale[wave][0][base + i] : 1.0f;
-        vsc[kb][i] = kV8 ? s_scale[wave][1][base + i] : 1.0f;
-      }
-    }
-    float sc[4][4];
+    float sc[4][4], vsc[4][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      const int base = 16 * kb + 4 * g4;
+      f32x4_t ksv = {1.f, 1.f, 1.f, 1.f}, vsv = {1.f, 1.f, 1.f, 1.f};
+      if (kK8) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
+      if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * kb + 4 * g4 + i;
-        float s = kK8 ? (sacc[kb][i] * ksc[kb][i]) * a.c_scale : sacc[kb][i] * a.c_scale;
+        const int t = t0 + base + i;
+        float s = kK8 ? (sacc[kb][i] * ksv[i]) * a.c_scale : sacc[kb][i] * a.c_scale;
         s = (t < t_end) ? s : -INFINITY;
         sc[kb][i] = s;
+        vsc[kb][i] = vsv[i];
         tmax = fmaxf(tmax, s);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
 
-    // --- online softmax update with an integer reference
+    // --- online softmax update with an integer reference (every tile holds
+    //     at least one valid token, so tmax is finite)
     const float m_new = fmaxf(m_run, ceilf(tmax));
     if (m_new != m_run) {
       const float alpha = (m_run == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new));
@@ -286,17 +308,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
             const int k2 = byte & 2;  // byte pair (k2, k2+1)
             const uint32_t sel = (uint32_t)(k2 + 4) | ((uint32_t)k2 << 8) |
                                  ((uint32_t)(k2 + 5) << 16) | ((uint32_t)(k2 + 1) << 24);
-            const uint32_t x = byte_perm(vraw[kp][j0][wsel], vraw[kp][j1][wsel], sel);
+            const uint32_t x = byte_perm(cur.v[kp][j0][wsel], cur.v[kp][j1][wsel], sel);
             av[jp] = e4m3x2_to_bf16x2(x, (byte & 1) != 0);
           } else {
             const int e = db >> 1;
             const uint32_t sel = (db & 1) ? 0x03020706u : 0x01000504u;
-            av[jp] = byte_perm(vraw[kp][j0][e], vraw[kp][j1][e], sel);
+            av[jp] = byte_perm(cur.v[kp][j0][e], cur.v[kp][j1][e], sel);
           }
         }
         acc[db] = mfma_16x16x32_bf16(av, pb[kp], acc[db]);
       }
     }
+    if (more) cur = nxt;
   }
 
   // --- normaliser of head c: sum the four lane groups
@@ -326,12 +349,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+  for (int idx = 4 * threadIdx.x; idx < G * D; idx += 4 * blockDim.x) {
     const int g = idx / D, d = idx % D;
-    float sum = 0.0f;
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += s_acc[w][g][d];
-    pacc[idx] = sum;
+    for (int w = 0; w < kWaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(&s_acc[w][g][d]);
+    *reinterpret_cast<f32x4_t*>(pacc + idx) = sum;
   }
   for (int g = threadIdx.x; g < G; g += blockDim.x) {
     float lsum = 0.0f;
@@ -346,7 +369,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   }
 }
 
-// Second kernel: merge the splits of each (sequence, query head).
+// Second kernel: merge the splits of each (sequence, query head).  The splits
+// are consumed in batches of kMergeBatch whose loads are all issued before
+// any is used, and the batches are combined online with power-of-two weights
+// (one memory round trip per batch, not per split).
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, int n_splits,
                                                            const float* __restrict__ part_acc,
@@ -359,22 +387,39 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
   if (g >= group) return;
   const float* ml = part_ml + (int64_t)bh * n_splits * group * 2;
   const float* pa = part_acc + (int64_t)bh * n_splits * group * D;
-  float m_star = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) m_star = fmaxf(m_star, ml[(s * group + g) * 2]);
-  float lsum = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (m_star != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float m = ml[(s * group + g) * 2];
-      if (m == -INFINITY) continue;
-      const float w = ldexpf(1.0f, (int)(m - m_star));
-      lsum += w * ml[(s * group + g) * 2 + 1];
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(pa + ((int64_t)s * group + g) * D + 4 * d4);
-      acc += w * x;
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch];
+    f32x4_t x[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int s = min(s0 + i, n_splits - 1);
+      const f32x2_t v = *reinterpret_cast<const f32x2_t*>(ml + ((int64_t)s * group + g) * 2);
+      m[i] = (s0 + i < n_splits) ? v[0] : -INFINITY;
+      l[i] = v[1];
+      x[i] = *reinterpret_cast<const f32x4_t*>(pa + ((int64_t)s * group + g) * D + 4 * d4);
+    }
+    float mb = m_run;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) mb = fmaxf(mb, m[i]);
+    if (mb == -INFINITY) continue;  // nothing yet
+    if (m_run != -INFINITY && mb != m_run) {
+      const float alpha = ldexpf(1.0f, (int)(m_run - mb));
+      l_run *= alpha;
+      acc *= alpha;
+    }
+    m_run = mb;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (m[i] == -INFINITY) continue;  // empty split: weight 0
+      const float w = ldexpf(1.0f, (int)(m[i] - m_run));
+      l_run += w * l[i];
+      acc += w * x[i];
     }
   }
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-  if (lsum > 0.0f) o = acc / lsum;
+  if (l_run > 0.0f) o = acc / l_run;
   // bh = b * hkv + h, output head h * group + g
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
