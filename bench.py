@@ -213,7 +213,7 @@ def bench_prefill(reps=20):
     from fp8_kv_cache_append_amd import binding, synth
     from fp8_kv_cache_append_amd.binding import KVCache
 
-    w = synth.prefill_workload()
+    w = synth.prefill_gqa7_d128()
     n = int(w.lens[0])
     bs, table, n_blocks = synth.block_layout(w)
     cache = KVCache.allocate("K8V8", n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda")
@@ -305,7 +305,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has one, and the decode path "
-              "has no cross-GPU step (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "has no cross-GPU step.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -313,7 +313,7 @@ def main():
 
     binding.lib()
     torch.cuda.set_device(0)
-    w = synth.decode_workload(2)
+    w = synth.decode_b16_gqa8_d128(2048)
     head, hb = bench_decode("K8V8", w, args.steps, args.warmup, args.copies)
     split_us = head["split_us"]
     achieved = head["kv_bytes"] / (split_us * 1e-6) / 1e9

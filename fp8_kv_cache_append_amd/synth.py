@@ -9,7 +9,7 @@ Every stream is counter-based: ``numpy.random.default_rng([seed, tag, i])``
 for a fixed integer tag per quantity and the sequence (or block) index ``i``,
 so one sequence can be regenerated without drawing the others.
 
-Workloads (value distributions as the benchmark configurations state them):
+Value distributions of the workloads:
 
 * ``normal``   K, V ~ N(0, 1).
 * ``outliers`` K, V ~ N(0, 1); each element independently multiplied by 10
@@ -36,7 +36,7 @@ def rng(seed: int, tag: str, index: int = 0) -> np.random.Generator:
 
 @dataclass
 class Workload:
-    """One decode or prefill configuration."""
+    """One decode or prefill workload."""
     name: str
     batch: int
     q_heads: int
@@ -64,27 +64,32 @@ class Workload:
         return int(self.lens.max()) if self.batch else 0
 
 
-def decode_workload(cfg: int, tokens: int | None = None, seed: int | None = None) -> Workload:
-    """The decode configurations 1-4 (``tokens`` picks the context for 3)."""
-    s = cfg if seed is None else seed
-    if cfg == 1:
-        return Workload("decode_b1_hq4_hkv1_d64_t128", 1, 4, 1, 64,
-                        np.full(1, 128, np.int32), "normal", seed=s)
-    if cfg in (2, 3):
-        t = 2048 if tokens is None else int(tokens)
-        return Workload(f"decode_b16_hq16_hkv2_d128_t{t}", 16, 16, 2, 128,
-                        np.full(16, t, np.int32), "outliers",
-                        modes=("K8V8", "K16V8", "BF16"), seed=s)
-    if cfg == 4:
-        lens = rng(s, "lens").integers(1024, 32768, size=64, endpoint=True)
-        return Workload("decode_b64_hq32_hkv8_d128_ragged_paged16", 64, 32, 8, 128,
-                        lens.astype(np.int32), "bias", block_size=16,
-                        shuffle_blocks=True, modes=("K8V8", "K16V8"), seed=s)
-    raise ValueError(f"no decode configuration {cfg}")
+def decode_b1_gqa4_d64(seed: int = 1) -> Workload:
+    """Decode, batch 1, 4 query / 1 KV head, head_dim 64, 128 keys, N(0,1)."""
+    return Workload("decode_b1_hq4_hkv1_d64_t128", 1, 4, 1, 64,
+                    np.full(1, 128, np.int32), "normal", seed=seed)
 
 
-def prefill_workload(seed: int = 5, tokens: int = 2048) -> Workload:
-    """Configuration 5: one causal sequence, 28 query / 4 KV heads, D 128."""
+def decode_b16_gqa8_d128(tokens: int = 2048, seed: int = 2) -> Workload:
+    """Decode, batch 16, 16 query / 2 KV heads, head_dim 128, ``tokens`` keys
+    per sequence, N(0,1) with 2 % x10 outliers, contiguous cache."""
+    return Workload(f"decode_b16_hq16_hkv2_d128_t{int(tokens)}", 16, 16, 2, 128,
+                    np.full(16, int(tokens), np.int32), "outliers",
+                    modes=("K8V8", "K16V8", "BF16"), seed=seed)
+
+
+def decode_b64_gqa4_ragged_paged(seed: int = 4) -> Workload:
+    """Decode, batch 64, 32 query / 8 KV heads, head_dim 128, lengths uniform
+    in [1024, 32768], 16-token blocks behind a shuffled table, keys biased by
+    +20 on 8 channels."""
+    lens = rng(seed, "lens").integers(1024, 32768, size=64, endpoint=True)
+    return Workload("decode_b64_hq32_hkv8_d128_ragged_paged16", 64, 32, 8, 128,
+                    lens.astype(np.int32), "bias", block_size=16,
+                    shuffle_blocks=True, modes=("K8V8", "K16V8"), seed=seed)
+
+
+def prefill_gqa7_d128(tokens: int = 2048, seed: int = 5) -> Workload:
+    """Causal prefill of one sequence, 28 query / 4 KV heads, head_dim 128."""
     return Workload(f"prefill_b1_t{tokens}_hq28_hkv4_d128", 1, 28, 4, 128,
                     np.full(1, tokens, np.int32), "normal", prefill=True, seed=seed)
 

@@ -62,7 +62,7 @@ def _run_case(mode, w, pairs=None):
 
 SHAPES = [
     # (q_heads, kv_heads, head_dim, lens, block_size)
-    (4, 1, 64, [128], 0),                                   # configuration 1
+    (4, 1, 64, [128], 0),                                   # B1 4q/1kv D64 128 keys
     (16, 2, 128, [300, 0, 1, 64, 65, 257, 512, 1000], 0),   # GQA 8, ragged, contiguous
     (32, 8, 128, [700, 16, 1, 1024, 33], 16),               # GQA 4, paged 16
     (28, 4, 128, [513, 2000, 64], 32),                      # GQA 7, paged 32
@@ -84,33 +84,34 @@ def test_decode_small_shapes(mode, shape):
     assert np.all(got[empty] == 0)
 
 
-def test_decode_config1():
-    w = synth.decode_workload(1)
+def test_decode_b1_gqa4_d64_t128():
+    w = synth.decode_b1_gqa4_d64()
     got, *ref = _run_case("K8V8", w)
-    _gate(got, *ref, "config1")
+    _gate(got, *ref, w.name)
 
 
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
-def test_decode_config2_full(mode):
-    w = synth.decode_workload(2)
+def test_decode_b16_gqa8_t2048_full(mode):
+    w = synth.decode_b16_gqa8_d128(2048)
     got, *ref = _run_case(mode, w)
-    _gate(got, *ref, ("config2", mode))
+    _gate(got, *ref, (w.name, mode))
 
 
 @pytest.mark.parametrize("tokens", [77, 512, 8192])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
-def test_decode_config3_sweep(mode, tokens):
-    w = synth.decode_workload(3, tokens=tokens)
+def test_decode_b16_gqa8_context_sweep(mode, tokens):
+    w = synth.decode_b16_gqa8_d128(tokens, seed=3)
     got, *ref = _run_case(mode, w)
-    _gate(got, *ref, ("config3", mode, tokens))
+    _gate(got, *ref, (w.name, mode))
 
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8"])
-def test_decode_config4_sampled(mode):
-    """Full configuration 4 on the GPU; the oracle computes sampled pairs
-    (shortest, longest and a spread of other sequences, several KV heads)."""
-    w = synth.decode_workload(4)
+def test_decode_b64_gqa4_ragged_paged_sampled(mode):
+    """The full ragged paged batch (64 sequences of 1024-32768 keys) on the
+    GPU; the oracle computes sampled pairs (shortest, longest and a spread of
+    other sequences, several KV heads)."""
+    w = synth.decode_b64_gqa4_ragged_paged()
     order = np.argsort(w.lens)
     pairs = [(int(order[0]), 0), (int(order[-1]), 7), (int(order[len(order) // 2]), 3),
              (5, 1), (17, 6), (40, 2)]
@@ -132,7 +133,7 @@ def test_decode_config4_sampled(mode):
         view = {key: np.ascontiguousarray(a[:, h]) for key, a in store.items()}
         ref = oracle.attend_rows(mode, q_bits[b, h * g:(h + 1) * g], view, int(w.lens[b]),
                                  w.sm_scale, bounds=True)
-        _gate(got[b, h * g:(h + 1) * g], *ref, ("config4", mode, b, h, int(w.lens[b])))
+        _gate(got[b, h * g:(h + 1) * g], *ref, (w.name, mode, b, h, int(w.lens[b])))
 
 
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
@@ -206,7 +207,7 @@ def test_merge_of_oracle_partials():
 def test_decode_repeat_bitwise_identical():
     """Repeated runs on fixed inputs give identical bits (no atomics, fixed
     reduction order): the standalone repeated-run harness of the FA page."""
-    w = synth.decode_workload(2)
+    w = synth.decode_b16_gqa8_d128(2048)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
     cache = make_cache("K8V8", w)

@@ -76,25 +76,25 @@ def test_prefill_small(mode, case):
 
 
 @pytest.mark.parametrize("mode", ["K8V8", "BF16"])
-def test_prefill_config5_sampled_rows(mode):
-    """Full configuration 5 (2048 tokens, 28/4 heads, D 128) on the GPU; the
+def test_prefill_t2048_gqa7_sampled_rows(mode):
+    """Full causal prefill of 2048 tokens (28/4 heads, D 128) on the GPU; the
     oracle checks sampled query rows, all heads: tile edges, the diagonal
     ends and random rows."""
-    w = synth.prefill_workload()
+    w = synth.prefill_gqa7_d128()
     n = int(w.lens[0])
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128, 1023, 1024, 2046, 2047],
                                      rng.integers(0, n, 24)]))
     got, ref, lo, hi = _case(mode, w.q_heads, w.kv_heads, w.head_dim, [n], [0], [n], 0,
                              seed=w.seed, rows=rows)
-    _gate(got[rows], ref[rows], lo[rows], hi[rows], ("config5", mode))
+    _gate(got[rows], ref[rows], lo[rows], hi[rows], (w.name, mode))
     assert not np.any(np.isnan(got))
 
 
 def test_prefill_repeat_bitwise_identical():
     """Standalone repeated-run harness (FA page, section 4): LDS double
     buffering must give identical bits run after run."""
-    w = synth.prefill_workload(tokens=512)
+    w = synth.prefill_gqa7_d128(tokens=512)
     n = int(w.lens[0])
     cache = make_cache("K8V8", w)
     k, v = synth.kv_sequence(w, 0)
