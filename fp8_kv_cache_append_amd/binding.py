@@ -41,7 +41,7 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p)]
 
@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
             "fp8kv_decode_merge": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
             "fp8kv_decode": (ctypes.c_int, [C, P, I32, P, I32, I32, F, P, P,
                                             ctypes.c_size_t, P]),
-            "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, F, P, P]),
+            "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, I32, F, P, P]),
             "fp8kv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
@@ -145,7 +145,8 @@ class KVCache:
     def desc(self) -> CacheDesc:
         return CacheDesc(MODES[self.mode], int(self.k.shape[0]), int(self.k.shape[1]),
                          int(self.k.shape[2]), int(self.k.shape[3]),
-                         int(self.block_table.shape[1]), _ptr(self.k), _ptr(self.v),
+                         int(self.block_table.shape[1]), int(self.block_table.shape[0]),
+                         _ptr(self.k), _ptr(self.v),
                          _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table))
 
 
@@ -203,8 +204,9 @@ def fp8kv_prefill(cache: KVCache, q, gqa_group: int, cu_q, q_pos0, seq_lens,
                   max_q_len: int, sm_scale: float, out, stream=None) -> None:
     d = cache.desc()
     _check(lib().fp8kv_prefill(ctypes.byref(d), _ptr(q), gqa_group, _ptr(cu_q), _ptr(q_pos0),
-                               _ptr(seq_lens), int(seq_lens.shape[0]), max_q_len, sm_scale,
-                               _ptr(out), _stream(stream)), "fp8kv_prefill")
+                               _ptr(seq_lens), int(seq_lens.shape[0]), int(q.shape[0]),
+                               max_q_len, sm_scale, _ptr(out), _stream(stream)),
+           "fp8kv_prefill")
 
 
 def fp8kv_strerror(status: int) -> str:

@@ -43,8 +43,10 @@ int validate_cache(const fp8kv_cache* c) {
   if (c->mode != FP8KV_K8V8 && c->mode != FP8KV_K16V8 && c->mode != FP8KV_BF16)
     return FP8KV_ERR_INVALID;
   if (c->head_dim != 64 && c->head_dim != 128) return FP8KV_ERR_UNSUPPORTED;
-  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->max_blocks_per_seq <= 0)
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->max_blocks_per_seq <= 0 ||
+      c->num_seqs <= 0)
     return FP8KV_ERR_INVALID;
+  if ((int64_t)c->max_blocks_per_seq * c->block_size > INT32_MAX) return FP8KV_ERR_INVALID;
   if (c->block_size <= 0 || c->block_size % 16 != 0) return FP8KV_ERR_INVALID;
   if (!c->k || !c->v || !c->block_table) return FP8KV_ERR_INVALID;
   if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->block_table, 4))
@@ -62,8 +64,8 @@ int validate_cache(const fp8kv_cache* c) {
 
 fp8kv::CacheView view_of(const fp8kv_cache* c) {
   return fp8kv::CacheView{c->mode, c->block_size, c->num_kv_heads, c->head_dim,
-                          c->max_blocks_per_seq, c->k, c->v, c->k_scale, c->v_scale,
-                          c->block_table};
+                          c->max_blocks_per_seq, c->num_seqs, c->num_blocks, c->k, c->v,
+                          c->k_scale, c->v_scale, c->block_table};
 }
 
 int launch_status(hipError_t e) {
@@ -75,6 +77,22 @@ int launch_status(hipError_t e) {
 float log2_scale(float sm_scale) { return (float)((double)sm_scale * kLog2e); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The split kernel reads the block ids of a split with one load per lane of
+// a 64-lane wave, so a split may touch at most 64 blocks.  Splits start at
+// multiples of chunk, hence at offsets into a block that are multiples of
+// g = gcd(chunk, block_size), the largest being block_size - g; the last
+// 16-key sub-block of the split then lies (block_size - g + chunk - 16) /
+// block_size blocks after the first.
+bool split_fits_table_window(int64_t chunk, int64_t bs) {
+  int64_t g = chunk, r = bs;
+  while (r != 0) {
+    const int64_t t = g % r;
+    g = r;
+    r = t;
+  }
+  return (bs - g + chunk - 16) / bs <= 63;
+}
 
 int plan(const fp8kv_cache* c, int32_t batch, int32_t max_seq_len, int32_t* chunk,
          int32_t* n_splits) {
@@ -95,7 +113,7 @@ int validate_decode_common(const fp8kv_cache* c, int32_t gqa, int32_t batch,
   if (st != FP8KV_OK) return st;
   if (gqa < 1) return FP8KV_ERR_INVALID;
   if (gqa > kMaxGroup) return FP8KV_ERR_UNSUPPORTED;
-  if (batch < 0 || max_seq_len < 0) return FP8KV_ERR_INVALID;
+  if (batch < 0 || max_seq_len < 0 || batch > c->num_seqs) return FP8KV_ERR_INVALID;
   if ((int64_t)max_seq_len > (int64_t)c->max_blocks_per_seq * c->block_size)
     return FP8KV_ERR_INVALID;
   return FP8KV_OK;
@@ -157,6 +175,7 @@ int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q, int32_t gq
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
+  if (!split_fits_table_window(chunk_tokens, cache->block_size)) return FP8KV_ERR_INVALID;
   if ((int64_t)n_splits * chunk_tokens < max_seq_len) return FP8KV_ERR_INVALID;
   const int64_t n_wg = (int64_t)batch * cache->num_kv_heads * n_splits;
   if (n_wg > INT32_MAX) return FP8KV_ERR_INVALID;
@@ -214,20 +233,23 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
 
 int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
                   const int32_t* cu_q, const int32_t* q_pos0, const int32_t* seq_lens,
-                  int32_t batch, int32_t max_q_len, float sm_scale, float* out, void* stream) {
+                  int32_t batch, int32_t total_q, int32_t max_q_len, float sm_scale, float* out,
+                  void* stream) {
   int st = validate_cache(cache);
   if (st != FP8KV_OK) return st;
-  if (gqa_group < 1 || batch < 0 || max_q_len < 0) return FP8KV_ERR_INVALID;
+  if (gqa_group < 1 || batch < 0 || max_q_len < 0 || total_q < 0 || batch > cache->num_seqs)
+    return FP8KV_ERR_INVALID;
   if (gqa_group > kMaxGroup) return FP8KV_ERR_UNSUPPORTED;
-  if (batch == 0 || max_q_len == 0) return FP8KV_OK;
+  if (batch == 0 || max_q_len == 0 || total_q == 0) return FP8KV_OK;
   if (!q || !cu_q || !q_pos0 || !seq_lens || !out) return FP8KV_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(cu_q, 4) || !aligned(q_pos0, 4) ||
       !aligned(seq_lens, 4))
     return FP8KV_ERR_INVALID;
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(fp8kv::launch_prefill(view_of(cache), q, gqa_group, cu_q, q_pos0,
-                                             seq_lens, batch, max_q_len, log2_scale(sm_scale),
-                                             out, static_cast<hipStream_t>(stream)));
+                                             seq_lens, batch, total_q, max_q_len,
+                                             log2_scale(sm_scale), out,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

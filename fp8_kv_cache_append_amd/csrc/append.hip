@@ -32,6 +32,8 @@ struct AppendArgs {
   int hkv;
   int bs;
   int mbps;
+  int num_seqs;
+  int num_blocks;
 };
 
 template <int MODE, int D>
@@ -49,7 +51,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int h = (int)(pair % a.hkv);
   const int seq = a.seq_idx[tok];
   const int p = a.pos[tok];
+  // Out-of-range device data is skipped, never followed (uniform per row).
+  if (seq < 0 || seq >= a.num_seqs || p < 0 || p >= a.mbps * a.bs) return;
   const int blk = a.table[(int64_t)seq * a.mbps + p / a.bs];
+  if (blk < 0 || blk >= a.num_blocks) return;
   const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
 
   const float* src = (is_v ? a.v_new : a.k_new) + pair * D + 4 * sub;
@@ -98,7 +103,7 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
                          const int32_t* seq_idx, const int32_t* pos, int n_tok,
                          hipStream_t stream) {
   AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs,
-               2 * (int64_t)n_tok * c.hkv, c.hkv, c.bs, c.mbps};
+               2 * (int64_t)n_tok * c.hkv, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
   switch (c.mode) {
     case kK8V8: return append_for_d<kK8V8>(c, a, stream);
     case kK16V8: return append_for_d<kK16V8>(c, a, stream);

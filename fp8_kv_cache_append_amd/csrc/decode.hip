@@ -55,6 +55,7 @@ struct DecodeArgs {
   int mbps;
   int chunk;
   int n_splits;
+  int num_blocks;
 };
 
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
@@ -62,7 +63,8 @@ constexpr int kTile = 64;     // tokens per tile
 constexpr int kMaxGroup = 16; // query heads per KV head (one MFMA column block)
 
 // Raw (still compressed) K/V of one 64-token tile in the registers of one
-// lane, plus the scales of the lane's own token (token t0 + lane).
+// lane, the scales of the lane's own token (token t0 + lane) and the
+// validity needed to neutralise keys outside the sequence.
 template <int MODE, int D>
 struct TileRegs {
   static constexpr bool K8 = (MODE == kK8V8);
@@ -71,75 +73,111 @@ struct TileRegs {
   static constexpr int KRAW = K8 ? KP : 2 * KP;          // 16-byte K loads per sub-block
   static constexpr int DPR = D / 16;
   static constexpr int VW = V8 ? DPR / 4 : DPR / 2;      // dwords of V per token
+  static constexpr int KE = K8 ? 1 : 2;                  // bytes per K element
+  static constexpr int VE = V8 ? 1 : 2;                  // bytes per V element
   u32x4_t k[4][KRAW];
   uint32_t v[2][8][VW];
   float ks, vs;
+  bool tok_ok;     // this lane's own token is before t_end in a valid block
+  bool blk_ok[4];  // block id of each 16-token sub-block is a valid block
+  bool full;       // all 64 tokens are before t_end and in valid blocks
 };
 
-// Issue the loads of the tile starting at token t0.  Tokens at or past t_end
-// are not read (their registers are zero).  tab holds, in lane e, the block
-// id of block t_begin / bs + e of the sequence; it is indexed with a
-// wave-uniform lane, so every block id is a scalar.
+// Per-lane byte offsets inside a 16-token sub-block; they do not depend on
+// the tile, so they are computed once per kernel.
+struct LaneOffsets {
+  uint32_t k;     // token c, d-piece of lane group g4
+  uint32_t v[4];  // tokens 4*g4 + jj, d = DPR*c
+};
+
+// Issue the loads of the tile starting at token t0.  tab holds, in lane e,
+// the block id of block t_begin / bs + e of the sequence; it is indexed with
+// a wave-uniform lane, so every block id is a scalar.  A 16-token sub-block
+// lies inside one block, so its first row (block * bs + slot) * hkv + h is one
+// scalar per sub-block (four scalar divisions per tile) and every load is a
+// scalar base plus a per-lane offset fixed for the kernel.
+//
+// Every load is issued unconditionally and stays inside the cache: a
+// sub-block whose block id is out of range reads block 0 instead (block_size
+// >= 16 keeps the lane offsets inside it), and a token at or past t_end
+// reads a slot of its own, valid block.  The values of such keys are
+// neutralised where they are used (score -inf, V and v_scale 0).  A fixed
+// number of loads in a fixed order lets the compiler wait for exactly the
+// loads each step needs instead of for all of them.
 template <int MODE, int D>
-__device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a, int t0,
-                                          int t_end, int tab, int e_base, int h, int g4, int c,
-                                          int lane) {
+__device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a,
+                                          const LaneOffsets& lo, int t0, int t_end, int tab,
+                                          int e_base, int h, int lane) {
   using T = TileRegs<MODE, D>;
-  int blk[4];
+  int64_t row0[4];
+  bool all_ok = t0 + 64 <= t_end;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    blk[kb] = __builtin_amdgcn_readlane(tab, min((t0 + 16 * kb) / a.bs - e_base, 63));
-  auto row_of = [&](int kb, int t) -> int64_t {
-    return ((int64_t)blk[kb] * a.bs + t % a.bs) * a.hkv + h;
-  };
-  {  // scales of token t0 + lane
-    const int t = t0 + lane;
-    const int kb = lane >> 4;
-    const int64_t rr = ((int64_t)(kb == 0 ? blk[0] : kb == 1 ? blk[1] : kb == 2 ? blk[2] : blk[3]) *
-                            a.bs + t % a.bs) * a.hkv + h;
-    r.ks = (T::K8 && t < t_end) ? a.ks[rr] : 0.0f;
-    r.vs = (T::V8 && t < t_end) ? a.vs[rr] : 0.0f;
+  for (int kb = 0; kb < 4; ++kb) {
+    const int tb = t0 + 16 * kb;
+    const int eb = tb / a.bs;
+    const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
+    r.blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
+    all_ok = all_ok && r.blk_ok[kb];
+    row0[kb] = r.blk_ok[kb] ? ((int64_t)blk * a.bs + (tb - eb * a.bs)) * a.hkv + h : h;
   }
+  r.full = all_ok;
+  {  // scales of token t0 + lane.  The sub-block is lane dependent, so its
+     // values are picked with selects: indexing the arrays with it would
+     // move them to scratch memory.
+    const int kb = lane >> 4;
+    const int64_t base = kb == 0 ? row0[0] : kb == 1 ? row0[1] : kb == 2 ? row0[2] : row0[3];
+    const bool bok = kb == 0 ? r.blk_ok[0] : kb == 1 ? r.blk_ok[1] : kb == 2 ? r.blk_ok[2]
+                                                                               : r.blk_ok[3];
+    r.tok_ok = t0 + lane < t_end && bok;
+    const int64_t rr = base + (int64_t)((lane & 15) * a.hkv);
+    r.ks = T::K8 ? a.ks[rr] : 1.0f;
+    r.vs = T::V8 ? a.vs[rr] : 1.0f;
+  }
+  // Loads half by half (K then V of keys 0-31, then of keys 32-63), so the
+  // first half can be computed while the second is in flight.
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {  // K: lane (g4, c) reads token 16*kb + c
-    const int t = t0 + 16 * kb + c;
-    const bool ok = t < t_end;
-    const int64_t rr = row_of(kb, t);
+  for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
-    for (int p = 0; p < T::KP; ++p) {
-      if (T::K8) {
-        const uint8_t* src = static_cast<const uint8_t*>(a.k) + rr * D + 64 * p + 16 * g4;
-        r.k[kb][p] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-        const uint16_t* src = static_cast<const uint16_t*>(a.k) + rr * D + 64 * p + 16 * g4;
-        r.k[kb][2 * p] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
-        r.k[kb][2 * p + 1] =
-            ok ? *reinterpret_cast<const u32x4_t*>(src + 8) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int kb = 2 * kp; kb < 2 * kp + 2; ++kb) {
+      const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + row0[kb] * (D * T::KE) + lo.k;
+#pragma unroll
+      for (int p = 0; p < T::KP; ++p) {
+        const uint8_t* src = kbase + 64 * T::KE * p;
+        if (T::K8) {
+          r.k[kb][p] = *reinterpret_cast<const u32x4_t*>(src);
+        } else {
+          r.k[kb][2 * p] = *reinterpret_cast<const u32x4_t*>(src);
+          r.k[kb][2 * p + 1] = *reinterpret_cast<const u32x4_t*>(src + 16);
+        }
       }
     }
-  }
-#pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {  // V: k-slot j of chunk kp -> token 32kp + 16(j/4) + 4g4 + j%4
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kb = 2 * kp + (j >> 2);
-      const int t = t0 + 16 * kb + 4 * g4 + (j & 3);
-      const bool ok = t < t_end;
-      const int64_t rr = row_of(kb, t);
-      const uint8_t* src = static_cast<const uint8_t*>(a.v) + (rr * D + T::DPR * c) * (T::V8 ? 1 : 2);
+      const uint8_t* src = static_cast<const uint8_t*>(a.v) + row0[kb] * (D * T::VE) + lo.v[j & 3];
       if constexpr (T::VW == 4) {
-        const u32x4_t w = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
 #pragma unroll
         for (int e = 0; e < 4; ++e) r.v[kp][j][e] = w[e];
       } else if constexpr (T::VW == 2) {
-        const u32x2_t w = ok ? *reinterpret_cast<const u32x2_t*>(src) : u32x2_t{0u, 0u};
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
         r.v[kp][j][0] = w[0];
         r.v[kp][j][1] = w[1];
       } else {
-        r.v[kp][j][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        r.v[kp][j][0] = *reinterpret_cast<const uint32_t*>(src);
       }
     }
   }
+}
+
+// max / sum over the four lane groups (lanes c, c+16, c+32, c+48) with the
+// gfx950 lane swaps: with both operands equal, the two results of a 32-lane
+// swap hold x[l] and x[l ^ 32], those of a 16-lane swap x[l] and x[l ^ 16].
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 template <int MODE, int D>
@@ -152,8 +190,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 
   __shared__ float s_scale[kWaves][2][kTile];
   __shared__ float s_m[kWaves][kMaxGroup];
-  __shared__ float s_l[kWaves][kMaxGroup];
-  __shared__ float s_acc[kWaves][kMaxGroup][D];
+  __shared__ float s_l[kWaves][4][kMaxGroup];
+  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kMaxGroup][D];
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -171,7 +209,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   // First round trip, all independent: the sequence length, the block ids
   // of this split (lane e: block t_begin / bs + e, index kept inside the
   // table row; ids past the sequence are never used) and Q.
-  const int len = a.seq_lens[b];
+  const int len = a.seq_lens[b];  // clamped below to the block-table capacity
   const int e_base = t_begin / a.bs;
   const int tab = a.table[(int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1)];
   u32x4_t qb[KC];  // Q^T as the B operand of QK: lane (g4, c) holds head c's d-set
@@ -184,11 +222,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       qb[kc] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  const int t_end = min(len, t_begin + a.chunk);
+  const int t_end = min(min(max(len, 0), a.mbps * a.bs), t_begin + a.chunk);
 
   float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
   float* pml = a.part_ml + ((int64_t)bh * a.n_splits + split) * G * 2;
-  if (t_begin >= t_end) {  // no key in this split
+  // The test below reads both the length and the block ids (no block id is
+  // INT_MIN, so the second term is always true).  Without it the compiler
+  // sinks the table load below the branch on the length, adding a whole
+  // memory round trip before the first K/V load.
+  const bool empty = (t_begin >= t_end) & (__builtin_amdgcn_readfirstlane(tab) != INT_MIN);
+  if (empty) {  // no key in this split
     for (int i = threadIdx.x; i < G; i += blockDim.x) {
       pml[2 * i] = -INFINITY;
       pml[2 * i + 1] = 0.0f;
@@ -196,106 +239,123 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     return;
   }
 
+  LaneOffsets lo;
+  lo.k = (uint32_t)(c * a.hkv) * (D * T::KE) + 16 * T::KE * g4;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    lo.v[jj] = (uint32_t)((4 * g4 + jj) * a.hkv) * (D * T::VE) + DPR * T::VE * c;
+
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
   float l_run = 0.0f;       // this lane's share of the normaliser of head c
   f32x4_t acc[DPR];
 #pragma unroll
   for (int j = 0; j < DPR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-  // Double buffer: the loads of tile i + kWaves are in flight while tile i
-  // is computed.
-  T cur, nxt;
-  if (wave < n_tiles)
-    load_tile<MODE, D>(cur, a, t_begin + wave * kTile, t_end, tab, e_base, h, g4, c, lane);
-
-  for (int tile = wave; tile < n_tiles; tile += kWaves) {
-    const int t0 = t_begin + tile * kTile;
-    const bool more = tile + kWaves < n_tiles;
-    if (more)
-      load_tile<MODE, D>(nxt, a, t0 + kWaves * kTile, t_end, tab, e_base, h, g4, c, lane);
-
-    // --- per-token scales of the tile -> LDS, then the four each lane needs.
-    // The wave writes and reads its own slice; LDS operations of one wave
-    // complete in order, and the previous tile's reads precede these writes
-    // in program order.
-    if (kK8) s_scale[wave][0][lane] = cur.ks;
-    if (kV8) s_scale[wave][1][lane] = cur.vs;
+  // One tile, in two halves of 32 keys (sub-blocks 2kp and 2kp+1, PV chunk
+  // kp): QK, an online-softmax step, PV.  The second half's data may still be
+  // arriving while the first is computed.  The scales are staged through this
+  // wave's slice of LDS (written and read by the same wave; its LDS operations
+  // complete in order, and the previous tile's reads precede these writes in
+  // program order).
+  auto compute = [&](const T& cur, int t0) {
+    // K scale with sm_scale * log2(e) folded in (one product per token),
+    // V scale as is.
+    if (kK8) s_scale[wave][0][lane] = cur.ks * a.c_scale;
+    if (kV8) s_scale[wave][1][lane] = cur.tok_ok ? cur.vs : 0.0f;
     __builtin_amdgcn_wave_barrier();
-
-    // --- QK on the matrix cores
-    f32x4_t sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        u32x4_t av;
-        if (kK8) {
-          const u32x4_t w = cur.k[kb][kc >> 1];
-          const uint32_t lo = w[2 * (kc & 1)], hi = w[2 * (kc & 1) + 1];
-          av = u32x4_t{e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
-                       e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi)};
-        } else {
-          av = cur.k[kb][kc];
-        }
-        s = mfma_16x16x32_bf16(av, qb[kc], s);
-      }
-      sacc[kb] = s;
-    }
-
-    // --- scores in log2 units, K scale folded in after the product
-    float sc[4][4], vsc[4][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int base = 16 * kb + 4 * g4;
-      f32x4_t ksv = {1.f, 1.f, 1.f, 1.f}, vsv = {1.f, 1.f, 1.f, 1.f};
-      if (kK8) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
-      if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + base + i;
-        float s = kK8 ? (sacc[kb][i] * ksv[i]) * a.c_scale : sacc[kb][i] * a.c_scale;
-        s = (t < t_end) ? s : -INFINITY;
-        sc[kb][i] = s;
-        vsc[kb][i] = vsv[i];
-        tmax = fmaxf(tmax, s);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-
-    // --- online softmax update with an integer reference (every tile holds
-    //     at least one valid token, so tmax is finite)
-    const float m_new = fmaxf(m_run, ceilf(tmax));
-    if (m_new != m_run) {
-      const float alpha = (m_run == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < DPR; ++j) acc[j] *= alpha;
-      m_run = m_new;
-    }
-
-    // --- P with the V scale folded in, rounded to bf16: B operand of PV
-    u32x4_t pb[2];
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
+      // --- QK on the matrix cores for sub-blocks 2kp, 2kp+1
+      f32x4_t sacc[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int kb = 2 * kp + hb;
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          u32x4_t av;
+          if (kK8) {
+            const u32x4_t w = cur.k[kb][kc >> 1];
+            const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
+            av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
+                         e4m3x2_to_bf16x2<false>(hi32), e4m3x2_to_bf16x2<true>(hi32)};
+          } else {
+            av = cur.k[kb][kc];
+          }
+          s = mfma_16x16x32_bf16(av, qb[kc], s);
+        }
+        sacc[hb] = s;
+      }
+
+      // --- scores in log2 units: (q . K) * (k_scale * sm_scale * log2 e);
+      //     k-slot j of the PV chunk is token 16*(2kp + j/4) + 4*g4 + j%4
+      float sc[8], vsc[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int kb = 2 * kp + hb;
+        const int base = 16 * kb + 4 * g4;
+        f32x4_t ksv = {a.c_scale, a.c_scale, a.c_scale, a.c_scale};
+        f32x4_t vsv = {1.f, 1.f, 1.f, 1.f};
+        if (kK8) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
+        if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = sacc[hb][i] * ksv[i];
+          if (!cur.full) {
+            const bool ok = (t0 + base + i < t_end) && cur.blk_ok[kb];
+            s = ok ? s : -INFINITY;
+          }
+          sc[4 * hb + i] = s;
+          vsc[4 * hb + i] = vsv[i];
+          tmax = fmaxf(tmax, s);
+        }
+      }
+      tmax = max_over_groups(tmax);
+
+      // --- online softmax step with an integer reference; a half with no
+      //     valid key (tmax = -inf) leaves the state unchanged
+      const float m_new = fmaxf(m_run, ceilf(tmax));
+      if (m_new != m_run) {
+        const float alpha = (m_run == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int j = 0; j < DPR; ++j) acc[j] *= alpha;
+        m_run = m_new;
+      }
+      // exp2(-inf - m) is 0 for finite m; m is -inf only while every score
+      // so far is -inf, and then the reference 0 avoids -inf - -inf.
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+
+      // --- P with the V scale folded in, rounded to bf16: B operand of PV
       float pv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int kb = 2 * kp + (j >> 2), i = j & 3;
-        const float p = exp2f(sc[kb][i] - m_run);
+        const float p = __builtin_amdgcn_exp2f(sc[j] - m_ref);
         l_run += p;
-        pv[j] = p * vsc[kb][i];
+        pv[j] = p * vsc[j];
       }
-      pb[kp] = u32x4_t{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
-                       f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
-    }
+      const u32x4_t pb = {f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
+                          f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
 
-    // --- PV on the matrix cores: V^T tile as the A operand
+      // --- V of keys outside the sequence may hold any bits (even NaN
+      //     codes): zero them so that P = 0 contributes exactly 0
+      uint32_t vv[8][T::VW];
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < T::VW; ++e) vv[j][e] = cur.v[kp][j][e];
+      if (!cur.full) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kb = 2 * kp + (j >> 2);
+          const bool ok = (t0 + 16 * kb + 4 * g4 + (j & 3) < t_end) && cur.blk_ok[kb];
+#pragma unroll
+          for (int e = 0; e < T::VW; ++e) vv[j][e] = ok ? vv[j][e] : 0u;
+        }
+      }
+
+      // --- PV on the matrix cores: V^T chunk as the A operand
 #pragma unroll
       for (int db = 0; db < DPR; ++db) {
         u32x4_t av;
@@ -308,62 +368,85 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
             const int k2 = byte & 2;  // byte pair (k2, k2+1)
             const uint32_t sel = (uint32_t)(k2 + 4) | ((uint32_t)k2 << 8) |
                                  ((uint32_t)(k2 + 5) << 16) | ((uint32_t)(k2 + 1) << 24);
-            const uint32_t x = byte_perm(cur.v[kp][j0][wsel], cur.v[kp][j1][wsel], sel);
+            const uint32_t x = byte_perm(vv[j0][wsel], vv[j1][wsel], sel);
             av[jp] = e4m3x2_to_bf16x2(x, (byte & 1) != 0);
           } else {
             const int e = db >> 1;
             const uint32_t sel = (db & 1) ? 0x03020706u : 0x01000504u;
-            av[jp] = byte_perm(cur.v[kp][j0][e], cur.v[kp][j1][e], sel);
+            av[jp] = byte_perm(vv[j0][e], vv[j1][e], sel);
           }
         }
-        acc[db] = mfma_16x16x32_bf16(av, pb[kp], acc[db]);
+        acc[db] = mfma_16x16x32_bf16(av, pb, acc[db]);
       }
     }
-    if (more) cur = nxt;
+  };
+
+  // Tiles are dealt round-robin to the waves.  Two register buffers
+  // alternate (no copy between them, so no wait is forced on the prefetch):
+  // the loads of the next tile are in flight while the current one is
+  // computed.
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  T buf0, buf1;
+  if (wave < n_tiles)
+    load_tile<MODE, D>(buf0, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane);
+  for (int tile = wave; tile < n_tiles; tile += 2 * kWaves) {
+    const int t0 = t_begin + tile * kTile;
+    if (tile + kWaves < n_tiles)
+      load_tile<MODE, D>(buf1, a, lo, t0 + kWaves * kTile, t_end, tab, e_base, h, lane);
+    compute(buf0, t0);
+    if (tile + kWaves >= n_tiles) break;
+    if (tile + 2 * kWaves < n_tiles)
+      load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane);
+    compute(buf1, t0 + kWaves * kTile);
   }
 
-  // --- normaliser of head c: sum the four lane groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
-  // --- merge the waves of the work-group (power-of-two weights)
-  if (g4 == 0) {
-    s_m[wave][c] = m_run;
-    s_l[wave][c] = l_run;
-  }
-  __syncthreads();
-  float m_star = -INFINITY;
+  // --- merge the waves of the work-group: one barrier.  Each wave leaves
+  //     its reference, its four lane-group shares of l and its accumulator
+  //     (relative to its own reference) in LDS; then every thread combines
+  //     the waves for its outputs with power-of-two weights.
+  s_l[wave][g4][c] = l_run;
+  if (g4 == 0) s_m[wave][c] = m_run;
+  if (c < G) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) m_star = fmaxf(m_star, s_m[w][c]);
-  const float wgt = (m_run == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run - m_star));
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t lo4, hi4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f32x4_t lo, hi;
+      for (int db = 0; db < 4; ++db) lo4[db] = acc[db][i];
+      *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][DPR * (4 * g4 + i)]) = lo4;
+      if constexpr (DPR == 8) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) lo[db] = acc[db][i] * wgt;
-    *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][DPR * (4 * g4 + i)]) = lo;
-    if constexpr (DPR == 8) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) hi[db] = acc[4 + db][i] * wgt;
-      *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][DPR * (4 * g4 + i) + 4]) = hi;
+        for (int db = 0; db < 4; ++db) hi4[db] = acc[4 + db][i];
+        *reinterpret_cast<f32x4_t*>(&s_acc[wave][c][DPR * (4 * g4 + i) + 4]) = hi4;
+      }
     }
   }
   __syncthreads();
   for (int idx = 4 * threadIdx.x; idx < G * D; idx += 4 * blockDim.x) {
     const int g = idx / D, d = idx % D;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += *reinterpret_cast<const f32x4_t*>(&s_acc[w][g][d]);
-    *reinterpret_cast<f32x4_t*>(pacc + idx) = sum;
-  }
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    float lsum = 0.0f;
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, s_m[w][g]);
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (s_m[w][g] != -INFINITY) lsum += ldexpf(s_l[w][g], (int)(s_m[w][g] - ms));
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][g];
+      if (mw == -INFINITY) continue;  // a wave without keys
+      sum += ldexpf(1.0f, (int)(mw - ms)) * *reinterpret_cast<const f32x4_t*>(&s_acc[w][g][d]);
+    }
+    *reinterpret_cast<f32x4_t*>(pacc + idx) = sum;
+  }
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    float ms = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, s_m[w][g]);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][g];
+      if (mw == -INFINITY) continue;
+      const float lw = (s_l[w][0][g] + s_l[w][1][g]) + (s_l[w][2][g] + s_l[w][3][g]);
+      lsum += ldexpf(lw, (int)(mw - ms));
+    }
     pml[2 * g] = ms;
     pml[2 * g + 1] = lsum;
   }
@@ -440,7 +523,7 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, hipStream_t stream) {
   DecodeArgs a{c.k, c.v, c.ks, c.vs, c.table, q, seq_lens, part_acc, part_ml,
-               c_scale, c.hkv, group, c.bs, c.mbps, chunk, n_splits};
+               c_scale, c.hkv, group, c.bs, c.mbps, chunk, n_splits, c.num_blocks};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   switch (c.mode) {
     case kK8V8: launch_partial_mode<kK8V8>(c, a, n_wg, stream); break;

@@ -13,6 +13,8 @@ struct CacheView {
   int hkv;    // KV heads
   int d;      // head_dim, 64 or 128
   int mbps;   // block-table row length
+  int num_seqs;    // block-table rows
+  int num_blocks;  // blocks in the cache
   void* k;
   void* v;
   float* ks;
@@ -37,7 +39,7 @@ hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_split
 
 hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
                           const int32_t* cu_q, const int32_t* q_pos0,
-                          const int32_t* seq_lens, int batch, int max_q_len,
+                          const int32_t* seq_lens, int batch, int total_q, int max_q_len,
                           float c_scale, float* out, hipStream_t stream);
 
 }  // namespace fp8kv

@@ -23,11 +23,10 @@
 // rescale an exact power of two.
 //
 // LDS reuse: tile j is written into buffer j & 1 before the barrier of
-// iteration j and read after it.  Buffer j & 1 was last read during
-// iteration j - 2's compute... more precisely: iteration j + 1 writes buffer
-// (j + 1) & 1, which was read in iteration j - 1; every wave has left
-// iteration j - 1 once it passes the barrier of iteration j, which precedes
-// that write in program order.  One barrier per tile is therefore enough.
+// iteration j and read after it.  Iteration j + 1 writes buffer (j + 1) & 1,
+// which was last read in iteration j - 1; every wave has left iteration j - 1
+// once it passes the barrier of iteration j, which precedes that write in
+// program order.  One barrier per tile is therefore enough.
 #include "device.h"
 #include "launch.h"
 
@@ -50,6 +49,8 @@ struct PrefillArgs {
   int bs;
   int mbps;
   int n_qt;  // query tiles per sequence (ceil(max_q_len / 64))
+  int total_q;
+  int num_blocks;
 };
 
 constexpr int kPWaves = 4;
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 s_v[2][kKT][S::LD];
   __shared__ float s_ks[2][kKT];
   __shared__ float s_vs[2][kKT];
+  __shared__ float s_ok[2][kKT];  // 1: the key's block id is valid, 0: key not read
 
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid >> 6);
@@ -92,13 +94,16 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_kernel(PrefillArgs a) {
   const int b = rest / a.n_qt;
   const int hk = h / a.group;
 
-  const int q_begin = a.cu_q[b];
-  const int n_q = a.cu_q[b + 1] - q_begin;
+  // Device data is clamped so that no access leaves the buffers: query rows
+  // stay inside [0, total_q), lengths inside the block-table capacity.
+  const int q_begin = min(max(a.cu_q[b], 0), a.total_q);
+  const int q_end = min(max(a.cu_q[b + 1], q_begin), a.total_q);
+  const int n_q = min(q_end - q_begin, a.n_qt * kQT);
   if (qt * kQT >= n_q) return;
   const int pos0 = a.q_pos0[b];
-  const int seq_len = a.seq_lens[b];
+  const int seq_len = min(max(a.seq_lens[b], 0), a.mbps * a.bs);
   const int last_q = min(qt * kQT + kQT, n_q) - 1;
-  const int kv_end = min(seq_len, pos0 + last_q + 1);  // keys past the tile's last query are skipped
+  const int kv_end = max(0, min(seq_len, pos0 + last_q + 1));  // keys past the last query: skipped
 
   // query row of this lane and its position (-1: padding row, sees nothing)
   const int qrow = qt * kQT + 16 * wave + c;
@@ -126,20 +131,24 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_kernel(PrefillArgs a) {
   // staging: thread -> (key tid / 4, quarter tid % 4 of the row)
   const int skey = tid >> 2, spart = tid & 3;
   u32x4_t kreg[S::KW], vreg[S::VW];
-  float ksreg = 0.0f, vsreg = 0.0f;
+  float ksreg = 0.0f, vsreg = 0.0f, okreg = 0.0f;
   auto load_tile = [&](int t0) {
     const int t = min(t0 + skey, kv_end - 1);
     const int blk = a.table[tab_row + t / a.bs];
-    const int64_t row = ((int64_t)blk * a.bs + t % a.bs) * a.hkv + hk;
+    const bool ok = (unsigned)blk < (unsigned)a.num_blocks;  // else: key not read
+    const int64_t row = ((int64_t)(ok ? blk : 0) * a.bs + t % a.bs) * a.hkv + hk;
     const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * S::KBYTES + spart * (S::KBYTES / 4);
     const uint8_t* vp = static_cast<const uint8_t*>(a.v) + row * S::VBYTES + spart * (S::VBYTES / 4);
 #pragma unroll
-    for (int i = 0; i < S::KW; ++i) kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
+    for (int i = 0; i < S::KW; ++i)
+      kreg[i] = ok ? reinterpret_cast<const u32x4_t*>(kp)[i] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < S::VW; ++i) vreg[i] = reinterpret_cast<const u32x4_t*>(vp)[i];
+    for (int i = 0; i < S::VW; ++i)
+      vreg[i] = ok ? reinterpret_cast<const u32x4_t*>(vp)[i] : u32x4_t{0u, 0u, 0u, 0u};
     if (spart == 0) {
-      ksreg = S::K8 ? a.ks[row] : 1.0f;
-      vsreg = S::V8 ? a.vs[row] : 1.0f;
+      ksreg = (S::K8 && ok) ? a.ks[row] : 1.0f;
+      vsreg = (S::V8 && ok) ? a.vs[row] : 1.0f;
+      okreg = ok ? 1.0f : 0.0f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -179,6 +188,7 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_kernel(PrefillArgs a) {
     if (spart == 0) {
       s_ks[buf][skey] = ksreg;
       s_vs[buf][skey] = vsreg;
+      s_ok[buf][skey] = okreg;
     }
   };
 
@@ -210,11 +220,12 @@ __global__ __launch_bounds__(64 * kPWaves) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const f32x4_t ksv = *reinterpret_cast<const f32x4_t*>(&s_ks[buf][16 * kb + 4 * g4]);
+      const f32x4_t okv = *reinterpret_cast<const f32x4_t*>(&s_ok[buf][16 * kb + 4 * g4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * kb + 4 * g4 + i;
         float s = S::K8 ? (sacc[kb][i] * ksv[i]) * a.c_scale : sacc[kb][i] * a.c_scale;
-        s = (t <= qpos && t < kv_end) ? s : -INFINITY;
+        s = (t <= qpos && t < kv_end && okv[i] != 0.0f) ? s : -INFINITY;
         sc[kb][i] = s;
         tmax = fmaxf(tmax, s);
       }
@@ -307,11 +318,11 @@ static void launch_prefill_mode(int d, const PrefillArgs& a, unsigned n_wg, hipS
 
 hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
                           const int32_t* cu_q, const int32_t* q_pos0,
-                          const int32_t* seq_lens, int batch, int max_q_len,
+                          const int32_t* seq_lens, int batch, int total_q, int max_q_len,
                           float c_scale, float* out, hipStream_t stream) {
   const int n_qt = (max_q_len + kQT - 1) / kQT;
   PrefillArgs a{c.k, c.v, c.ks, c.vs, c.table, q, cu_q, q_pos0, seq_lens, out,
-                c_scale, c.hkv, group, c.bs, c.mbps, n_qt};
+                c_scale, c.hkv, group, c.bs, c.mbps, n_qt, total_q, c.num_blocks};
   const int64_t n_wg = (int64_t)batch * n_qt * c.hkv * group;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   switch (c.mode) {

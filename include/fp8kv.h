@@ -14,10 +14,14 @@
  * cleared) before returning, so it does not leak into later calls on the
  * stream.
  *
- * Device-side preconditions that are NOT checked (reading device memory
- * would need a synchronisation): every `pos`, `seq_idx`, `seq_lens` entry is
- * in range for the cache and block table, the block-table entries a sequence
- * uses are valid block ids, and inputs are finite.
+ * Device-side data (positions, sequence indices, lengths, block-table
+ * entries) cannot be checked on the host without a synchronisation.  The
+ * kernels therefore guard every index they read: an append row whose
+ * sequence index, position or block id is out of range is not written, a
+ * length is clamped to the block-table capacity, and a key whose block id is
+ * out of range is not read (it does not take part in the attention).  The
+ * results for such inputs are unspecified but no access leaves the buffers
+ * the descriptor describes.  Inputs must be finite.
  *
  * Sources (page titles as published):
  *   [SKILL] "kadirnar/kernel-agent/fp8-kv-cache": sections "Storage"
@@ -69,8 +73,8 @@ typedef enum {
  *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 only
  *                   (NULL otherwise)
  *   v_scale         same shape, K8V8 and K16V8 (NULL for BF16)
- *   block_table     int32 [batch][max_blocks_per_seq]; token t of sequence b
- *                   is slot t % block_size of block
+ *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
+ *                   b is slot t % block_size of block
  *                   block_table[b * max_blocks_per_seq + t / block_size]
  * A contiguous cache [B][T][Hkv][D] is block_size = T with block_table[b] = b.
  * Requirements: head_dim 64 or 128; block_size a multiple of 16; k, v 16-byte
@@ -83,6 +87,7 @@ typedef struct fp8kv_cache {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t max_blocks_per_seq;
+  int32_t num_seqs;            /* rows of block_table */
   void* k;
   void* v;
   float* k_scale;
@@ -137,8 +142,13 @@ size_t fp8kv_decode_workspace_bytes(const fp8kv_cache* cache, int32_t batch,
  *   seq_lens     device int32 [batch], 0 <= seq_lens[b] <= max_seq_len
  *   part_acc     device fp32 [batch][num_kv_heads][n_splits][G][head_dim]
  *   part_ml      device fp32 [batch][num_kv_heads][n_splits][G][2] = (M, l)
- * chunk_tokens must be a positive multiple of 256; n_splits >=
- * ceil(max_seq_len / chunk_tokens).  gqa_group in 1..16.
+ * chunk_tokens must be a positive multiple of 64 and a split may span at
+ * most 64 blocks: with g = gcd(chunk_tokens, block_size),
+ * (block_size - g + chunk_tokens - 16) / block_size <= 63.  This holds for
+ * every chunk_tokens <= 64 * block_size that block_size divides or that
+ * divides block_size, and for every plan fp8kv_decode_plan returns;
+ * otherwise FP8KV_ERR_INVALID.  n_splits >= ceil(max_seq_len / chunk_tokens).
+ * gqa_group in 1..16.
  */
 int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q,
                          int32_t gqa_group, const int32_t* seq_lens,
@@ -177,7 +187,8 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q,
  * Per row the result equals decode attention over its visible keys; a row
  * with no visible key outputs 0.
  *   q        device bf16 [total_q][num_kv_heads * gqa_group][head_dim]
- *   cu_q     device int32 [batch + 1], cu_q[0] = 0, non-decreasing
+ *   cu_q     device int32 [batch + 1], cu_q[0] = 0, non-decreasing, at most
+ *            total_q (rows outside [0, total_q) are neither read nor written)
  *   q_pos0, seq_lens  device int32 [batch]
  *   max_q_len  >= every cu_q[b+1] - cu_q[b]
  *   out      device fp32 [total_q][num_kv_heads * gqa_group][head_dim]
@@ -185,8 +196,8 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q,
 int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q,
                   int32_t gqa_group, const int32_t* cu_q,
                   const int32_t* q_pos0, const int32_t* seq_lens,
-                  int32_t batch, int32_t max_q_len, float sm_scale,
-                  float* out, void* stream);
+                  int32_t batch, int32_t total_q, int32_t max_q_len,
+                  float sm_scale, float* out, void* stream);
 
 /* Static description of a status code. */
 const char* fp8kv_strerror(int status);

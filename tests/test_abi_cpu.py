@@ -49,7 +49,7 @@ def test_strerror():
 
 def _desc(**kw):
     base = dict(mode=0, num_blocks=4, block_size=16, num_kv_heads=2, head_dim=128,
-                max_blocks_per_seq=4, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
+                max_blocks_per_seq=4, num_seqs=16, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
                 block_table=FAKE)
     base.update(kw)
     return CacheDesc(**base)
@@ -61,6 +61,7 @@ BAD_CACHES = [
     (dict(block_size=8), -1),
     (dict(block_size=0), -1),
     (dict(num_kv_heads=0), -1),
+    (dict(num_seqs=0), -1),
     (dict(k=None), -1),
     (dict(k=FAKE + 4), -1),          # codes must be 16-byte aligned
     (dict(k_scale=None), -1),        # K8V8 needs both scales
@@ -100,7 +101,8 @@ def test_decode_plan():
     d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
     assert _plan(d, 16, 8, 2048) == (0, 256, 8)
     # paged B64 x 8 KV heads up to 32768 tokens: longer splits, bounded grid
-    d = _desc(num_blocks=70000, block_size=16, num_kv_heads=8, max_blocks_per_seq=2048)
+    d = _desc(num_blocks=70000, block_size=16, num_kv_heads=8, max_blocks_per_seq=2048,
+              num_seqs=64)
     r, c, s = _plan(d, 64, 4, 32768)
     assert r == 0 and c == 1024 and s == 32
     assert _plan(d, 64, 17, 32768)[0] == -4
@@ -130,6 +132,16 @@ def test_decode_rejects_bad_arguments():
     assert lib.fp8kv_decode_partial(*args, 100, 32, FAKE, FAKE, None) == -1
     assert lib.fp8kv_decode_partial(*args, 256, 7, FAKE, FAKE, None) == -1
     assert lib.fp8kv_decode_partial(*args, 256, 8, FAKE + 4, FAKE, None) == -1
+    small = _desc(num_blocks=16, block_size=16, max_blocks_per_seq=128)
+    assert lib.fp8kv_decode_partial(ctypes.byref(small), FAKE, 8, FAKE, 16, 2048, 0.1,
+                                    2048, 1, FAKE, FAKE, None) == -1   # > 64 blocks a split
+    # a chunk <= 64 * block_size whose splits start inside a block can still
+    # reach 65 blocks (block_size 112, chunk 7104: split 1 starts at slot 48)
+    odd = _desc(num_blocks=16, block_size=112, max_blocks_per_seq=200)
+    assert lib.fp8kv_decode_partial(ctypes.byref(odd), FAKE, 8, FAKE, 16, 14208, 0.1,
+                                    7104, 2, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_plan(ctypes.byref(d), 17, 8, 2048, ctypes.byref(ctypes.c_int32()),
+                                 ctypes.byref(ctypes.c_int32())) == -1  # batch > table rows
     # merge shape checks
     assert lib.fp8kv_decode_merge(4, 2, 17, 128, 4, FAKE, FAKE, FAKE, None) == -4
     assert lib.fp8kv_decode_merge(4, 2, 8, 96, 4, FAKE, FAKE, FAKE, None) == -4
@@ -140,9 +152,39 @@ def test_decode_rejects_bad_arguments():
 def test_prefill_rejects_bad_arguments():
     lib = binding.lib()
     d = _desc()
-    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 17, FAKE, FAKE, FAKE, 1, 64, 0.1,
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 17, FAKE, FAKE, FAKE, 1, 64, 64, 0.1,
                              FAKE, None) == -4
-    assert lib.fp8kv_prefill(ctypes.byref(d), None, 8, FAKE, FAKE, FAKE, 1, 64, 0.1,
+    assert lib.fp8kv_prefill(ctypes.byref(d), None, 8, FAKE, FAKE, FAKE, 1, 64, 64, 0.1,
                              FAKE, None) == -1
-    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 0, 64, 0.1,
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 1, -1, 64, 0.1,
+                             FAKE, None) == -1
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 17, 64, 64, 0.1,
+                             FAKE, None) == -1   # batch > table rows
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 0, 64, 64, 0.1,
                              FAKE, None) == 0
+
+
+def _max_blocks_spanned(chunk, bs):
+    """Brute force: most block-table entries a split touches (its keys
+    [s*chunk, (s+1)*chunk) in 16-key sub-blocks); the start offsets into a
+    block repeat after bs splits, so those cover every case."""
+    return max((s * chunk + chunk - 16) // bs - (s * chunk) // bs + 1 for s in range(bs))
+
+
+def test_split_window_rule_matches_brute_force():
+    """Every (block_size, chunk) whose splits can touch more than 64 blocks is
+    rejected, and every plan the library chooses touches at most 64."""
+    lib = binding.lib()
+    for bs in range(16, 1025, 16):
+        for chunk in range(64, 64 * bs + 1, 64):
+            if _max_blocks_spanned(chunk, bs) <= 64:
+                continue
+            d = _desc(num_blocks=16, block_size=bs, max_blocks_per_seq=4096)
+            st = lib.fp8kv_decode_partial(ctypes.byref(d), FAKE, 8, FAKE, 16, chunk, 0.1,
+                                          chunk, 1, FAKE, FAKE, None)
+            assert st == -1, (bs, chunk)
+        d = _desc(num_blocks=16, block_size=bs, num_kv_heads=8,
+                  max_blocks_per_seq=(1 << 20) // bs, num_seqs=64)
+        for L in (1, 300, 5000, (1 << 20) // bs * bs):
+            r, c, s = _plan(d, 64, 4, L)
+            assert r == 0 and _max_blocks_spanned(c, bs) <= 64, (bs, L, c)
