@@ -2,9 +2,12 @@
 K16V8 vs BF16, on one MI355X.
 
 Step: one decode step of batch 16, 16 query / 2 KV heads (GQA 8), head_dim
-128, 2048 cached keys per sequence (e4m3 K/V, N(0,1) with 2 % x10 outliers):
-  fp8kv_append (one new token per sequence, written at position 2047)
-  fp8kv_decode_partial (split kernel) + fp8kv_decode_merge (merge kernel).
+128, 2048 keys per sequence (e4m3 K/V, N(0,1) with 2 % x10 outliers):
+  fp8kv_decode_append_partial: the split kernel, which also quantises and
+    stores each sequence's new token (position 2047) and attends it;
+  fp8kv_decode_merge: the merge kernel.
+The same step as three kernels (fp8kv_append, fp8kv_decode_partial,
+fp8kv_decode_merge) is timed too and reported as unfused_step_us.
 The headline value is K8V8 KV bytes per step / time per step, HBM-cold: the
 step rotates over 64 copies of the cache (> 1 GB, larger than the 256 MB
 Infinity Cache), so no copy is cache-resident when it is read.  All steps of
@@ -93,53 +96,70 @@ class DecodeBench:
         self.graph = None
 
     def split(self, i: int):
+        """The step's first kernel: fused append of the new token + split
+        partials."""
         w = self.w
-        self.binding.fp8kv_decode_partial(self.caches[i % len(self.caches)], self.q, w.group,
-                                          self.lens, self.max_len, w.sm_scale, self.chunk,
-                                          self.splits, self.pacc, self.pml)
+        self.binding.fp8kv_decode_append_partial(
+            self.caches[i % len(self.caches)], self.k_new, self.v_new, self.q, w.group,
+            self.lens, self.max_len, w.sm_scale, self.chunk, self.splits, self.pacc, self.pml)
 
     def step(self, i: int, ev=None):
+        """One decode step: append each sequence's new token (fused into the
+        split kernel), split partials, merge."""
         b, w = self.binding, self.w
-        c = self.caches[i % len(self.caches)]
         if ev: ev[0].record()
-        b.fp8kv_append(c, self.k_new, self.v_new, self.seq_idx, self.pos)
+        self.split(i)
         if ev: ev[1].record()
-        b.fp8kv_decode_partial(c, self.q, w.group, self.lens, self.max_len, w.sm_scale,
-                               self.chunk, self.splits, self.pacc, self.pml)
-        if ev: ev[2].record()
         b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
                              self.pacc, self.pml, self.out)
-        if ev: ev[3].record()
+        if ev: ev[2].record()
+
+    def step_unfused(self, i: int):
+        """The same step as three kernels: append, split, merge."""
+        b, w = self.binding, self.w
+        c = self.caches[i % len(self.caches)]
+        b.fp8kv_append(c, self.k_new, self.v_new, self.seq_idx, self.pos)
+        b.fp8kv_decode_partial(c, self.q, w.group, self.lens, self.max_len, w.sm_scale,
+                               self.chunk, self.splits, self.pacc, self.pml)
+        b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
+                             self.pacc, self.pml, self.out)
+
+    def _graph(self, fn):
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(self.copies):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
 
     def capture(self):
         torch = self.torch
-        self.step(0)  # eager call first: the library's one-time device check
+        self.step(0)  # eager calls first: the library's one-time device check
+        self.step_unfused(0)
         torch.cuda.synchronize()
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            for i in range(self.copies):
-                self.step(i)
+        self.graph = self._graph(self.step)
+        self.split_graph = self._graph(self.split)
+        self.unfused_graph = self._graph(self.step_unfused)
+
+    def graph_avg_ms(self, graph, replays: int) -> float:
+        """Average time of one rotation entry of `graph` (ms), back to back."""
+        torch = self.torch
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        graph.replay()
         torch.cuda.synchronize()
-        self.split_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.split_graph):
-            for i in range(self.copies):
-                self.split(i)
+        t0.record()
+        for _ in range(replays):
+            graph.replay()
+        t1.record()
         torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / (replays * self.copies)
 
     def split_avg_ms(self, replays: int) -> float:
         """Average duration of one split-kernel launch: the split kernel alone
         over the rotation, back to back in a graph, between two events."""
-        torch = self.torch
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        self.split_graph.replay()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(replays):
-            self.split_graph.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (replays * self.copies)
+        return self.graph_avg_ms(self.split_graph, replays)
 
     def run(self, replays: int, kernel_events: bool = False):
         """Replay the rotation `replays` times between two events (ms).
@@ -158,7 +178,7 @@ class DecodeBench:
         t1.record()
         ev = None
         if kernel_events:
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                   for _ in range(self.copies)]
             for i in range(self.copies):
                 self.step(i, ev[i])
@@ -167,12 +187,12 @@ class DecodeBench:
         return t0.elapsed_time(t1)  # ms
 
     def kernel_ms(self):
-        """Mean per-launch durations (ms) of append, split and merge."""
+        """Mean per-launch durations (ms) of the split kernel (with the fused
+        append) and the merge kernel."""
         ev = self.events
-        app = [ev[i][0].elapsed_time(ev[i][1]) for i in range(self.copies)]
-        spl = [ev[i][1].elapsed_time(ev[i][2]) for i in range(self.copies)]
-        mrg = [ev[i][2].elapsed_time(ev[i][3]) for i in range(self.copies)]
-        return float(np.mean(app)), float(np.mean(spl)), float(np.mean(mrg))
+        spl = [ev[i][0].elapsed_time(ev[i][1]) for i in range(self.copies)]
+        mrg = [ev[i][1].elapsed_time(ev[i][2]) for i in range(self.copies)]
+        return float(np.mean(spl)), float(np.mean(mrg))
 
 
 def bench_decode(mode, w, steps, warmup, copies):
@@ -182,14 +202,15 @@ def bench_decode(mode, w, steps, warmup, copies):
     bench.run(max(1, math.ceil(warmup / copies)))
     ms = bench.run(reps, kernel_events=True)
     n_steps = reps * copies
-    app, spl, mrg = bench.kernel_ms()
+    spl, mrg = bench.kernel_ms()
     split_avg = bench.split_avg_ms(reps)
+    unfused = bench.graph_avg_ms(bench.unfused_graph, reps)
     step_ms = ms / n_steps
     res = {"ms_per_step": step_ms, "steps": n_steps, "kv_bytes": bench.kv_bytes,
            "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
-           "kernel_us_event_pairs": {"append": app * 1e3, "split": spl * 1e3,
-                                     "merge": mrg * 1e3},
+           "kernel_us_event_pairs": {"split_with_append": spl * 1e3, "merge": mrg * 1e3},
            "split_us": split_avg * 1e3,
+           "unfused_step_us": unfused * 1e3,
            "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
     res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
     return res, bench
@@ -346,21 +367,24 @@ def main():
                    "head_dim": w.head_dim, "cached_tokens": int(w.lens[0]),
                    "kv_format": "e4m3 + fp32 scale per (token, KV head)",
                    "cache_state": f"HBM-cold, rotating {args.copies} copies",
-                   "step": "append 1 token/seq + split kernel + merge kernel",
+                   "step": "split kernel with the append of 1 token/seq fused in + "
+                           "merge kernel",
                    "split_plan": head["split_plan"]},
         "us_per_step": head["ms_per_step"] * 1e3,
         "pct_roofline": head["pct_roofline"],
         "split_us": head["split_us"],
         "kernel_us_event_pairs": head["kernel_us_event_pairs"],
+        "unfused_step_us": head["unfused_step_us"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "decode_partial_kernel<K8V8,128>",
+                     "kernel": "decode_partial_kernel<K8V8,128,append>",
                      "bytes_per_launch": head["kv_bytes"],
                      "kernel_source_hash": khash},
         "cpu_baseline": cpu,
     }
     if extras:
-        keys = ("ms_per_step", "kv_gbs", "pct_roofline", "split_us", "kernel_us_event_pairs")
+        keys = ("ms_per_step", "kv_gbs", "pct_roofline", "split_us", "kernel_us_event_pairs",
+                "unfused_step_us")
         rec["modes"] = {"K8V8": {k: head[k] for k in keys}}
         for mode in ("K16V8", "BF16"):
             rec["modes"][mode] = {k: extras[mode][k] for k in keys}

@@ -27,7 +27,8 @@ FP8KV_ERR_UNSUPPORTED = -4
 # Every symbol include/fp8kv.h declares.
 EXPORTS = ("fp8kv_append", "fp8kv_decode_plan", "fp8kv_decode_workspace_bytes",
            "fp8kv_decode_partial", "fp8kv_decode_merge", "fp8kv_decode",
-           "fp8kv_prefill", "fp8kv_strerror")
+           "fp8kv_decode_append", "fp8kv_decode_append_partial", "fp8kv_prefill",
+           "fp8kv_strerror")
 
 
 class Fp8kvError(RuntimeError):
@@ -69,6 +70,10 @@ def lib() -> ctypes.CDLL:
             "fp8kv_decode_merge": (ctypes.c_int, [I32, I32, I32, I32, I32, P, P, P, P]),
             "fp8kv_decode": (ctypes.c_int, [C, P, I32, P, I32, I32, F, P, P,
                                             ctypes.c_size_t, P]),
+            "fp8kv_decode_append": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F, P, P,
+                                                   ctypes.c_size_t, P]),
+            "fp8kv_decode_append_partial": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F,
+                                                           I32, I32, P, P, P]),
             "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, I32, F, P, P]),
             "fp8kv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         }
@@ -198,6 +203,28 @@ def fp8kv_decode(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
     _check(lib().fp8kv_decode(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
                               int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
                               _ptr(workspace), ws_bytes, _stream(stream)), "fp8kv_decode")
+
+
+def fp8kv_decode_append(cache: KVCache, k_new, v_new, q, gqa_group: int, seq_lens,
+                        max_seq_len: int, sm_scale: float, out, workspace, stream=None) -> None:
+    """Store each sequence's new token (k_new, v_new: fp32 [batch, Hkv, D]) at
+    position seq_lens[b] - 1, then decode over seq_lens[b] keys."""
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8kv_decode_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                     gqa_group, _ptr(seq_lens), int(seq_lens.shape[0]),
+                                     max_seq_len, sm_scale, _ptr(out), _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "fp8kv_decode_append")
+
+
+def fp8kv_decode_append_partial(cache: KVCache, k_new, v_new, q, gqa_group: int, seq_lens,
+                                max_seq_len: int, sm_scale: float, chunk_tokens: int,
+                                n_splits: int, part_acc, part_ml, stream=None) -> None:
+    d = cache.desc()
+    _check(lib().fp8kv_decode_append_partial(
+        ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), gqa_group, _ptr(seq_lens),
+        int(seq_lens.shape[0]), max_seq_len, sm_scale, chunk_tokens, n_splits, _ptr(part_acc),
+        _ptr(part_ml), _stream(stream)), "fp8kv_decode_append_partial")
 
 
 def fp8kv_prefill(cache: KVCache, q, gqa_group: int, cu_q, q_pos0, seq_lens,

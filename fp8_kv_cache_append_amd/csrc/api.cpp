@@ -168,10 +168,12 @@ size_t fp8kv_decode_workspace_bytes(const fp8kv_cache* cache, int32_t batch,
          sizeof(float);
 }
 
-int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
-                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
-                         float sm_scale, int32_t chunk_tokens, int32_t n_splits,
-                         float* part_acc, float* part_ml, void* stream) {
+namespace {
+
+int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new,
+                        const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens,
+                        int32_t batch, int32_t max_seq_len, float sm_scale, int32_t chunk_tokens,
+                        int32_t n_splits, float* part_acc, float* part_ml, void* stream) {
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
@@ -184,10 +186,33 @@ int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q, int32_t gq
   if (!aligned(q, 16) || !aligned(seq_lens, 4) || !aligned(part_acc, 16) ||
       !aligned(part_ml, 8))
     return FP8KV_ERR_INVALID;
+  if ((k_new == nullptr) != (v_new == nullptr)) return FP8KV_ERR_INVALID;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return FP8KV_ERR_INVALID;
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(fp8kv::launch_decode_partial(
       view_of(cache), q, gqa_group, seq_lens, batch, log2_scale(sm_scale), chunk_tokens,
-      n_splits, part_acc, part_ml, static_cast<hipStream_t>(stream)));
+      n_splits, part_acc, part_ml, k_new, v_new, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
+                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                         float sm_scale, int32_t chunk_tokens, int32_t n_splits,
+                         float* part_acc, float* part_ml, void* stream) {
+  return decode_partial_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch,
+                             max_seq_len, sm_scale, chunk_tokens, n_splits, part_acc, part_ml,
+                             stream);
+}
+
+int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
+                                const float* v_new, const uint16_t* q, int32_t gqa_group,
+                                const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                float sm_scale, int32_t chunk_tokens, int32_t n_splits,
+                                float* part_acc, float* part_ml, void* stream) {
+  if (batch > 0 && n_splits > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
+  return decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
+                             sm_scale, chunk_tokens, n_splits, part_acc, part_ml, stream);
 }
 
 int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
@@ -207,9 +232,12 @@ int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
                                                   static_cast<hipStream_t>(stream)));
 }
 
-int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
-                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
-                 float* out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new,
+                const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
+                int32_t max_seq_len, float sm_scale, float* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int32_t chunk = 0, splits = 0;
   int st = fp8kv_decode_plan(cache, batch, gqa_group, max_seq_len, &chunk, &splits);
   if (st != FP8KV_OK) return st;
@@ -224,11 +252,29 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
   if (!out || !aligned(out, 16)) return FP8KV_ERR_INVALID;
   if (splits > 0 && (!q || !seq_lens || !aligned(q, 16) || !aligned(seq_lens, 4)))
     return FP8KV_ERR_INVALID;
-  st = fp8kv_decode_partial(cache, q, gqa_group, seq_lens, batch, max_seq_len, sm_scale, chunk,
-                            splits, part_acc, part_ml, stream);
+  st = decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
+                           sm_scale, chunk, splits, part_acc, part_ml, stream);
   if (st != FP8KV_OK) return st;
   return fp8kv_decode_merge(batch, cache->num_kv_heads, gqa_group, cache->head_dim, splits,
                             part_acc, part_ml, out, stream);
+}
+
+}  // namespace
+
+int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
+                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                 float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, stream);
+}
+
+int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new, const float* v_new,
+                        const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens,
+                        int32_t batch, int32_t max_seq_len, float sm_scale, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && max_seq_len > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
+  return decode_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, stream);
 }
 
 int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,

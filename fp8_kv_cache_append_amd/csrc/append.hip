@@ -7,12 +7,9 @@
 // Mapping: a row of D fp32 values is read by D/4 lanes with one 16-byte load
 // each (32 lanes for D = 128, 16 for D = 64), so a wave covers the K row and
 // the V row of one or two (token, head) pairs and every HBM access is a full,
-// coalesced 16-byte-per-lane transaction.  The row maximum is a butterfly
-// over those lanes.  The quotient x / scale uses the correctly rounded fp32
-// division (no reciprocal, no fast-math) so the codes are bit-exact with the
-// definition; v_cvt_pk_fp8_f32 rounds to nearest even onto OCP e4m3fn, and
-// the explicit clamp to +-448 makes rows whose scale is an fp32 subnormal
-// saturate instead of overflowing.
+// coalesced 16-byte-per-lane transaction.  The arithmetic (row_amax,
+// e4m3_codes4, bf16x4 in device.h) is shared with the fused append of the
+// split-KV decode, so both write the same bytes.
 #include "device.h"
 #include "launch.h"
 
@@ -62,28 +59,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const bool quantise = (MODE == kK8V8) || (MODE == kK16V8 && is_v);
   if (quantise) {
-    float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-#pragma unroll
-    for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const float scale = amax / kE4M3Max;  // correctly rounded fp32 division
-    uint32_t codes = 0;
-    if (scale != 0.0f) {
-      const float y0 = fminf(fmaxf(x.x / scale, -kE4M3Max), kE4M3Max);
-      const float y1 = fminf(fmaxf(x.y / scale, -kE4M3Max), kE4M3Max);
-      const float y2 = fminf(fmaxf(x.z / scale, -kE4M3Max), kE4M3Max);
-      const float y3 = fminf(fmaxf(x.w / scale, -kE4M3Max), kE4M3Max);
-      codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-      codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
-    }
+    const float scale = row_amax<kLanesPerRow>(x) / kE4M3Max;  // correctly rounded
     uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
-    *reinterpret_cast<uint32_t*>(dst) = codes;
+    *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x, scale);
     if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
   } else {
-    u32x2_t w;
-    w[0] = f32x2_to_bf16x2(x.x, x.y);
-    w[1] = f32x2_to_bf16x2(x.z, x.w);
     uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
-    *reinterpret_cast<u32x2_t*>(dst) = w;
+    *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x);
   }
 }
 

@@ -48,6 +48,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* part_acc;
   float* part_ml;
+  const float* k_new;  // fused append: the step's new K/V rows, fp32
+  const float* v_new;  //   [batch][hkv][D]; unused by the plain decode
   float c_scale;  // sm_scale * log2(e)
   int hkv;
   int group;
@@ -180,7 +182,13 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-template <int MODE, int D>
+// APPEND: the decode step's new token of sequence b (fp32 rows k_new[b],
+// v_new[b]) sits at position seq_lens[b] - 1.  The work-group whose split
+// holds that position quantises it by the storage rule, writes it to its
+// cache slot (the only write of that slot) and substitutes it for the slot's
+// previous bytes in the registers of the tile being attended, so the append
+// costs no kernel of its own and no extra memory round trip.
+template <int MODE, int D, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
   using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
@@ -192,6 +200,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][4][kMaxGroup];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kMaxGroup][D];
+  // fused append: the new token's K bytes, V bytes (each at most 2D) and
+  // scales, in cache layout, for the wave that attends it
+  __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -222,6 +233,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       qb[kc] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  // Fused append: lanes [0, D/4) hold four values of the K row, lanes
+  // [D/4, D/2) four of the V row (loaded with the first round trip).
+  constexpr int kLR = D / 4;  // lanes per row
+  float4 xnew = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (APPEND) {
+    if (lane < 2 * kLR)
+      xnew = *reinterpret_cast<const float4*>((lane < kLR ? a.k_new : a.v_new) +
+                                              ((int64_t)b * a.hkv + h) * D + 4 * (lane % kLR));
+  }
   const int t_end = min(min(max(len, 0), a.mbps * a.bs), t_begin + a.chunk);
 
   float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
@@ -244,6 +264,92 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
     lo.v[jj] = (uint32_t)((4 * g4 + jj) * a.hkv) * (D * T::VE) + DPR * T::VE * c;
+
+  // Fused append: the new token (position len - 1, only if it lies inside
+  // the block table) belongs to this split's tiles; the wave that attends it
+  // quantises and stores it and keeps its bytes in LDS for the substitution.
+  int pos_n = -1;  // wave-uniform; -1: this wave does not attend the new token
+  if constexpr (APPEND) {
+    const int p = len - 1;
+    if (len >= 1 && len <= a.mbps * a.bs && p >= t_begin && p < t_end &&
+        ((p - t_begin) / kTile) % kWaves == wave) {
+      pos_n = p;
+      const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
+      const bool is_v = lane >= kLR;
+      const bool quantise = kK8 || (kV8 && is_v);
+      const float scale = row_amax<kLR>(xnew) / kE4M3Max;
+      const int sub = lane % kLR;
+      if (lane < 2 * kLR) {
+        const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
+        const bool store = (unsigned)blk < (unsigned)a.num_blocks;  // else: key excluded
+        // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
+        uint32_t* img = s_new + (is_v ? D / 2 : 0);
+        if (quantise) {
+          const uint32_t codes = e4m3_codes4(xnew, scale);
+          img[sub] = codes;
+          if (store) {
+            uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
+            *reinterpret_cast<uint32_t*>(dst + 4 * sub) = codes;
+            if (sub == 0) const_cast<float*>(is_v ? a.vs : a.ks)[row] = scale;
+          }
+          if (sub == 0) s_new[D + (is_v ? 1 : 0)] = __float_as_uint(scale);
+        } else {
+          const u32x2_t w = bf16x4(xnew);
+          *reinterpret_cast<u32x2_t*>(img + 2 * sub) = w;
+          if (store) {
+            uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
+            *reinterpret_cast<u32x2_t*>(dst + 4 * sub) = w;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  pos_n = wave_uniform(pos_n);
+
+  // Substitute the new token for its slot's previous bytes in tile r
+  // (t0 <= pos_n < t0 + 64): K of token c in lanes (*, c), V of token
+  // 4*g4 + jj in lanes (g4, *), scales in lane t.  Every register is written
+  // through a select: a store to the one matching element would index the
+  // arrays with a runtime value and move them to scratch memory.
+  auto patch = [&](T& r, int t0) __attribute__((always_inline)) {
+    const int tn = pos_n - t0, kbn = tn >> 4, cn = tn & 15;
+    const uint8_t* img = reinterpret_cast<const uint8_t*>(s_new);
+    u32x4_t nk[T::KRAW];
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p) {
+      const uint8_t* src = img + (64 * p + 16 * g4) * T::KE;
+      if (kK8) {
+        nk[p] = *reinterpret_cast<const u32x4_t*>(src);
+      } else {
+        nk[2 * p] = *reinterpret_cast<const u32x4_t*>(src);
+        nk[2 * p + 1] = *reinterpret_cast<const u32x4_t*>(src + 16);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bool sel = (c == cn) && (kb == kbn);
+#pragma unroll
+      for (int q = 0; q < T::KRAW; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.k[kb][q][e] = sel ? nk[q][e] : r.k[kb][q][e];
+    }
+    uint32_t nv[T::VW];
+    const uint32_t* vimg = s_new + D / 2 + (DPR * T::VE / 4) * c;
+#pragma unroll
+    for (int e = 0; e < T::VW; ++e) nv[e] = vimg[e];
+    const int jn = ((kbn & 1) << 2) | (cn & 3);
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool sel = (g4 == (cn >> 2)) && (kp == (kbn >> 1)) && (j == jn);
+#pragma unroll
+        for (int e = 0; e < T::VW; ++e) r.v[kp][j][e] = sel ? nv[e] : r.v[kp][j][e];
+      }
+    if (kK8) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
+    if (kV8) r.vs = (lane == tn) ? __uint_as_float(s_new[D + 1]) : r.vs;
+  };
 
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
   float l_run = 0.0f;       // this lane's share of the normaliser of head c
@@ -393,10 +499,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     const int t0 = t_begin + tile * kTile;
     if (tile + kWaves < n_tiles)
       load_tile<MODE, D>(buf1, a, lo, t0 + kWaves * kTile, t_end, tab, e_base, h, lane);
+    if (APPEND && pos_n >= t0 && pos_n < t0 + kTile) patch(buf0, t0);
     compute(buf0, t0);
     if (tile + kWaves >= n_tiles) break;
     if (tile + 2 * kWaves < n_tiles)
       load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane);
+    if (APPEND && pos_n >= t0 + kWaves * kTile && pos_n < t0 + (kWaves + 1) * kTile)
+      patch(buf1, t0 + kWaves * kTile);
     compute(buf1, t0 + kWaves * kTile);
   }
 
@@ -507,29 +616,39 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
-template <int MODE>
+template <int MODE, bool APPEND>
 static void launch_partial_mode(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                                 hipStream_t stream) {
   if (c.d == 128)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128>), dim3(n_wg), dim3(64 * kWaves), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND>), dim3(n_wg),
+                       dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64>), dim3(n_wg), dim3(64 * kWaves), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND>), dim3(n_wg),
+                       dim3(64 * kWaves), 0, stream, a);
+}
+
+template <bool APPEND>
+static void launch_partial_append(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
+                                  hipStream_t stream) {
+  switch (c.mode) {
+    case kK8V8: launch_partial_mode<kK8V8, APPEND>(c, a, n_wg, stream); break;
+    case kK16V8: launch_partial_mode<kK16V8, APPEND>(c, a, n_wg, stream); break;
+    default: launch_partial_mode<kBF16, APPEND>(c, a, n_wg, stream); break;
+  }
 }
 
 hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int group,
                                  const int32_t* seq_lens, int batch, float c_scale,
                                  int chunk, int n_splits, float* part_acc,
-                                 float* part_ml, hipStream_t stream) {
-  DecodeArgs a{c.k, c.v, c.ks, c.vs, c.table, q, seq_lens, part_acc, part_ml,
+                                 float* part_ml, const float* k_new, const float* v_new,
+                                 hipStream_t stream) {
+  DecodeArgs a{c.k, c.v, c.ks, c.vs, c.table, q, seq_lens, part_acc, part_ml, k_new, v_new,
                c_scale, c.hkv, group, c.bs, c.mbps, chunk, n_splits, c.num_blocks};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
-  switch (c.mode) {
-    case kK8V8: launch_partial_mode<kK8V8>(c, a, n_wg, stream); break;
-    case kK16V8: launch_partial_mode<kK16V8>(c, a, n_wg, stream); break;
-    default: launch_partial_mode<kBF16>(c, a, n_wg, stream); break;
-  }
+  if (k_new)
+    launch_partial_append<true>(c, a, n_wg, stream);
+  else
+    launch_partial_append<false>(c, a, n_wg, stream);
   return hipGetLastError();
 }
 

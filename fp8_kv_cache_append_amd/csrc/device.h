@@ -56,4 +56,37 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Storage rule of a (token, KV head) row ("kadirnar/kernel-agent/fp8-kv-cache",
+// section "Storage"), for a row of D values held four per lane by D/4
+// consecutive, aligned lanes.
+//
+// row_amax: max |x| over the row (a butterfly inside the lane group; exact).
+template <int LANES_PER_ROW>
+__device__ __forceinline__ float row_amax(float4 x) {
+  float m = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+#pragma unroll
+  for (int o = LANES_PER_ROW / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// Four codes of the row with scale = amax / 448: the correctly rounded fp32
+// quotient x / scale (no reciprocal, no fast math), clamped to +-448 so that a
+// row whose scale is an fp32 subnormal saturates, then rounded to nearest
+// even onto OCP e4m3fn by v_cvt_pk_fp8_f32.  A zero scale gives zero codes.
+__device__ __forceinline__ uint32_t e4m3_codes4(float4 x, float scale) {
+  if (scale == 0.0f) return 0u;
+  const float y0 = fminf(fmaxf(x.x / scale, -kE4M3Max), kE4M3Max);
+  const float y1 = fminf(fmaxf(x.y / scale, -kE4M3Max), kE4M3Max);
+  const float y2 = fminf(fmaxf(x.z / scale, -kE4M3Max), kE4M3Max);
+  const float y3 = fminf(fmaxf(x.w / scale, -kE4M3Max), kE4M3Max);
+  uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
+}
+
+// Four values rounded to bf16 (nearest even): the K row of the K16V8 control
+// and both rows of the BF16 control.
+__device__ __forceinline__ u32x2_t bf16x4(float4 x) {
+  return u32x2_t{f32x2_to_bf16x2(x.x, x.y), f32x2_to_bf16x2(x.z, x.w)};
+}
+
 }  // namespace fp8kv

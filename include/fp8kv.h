@@ -34,6 +34,8 @@
  *           softmax tile by tile), "NVIDIA Hopper" path 3 (K16/V8, the
  *           no-K-transform control), "Collect the profiler evidence" (dtype
  *           controls including K16/V16).
+ *   [FQ]    "Fused KV-cache quantization": "Latency analysis" (the
+ *           separate cache-write kernel is one part of the decode gap).
  *   [FA]    "03 . 8n - FA-style tiled prefill attention": sections 2.1
  *           (online softmax), 3.1 (64-token query tiles, GQA slicing,
  *           positions are data, causal mask) and 3.2/3.3 (a row with no
@@ -178,6 +180,40 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q,
                  int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
                  int32_t max_seq_len, float sm_scale, float* out,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode step with the append fused in ([SKILL] Storage; [FQ] Latency
+ * analysis): for every sequence b with 1 <= seq_lens[b] <= the block-table
+ * capacity, the step's new token (k_new[b], v_new[b]) is stored at position
+ * seq_lens[b] - 1 exactly as fp8kv_append stores it (same codes, scales and
+ * bf16 bytes; not written if that position's block id is out of range), and
+ * then attended with the rest of the sequence: the result equals
+ * fp8kv_append followed by fp8kv_decode, in the two kernels of the split-KV
+ * decode instead of three.  The slot is written by the work-group whose
+ * split holds it, so it must not lie in keys that another sequence of the
+ * same call attends (shared blocks must be full).
+ *   k_new, v_new  device fp32 [batch][num_kv_heads][head_dim], 16-byte aligned
+ * Other arguments and the workspace as for fp8kv_decode.
+ */
+int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new,
+                        const float* v_new, const uint16_t* q,
+                        int32_t gqa_group, const int32_t* seq_lens,
+                        int32_t batch, int32_t max_seq_len, float sm_scale,
+                        float* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * The first kernel of fp8kv_decode_append on its own: the fused append and
+ * the split partials, arguments as for fp8kv_decode_partial plus k_new and
+ * v_new; fp8kv_decode_merge completes the step.
+ */
+int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
+                                const float* v_new, const uint16_t* q,
+                                int32_t gqa_group, const int32_t* seq_lens,
+                                int32_t batch, int32_t max_seq_len,
+                                float sm_scale, int32_t chunk_tokens,
+                                int32_t n_splits, float* part_acc,
+                                float* part_ml, void* stream);
 
 /*
  * Causal prefill attention ([FA] 3.1): queries of sequence b are rows

@@ -149,6 +149,19 @@ def test_decode_rejects_bad_arguments():
     assert lib.fp8kv_decode_merge(0, 2, 8, 128, 4, None, None, None, None) == 0
 
 
+def test_decode_append_rejects_bad_arguments():
+    lib = binding.lib()
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    args = (FAKE, 8, FAKE, 16, 2048, 0.1, FAKE, FAKE, 10 ** 9, None)
+    assert lib.fp8kv_decode_append(ctypes.byref(d), None, FAKE, *args) == -1   # no K rows
+    assert lib.fp8kv_decode_append(ctypes.byref(d), FAKE, None, *args) == -1   # no V rows
+    assert lib.fp8kv_decode_append(ctypes.byref(d), FAKE + 4, FAKE, *args) == -1  # misaligned
+    assert lib.fp8kv_decode_append(ctypes.byref(d), FAKE, FAKE, FAKE, 8, FAKE, 16, 2048, 0.1,
+                                   FAKE, FAKE, 16, None) == -2                  # workspace
+    assert lib.fp8kv_decode_append(ctypes.byref(d), None, None, FAKE, 8, FAKE, 0, 0, 0.1,
+                                   FAKE, None, 0, None) == 0                    # empty batch
+
+
 def test_prefill_rejects_bad_arguments():
     lib = binding.lib()
     d = _desc()
