@@ -18,7 +18,10 @@ timed replays (see DecodeBench.run).
 
 Extra fields: the K16V8 and BF16 controls (same protocol), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
-the roofline of the split kernel and the CPU oracle as a baseline.
+the context sweep of the same shape at 77/512/2048/8192 keys in all three
+modes with the K8V8-vs-K16V8 break-even, the ragged batch-64 paged workload
+(32q/8kv, lengths 1024..32768, K8V8 and K16V8), the roofline of the split
+kernel and the CPU oracle as a baseline.
 """
 from __future__ import annotations
 
@@ -216,6 +219,113 @@ def bench_decode(mode, w, steps, warmup, copies):
     return res, bench
 
 
+def bench_sweep(steps, warmup, copies, head):
+    """The context sweep of the B16 16q/2kv D128 shape at 77, 512, 2048 and
+    8192 keys, all three modes, HBM-cold as the headline; the K8V8-vs-K16V8
+    break-even is the first length where the K8V8 step is faster (linear
+    interpolation of the step time over the swept lengths)."""
+    from fp8_kv_cache_append_amd import synth
+
+    table = {}
+    for tokens in (77, 512, 2048, 8192):
+        w = synth.decode_b16_gqa8_d128(tokens)
+        row = {}
+        for mode in ("K8V8", "K16V8", "BF16"):
+            if tokens == 2048 and mode == "K8V8":
+                r = head
+            else:
+                r, _ = bench_decode(mode, w, steps, warmup, copies)
+            row[mode] = {"us_per_step": r["ms_per_step"] * 1e3, "split_us": r["split_us"],
+                         "kv_gbs": r["kv_gbs"], "pct_roofline": r["pct_roofline"],
+                         "unfused_step_us": r["unfused_step_us"]}
+        row["K8V8_speedup_vs_K16V8"] = row["K16V8"]["us_per_step"] / row["K8V8"]["us_per_step"]
+        row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
+        table[str(tokens)] = row
+    lens = [77, 512, 2048, 8192]
+    diff = [table[str(t)]["K16V8"]["us_per_step"] - table[str(t)]["K8V8"]["us_per_step"]
+            for t in lens]
+    be = None
+    if diff[0] > 0:
+        be = f"<= {lens[0]}"
+    else:
+        for i in range(1, len(lens)):
+            if diff[i] > 0:
+                t0, t1, d0, d1 = lens[i - 1], lens[i], diff[i - 1], diff[i]
+                be = round(t0 + (t1 - t0) * (-d0) / (d1 - d0))
+                break
+    return {"tokens": table, "k8v8_vs_k16v8_break_even_tokens": be}
+
+
+def bench_ragged(mode, replays=20, steps=8):
+    """Batch 64, 32q/8kv, D128, lengths uniform in [1024, 32768], paged
+    16-token blocks behind a shuffled table, biased keys.  The cache (2.3 GB
+    K8V8, 3.4 GB K16V8) is far larger than the Infinity Cache, so one copy is
+    HBM-cold.  Filled from device-generated K/V of the same distributions."""
+    import torch
+    from fp8_kv_cache_append_amd import binding, synth
+    from fp8_kv_cache_append_amd.binding import KVCache
+
+    dev = "cuda"
+    w = synth.decode_b64_gqa4_ragged_paged()
+    bs, table, n_blocks = synth.block_layout(w)
+    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+    k_last, v_last = [], []
+    for b in range(w.batch):
+        n = int(w.lens[b])
+        k, v = synth.kv_sequence_device(w, b, dev)
+        seq = torch.full((n,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(n, dtype=torch.int32, device=dev)
+        binding.fp8kv_append(cache, k, v, seq, pos)
+        k_last.append(k[-1].clone())
+        v_last.append(v[-1].clone())
+        torch.cuda.synchronize()
+        del k, v, seq, pos
+    k_new, v_new = torch.stack(k_last).contiguous(), torch.stack(v_last).contiguous()
+    q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
+    q = torch.from_numpy(q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
+    max_len = int(w.lens.max())
+    chunk, splits = binding.fp8kv_decode_plan(cache, w.batch, w.group, max_len)
+    pacc = torch.empty((w.batch, w.kv_heads, splits, w.group, w.head_dim), device=dev)
+    pml = torch.empty((w.batch, w.kv_heads, splits, w.group, 2), device=dev)
+    out = torch.empty((w.batch, w.q_heads, w.head_dim), device=dev)
+
+    def split():
+        binding.fp8kv_decode_append_partial(cache, k_new, v_new, q, w.group, lens, max_len,
+                                            w.sm_scale, chunk, splits, pacc, pml)
+
+    def step():
+        split()
+        binding.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, splits, pacc,
+                                   pml, out)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(replays):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / (replays * steps)
+
+    step_us, split_us = timed(step), timed(split)
+    kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](w.head_dim)
+    return {"workload": w.name, "mode": mode, "us_per_step": step_us, "split_us": split_us,
+            "kv_bytes": kv_bytes, "kv_gbs": kv_bytes / (step_us * 1e-6) / 1e9,
+            "split_kv_gbs": kv_bytes / (split_us * 1e-6) / 1e9,
+            "pct_roofline": 100.0 * kv_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "split_plan": {"chunk_tokens": chunk, "n_splits": splits}}
+
+
 def bench_warm(mode, w, steps, copies):
     """The same graph of steps on one copy of the cache: L2/MALL-warm,
     labelled as such (it can exceed the HBM rate)."""
@@ -347,6 +457,9 @@ def main():
             extras[mode] = r
         extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
         extras["prefill"] = bench_prefill()
+        extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
+                                      args.copies, head)
+        extras["ragged"] = {m: bench_ragged(m) for m in ("K8V8", "K16V8")}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     rec = {
@@ -392,6 +505,8 @@ def main():
         rec["speedup_vs_k16v8"] = extras["K16V8"]["ms_per_step"] / head["ms_per_step"]
         rec["warm_l2_mall"] = extras["K8V8_warm"]
         rec["prefill"] = extras["prefill"]
+        rec["context_sweep"] = extras["sweep"]
+        rec["ragged_b64_paged"] = extras["ragged"]
     print(json.dumps(rec), flush=True)
 
 

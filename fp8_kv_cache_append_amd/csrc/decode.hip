@@ -10,10 +10,14 @@
 // and advances the online softmax tile by tile.  The unnormalised partial
 // (M, l, acc) goes to HBM; a second kernel merges the splits.
 //
-// Softmax reference.  M is an integer in log2 units (the running maximum of
-// the scores rounded up).  Every rescale 2^(M_old - M_new) is then an exact
-// power of two, and since bf16 rounding commutes with power-of-two scaling the
-// rounded P does not depend on how the keys are cut into tiles and splits.
+// Softmax reference.  M is an integer in log2 units.  Every rescale
+// 2^(M_old - M_new) is then an exact power of two, and since bf16 rounding
+// commutes with power-of-two scaling the rounded P does not depend on which
+// integer is used, nor on how the keys are cut into tiles and splits.  The
+// reference is set from the first scores seen (rounded up) and moves only
+// when a later maximum exceeds it by more than kLazy: p = 2^(s - M) then stays
+// below 2^kLazy, and the rescale of the accumulator, which would otherwise
+// follow almost every step, becomes rare.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, lane l = 16*g4 + c):
 //   QK   S^T[t][head] = K[t][:] . Q[head][:]  A = K tile (16 tokens x 32 d),
@@ -63,6 +67,7 @@ struct DecodeArgs {
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kMaxGroup = 16; // query heads per KV head (one MFMA column block)
+constexpr float kLazy = 8.0f; // log2 units the scores may exceed the reference by
 
 // Raw (still compressed) K/V of one 64-token tile in the registers of one
 // lane, the scales of the lane's own token (token t0 + lane) and the
@@ -88,8 +93,9 @@ struct TileRegs {
 // Per-lane byte offsets inside a 16-token sub-block; they do not depend on
 // the tile, so they are computed once per kernel.
 struct LaneOffsets {
-  uint32_t k;     // token c, d-piece of lane group g4
-  uint32_t v[4];  // tokens 4*g4 + jj, d = DPR*c
+  uint32_t k;        // token c, d-piece of lane group g4
+  uint32_t v;        // token 4*g4, d = DPR*c
+  uint32_t v_token;  // bytes from one token's row to the next (uniform)
 };
 
 // Issue the loads of the tile starting at token t0.  tab holds, in lane e,
@@ -156,7 +162,8 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int kb = 2 * kp + (j >> 2);
-      const uint8_t* src = static_cast<const uint8_t*>(a.v) + row0[kb] * (D * T::VE) + lo.v[j & 3];
+      const uint8_t* src = static_cast<const uint8_t*>(a.v) + row0[kb] * (D * T::VE) +
+                           (j & 3) * lo.v_token + lo.v;
       if constexpr (T::VW == 4) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
 #pragma unroll
@@ -189,7 +196,8 @@ __device__ __forceinline__ float max_over_groups(float x) {
 // previous bytes in the registers of the tile being attended, so the append
 // costs no kernel of its own and no extra memory round trip.
 template <int MODE, int D, bool APPEND>
-__global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
+void decode_partial_kernel(DecodeArgs a) {
   using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
@@ -200,6 +208,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][4][kMaxGroup];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kMaxGroup][D];
+  __shared__ u32x4_t s_q[KC][64];
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
   __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
@@ -223,24 +232,28 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int len = a.seq_lens[b];  // clamped below to the block-table capacity
   const int e_base = t_begin / a.bs;
   const int tab = a.table[(int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1)];
-  u32x4_t qb[KC];  // Q^T as the B operand of QK: lane (g4, c) holds head c's d-set
+  // Q^T, the B operand of QK, in LDS in operand order: s_q[kc][lane] is lane
+  // (g4, c)'s 16 bytes of head c for k-chunk kc.  Each wave loads a share.
   {
     const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
+    for (int kc = wave; kc < KC; kc += kWaves) {
       const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      qb[kc] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
+      s_q[kc][lane] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
   // Fused append: lanes [0, D/4) hold four values of the K row, lanes
-  // [D/4, D/2) four of the V row (loaded with the first round trip).
+  // [D/4, D/2) four of the V row, loaded with the first round trip.  Every
+  // lane loads (the lanes past D/2 repeat the first ones): a load under a
+  // lane condition would make the compiler wait for all later loads, tile
+  // data included, before the values can be used.
   constexpr int kLR = D / 4;  // lanes per row
   float4 xnew = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (APPEND) {
-    if (lane < 2 * kLR)
-      xnew = *reinterpret_cast<const float4*>((lane < kLR ? a.k_new : a.v_new) +
-                                              ((int64_t)b * a.hkv + h) * D + 4 * (lane % kLR));
+    const int l2 = lane & (2 * kLR - 1);
+    xnew = *reinterpret_cast<const float4*>((l2 < kLR ? a.k_new : a.v_new) +
+                                            ((int64_t)b * a.hkv + h) * D + 4 * (l2 % kLR));
   }
   const int t_end = min(min(max(len, 0), a.mbps * a.bs), t_begin + a.chunk);
 
@@ -261,59 +274,80 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 
   LaneOffsets lo;
   lo.k = (uint32_t)(c * a.hkv) * (D * T::KE) + 16 * T::KE * g4;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    lo.v[jj] = (uint32_t)((4 * g4 + jj) * a.hkv) * (D * T::VE) + DPR * T::VE * c;
+  lo.v = (uint32_t)(4 * g4 * a.hkv) * (D * T::VE) + DPR * T::VE * c;
+  lo.v_token = (uint32_t)wave_uniform(a.hkv * D * T::VE);
 
   // Fused append: the new token (position len - 1, only if it lies inside
   // the block table) belongs to this split's tiles; the wave that attends it
-  // quantises and stores it and keeps its bytes in LDS for the substitution.
+  // quantises and stores it (after issuing its first tile's loads, so the
+  // work overlaps their latency) and keeps its bytes in LDS for the
+  // substitution.
   int pos_n = -1;  // wave-uniform; -1: this wave does not attend the new token
   if constexpr (APPEND) {
     const int p = len - 1;
     if (len >= 1 && len <= a.mbps * a.bs && p >= t_begin && p < t_end &&
-        ((p - t_begin) / kTile) % kWaves == wave) {
+        ((p - t_begin) / kTile) % kWaves == wave)
       pos_n = p;
-      const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
-      const bool is_v = lane >= kLR;
-      const bool quantise = kK8 || (kV8 && is_v);
-      const float scale = row_amax<kLR>(xnew) / kE4M3Max;
-      const int sub = lane % kLR;
-      if (lane < 2 * kLR) {
-        const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
-        const bool store = (unsigned)blk < (unsigned)a.num_blocks;  // else: key excluded
-        // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
-        uint32_t* img = s_new + (is_v ? D / 2 : 0);
-        if (quantise) {
-          const uint32_t codes = e4m3_codes4(xnew, scale);
-          img[sub] = codes;
-          if (store) {
-            uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
-            *reinterpret_cast<uint32_t*>(dst + 4 * sub) = codes;
-            if (sub == 0) const_cast<float*>(is_v ? a.vs : a.ks)[row] = scale;
-          }
-          if (sub == 0) s_new[D + (is_v ? 1 : 0)] = __float_as_uint(scale);
-        } else {
-          const u32x2_t w = bf16x4(xnew);
-          *reinterpret_cast<u32x2_t*>(img + 2 * sub) = w;
-          if (store) {
-            uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
-            *reinterpret_cast<u32x2_t*>(dst + 4 * sub) = w;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
   }
   pos_n = wave_uniform(pos_n);
+  auto append_new = [&]() __attribute__((always_inline)) {
+    const int p = pos_n;
+    const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
+    const bool is_v = lane >= kLR;
+    const bool quantise = kK8 || (kV8 && is_v);
+    const float scale = row_amax<kLR>(xnew) / kE4M3Max;
+    const int sub = lane % kLR;
+    if (lane < 2 * kLR) {
+      // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
+      uint32_t* img = s_new + (is_v ? D / 2 : 0);
+      if (quantise) {
+        img[sub] = e4m3_codes4(xnew, scale);
+        if (sub == 0) s_new[D + (is_v ? 1 : 0)] = __float_as_uint(scale);
+      } else {
+        *reinterpret_cast<u32x2_t*>(img + 2 * sub) = bf16x4(xnew);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  // The fused append's only write of the slot: the bytes of the LDS image
+  // (the same as fp8kv_append writes).  Issued after the last tile has been
+  // consumed, because on gfx9 stores share the load counter: a store among
+  // the tile loads would make every wait for tile data wait for it too.
+  auto store_new = [&]() __attribute__((always_inline)) {
+    const int p = pos_n;
+    const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
+    if ((unsigned)blk >= (unsigned)a.num_blocks || lane >= 2 * kLR) return;  // key excluded
+    const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
+    const bool is_v = lane >= kLR;
+    const bool quantise = kK8 || (kV8 && is_v);
+    const int sub = lane % kLR;
+    const uint32_t* img = s_new + (is_v ? D / 2 : 0);
+    if (quantise) {
+      uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
+      *reinterpret_cast<uint32_t*>(dst + 4 * sub) = img[sub];
+      if (sub == 0)
+        const_cast<float*>(is_v ? a.vs : a.ks)[row] = __uint_as_float(s_new[D + (is_v ? 1 : 0)]);
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
+      *reinterpret_cast<u32x2_t*>(dst + 4 * sub) = *reinterpret_cast<const u32x2_t*>(img + 2 * sub);
+    }
+  };
 
-  // Substitute the new token for its slot's previous bytes in tile r
+  // Substitute the new token for its slot's previous bytes in a tile
   // (t0 <= pos_n < t0 + 64): K of token c in lanes (*, c), V of token
-  // 4*g4 + jj in lanes (g4, *), scales in lane t.  Every register is written
-  // through a select: a store to the one matching element would index the
-  // arrays with a runtime value and move them to scratch memory.
-  auto patch = [&](T& r, int t0) __attribute__((always_inline)) {
+  // 4*g4 + jj in lanes (g4, *), scales in lane t.  Each half of the tile is
+  // patched just before it is used, so the wait for the half's data stays
+  // per half.  Every register is written through a select: a store to the
+  // one matching element would index the arrays with a runtime value and
+  // move them to scratch memory.
+  auto patch_scales = [&](T& r, int t0) __attribute__((always_inline)) {
+    const int tn = pos_n - t0;
+    if (kK8) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
+    if (kV8) r.vs = (lane == tn) ? __uint_as_float(s_new[D + 1]) : r.vs;
+  };
+  auto patch_half = [&](T& r, int t0, int kp) __attribute__((always_inline)) {
     const int tn = pos_n - t0, kbn = tn >> 4, cn = tn & 15;
+    if ((kbn >> 1) != kp) return;  // wave-uniform
     const uint8_t* img = reinterpret_cast<const uint8_t*>(s_new);
     u32x4_t nk[T::KRAW];
 #pragma unroll
@@ -327,12 +361,13 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bool sel = (c == cn) && (kb == kbn);
+    for (int hb = 0; hb < 2; ++hb) {
+      const bool sel = (c == cn) && ((kbn & 1) == hb);
 #pragma unroll
       for (int q = 0; q < T::KRAW; ++q)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r.k[kb][q][e] = sel ? nk[q][e] : r.k[kb][q][e];
+        for (int e = 0; e < 4; ++e)
+          r.k[2 * kp + hb][q][e] = sel ? nk[q][e] : r.k[2 * kp + hb][q][e];
     }
     uint32_t nv[T::VW];
     const uint32_t* vimg = s_new + D / 2 + (DPR * T::VE / 4) * c;
@@ -340,15 +375,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     for (int e = 0; e < T::VW; ++e) nv[e] = vimg[e];
     const int jn = ((kbn & 1) << 2) | (cn & 3);
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp)
+    for (int j = 0; j < 8; ++j) {
+      const bool sel = (g4 == (cn >> 2)) && (j == jn);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool sel = (g4 == (cn >> 2)) && (kp == (kbn >> 1)) && (j == jn);
-#pragma unroll
-        for (int e = 0; e < T::VW; ++e) r.v[kp][j][e] = sel ? nv[e] : r.v[kp][j][e];
-      }
-    if (kK8) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
-    if (kV8) r.vs = (lane == tn) ? __uint_as_float(s_new[D + 1]) : r.vs;
+      for (int e = 0; e < T::VW; ++e) r.v[kp][j][e] = sel ? nv[e] : r.v[kp][j][e];
+    }
   };
 
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
@@ -363,7 +394,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   // wave's slice of LDS (written and read by the same wave; its LDS operations
   // complete in order, and the previous tile's reads precede these writes in
   // program order).
-  auto compute = [&](const T& cur, int t0) {
+  auto compute = [&](T& cur, int t0) {
+    const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
+    if (has_new) patch_scales(cur, t0);
     // K scale with sm_scale * log2(e) folded in (one product per token),
     // V scale as is.
     if (kK8) s_scale[wave][0][lane] = cur.ks * a.c_scale;
@@ -371,6 +404,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
+      if (has_new) patch_half(cur, t0, kp);
       // --- QK on the matrix cores for sub-blocks 2kp, 2kp+1
       f32x4_t sacc[2];
 #pragma unroll
@@ -388,7 +422,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
           } else {
             av = cur.k[kb][kc];
           }
-          s = mfma_16x16x32_bf16(av, qb[kc], s);
+          s = mfma_16x16x32_bf16(av, s_q[kc][lane], s);
         }
         sacc[hb] = s;
       }
@@ -419,15 +453,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       }
       tmax = max_over_groups(tmax);
 
-      // --- online softmax step with an integer reference; a half with no
-      //     valid key (tmax = -inf) leaves the state unchanged
-      const float m_new = fmaxf(m_run, ceilf(tmax));
-      if (m_new != m_run) {
-        const float alpha = (m_run == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run - m_new));
+      // --- online softmax step with a lazily moved integer reference; a
+      //     half with no valid key (tmax = -inf) leaves the state unchanged
+      const float t_ref = ceilf(tmax);
+      if (m_run == -INFINITY) {
+        m_run = t_ref;  // l and acc are still zero: nothing to rescale
+      } else if (t_ref > m_run + kLazy) {
+        const float alpha = ldexpf(1.0f, (int)(m_run - t_ref));
         l_run *= alpha;
 #pragma unroll
         for (int j = 0; j < DPR; ++j) acc[j] *= alpha;
-        m_run = m_new;
+        m_run = t_ref;
       }
       // exp2(-inf - m) is 0 for finite m; m is -inf only while every score
       // so far is -inf, and then the reference 0 avoids -inf - -inf.
@@ -445,12 +481,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
                           f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
 
       // --- V of keys outside the sequence may hold any bits (even NaN
-      //     codes): zero them so that P = 0 contributes exactly 0
-      uint32_t vv[8][T::VW];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int e = 0; e < T::VW; ++e) vv[j][e] = cur.v[kp][j][e];
+      //     codes): zero them in place so that P = 0 contributes exactly 0
+      auto& vv = cur.v[kp];
       if (!cur.full) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -493,21 +525,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   // computed.
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   T buf0, buf1;
-  if (wave < n_tiles)
-    load_tile<MODE, D>(buf0, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane);
+  // Unconditional (a wave without a tile reloads the split's first one, an
+  // L2 hit it never uses): loads under a branch make the compiler wait for
+  // all of them wherever a value loaded before the branch is used.
+  load_tile<MODE, D>(buf0, a, lo, t_begin + (wave < n_tiles ? wave * kTile : 0), t_end, tab,
+                     e_base, h, lane);
+  if (APPEND && pos_n >= 0) append_new();
+  __syncthreads();  // s_q complete (after the first tile's loads are in flight)
   for (int tile = wave; tile < n_tiles; tile += 2 * kWaves) {
     const int t0 = t_begin + tile * kTile;
     if (tile + kWaves < n_tiles)
       load_tile<MODE, D>(buf1, a, lo, t0 + kWaves * kTile, t_end, tab, e_base, h, lane);
-    if (APPEND && pos_n >= t0 && pos_n < t0 + kTile) patch(buf0, t0);
     compute(buf0, t0);
     if (tile + kWaves >= n_tiles) break;
     if (tile + 2 * kWaves < n_tiles)
       load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane);
-    if (APPEND && pos_n >= t0 + kWaves * kTile && pos_n < t0 + (kWaves + 1) * kTile)
-      patch(buf1, t0 + kWaves * kTile);
     compute(buf1, t0 + kWaves * kTile);
   }
+  if (APPEND && pos_n >= 0) store_new();
 
   // --- merge the waves of the work-group: one barrier.  Each wave leaves
   //     its reference, its four lane-group shares of l and its accumulator

@@ -22,6 +22,12 @@ struct CacheView {
   const int32_t* table;
 };
 
+// Work-groups of the split kernel one compute unit holds at once: two where a
+// lane's registers fit in 256 (the e4m3 K tile of K8V8, and every D = 64
+// tile), else one.  The kernel's launch bounds and the split plan both use it.
+constexpr int split_wgs_per_cu(int mode, int d) { return (mode == 0 || d == 64) ? 2 : 1; }
+constexpr int kComputeUnits = 256;  // MI355X
+
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
                          const int32_t* seq_idx, const int32_t* pos, int n_tok,
                          hipStream_t stream);

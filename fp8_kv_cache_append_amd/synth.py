@@ -149,3 +149,25 @@ def block_layout(w: Workload, capacity: int | None = None):
         table[b, :per[b]] = ids[start:start + per[b]]
         start += int(per[b])
     return bs, table, n_blocks
+
+
+def kv_sequence_device(w: Workload, b: int, device="cuda"):
+    """fp32 K and V of sequence ``b`` drawn on the device (torch's seeded
+    generator): the same distributions as kv_sequence, other values.  For
+    benchmark caches of gigabytes, where host generation would dominate."""
+    import torch
+    n = int(w.lens[b])
+    g = torch.Generator(device=device)
+    g.manual_seed((int(w.seed) * 1_000_003 + int(b)) * 7 + 1)
+    shape = (n, w.kv_heads, w.head_dim)
+    k = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if w.dist == "outliers":
+        k = torch.where(torch.rand(shape, generator=g, device=device) < 0.02, k * 10.0, k)
+        v = torch.where(torch.rand(shape, generator=g, device=device) < 0.02, v * 10.0, v)
+    elif w.dist == "bias":
+        ch = torch.from_numpy(bias_channels(w.seed, w.head_dim)).to(device)
+        k[:, :, ch] += 20.0
+    elif w.dist != "normal":
+        raise ValueError(w.dist)
+    return k, v

@@ -109,6 +109,15 @@ def test_decode_plan():
     assert _plan(d, 64, 0, 32768)[0] == -1
     assert _plan(d, 64, 4, 32768 + 1)[0] == -1   # beyond the block table
     assert _plan(d, 0, 4, 0) == (0, 256, 0)
+    # contiguous B16 x 2 KV heads x 8192 tokens: the grid must fit the units
+    # at once (512 work-groups for K8V8, 256 for K16V8/BF16 at head_dim 128)
+    d = _desc(num_blocks=16, block_size=8192, max_blocks_per_seq=1)
+    assert _plan(d, 16, 8, 8192) == (0, 512, 16)
+    d16 = _desc(mode=1, num_blocks=16, block_size=8192, max_blocks_per_seq=1, k_scale=None)
+    assert _plan(d16, 16, 8, 8192) == (0, 1024, 8)
+    d64 = _desc(mode=2, num_blocks=16, block_size=8192, max_blocks_per_seq=1, head_dim=64,
+                k_scale=None, v_scale=None)
+    assert _plan(d64, 16, 8, 8192) == (0, 512, 16)
 
 
 def test_workspace_bytes():

@@ -140,8 +140,11 @@ def test_decode_b64_gqa4_ragged_paged_sampled(mode):
 @pytest.mark.parametrize("chunk", [64, 256, 1024])
 def test_partials_match_oracle_online(mode, chunk):
     """The split kernel's (M, l, acc) against the oracle's online form with
-    64-key tiles and the same splits.  M may differ by one where a score sits
-    within rounding of an integer, so values are compared as acc * 2^M."""
+    64-key tiles and the same splits, compared as l * 2^M and acc * 2^M.  The
+    kernel's reference M is an integer that only moves when the scores exceed
+    it by more than 8 (log2 units), so it can sit below the oracle's running
+    ceiling by up to 8, and above it by one where a score lies within
+    rounding of an integer."""
     lens = np.array([1500, 100, 64], np.int32)
     w = synth.Workload("t", 3, 16, 2, 128, lens, "outliers", seed=77)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
@@ -160,7 +163,8 @@ def test_partials_match_oracle_online(mode, chunk):
             gm, gl, ga = pml[b, h, :ns, :, 0], pml[b, h, :ns, :, 1], pacc[b, h, :ns]
             assert np.array_equal(np.isinf(gm), np.isinf(rm)), (b, h)
             fin = np.isfinite(rm)
-            assert np.all(np.abs(gm[fin] - rm[fin]) <= 1), (b, h)
+            assert np.all(gm[fin] - rm[fin] <= 1), (b, h)
+            assert np.all(rm[fin] - gm[fin] <= 9), (b, h)
             assert np.all(gm[fin] == np.round(gm[fin]))
             sg = np.exp2(np.where(fin, gm, 0.0))
             sr = np.exp2(np.where(fin, rm, 0.0))
