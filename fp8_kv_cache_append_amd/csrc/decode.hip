@@ -179,6 +179,13 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
   }
 }
 
+// KV head of pair index pi (sequence pi / hkv): rotated by the sequence, so
+// that pairs 8k + x (one XCD) cover every head.
+__device__ __forceinline__ int rotated_head(int pi, int hkv) {
+  const int b = pi / hkv;
+  return (pi % hkv + hkv - b % hkv) % hkv;
+}
+
 // max / sum over the four lane groups (lanes c, c+16, c+32, c+48) with the
 // gfx950 lane swaps: with both operands equal, the two results of a 32-lane
 // swap hold x[l] and x[l ^ 32], those of a 16-lane swap x[l] and x[l ^ 16].
@@ -212,17 +219,38 @@ void decode_partial_kernel(DecodeArgs a) {
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
   __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
+  //   s_new[D], s_new[D+1]: K and V scale; s_new[D+2], s_new[D+3]: the
+  //   slot's cache row (low, high word; high word ~0u: not stored)
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4;   // k-slot group of the lane
   const int c = lane & 15;    // row / column of the lane
 
+  // Work-group -> (sequence, KV head, split).  Consecutive work-groups are
+  // dealt round-robin to the eight XCDs (each with its own L2), so
+  // work-group wg runs on XCD wg % 8.  When the (sequence, KV head) pairs
+  // come in multiples of eight, XCD x gets whole pairs (pair index
+  // pi = 8k + x), their splits consecutive in its dispatch order; the KV
+  // head is rotated by the sequence (h = (pi - b) mod Hkv), so every XCD
+  // gets every head and every sequence once: equal work per XCD however
+  // the lengths are spread, Q and block ids reused from one L2, and no XCD
+  // confined to one head's rows of the cache.  The merge kernel maps pair
+  // pi to the same XCD and finds the partials in that L2.
   const int wg = blockIdx.x;
-  const int split = wg % a.n_splits;
-  const int bh = wg / a.n_splits;  // b * hkv + h
-  const int h = bh % a.hkv;
-  const int b = bh / a.hkv;
+  const int pairs = gridDim.x / a.n_splits;
+  int pi, split;
+  if ((pairs & 7) == 0) {
+    const int q = wg >> 3;
+    pi = (q / a.n_splits) * 8 + (wg & 7);
+    split = q % a.n_splits;
+  } else {
+    pi = wg % pairs;
+    split = wg / pairs;
+  }
+  const int b = pi / a.hkv;
+  const int h = rotated_head(pi, a.hkv);
+  const int bh = b * a.hkv + h;
   const int G = a.group;
   const int t_begin = split * a.chunk;
 
@@ -297,6 +325,13 @@ void decode_partial_kernel(DecodeArgs a) {
     const bool quantise = kK8 || (kV8 && is_v);
     const float scale = row_amax<kLR>(xnew) / kE4M3Max;
     const int sub = lane % kLR;
+    if (lane == 0) {
+      const int64_t row = (unsigned)blk < (unsigned)a.num_blocks
+                              ? ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h
+                              : -1;  // invalid block: not stored, key excluded
+      s_new[D + 2] = (uint32_t)row;
+      s_new[D + 3] = (uint32_t)((uint64_t)row >> 32);
+    }
     if (lane < 2 * kLR) {
       // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
       uint32_t* img = s_new + (is_v ? D / 2 : 0);
@@ -314,10 +349,9 @@ void decode_partial_kernel(DecodeArgs a) {
   // consumed, because on gfx9 stores share the load counter: a store among
   // the tile loads would make every wait for tile data wait for it too.
   auto store_new = [&]() __attribute__((always_inline)) {
-    const int p = pos_n;
-    const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
-    if ((unsigned)blk >= (unsigned)a.num_blocks || lane >= 2 * kLR) return;  // key excluded
-    const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
+    const int64_t row =
+        (int64_t)(((uint64_t)s_new[D + 3] << 32) | (uint64_t)s_new[D + 2]);
+    if (row < 0 || lane >= 2 * kLR) return;  // invalid block: key excluded
     const bool is_v = lane >= kLR;
     const bool quantise = kK8 || (kV8 && is_v);
     const int sub = lane % kLR;
@@ -608,7 +642,8 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
                                                            const float* __restrict__ part_ml,
                                                            float* __restrict__ out) {
   constexpr int L = D / 4;  // lanes per head, four values each
-  const int bh = blockIdx.x;
+  const int pi = blockIdx.x;  // pair index, mapped as in the split kernel
+  const int bh = (pi / hkv) * hkv + rotated_head(pi, hkv);
   const int g = threadIdx.x / L;
   const int d4 = threadIdx.x % L;
   if (g >= group) return;
