@@ -186,15 +186,6 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
   return (pi % hkv + hkv - b % hkv) % hkv;
 }
 
-// max / sum over the four lane groups (lanes c, c+16, c+32, c+48) with the
-// gfx950 lane swaps: with both operands equal, the two results of a 32-lane
-// swap hold x[l] and x[l ^ 32], those of a 16-lane swap x[l] and x[l ^ 16].
-__device__ __forceinline__ float max_over_groups(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
 
 // APPEND: the decode step's new token of sequence b (fp32 rows k_new[b],
 // v_new[b]) sits at position seq_lens[b] - 1.  The work-group whose split

@@ -56,6 +56,16 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// max / sum over the four lane groups (lanes c, c+16, c+32, c+48) with the
+// gfx950 lane swaps: with both operands equal, the two results of a 32-lane
+// swap hold x[l] and x[l ^ 32], those of a 16-lane swap x[l] and x[l ^ 16].
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // Storage rule of a (token, KV head) row ("kadirnar/kernel-agent/fp8-kv-cache",
 // section "Storage"), for a row of D values held four per lane by D/4
 // consecutive, aligned lanes.
