@@ -24,7 +24,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2}
+MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3}
+K_E4M3 = ("K8V8", "K8V16")   # modes whose K side is e4m3 codes + scale
+V_E4M3 = ("K8V8", "K16V8")   # modes whose V side is e4m3 codes + scale
 
 _lib = None
 
@@ -129,17 +131,20 @@ def quantize_rows(x):
 def store_rows(mode: str, k, v) -> dict:
     """What the cache holds for fp32 K and V rows in the given mode.
 
-    Keys: k8/ks (K8V8), k16 (K16V8, BF16), v8/vs (K8V8, K16V8), v16 (BF16).
+    Keys: k8/ks (K8V8, K8V16), k16 (K16V8, BF16), v8/vs (K8V8, K16V8),
+    v16 (BF16, K8V16).
     """
+    if mode not in MODES:
+        raise ValueError(mode)
     out = {}
-    if mode == "K8V8":
+    if mode in K_E4M3:
         out["k8"], out["ks"] = quantize_rows(k)
     else:
         out["k16"] = bf16_round_f32(k)
-    if mode == "BF16":
-        out["v16"] = bf16_round_f32(v)
-    else:
+    if mode in V_E4M3:
         out["v8"], out["vs"] = quantize_rows(v)
+    else:
+        out["v16"] = bf16_round_f32(v)
     return out
 
 

@@ -133,22 +133,26 @@ typedef struct {
   const float *ks, *vs;
 } kv_view;
 
+/* Which side of the cache holds e4m3 codes with a scale (else bf16). */
+static int k_is_e4m3(int mode) { return mode == ORC_K8V8 || mode == ORC_K8V16; }
+static int v_is_e4m3(int mode) { return mode == ORC_K8V8 || mode == ORC_K16V8; }
+
 static double k_elem(const kv_view* kv, int t, int j) {
-  if (kv->mode == ORC_K8V8) return orc_e4m3_value(kv->k8[(size_t)t * kv->d + j]);
+  if (k_is_e4m3(kv->mode)) return orc_e4m3_value(kv->k8[(size_t)t * kv->d + j]);
   return orc_bf16_value(kv->k16[(size_t)t * kv->d + j]);
 }
 
 static double v_elem(const kv_view* kv, int t, int j) {
-  if (kv->mode == ORC_BF16) return orc_bf16_value(kv->v16[(size_t)t * kv->d + j]);
-  return orc_e4m3_value(kv->v8[(size_t)t * kv->d + j]);
+  if (v_is_e4m3(kv->mode)) return orc_e4m3_value(kv->v8[(size_t)t * kv->d + j]);
+  return orc_bf16_value(kv->v16[(size_t)t * kv->d + j]);
 }
 
 static double k_scale(const kv_view* kv, int t) {
-  return kv->mode == ORC_K8V8 ? (double)kv->ks[t] : 1.0;
+  return k_is_e4m3(kv->mode) ? (double)kv->ks[t] : 1.0;
 }
 
 static double v_scale(const kv_view* kv, int t) {
-  return kv->mode == ORC_BF16 ? 1.0 : (double)kv->vs[t];
+  return v_is_e4m3(kv->mode) ? (double)kv->vs[t] : 1.0;
 }
 
 /* Score in log2 units: (q . K_t) * k_scale_t * sm_scale * log2(e).

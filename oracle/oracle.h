@@ -47,7 +47,9 @@
 extern "C" {
 #endif
 
-enum { ORC_K8V8 = 0, ORC_K16V8 = 1, ORC_BF16 = 2 };
+/* Cache formats: K8V8 (both e4m3 + scale), K16V8 (K bf16, V e4m3 + scale),
+ * BF16 (both bf16), K8V16 (K e4m3 + scale, V bf16). */
+enum { ORC_K8V8 = 0, ORC_K16V8 = 1, ORC_BF16 = 2, ORC_K8V16 = 3 };
 
 /* Value of an OCP e4m3fn code (NaN for 0x7F / 0xFF). */
 double orc_e4m3_value(uint8_t code);
@@ -77,10 +79,10 @@ void orc_quantize_rows(const float* x, int64_t n_rows, int d,
  * Attention of n_rows query rows against one KV head's keys.
  *
  *   q      bf16 bits [n_rows][d]
- *   k8/ks  K8V8: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
- *   k16    K16V8 and BF16: bf16 bits [n_keys][d]
- *   v8/vs  K8V8 and K16V8: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
- *   v16    BF16: bf16 bits [n_keys][d]
+ *   k8/ks  K8V8, K8V16: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
+ *   k16    K16V8, BF16: bf16 bits [n_keys][d]
+ *   v8/vs  K8V8, K16V8: e4m3 codes [n_keys][d] and fp32 scales [n_keys]
+ *   v16    BF16, K8V16: bf16 bits [n_keys][d]
  *   n_valid[r]  keys 0 .. n_valid[r]-1 are visible to row r
  *   round_p     1: P rounded to bf16 (the method); 0: unrounded (for pins)
  *   out    fp64 [n_rows][d]

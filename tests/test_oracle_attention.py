@@ -26,15 +26,23 @@ from golden_io import attention_case
 GATE_REL = 1e-3
 
 
+# Which side each mode stores as e4m3 codes + fp32 scale (the rest is bf16),
+# written out here independently of the oracle's own tables.
+_K8 = {"K8V8": True, "K16V8": False, "BF16": False, "K8V16": True}
+_V8 = {"K8V8": True, "K16V8": True, "BF16": False, "K8V16": False}
+
+
 def _deq(mode, store):
-    if mode == "K8V8":
+    assert set(store) == ({"k8", "ks"} if _K8[mode] else {"k16"}) | (
+        {"v8", "vs"} if _V8[mode] else {"v16"}), (mode, sorted(store))
+    if _K8[mode]:
         k = oracle.e4m3_value(store["k8"]) * store["ks"][..., None].astype(np.float64)
     else:
         k = oracle.bf16_value(store["k16"])
-    if mode == "BF16":
-        v = oracle.bf16_value(store["v16"])
-    else:
+    if _V8[mode]:
         v = oracle.e4m3_value(store["v8"]) * store["vs"][..., None].astype(np.float64)
+    else:
+        v = oracle.bf16_value(store["v16"])
     return k, v
 
 
@@ -92,7 +100,7 @@ def test_attention_golden():
 
 # ------------------------------------------------------------ brute force
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("g", [1, 2, 4, 7])
 def test_unrounded_equals_textbook_softmax(mode, g):
     hkv = 2
@@ -138,7 +146,7 @@ def _nearest_bf16(x: float) -> float:
     return math.copysign(best[1], x)
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 def test_single_key_closed_form(mode):
     """One key: M = ceil(s), p = 2^(s - M), o = bf16(p * vs) * V / p."""
     rng = np.random.default_rng(41)
@@ -151,7 +159,7 @@ def test_single_key_closed_form(mode):
         kd, _ = _deq(mode, store)
         s = float(kd[0, 0] @ oracle.bf16_value(q_bits[0, 0])) * sm * math.log2(math.e)
         p = 2.0 ** (s - math.ceil(s))
-        if mode == "BF16":
+        if not _V8[mode]:
             vs, vhat = 1.0, oracle.bf16_value(store["v16"][0, 0])
         else:
             vs, vhat = float(store["vs"][0, 0]), oracle.e4m3_value(store["v8"][0, 0])
@@ -193,7 +201,7 @@ def test_rounding_is_after_the_v_scale_fold():
 
 # ------------------------------------------------------------ online == two-pass
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("tile,split", [(16, 64), (64, 64), (64, 256), (7, 30), (64, 10000)])
 def test_online_split_equals_two_pass(mode, tile, split):
     q_bits, ks, vs = _inputs(5, b=1, hq=8, hkv=1, d=32, t=300)
@@ -342,12 +350,12 @@ def _fp32_attention(mode, q_bits, k, v, sm):
     kind of result a GPU produces."""
     import torch
     store = oracle.store_rows(mode, k, v)
-    b_k = (oracle.e4m3_value(store["k8"]) if mode == "K8V8"
+    b_k = (oracle.e4m3_value(store["k8"]) if _K8[mode]
            else oracle.bf16_value(store["k16"])).astype(np.float32)
-    b_v = (oracle.bf16_value(store["v16"]) if mode == "BF16"
-           else oracle.e4m3_value(store["v8"])).astype(np.float64)
-    ks = store["ks"] if mode == "K8V8" else np.ones(k.shape[:2], np.float32)
-    vs = store["vs"] if mode != "BF16" else np.ones(k.shape[:2], np.float32)
+    b_v = (oracle.e4m3_value(store["v8"]) if _V8[mode]
+           else oracle.bf16_value(store["v16"])).astype(np.float64)
+    ks = store["ks"] if _K8[mode] else np.ones(k.shape[:2], np.float32)
+    vs = store["vs"] if _V8[mode] else np.ones(k.shape[:2], np.float32)
     q = oracle.bf16_value(q_bits).astype(np.float32)
     hq, hkv = q.shape[0], k.shape[1]
     g = hq // hkv
@@ -365,7 +373,7 @@ def _fp32_attention(mode, q_bits, k, v, sm):
     return out
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 def test_rounding_bounds_contain_an_fp32_computation(mode):
     """[lo, hi] holds every output reachable by rounding an ambiguous P either
     way, so an independent fp32 computation must land inside it (up to the
