@@ -18,8 +18,9 @@ timed replays (see DecodeBench.run).
 
 Extra fields: the K16V8 and BF16 controls (same protocol), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
-the context sweep of the same shape at 77/512/2048/8192 keys in all three
-modes with the K8V8-vs-K16V8 break-even, the ragged batch-64 paged workload
+the context sweep of the same shape at 77/512/2048/8192 keys in all four
+modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
+per-side savings against BF16, the ragged batch-64 paged workload
 (32q/8kv, lengths 1024..32768, K8V8 and K16V8), the roofline of the split
 kernel and the CPU oracle as a baseline.
 """
@@ -40,7 +41,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-ROW_BYTES = {"K8V8": lambda d: 2 * d + 8, "K16V8": lambda d: 3 * d + 4, "BF16": lambda d: 4 * d}
+ROW_BYTES = {"K8V8": lambda d: 2 * d + 8, "K16V8": lambda d: 3 * d + 4, "BF16": lambda d: 4 * d,
+             "K8V16": lambda d: 3 * d + 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_k8v8_b16_t2048_traffic.json")
 KERNEL_SOURCES = ["fp8_kv_cache_append_amd/csrc/decode.hip",
                   "fp8_kv_cache_append_amd/csrc/device.h"]
@@ -221,7 +223,7 @@ def bench_decode(mode, w, steps, warmup, copies):
 
 def bench_sweep(steps, warmup, copies, head):
     """The context sweep of the B16 16q/2kv D128 shape at 77, 512, 2048 and
-    8192 keys, all three modes, HBM-cold as the headline; the K8V8-vs-K16V8
+    8192 keys, all four modes, HBM-cold as the headline; the K8V8-vs-K16V8
     break-even is the first length where the K8V8 step is faster (linear
     interpolation of the step time over the swept lengths)."""
     from fp8_kv_cache_append_amd import synth
@@ -230,7 +232,7 @@ def bench_sweep(steps, warmup, copies, head):
     for tokens in (77, 512, 2048, 8192):
         w = synth.decode_b16_gqa8_d128(tokens)
         row = {}
-        for mode in ("K8V8", "K16V8", "BF16"):
+        for mode in ("K8V8", "K16V8", "BF16", "K8V16"):
             if tokens == 2048 and mode == "K8V8":
                 r = head
             else:
@@ -240,6 +242,15 @@ def bench_sweep(steps, warmup, copies, head):
                          "unfused_step_us": r["unfused_step_us"]}
         row["K8V8_speedup_vs_K16V8"] = row["K16V8"]["us_per_step"] / row["K8V8"]["us_per_step"]
         row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
+        # time the BF16 control saves by storing one side in e4m3 ("Account
+        # for V preparation"): K side alone (K8V16), V side alone (K16V8),
+        # both (K8V8); the fraction hidden is the both-sides saving over the
+        # sum of the single-side ones
+        t_bf16 = row["BF16"]["us_per_step"]
+        sav_k = t_bf16 - row["K8V16"]["us_per_step"]
+        sav_v = t_bf16 - row["K16V8"]["us_per_step"]
+        sav_kv = t_bf16 - row["K8V8"]["us_per_step"]
+        row["saving_us"] = {"K_only": sav_k, "V_only": sav_v, "K_and_V": sav_kv}
         table[str(tokens)] = row
     lens = [77, 512, 2048, 8192]
     diff = [table[str(t)]["K16V8"]["us_per_step"] - table[str(t)]["K8V8"]["us_per_step"]

@@ -16,7 +16,9 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfp8kv.so")
 
-MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2}
+MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3}
+K_E4M3 = ("K8V8", "K8V16")   # K side: uint8 e4m3 codes + fp32 scale (else bf16)
+V_E4M3 = ("K8V8", "K16V8")   # V side: uint8 e4m3 codes + fp32 scale (else bf16)
 
 FP8KV_OK = 0
 FP8KV_ERR_INVALID = -1
@@ -116,7 +118,8 @@ class KVCache:
     """A paged cache in device memory plus its C descriptor.
 
     k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
-    k_scale, v_scale: float32 [num_blocks, block_size, Hkv] or None;
+    k_scale, v_scale: float32 [num_blocks, block_size, Hkv] for an e4m3 side,
+    else None;
     block_table: int32 [batch, max_blocks_per_seq].
     """
     mode: str
@@ -130,12 +133,11 @@ class KVCache:
     def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
                  head_dim: int, block_table, device="cuda") -> "KVCache":
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
-        kd = torch.uint8 if mode == "K8V8" else torch.bfloat16
-        vd = torch.bfloat16 if mode == "BF16" else torch.uint8
-        k = torch.zeros(shape, dtype=kd, device=device)
-        v = torch.zeros(shape, dtype=vd, device=device)
-        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if mode == "K8V8" else None
-        vs = torch.zeros(shape[:3], dtype=torch.float32, device=device) if mode != "BF16" else None
+        k8, v8 = mode in K_E4M3, mode in V_E4M3
+        k = torch.zeros(shape, dtype=torch.uint8 if k8 else torch.bfloat16, device=device)
+        v = torch.zeros(shape, dtype=torch.uint8 if v8 else torch.bfloat16, device=device)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if k8 else None
+        vs = torch.zeros(shape[:3], dtype=torch.float32, device=device) if v8 else None
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
         return cls(mode, k, v, ks, vs, bt)
 

@@ -40,7 +40,8 @@ int check_device() {
 
 int validate_cache(const fp8kv_cache* c) {
   if (!c) return FP8KV_ERR_INVALID;
-  if (c->mode != FP8KV_K8V8 && c->mode != FP8KV_K16V8 && c->mode != FP8KV_BF16)
+  if (c->mode != FP8KV_K8V8 && c->mode != FP8KV_K16V8 && c->mode != FP8KV_BF16 &&
+      c->mode != FP8KV_K8V16)
     return FP8KV_ERR_INVALID;
   if (c->head_dim != 64 && c->head_dim != 128) return FP8KV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->max_blocks_per_seq <= 0 ||
@@ -51,8 +52,8 @@ int validate_cache(const fp8kv_cache* c) {
   if (!c->k || !c->v || !c->block_table) return FP8KV_ERR_INVALID;
   if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->block_table, 4))
     return FP8KV_ERR_INVALID;
-  const bool need_ks = c->mode == FP8KV_K8V8;
-  const bool need_vs = c->mode != FP8KV_BF16;
+  const bool need_ks = fp8kv::k_is_e4m3(c->mode);
+  const bool need_vs = fp8kv::v_is_e4m3(c->mode);
   // A scale pointer must be present exactly when the mode stores that scale:
   // a mismatch means the caller and the cache disagree about the format.
   if (need_ks != (c->k_scale != nullptr)) return FP8KV_ERR_INVALID;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const float* src = (is_v ? a.v_new : a.k_new) + pair * D + 4 * sub;
   const float4 x = *reinterpret_cast<const float4*>(src);
 
-  const bool quantise = (MODE == kK8V8) || (MODE == kK16V8 && is_v);
+  const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
   if (quantise) {
     const float scale = row_amax<kLanesPerRow>(x) / kE4M3Max;  // correctly rounded
     uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
@@ -89,6 +89,7 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
   switch (c.mode) {
     case kK8V8: return append_for_d<kK8V8>(c, a, stream);
     case kK16V8: return append_for_d<kK16V8>(c, a, stream);
+    case kK8V16: return append_for_d<kK8V16>(c, a, stream);
     default: return append_for_d<kBF16>(c, a, stream);
   }
 }

@@ -74,8 +74,8 @@ constexpr float kLazy = 8.0f; // log2 units the scores may exceed the reference 
 // validity needed to neutralise keys outside the sequence.
 template <int MODE, int D>
 struct TileRegs {
-  static constexpr bool K8 = (MODE == kK8V8);
-  static constexpr bool V8 = (MODE != kBF16);
+  static constexpr bool K8 = k_is_e4m3(MODE);
+  static constexpr bool V8 = v_is_e4m3(MODE);
   static constexpr int KP = D / 64;                      // 16-element pieces
   static constexpr int KRAW = K8 ? KP : 2 * KP;          // 16-byte K loads per sub-block
   static constexpr int DPR = D / 16;
@@ -313,7 +313,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int p = pos_n;
     const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
     const bool is_v = lane >= kLR;
-    const bool quantise = kK8 || (kV8 && is_v);
+    const bool quantise = is_v ? kV8 : kK8;
     const float scale = row_amax<kLR>(xnew) / kE4M3Max;
     const int sub = lane % kLR;
     if (lane == 0) {
@@ -344,7 +344,7 @@ void decode_partial_kernel(DecodeArgs a) {
         (int64_t)(((uint64_t)s_new[D + 3] << 32) | (uint64_t)s_new[D + 2]);
     if (row < 0 || lane >= 2 * kLR) return;  // invalid block: key excluded
     const bool is_v = lane >= kLR;
-    const bool quantise = kK8 || (kV8 && is_v);
+    const bool quantise = is_v ? kV8 : kK8;
     const int sub = lane % kLR;
     const uint32_t* img = s_new + (is_v ? D / 2 : 0);
     if (quantise) {
@@ -694,6 +694,7 @@ static void launch_partial_append(const CacheView& c, const DecodeArgs& a, unsig
   switch (c.mode) {
     case kK8V8: launch_partial_mode<kK8V8, APPEND>(c, a, n_wg, stream); break;
     case kK16V8: launch_partial_mode<kK16V8, APPEND>(c, a, n_wg, stream); break;
+    case kK8V16: launch_partial_mode<kK8V16, APPEND>(c, a, n_wg, stream); break;
     default: launch_partial_mode<kBF16, APPEND>(c, a, n_wg, stream); break;
   }
 }

@@ -13,7 +13,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-enum { kK8V8 = 0, kK16V8 = 1, kBF16 = 2 };
 
 constexpr float kE4M3Max = 448.0f;
 constexpr float kLog2e = 1.4426950408889634f;

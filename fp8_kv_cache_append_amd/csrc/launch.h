@@ -7,8 +7,14 @@
 
 namespace fp8kv {
 
+// Cache formats: which side holds e4m3 codes + an fp32 scale per (token,
+// KV head); the other side, if any, holds bf16.
+enum { kK8V8 = 0, kK16V8 = 1, kBF16 = 2, kK8V16 = 3 };
+constexpr bool k_is_e4m3(int mode) { return mode == kK8V8 || mode == kK8V16; }
+constexpr bool v_is_e4m3(int mode) { return mode == kK8V8 || mode == kK16V8; }
+
 struct CacheView {
-  int mode;   // kK8V8 / kK16V8 / kBF16
+  int mode;   // kK8V8 / kK16V8 / kBF16 / kK8V16
   int bs;     // tokens per block (multiple of 16)
   int hkv;    // KV heads
   int d;      // head_dim, 64 or 128
@@ -25,7 +31,7 @@ struct CacheView {
 // Work-groups of the split kernel one compute unit holds at once: two where a
 // lane's registers fit in 256 (the e4m3 K tile of K8V8, and every D = 64
 // tile), else one.  The kernel's launch bounds and the split plan both use it.
-constexpr int split_wgs_per_cu(int mode, int d) { return (mode == 0 || d == 64) ? 2 : 1; }
+constexpr int split_wgs_per_cu(int mode, int d) { return (mode == kK8V8 || d == 64) ? 2 : 1; }
 constexpr int kComputeUnits = 256;  // MI355X
 
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,

@@ -67,8 +67,8 @@ constexpr float kPLazy = 8.0f;  // log2 units the scores may exceed the referenc
 
 template <int MODE, int D>
 struct PrefillShape {
-  static constexpr bool K8 = (MODE == kK8V8);
-  static constexpr bool V8 = (MODE != kBF16);
+  static constexpr bool K8 = k_is_e4m3(MODE);
+  static constexpr bool V8 = v_is_e4m3(MODE);
   static constexpr int LDK = D + 8;                          // LDS K row (bf16), padded
   static constexpr int LDV = kKT + 8;                        // LDS V^T row (bf16), padded
   static constexpr int KBYTES = K8 ? D : 2 * D;              // bytes of one K row in HBM
@@ -439,6 +439,7 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
   switch (c.mode) {
     case kK8V8: launch_prefill_mode<kK8V8>(c.d, a, (unsigned)n_wg, stream); break;
     case kK16V8: launch_prefill_mode<kK16V8>(c.d, a, (unsigned)n_wg, stream); break;
+    case kK8V16: launch_prefill_mode<kK8V16>(c.d, a, (unsigned)n_wg, stream); break;
     default: launch_prefill_mode<kBF16>(c.d, a, (unsigned)n_wg, stream); break;
   }
   return hipGetLastError();

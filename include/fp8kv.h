@@ -51,12 +51,18 @@
 extern "C" {
 #endif
 
-/* Cache element formats ([SKILL] Storage; [HW] Hopper path 3 and the dtype
- * controls).
+/* Cache element formats ([SKILL] Storage; [HW] Hopper path 3, "Account for
+ * V preparation" and the dtype controls of "Collect the profiler evidence").
  *   FP8KV_K8V8   K and V: uint8 e4m3 codes + fp32 scale per (token, KV head)
- *   FP8KV_K16V8  K: bf16; V: e4m3 codes + fp32 scale
- *   FP8KV_BF16   K and V: bf16 (no scales) */
-typedef enum { FP8KV_K8V8 = 0, FP8KV_K16V8 = 1, FP8KV_BF16 = 2 } fp8kv_mode;
+ *   FP8KV_K16V8  K: bf16; V: e4m3 codes + fp32 scale (no K preparation)
+ *   FP8KV_BF16   K and V: bf16 (no scales)
+ *   FP8KV_K8V16  K: e4m3 codes + fp32 scale; V: bf16 (no V preparation) */
+typedef enum {
+  FP8KV_K8V8 = 0,
+  FP8KV_K16V8 = 1,
+  FP8KV_BF16 = 2,
+  FP8KV_K8V16 = 3
+} fp8kv_mode;
 
 typedef enum {
   FP8KV_OK = 0,
@@ -71,10 +77,10 @@ typedef enum {
  * caller).  Layout, token-major within a block:
  *   k, v            [num_blocks][block_size][num_kv_heads][head_dim]
  *                   K8V8: uint8 codes for both; K16V8: k bf16, v uint8;
- *                   BF16: bf16 for both
- *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 only
- *                   (NULL otherwise)
- *   v_scale         same shape, K8V8 and K16V8 (NULL for BF16)
+ *                   BF16: bf16 for both; K8V16: k uint8, v bf16
+ *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 and
+ *                   K8V16 (NULL otherwise)
+ *   v_scale         same shape, K8V8 and K16V8 (NULL otherwise)
  *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
  *                   b is slot t % block_size of block
  *                   block_table[b * max_blocks_per_seq + t / block_size]

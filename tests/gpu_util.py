@@ -49,16 +49,16 @@ def read_rows(cache: KVCache, b: int, n: int) -> dict:
     def grab(x):
         return x[blk, slot].cpu()
 
-    if cache.mode == "K8V8":
+    if cache.mode in binding.K_E4M3:
         out["k8"] = grab(cache.k).numpy()
         out["ks"] = grab(cache.k_scale).numpy()
     else:
         out["k16"] = grab(cache.k).view(torch.int16).numpy().view(np.uint16)
-    if cache.mode == "BF16":
-        out["v16"] = grab(cache.v).view(torch.int16).numpy().view(np.uint16)
-    else:
+    if cache.mode in binding.V_E4M3:
         out["v8"] = grab(cache.v).numpy()
         out["vs"] = grab(cache.v_scale).numpy()
+    else:
+        out["v16"] = grab(cache.v).view(torch.int16).numpy().view(np.uint16)
     return out
 
 

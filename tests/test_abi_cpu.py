@@ -56,7 +56,9 @@ def _desc(**kw):
 
 
 BAD_CACHES = [
-    (dict(mode=3), -1),
+    (dict(mode=4), -1),
+    (dict(mode=3), -1),                 # K8V16 stores no V scale: v_scale must be NULL
+    (dict(mode=3, v_scale=None, k_scale=None), -1),   # ... but a K scale
     (dict(head_dim=96), -4),
     (dict(block_size=8), -1),
     (dict(block_size=0), -1),

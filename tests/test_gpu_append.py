@@ -48,7 +48,7 @@ def _assert_rows_equal(got, want, ctx):
             assert np.array_equal(g, w), (ctx, key, np.argwhere(g != w)[:5])
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("d,hkv,bs", [(128, 2, 16), (64, 4, 32), (128, 8, 0)])
 def test_append_bit_exact(mode, d, hkv, bs):
     lens = np.array([37, 160, 1, 64], np.int32)
@@ -168,12 +168,13 @@ def test_append_bf16_rounding_sweep():
     x = bits.view(np.float32)
     x[~np.isfinite(x) | (np.abs(x) > 3.3e38)] = 1.0
     w = synth.Workload("t", 1, 1, 1, 128, np.array([n], np.int32))
-    for mode in ("K16V8", "BF16"):
+    for mode in ("K16V8", "BF16", "K8V16"):
         cache = make_cache(mode, w)
         append_seq(cache, 0, x, x)
         got = read_rows(cache, 0, n)
-        assert np.array_equal(got["k16"], oracle.bf16_round_f32(x))
-        if mode == "BF16":
+        if mode != "K8V16":
+            assert np.array_equal(got["k16"], oracle.bf16_round_f32(x))
+        if mode != "K16V8":
             assert np.array_equal(got["v16"], oracle.bf16_round_f32(x))
 
 

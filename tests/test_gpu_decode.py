@@ -71,7 +71,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
 def test_decode_small_shapes(mode, shape):
     hq, hkv, d, lens, bs = shape
@@ -90,7 +90,7 @@ def test_decode_b1_gqa4_d64_t128():
     _gate(got, *ref, w.name)
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 def test_decode_b16_gqa8_t2048_full(mode):
     w = synth.decode_b16_gqa8_d128(2048)
     got, *ref = _run_case(mode, w)
@@ -98,7 +98,7 @@ def test_decode_b16_gqa8_t2048_full(mode):
 
 
 @pytest.mark.parametrize("tokens", [77, 512, 8192])
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 def test_decode_b16_gqa8_context_sweep(mode, tokens):
     w = synth.decode_b16_gqa8_d128(tokens, seed=3)
     got, *ref = _run_case(mode, w)
@@ -136,7 +136,7 @@ def test_decode_b64_gqa4_ragged_paged_sampled(mode):
         _gate(got[b, h * g:(h + 1) * g], *ref, (w.name, mode, b, h, int(w.lens[b])))
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("chunk", [64, 256, 1024])
 def test_partials_match_oracle_online(mode, chunk):
     """The split kernel's (M, l, acc) against the oracle's online form with

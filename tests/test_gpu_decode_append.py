@@ -75,7 +75,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
 def test_fused_append_matches_append_then_decode(mode, shape):
     hq, hkv, d, lens, bs = shape

@@ -67,7 +67,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"hq{c[0]}_hkv{c[1]}_d{c[2]}_n{sum(c[3])}")
 def test_prefill_small(mode, case):
     hq, hkv, d, n_q, q_pos0, lens, bs = case
