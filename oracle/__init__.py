@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.orc_bf16_round_array_f32.argtypes = [P, P, ctypes.c_size_t]
         L.orc_quantize_rows.restype = None
         L.orc_quantize_rows.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, P]
+        L.orc_dequantize_rows.restype = None
+        L.orc_dequantize_rows.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, P]
         L.orc_attend_rows.restype = None
         L.orc_attend_rows.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
@@ -126,6 +128,19 @@ def quantize_rows(x):
     scales = np.empty(x.shape[:-1], dtype=np.float32)
     lib().orc_quantize_rows(_ptr(x), n, d, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def dequantize_rows(codes, scales):
+    """bf16 bits of bf16(fp32(value(code) * scale)) per element (the unfused
+    control's conversion); codes uint8 [..., D], scales fp32 [...]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    d = codes.shape[-1]
+    n = codes.size // d if d else 0
+    assert scales.shape == codes.shape[:-1]
+    out = np.empty(codes.shape, dtype=np.uint16)
+    lib().orc_dequantize_rows(_ptr(codes), _ptr(scales), n, d, _ptr(out))
+    return out
 
 
 def store_rows(mode: str, k, v) -> dict:

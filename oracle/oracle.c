@@ -124,6 +124,19 @@ void orc_quantize_rows(const float* x, int64_t n_rows, int d, uint8_t* codes,
   }
 }
 
+void orc_dequantize_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
+                         int d, uint16_t* out) {
+  int64_t r;
+  int j;
+  for (r = 0; r < n_rows; ++r) {
+    for (j = 0; j < d; ++j) {
+      /* every e4m3 value is exact in fp32; the product is rounded once */
+      const float prod = (float)orc_e4m3_value(codes[r * d + j]) * scales[r];
+      out[r * d + j] = orc_bf16_round((double)prod);
+    }
+  }
+}
+
 /* ---- attention -------------------------------------------------------- */
 
 typedef struct {

@@ -75,6 +75,12 @@ void orc_bf16_round_array_f32(const float* x, uint16_t* bits, size_t n);
 void orc_quantize_rows(const float* x, int64_t n_rows, int d,
                        uint8_t* codes, float* scales);
 
+/* The unfused control's conversion of stored rows to bf16: per element
+ * bf16(fp32(value(code) * scale)), the fp32 product rounded to nearest and
+ * then to the nearest-even bf16.  Returns bf16 bit patterns. */
+void orc_dequantize_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
+                         int d, uint16_t* out);
+
 /*
  * Attention of n_rows query rows against one KV head's keys.
  *

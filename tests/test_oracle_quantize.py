@@ -118,3 +118,52 @@ def test_bf16_store_rows():
     assert np.array_equal(s["v8"], c) and np.array_equal(s["vs"], sc)
     b = oracle.store_rows("BF16", k, v)
     assert set(b) == {"k16", "v16"}
+
+
+# ------------------------------------------------------------ dequantisation
+
+def _dequant_reference(codes, scales):
+    """Independent: the e4m3 value table times the scale as an IEEE fp32
+    product (numpy, round to nearest), then torch's RNE cast to bfloat16."""
+    import torch
+    vals = oracle.e4m3_value(codes).astype(np.float32)
+    prod = (vals * scales[..., None].astype(np.float32)).astype(np.float32)
+    return torch.from_numpy(prod).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_dequantize_matches_fp32_product_then_bf16():
+    rng = np.random.default_rng(71)
+    scales = np.concatenate([
+        np.float32(2.0) ** rng.integers(-149, 0, 16).astype(np.float32),   # powers of two
+        rng.random(24, dtype=np.float32) * np.float32(4.0),
+        (rng.random(12, dtype=np.float32) * np.float32(1e-38)),            # subnormal scales
+        np.float32([0.0, 1.0, 1.0 / 448.0, 3.4e38 / 448.0]),
+    ]).astype(np.float32)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (scales.size, 1))
+    codes[:, [0x7F, 0xFF]] = 0                      # no NaN codes in a stored row
+    got = oracle.dequantize_rows(codes, scales)
+    assert np.array_equal(got, _dequant_reference(codes, scales))
+
+
+def test_dequantize_power_of_two_scale_is_exact():
+    """e4m3 values have 4 significant bits (bf16: 8), so with a power-of-two
+    scale inside the normal range the result is the exact product."""
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256).copy()
+    codes[0, [0x7F, 0xFF]] = 0
+    for e in (-20, -6, 0, 5):
+        s = np.array([2.0 ** e], np.float32)
+        got = oracle.bf16_value(oracle.dequantize_rows(codes, s))
+        want = oracle.e4m3_value(codes).astype(np.float64) * 2.0 ** e
+        assert np.array_equal(got, want), e
+
+
+def test_dequantize_round_trip_error():
+    """dequant(quant(x)) is within half an e4m3 step (times the scale) of x,
+    plus the bf16 rounding of the result."""
+    rng = np.random.default_rng(72)
+    x = (rng.standard_normal((200, 64)) * 3).astype(np.float32)
+    codes, scales = oracle.quantize_rows(x)
+    y = oracle.bf16_value(oracle.dequantize_rows(codes, scales))
+    err = np.abs(y - x.astype(np.float64))
+    bound = (np.abs(x) * 2.0 ** -4 + scales[:, None] * 2.0 ** -10) + np.abs(y) * 2.0 ** -8
+    assert np.all(err <= bound)
