@@ -7,7 +7,10 @@ Step: one decode step of batch 16, 16 query / 2 KV heads (GQA 8), head_dim
     stores each sequence's new token (position 2047) and attends it;
   fp8kv_decode_merge: the merge kernel.
 The same step as three kernels (fp8kv_append, fp8kv_decode_partial,
-fp8kv_decode_merge) is timed too and reported as unfused_step_us.
+fp8kv_decode_merge) is timed too and reported as unfused_step_us, and the
+unfused control -- append, the whole cache dequantised to bf16 in HBM
+(fp8kv_dequantize), BF16 split + merge on the copy -- as
+dequant_then_bf16_step_us.
 The headline value is K8V8 KV bytes per step / time per step, HBM-cold: the
 step rotates over 64 copies of the cache (> 1 GB, larger than the 256 MB
 Infinity Cache), so no copy is cache-resident when it is read.  All steps of
@@ -99,6 +102,14 @@ class DecodeBench:
         self.out = torch.empty((w.batch, w.q_heads, d), device=dev)
         self.kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](d)
         self.graph = None
+        self.dq = None
+        if mode == "K8V8":
+            # the unfused control: the cache dequantised to bf16 in HBM, then
+            # the BF16 kernels on the copy
+            self.dq = KVCache.allocate("BF16", n_blocks, bs, w.kv_heads, d, table, dev)
+            self.dq_chunk, self.dq_splits = binding.fp8kv_decode_plan(self.dq, w.batch, g, n)
+            self.dq_pacc = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, d), device=dev)
+            self.dq_pml = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, 2), device=dev)
 
     def split(self, i: int):
         """The step's first kernel: fused append of the new token + split
@@ -129,6 +140,18 @@ class DecodeBench:
         b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
                              self.pacc, self.pml, self.out)
 
+    def step_unfused_dequant(self, i: int):
+        """The unfused control's step: append, dequantise the whole cache to
+        bf16, BF16 split + merge over the copy."""
+        b, w = self.binding, self.w
+        c = self.caches[i % len(self.caches)]
+        b.fp8kv_append(c, self.k_new, self.v_new, self.seq_idx, self.pos)
+        b.fp8kv_dequantize(c, self.dq)
+        b.fp8kv_decode_partial(self.dq, self.q, w.group, self.lens, self.max_len, w.sm_scale,
+                               self.dq_chunk, self.dq_splits, self.dq_pacc, self.dq_pml)
+        b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.dq_splits,
+                             self.dq_pacc, self.dq_pml, self.out)
+
     def _graph(self, fn):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
@@ -146,6 +169,11 @@ class DecodeBench:
         self.graph = self._graph(self.step)
         self.split_graph = self._graph(self.split)
         self.unfused_graph = self._graph(self.step_unfused)
+        self.dq_graph = None
+        if self.dq is not None:
+            self.step_unfused_dequant(0)
+            torch.cuda.synchronize()
+            self.dq_graph = self._graph(self.step_unfused_dequant)
 
     def graph_avg_ms(self, graph, replays: int) -> float:
         """Average time of one rotation entry of `graph` (ms), back to back."""
@@ -210,12 +238,14 @@ def bench_decode(mode, w, steps, warmup, copies):
     spl, mrg = bench.kernel_ms()
     split_avg = bench.split_avg_ms(reps)
     unfused = bench.graph_avg_ms(bench.unfused_graph, reps)
+    dq = bench.graph_avg_ms(bench.dq_graph, reps) if bench.dq_graph is not None else None
     step_ms = ms / n_steps
     res = {"ms_per_step": step_ms, "steps": n_steps, "kv_bytes": bench.kv_bytes,
            "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
            "kernel_us_event_pairs": {"split_with_append": spl * 1e3, "merge": mrg * 1e3},
            "split_us": split_avg * 1e3,
            "unfused_step_us": unfused * 1e3,
+           "dequant_then_bf16_step_us": None if dq is None else dq * 1e3,
            "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
     res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
     return res, bench
@@ -499,6 +529,7 @@ def main():
         "split_us": head["split_us"],
         "kernel_us_event_pairs": head["kernel_us_event_pairs"],
         "unfused_step_us": head["unfused_step_us"],
+        "dequant_then_bf16_step_us": head["dequant_then_bf16_step_us"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_partial_kernel<K8V8,128,append>",

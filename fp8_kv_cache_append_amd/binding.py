@@ -30,7 +30,7 @@ FP8KV_ERR_UNSUPPORTED = -4
 EXPORTS = ("fp8kv_append", "fp8kv_decode_plan", "fp8kv_decode_workspace_bytes",
            "fp8kv_decode_partial", "fp8kv_decode_merge", "fp8kv_decode",
            "fp8kv_decode_append", "fp8kv_decode_append_partial", "fp8kv_prefill",
-           "fp8kv_strerror")
+           "fp8kv_dequantize", "fp8kv_strerror")
 
 
 class Fp8kvError(RuntimeError):
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "fp8kv_decode_append_partial": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F,
                                                            I32, I32, P, P, P]),
             "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, I32, F, P, P]),
+            "fp8kv_dequantize": (ctypes.c_int, [C, C, P]),
             "fp8kv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
@@ -236,6 +237,14 @@ def fp8kv_prefill(cache: KVCache, q, gqa_group: int, cu_q, q_pos0, seq_lens,
                                _ptr(seq_lens), int(seq_lens.shape[0]), int(q.shape[0]),
                                max_q_len, sm_scale, _ptr(out), _stream(stream)),
            "fp8kv_prefill")
+
+
+def fp8kv_dequantize(src: KVCache, dst: KVCache, stream=None) -> None:
+    """Convert every row of src into dst (a BF16-mode cache of the same
+    geometry): the unfused control."""
+    ds, dd = src.desc(), dst.desc()
+    _check(lib().fp8kv_dequantize(ctypes.byref(ds), ctypes.byref(dd), _stream(stream)),
+           "fp8kv_dequantize")
 
 
 def fp8kv_strerror(status: int) -> str:

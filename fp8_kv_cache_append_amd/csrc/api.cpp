@@ -281,6 +281,20 @@ int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new, const floa
                      sm_scale, out, workspace, workspace_bytes, stream);
 }
 
+int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst, void* stream) {
+  int st = validate_cache(src);
+  if (st != FP8KV_OK) return st;
+  if ((st = validate_cache(dst)) != FP8KV_OK) return st;
+  if (dst->mode != FP8KV_BF16 || dst->num_blocks != src->num_blocks ||
+      dst->block_size != src->block_size || dst->num_kv_heads != src->num_kv_heads ||
+      dst->head_dim != src->head_dim)
+    return FP8KV_ERR_INVALID;
+  if (dst->k == src->k || dst->v == src->v) return FP8KV_ERR_INVALID;  // no in-place
+  if ((st = check_device()) != FP8KV_OK) return st;
+  return launch_status(
+      fp8kv::launch_dequantize(view_of(src), view_of(dst), static_cast<hipStream_t>(stream)));
+}
+
 int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
                   const int32_t* cu_q, const int32_t* q_pos0, const int32_t* seq_lens,
                   int32_t batch, int32_t total_q, int32_t max_q_len, float sm_scale, float* out,

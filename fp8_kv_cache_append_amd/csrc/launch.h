@@ -52,6 +52,9 @@ hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_split
                                const float* part_acc, const float* part_ml, float* out,
                                hipStream_t stream);
 
+// Every row of src into dst (BF16 mode, same geometry).
+hipError_t launch_dequantize(const CacheView& src, const CacheView& dst, hipStream_t stream);
+
 hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
                           const int32_t* cu_q, const int32_t* q_pos0,
                           const int32_t* seq_lens, int batch, int total_q, int max_q_len,

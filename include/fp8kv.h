@@ -244,6 +244,19 @@ int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q,
                   int32_t batch, int32_t total_q, int32_t max_q_len,
                   float sm_scale, float* out, void* stream);
 
+/*
+ * The unfused control ("Fused KV-cache quantization"; [HW] Collect the
+ * profiler evidence): every row of src, in any mode, converted into dst, a
+ * BF16-mode cache of the same num_blocks, block_size, num_kv_heads and
+ * head_dim (its own buffers; block tables are not read).  An e4m3 element
+ * becomes bf16(fp32(value(code) * scale)) -- the fp32 product rounded once,
+ * then to the nearest-even bf16; a bf16 element is copied.  Attention on dst
+ * with the BF16 kernels is then the pipeline that dequantises the cache in
+ * HBM instead of converting only the active tile on chip.
+ */
+int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst,
+                     void* stream);
+
 /* Static description of a status code. */
 const char* fp8kv_strerror(int status);
 

@@ -212,3 +212,17 @@ def test_split_window_rule_matches_brute_force():
         for L in (1, 300, 5000, (1 << 20) // bs * bs):
             r, c, s = _plan(d, 64, 4, L)
             assert r == 0 and _max_blocks_spanned(c, bs) <= 64, (bs, L, c)
+
+
+def test_dequantize_rejects_bad_arguments():
+    lib = binding.lib()
+    src = _desc()                                              # K8V8
+    good = _desc(mode=2, k=FAKE + 4096, v=FAKE + 8192, k_scale=None, v_scale=None)
+    not_bf16 = _desc(mode=1, k=FAKE + 4096, v=FAKE + 8192, k_scale=None)
+    other_shape = _desc(mode=2, k=FAKE + 4096, v=FAKE + 8192, k_scale=None, v_scale=None,
+                        num_blocks=5)
+    in_place = _desc(mode=2, k_scale=None, v_scale=None)
+    for dst in (not_bf16, other_shape, in_place):
+        assert lib.fp8kv_dequantize(ctypes.byref(src), ctypes.byref(dst), None) == -1
+    assert lib.fp8kv_dequantize(None, ctypes.byref(good), None) == -1
+    assert lib.fp8kv_dequantize(ctypes.byref(src), None, None) == -1
