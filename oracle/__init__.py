@@ -65,6 +65,15 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
             P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, P, P, P, P]
+        L.orc_attend_rows_q8.restype = None
+        L.orc_attend_rows_q8.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P]
+        L.orc_attend_rows_online_q8.restype = None
+        L.orc_attend_rows_online_q8.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, P, P, P, P]
         _lib = L
     return _lib
 
@@ -143,6 +152,14 @@ def dequantize_rows(codes, scales):
     return out
 
 
+def quantize_q(q_bits):
+    """Narrow QK: the bf16 query rows quantised once per decode step like
+    cache rows (hardware notes, "Operating model" path 2).  q_bits uint16
+    [..., D]; returns (codes uint8 [..., D], q_scale fp32 [...])."""
+    q = bf16_value(q_bits).astype(np.float32)   # exact: bf16 is an fp32 prefix
+    return quantize_rows(q)
+
+
 def store_rows(mode: str, k, v) -> dict:
     """What the cache holds for fp32 K and V rows in the given mode.
 
@@ -173,39 +190,58 @@ def _head_view(store: dict, h: int) -> dict:
     return out
 
 
+def _kv_args(kv: dict):
+    return (_ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("k16"), np.uint16)),
+            _ptr(_c(kv.get("ks"), np.float32)), _ptr(_c(kv.get("v8"), np.uint8)),
+            _ptr(_c(kv.get("v16"), np.uint16)), _ptr(_c(kv.get("vs"), np.float32)))
+
+
 def attend_rows(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
-                round_p: bool = True, bounds: bool = False):
+                round_p: bool = True, bounds: bool = False, q8=None):
     """Two-pass attention of query rows q_bits [R, D] against one KV head.
 
     kv holds the stores of that head ([T, D] and [T]); n_valid[r] keys are
     visible to row r.  Returns fp64 [R, D]; with bounds=True returns
     (out, lo, hi) where [lo, hi] holds every output reachable by rounding an
     ambiguous P (one within fp32 noise of a bf16 midpoint) either way.
+    q8 = (codes uint8 [R, D], q_scale fp32 [R]): narrow QK on these query
+    codes instead of q_bits (which may then be None).
     """
-    q_bits = _c(q_bits, np.uint16)
-    r, d = q_bits.shape
+    if q8 is None:
+        q_bits = _c(q_bits, np.uint16)
+        r, d = q_bits.shape
+    else:
+        qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
+        r, d = qc.shape
+        assert qs.shape == (r,)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
     out = np.empty((r, d), dtype=np.float64)
     lo = np.empty((r, d), dtype=np.float64) if bounds else None
     hi = np.empty((r, d), dtype=np.float64) if bounds else None
-    lib().orc_attend_rows(
-        MODES[mode], d, r, _ptr(q_bits), n_keys,
-        _ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("k16"), np.uint16)),
-        _ptr(_c(kv.get("ks"), np.float32)), _ptr(_c(kv.get("v8"), np.uint8)),
-        _ptr(_c(kv.get("v16"), np.uint16)), _ptr(_c(kv.get("vs"), np.float32)),
-        _ptr(n_valid), float(sm_scale), int(bool(round_p)), _ptr(out), _ptr(lo), _ptr(hi))
+    tail = (_ptr(n_valid), float(sm_scale), int(bool(round_p)), _ptr(out), _ptr(lo), _ptr(hi))
+    if q8 is None:
+        lib().orc_attend_rows(MODES[mode], d, r, _ptr(q_bits), n_keys, *_kv_args(kv), *tail)
+    else:
+        lib().orc_attend_rows_q8(MODES[mode], d, r, _ptr(qc), _ptr(qs), n_keys, *_kv_args(kv),
+                                 *tail)
     return (out, lo, hi) if bounds else out
 
 
 def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
-                       tile: int, split: int, round_p: bool = True):
+                       tile: int, split: int, round_p: bool = True, q8=None):
     """Online (tiled, split, merged) attention; see orc_attend_rows_online.
 
     Returns (out [R, D], part_acc [S, R, D], part_l [S, R], part_m [S, R]).
+    q8 as for attend_rows.
     """
-    q_bits = _c(q_bits, np.uint16)
-    r, d = q_bits.shape
+    if q8 is None:
+        q_bits = _c(q_bits, np.uint16)
+        r, d = q_bits.shape
+    else:
+        qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
+        r, d = qc.shape
+        assert qs.shape == (r,)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
     n_splits = -(-n_keys // split) if n_keys else 0
@@ -213,13 +249,14 @@ def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     pacc = np.empty((max(n_splits, 1), r, d), dtype=np.float64)
     pl = np.empty((max(n_splits, 1), r), dtype=np.float64)
     pm = np.empty((max(n_splits, 1), r), dtype=np.float64)
-    lib().orc_attend_rows_online(
-        MODES[mode], d, r, _ptr(q_bits), n_keys,
-        _ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("k16"), np.uint16)),
-        _ptr(_c(kv.get("ks"), np.float32)), _ptr(_c(kv.get("v8"), np.uint8)),
-        _ptr(_c(kv.get("v16"), np.uint16)), _ptr(_c(kv.get("vs"), np.float32)),
-        _ptr(n_valid), float(sm_scale), int(bool(round_p)), int(tile),
-        int(split), _ptr(pacc), _ptr(pl), _ptr(pm), _ptr(out))
+    tail = (_ptr(n_valid), float(sm_scale), int(bool(round_p)), int(tile), int(split),
+            _ptr(pacc), _ptr(pl), _ptr(pm), _ptr(out))
+    if q8 is None:
+        lib().orc_attend_rows_online(MODES[mode], d, r, _ptr(q_bits), n_keys, *_kv_args(kv),
+                                     *tail)
+    else:
+        lib().orc_attend_rows_online_q8(MODES[mode], d, r, _ptr(qc), _ptr(qs), n_keys,
+                                        *_kv_args(kv), *tail)
     return out, pacc[:n_splits], pl[:n_splits], pm[:n_splits]
 
 
@@ -231,17 +268,19 @@ def _n_keys(kv: dict) -> int:
 
 
 def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
-           pairs=None, round_p: bool = True, bounds: bool = False):
+           pairs=None, round_p: bool = True, bounds: bool = False, q8: bool = False):
     """Decode attention from the fp32 K/V of each sequence.
 
     q_bits  bf16 bits [B, Hq, D]
     k_seqs  list of B fp32 arrays [len_b, Hkv, D] (v_seqs alike)
     pairs   optional iterable of (b, kv_head) to compute; other rows are NaN
+    q8      narrow QK: Q quantised once (quantize_q), scores on its codes
     Returns fp64 [B, Hq, D] (with bounds=True: (out, lo, hi), see
     attend_rows).  The oracle quantises each sequence itself.
     """
     q_bits = np.asarray(q_bits, dtype=np.uint16)
     b_n, hq, d = q_bits.shape
+    qc, qs = quantize_q(q_bits) if q8 else (None, None)
     out = np.full((b_n, hq, d), np.nan)
     lo, hi = out.copy(), out.copy()
     if b_n == 0:
@@ -259,7 +298,9 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
         for h in heads:
             rows = q_bits[b, h * g:(h + 1) * g]
             sl = slice(h * g, (h + 1) * g)
-            res = attend_rows(mode, rows, _head_view(store, h), n, sm_scale, round_p, bounds)
+            rq8 = (qc[b, sl], qs[b, sl]) if q8 else None
+            res = attend_rows(mode, rows, _head_view(store, h), n, sm_scale, round_p, bounds,
+                              q8=rq8)
             if bounds:
                 out[b, sl], lo[b, sl], hi[b, sl] = res
             else:

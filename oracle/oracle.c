@@ -202,13 +202,29 @@ static double p_window(const kv_view* kv, const double* qv, int t, double c) {
          ldexp(1.0, -20);
 }
 
-void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
-                     int n_keys, const uint8_t* k8, const uint16_t* k16,
-                     const float* ks, const uint8_t* v8, const uint16_t* v16,
-                     const float* vs, const int32_t* n_valid, float sm_scale,
-                     int round_p, double* out, double* out_lo, double* out_hi) {
+/* Query row r as fp64 values, and the row's score constant: bf16 rows
+ * (q16) are their values with c = sm_scale * log2(e); e4m3 rows (q8) are the
+ * code values, and the row's scale joins the constant outside the dot
+ * product (CDNA 3 section of the hardware notes). */
+static double query_row(int d, int r, const uint16_t* q16, const uint8_t* q8,
+                        const float* q_scale, double c, double* qv) {
+  int j;
+  if (q8) {
+    for (j = 0; j < d; ++j) qv[j] = orc_e4m3_value(q8[(size_t)r * d + j]);
+    return c * (double)q_scale[r];
+  }
+  for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q16[(size_t)r * d + j]);
+  return c;
+}
+
+static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
+                        const uint8_t* q8, const float* q_scale, int n_keys,
+                        const uint8_t* k8, const uint16_t* k16, const float* ks,
+                        const uint8_t* v8, const uint16_t* v16, const float* vs,
+                        const int32_t* n_valid, float sm_scale, int round_p,
+                        double* out, double* out_lo, double* out_hi) {
   kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
-  double c = (double)sm_scale * ORC_LOG2E;
+  const double c0 = (double)sm_scale * ORC_LOG2E;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
   double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
@@ -220,7 +236,7 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
     int nv = clamp_valid(n_valid[r], n_keys);
     double smax = -INFINITY, m, l = 0.0;
     double* o = out + (size_t)r * d;
-    for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q[(size_t)r * d + j]);
+    const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
     if (nv == 0) { /* no visible key: the row outputs 0 */
       for (j = 0; j < d; ++j) o[j] = 0.0;
       if (bounds)
@@ -267,16 +283,34 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
   free(ahi);
 }
 
-void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
-                            int n_keys, const uint8_t* k8, const uint16_t* k16,
-                            const float* ks, const uint8_t* v8,
-                            const uint16_t* v16, const float* vs,
-                            const int32_t* n_valid, float sm_scale,
-                            int round_p, int tile, int split,
-                            double* part_acc, double* part_l, double* part_m,
-                            double* out) {
+void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
+                     int n_keys, const uint8_t* k8, const uint16_t* k16,
+                     const float* ks, const uint8_t* v8, const uint16_t* v16,
+                     const float* vs, const int32_t* n_valid, float sm_scale,
+                     int round_p, double* out, double* out_lo, double* out_hi) {
+  attend_rows(mode, d, n_rows, q, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+              sm_scale, round_p, out, out_lo, out_hi);
+}
+
+void orc_attend_rows_q8(int mode, int d, int n_rows, const uint8_t* q8,
+                        const float* q_scale, int n_keys, const uint8_t* k8,
+                        const uint16_t* k16, const float* ks, const uint8_t* v8,
+                        const uint16_t* v16, const float* vs,
+                        const int32_t* n_valid, float sm_scale, int round_p,
+                        double* out, double* out_lo, double* out_hi) {
+  attend_rows(mode, d, n_rows, NULL, q8, q_scale, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+              sm_scale, round_p, out, out_lo, out_hi);
+}
+
+static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
+                               const uint8_t* q8, const float* q_scale, int n_keys,
+                               const uint8_t* k8, const uint16_t* k16, const float* ks,
+                               const uint8_t* v8, const uint16_t* v16, const float* vs,
+                               const int32_t* n_valid, float sm_scale, int round_p,
+                               int tile, int split, double* part_acc, double* part_l,
+                               double* part_m, double* out) {
   kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
-  double c = (double)sm_scale * ORC_LOG2E;
+  const double c0 = (double)sm_scale * ORC_LOG2E;
   int n_splits = n_keys > 0 ? (n_keys + split - 1) / split : 0;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
   double* s = (double*)malloc(sizeof(double) * (size_t)tile);
@@ -288,7 +322,7 @@ void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
   for (r = 0; r < n_rows; ++r) {
     int nv = clamp_valid(n_valid[r], n_keys);
     double mstar = -INFINITY, lsum = 0.0;
-    for (j = 0; j < d; ++j) qv[j] = orc_bf16_value(q[(size_t)r * d + j]);
+    const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
     for (sp = 0; sp < n_splits; ++sp) {
       int k_lo = sp * split;
       int k_hi = k_lo + split < n_keys ? k_lo + split : n_keys;
@@ -343,4 +377,27 @@ void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
   free(sacc);
   free(sl);
   free(sm);
+}
+
+void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
+                            int n_keys, const uint8_t* k8, const uint16_t* k16,
+                            const float* ks, const uint8_t* v8,
+                            const uint16_t* v16, const float* vs,
+                            const int32_t* n_valid, float sm_scale,
+                            int round_p, int tile, int split,
+                            double* part_acc, double* part_l, double* part_m,
+                            double* out) {
+  attend_rows_online(mode, d, n_rows, q, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs,
+                     n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
+}
+
+void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
+                               const float* q_scale, int n_keys, const uint8_t* k8,
+                               const uint16_t* k16, const float* ks, const uint8_t* v8,
+                               const uint16_t* v16, const float* vs,
+                               const int32_t* n_valid, float sm_scale, int round_p,
+                               int tile, int split, double* part_acc, double* part_l,
+                               double* part_m, double* out) {
+  attend_rows_online(mode, d, n_rows, NULL, q8, q_scale, n_keys, k8, k16, ks, v8, v16, vs,
+                     n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
 }

@@ -134,6 +134,32 @@ void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
                             double* part_acc, double* part_l, double* part_m,
                             double* out);
 
+/*
+ * Narrow QK (path 2 of the "Operating model" section of the hardware notes,
+ * and its "Use a native narrow QK path" item): the query rows are quantised
+ * once per decode step exactly like cache rows (orc_quantize_rows: q_scale =
+ * fp32(amax / 448), codes e4m3(fp32(q / q_scale))) and the score takes the
+ * code values, with the row's scale outside the dot product (CDNA 3
+ * section):
+ *   s_t = (sum_d value(qc_d) * K_td) * q_scale * ks_t * sm_scale * log2(e)
+ * Everything after the score is as above.  q8: e4m3 codes [n_rows][d];
+ * q_scale: fp32 [n_rows].  Other arguments as for the bf16 forms.
+ */
+void orc_attend_rows_q8(int mode, int d, int n_rows, const uint8_t* q8,
+                        const float* q_scale, int n_keys, const uint8_t* k8,
+                        const uint16_t* k16, const float* ks, const uint8_t* v8,
+                        const uint16_t* v16, const float* vs,
+                        const int32_t* n_valid, float sm_scale, int round_p,
+                        double* out, double* out_lo, double* out_hi);
+
+void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
+                               const float* q_scale, int n_keys, const uint8_t* k8,
+                               const uint16_t* k16, const float* ks, const uint8_t* v8,
+                               const uint16_t* v16, const float* vs,
+                               const int32_t* n_valid, float sm_scale, int round_p,
+                               int tile, int split, double* part_acc, double* part_l,
+                               double* part_m, double* out);
+
 #ifdef __cplusplus
 }
 #endif
