@@ -189,16 +189,26 @@ static int clamp_valid(int nv, int n_keys) {
   return nv > n_keys ? n_keys : nv;
 }
 
+/* Narrow QK: the error allowed to the matrix instruction's own sum of the d
+ * exact code products, relative to their absolute sum.  The instruction's
+ * sum is not the correctly rounded fp32 one (it rounds, unbiased, at about
+ * 2^-13 of that absolute sum: measured worst 2^-12.2 over 32768 dot products
+ * of random codes on gfx950); 2^-10 leaves a margin of four. */
+#define ORC_NARROW_SUM_ERR 0x1p-10
+
 /* Bound on |fp32 score - exact score| in log2 units for any summation order
  * of the d exact products (the classic (n-1)u sum|x_i| bound, doubled, plus
- * the roundings of the two scale products), as a relative window on
- * p = 2^(s - M) with 2^-20 added for an fp32 exp2 within a few ulp. */
-static double p_window(const kv_view* kv, const double* qv, int t, double c) {
+ * the roundings of the scale products; on the narrow path also the
+ * instruction's sum error above), as a relative window on p = 2^(s - M)
+ * with 2^-20 added for an fp32 exp2 within a few ulp. */
+static double p_window(const kv_view* kv, const double* qv, int t, double c, int narrow) {
   double sabs = 0.0;
   int j;
   for (j = 0; j < kv->d; ++j) sabs += fabs(qv[j] * k_elem(kv, t, j));
   sabs *= fabs(k_scale(kv, t) * c);
-  return 0.6931471805599453 * 2.0 * (double)(kv->d + 4) * ldexp(1.0, -24) * sabs +
+  return 0.6931471805599453 *
+             (2.0 * (double)(kv->d + 4) * ldexp(1.0, -24) +
+              (narrow ? ORC_NARROW_SUM_ERR : 0.0)) * sabs +
          ldexp(1.0, -20);
 }
 
@@ -259,7 +269,7 @@ static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
       if (bounds) {
         /* Both bf16 neighbours are valid roundings when p * v_scale lies
          * within fp32 noise of a rounding midpoint. */
-        double win = round_p ? p_window(&kv, qv, t, c) : 0.0;
+        double win = round_p ? p_window(&kv, qv, t, c, q8 != NULL) : 0.0;
         double wa = round_p ? p_folded(&kv, p * (1.0 - win), t, 1) : w;
         double wb = round_p ? p_folded(&kv, p * (1.0 + win), t, 1) : w;
         for (j = 0; j < d; ++j) {

@@ -14,6 +14,8 @@ values and the row's scale sits outside the dot product (CDNA 3 section).
 * The online form (tiles, splits, power-of-two merge) equals the two-pass
   form on the narrow path too.
 * Negative control: dropping the query scale moves the output past the gate.
+* The narrow path's rounding interval also allows the matrix instruction's
+  sum error: on lossless queries it contains the bf16 path's interval.
 * The narrow path's error against bf16 Q is reported in its expected range.
 """
 import numpy as np
@@ -122,3 +124,18 @@ def test_narrow_error_against_bf16_q_in_expected_range():
     err = oracle.rel_l2(narrow, wide)
     print(f"narrow QK vs bf16 Q (K8V8): rel_l2 = {err:.4f}")
     assert 0.005 < err < 0.2
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_narrow_rounding_interval_contains_the_bf16_one(mode):
+    rng = np.random.default_rng(6)
+    q_bits, _, _ = _lossless_q(rng, 1, 8, 64)
+    _, ks, vs = _inputs(7, b=1, hq=8, hkv=1, d=64, t=90)
+    sm = 1.0 / 8.0
+    w, wlo, whi = oracle.decode(mode, q_bits, ks, vs, sm, bounds=True)
+    n, nlo, nhi = oracle.decode(mode, q_bits, ks, vs, sm, bounds=True, q8=True)
+    assert oracle.rel_l2(n, w) < 1e-12
+    tol = 1e-12 * (np.abs(w) + 1)
+    assert np.all(nlo <= wlo + tol) and np.all(nhi >= whi - tol)
+    assert np.all(nlo <= n + tol) and np.all(n <= nhi + tol)
+    assert np.sum(nhi - nlo) > np.sum(whi - wlo)   # strictly wider somewhere
