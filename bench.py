@@ -19,6 +19,11 @@ timed region).  Per-kernel durations come from HIP event pairs around each
 kernel of one more rotation, launched on the same stream right behind the
 timed replays (see DecodeBench.run).
 
+Narrow QK (fp8kv_decode_append_q8: Q quantised to e4m3 in the split kernel,
+fp8 QK) is timed on the same rotation for the e4m3-K modes
+(narrow_qk_step_us), with its output's relative L2 against the bf16-Q step
+(narrow_qk_vs_bf16q_rel_l2: the Q rounding's cost).
+
 Extra fields: the K16V8 and BF16 controls (same protocol), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
 the context sweep of the same shape at 77/512/2048/8192 keys in all four
@@ -101,6 +106,12 @@ class DecodeBench:
         self.pml = torch.empty((w.batch, w.kv_heads, self.splits, g, 2), device=dev)
         self.out = torch.empty((w.batch, w.q_heads, d), device=dev)
         self.kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](d)
+        # narrow QK (Q quantised to e4m3 in the kernel): e4m3-K modes only
+        self.narrow = mode in ("K8V8", "K8V16")
+        if self.narrow:
+            ws_bytes = binding.fp8kv_decode_workspace_bytes(base, w.batch, g, n)
+            self.ws = torch.empty(ws_bytes // 4 + 4, device=dev)
+            self.out_q8 = torch.empty_like(self.out)
         self.graph = None
         self.dq = None
         if mode == "K8V8":
@@ -129,6 +140,14 @@ class DecodeBench:
         b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
                              self.pacc, self.pml, self.out)
         if ev: ev[2].record()
+
+    def step_q8(self, i: int):
+        """The same step with narrow QK (fp8kv_decode_append_q8: the same two
+        kernels, Q quantised in the split kernel, fp8 QK)."""
+        w = self.w
+        self.binding.fp8kv_decode_append_q8(
+            self.caches[i % len(self.caches)], self.k_new, self.v_new, self.q, w.group,
+            self.lens, self.max_len, w.sm_scale, self.out_q8, self.ws)
 
     def step_unfused(self, i: int):
         """The same step as three kernels: append, split, merge."""
@@ -169,6 +188,11 @@ class DecodeBench:
         self.graph = self._graph(self.step)
         self.split_graph = self._graph(self.split)
         self.unfused_graph = self._graph(self.step_unfused)
+        self.q8_graph = None
+        if self.narrow:
+            self.step_q8(0)
+            torch.cuda.synchronize()
+            self.q8_graph = self._graph(self.step_q8)
         self.dq_graph = None
         if self.dq is not None:
             self.step_unfused_dequant(0)
@@ -239,6 +263,16 @@ def bench_decode(mode, w, steps, warmup, copies):
     split_avg = bench.split_avg_ms(reps)
     unfused = bench.graph_avg_ms(bench.unfused_graph, reps)
     dq = bench.graph_avg_ms(bench.dq_graph, reps) if bench.dq_graph is not None else None
+    q8 = bench.graph_avg_ms(bench.q8_graph, reps) if bench.q8_graph is not None else None
+    q8_err = None
+    if q8 is not None:
+        # narrow against bf16-Q outputs of the same step on the same cache
+        bench.step(0)
+        bench.step_q8(0)
+        bench.torch.cuda.synchronize()
+        a = bench.out_q8.double()
+        r = bench.out.double()
+        q8_err = float(((a - r).norm() / r.norm()).item())
     step_ms = ms / n_steps
     res = {"ms_per_step": step_ms, "steps": n_steps, "kv_bytes": bench.kv_bytes,
            "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
@@ -246,6 +280,8 @@ def bench_decode(mode, w, steps, warmup, copies):
            "split_us": split_avg * 1e3,
            "unfused_step_us": unfused * 1e3,
            "dequant_then_bf16_step_us": None if dq is None else dq * 1e3,
+           "narrow_qk_step_us": None if q8 is None else q8 * 1e3,
+           "narrow_qk_vs_bf16q_rel_l2": q8_err,
            "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
     res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
     return res, bench
@@ -269,7 +305,8 @@ def bench_sweep(steps, warmup, copies, head):
                 r, _ = bench_decode(mode, w, steps, warmup, copies)
             row[mode] = {"us_per_step": r["ms_per_step"] * 1e3, "split_us": r["split_us"],
                          "kv_gbs": r["kv_gbs"], "pct_roofline": r["pct_roofline"],
-                         "unfused_step_us": r["unfused_step_us"]}
+                         "unfused_step_us": r["unfused_step_us"],
+                         "narrow_qk_step_us": r["narrow_qk_step_us"]}
         row["K8V8_speedup_vs_K16V8"] = row["K16V8"]["us_per_step"] / row["K8V8"]["us_per_step"]
         row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
         # time the BF16 control saves by storing one side in e4m3 ("Account
@@ -530,6 +567,8 @@ def main():
         "kernel_us_event_pairs": head["kernel_us_event_pairs"],
         "unfused_step_us": head["unfused_step_us"],
         "dequant_then_bf16_step_us": head["dequant_then_bf16_step_us"],
+        "narrow_qk_step_us": head["narrow_qk_step_us"],
+        "narrow_qk_vs_bf16q_rel_l2": head["narrow_qk_vs_bf16q_rel_l2"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_partial_kernel<K8V8,128,append>",

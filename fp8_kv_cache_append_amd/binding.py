@@ -29,8 +29,8 @@ FP8KV_ERR_UNSUPPORTED = -4
 # Every symbol include/fp8kv.h declares.
 EXPORTS = ("fp8kv_append", "fp8kv_decode_plan", "fp8kv_decode_workspace_bytes",
            "fp8kv_decode_partial", "fp8kv_decode_merge", "fp8kv_decode",
-           "fp8kv_decode_append", "fp8kv_decode_append_partial", "fp8kv_prefill",
-           "fp8kv_dequantize", "fp8kv_strerror")
+           "fp8kv_decode_append", "fp8kv_decode_append_partial", "fp8kv_decode_q8",
+           "fp8kv_decode_append_q8", "fp8kv_prefill", "fp8kv_dequantize", "fp8kv_strerror")
 
 
 class Fp8kvError(RuntimeError):
@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_size_t, P]),
             "fp8kv_decode_append": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F, P, P,
                                                    ctypes.c_size_t, P]),
+            "fp8kv_decode_q8": (ctypes.c_int, [C, P, I32, P, I32, I32, F, P, P,
+                                               ctypes.c_size_t, P]),
+            "fp8kv_decode_append_q8": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F, P, P,
+                                                      ctypes.c_size_t, P]),
             "fp8kv_decode_append_partial": (ctypes.c_int, [C, P, P, P, I32, P, I32, I32, F,
                                                            I32, I32, P, P, P]),
             "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, I32, F, P, P]),
@@ -206,6 +210,28 @@ def fp8kv_decode(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
     _check(lib().fp8kv_decode(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
                               int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
                               _ptr(workspace), ws_bytes, _stream(stream)), "fp8kv_decode")
+
+
+def fp8kv_decode_q8(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
+                    sm_scale: float, out, workspace, stream=None) -> None:
+    """fp8kv_decode with narrow QK (Q quantised to e4m3 in the kernel)."""
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8kv_decode_q8(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
+                                 int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "fp8kv_decode_q8")
+
+
+def fp8kv_decode_append_q8(cache: KVCache, k_new, v_new, q, gqa_group: int, seq_lens,
+                           max_seq_len: int, sm_scale: float, out, workspace,
+                           stream=None) -> None:
+    """fp8kv_decode_append with narrow QK."""
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fp8kv_decode_append_q8(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                        gqa_group, _ptr(seq_lens), int(seq_lens.shape[0]),
+                                        max_seq_len, sm_scale, _ptr(out), _ptr(workspace),
+                                        ws_bytes, _stream(stream)), "fp8kv_decode_append_q8")
 
 
 def fp8kv_decode_append(cache: KVCache, k_new, v_new, q, gqa_group: int, seq_lens,

@@ -177,9 +177,12 @@ namespace {
 int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new,
                         const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens,
                         int32_t batch, int32_t max_seq_len, float sm_scale, int32_t chunk_tokens,
-                        int32_t n_splits, float* part_acc, float* part_ml, void* stream) {
+                        int32_t n_splits, float* part_acc, float* part_ml, bool q8,
+                        void* stream) {
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
+  if (q8 && cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16)
+    return FP8KV_ERR_UNSUPPORTED;  // narrow QK takes the K codes as they are
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
   if (!split_fits_table_window(chunk_tokens, cache->block_size)) return FP8KV_ERR_INVALID;
   if ((int64_t)n_splits * chunk_tokens < max_seq_len) return FP8KV_ERR_INVALID;
@@ -195,7 +198,7 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(fp8kv::launch_decode_partial(
       view_of(cache), q, gqa_group, seq_lens, batch, log2_scale(sm_scale), chunk_tokens,
-      n_splits, part_acc, part_ml, k_new, v_new, static_cast<hipStream_t>(stream)));
+      n_splits, part_acc, part_ml, k_new, v_new, q8, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -206,7 +209,7 @@ int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q, int32_t gq
                          float* part_acc, float* part_ml, void* stream) {
   return decode_partial_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch,
                              max_seq_len, sm_scale, chunk_tokens, n_splits, part_acc, part_ml,
-                             stream);
+                             false, stream);
 }
 
 int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
@@ -216,7 +219,7 @@ int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
                                 float* part_acc, float* part_ml, void* stream) {
   if (batch > 0 && n_splits > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
   return decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
-                             sm_scale, chunk_tokens, n_splits, part_acc, part_ml, stream);
+                             sm_scale, chunk_tokens, n_splits, part_acc, part_ml, false, stream);
 }
 
 int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
@@ -241,10 +244,12 @@ namespace {
 int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new,
                 const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
                 int32_t max_seq_len, float sm_scale, float* out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, bool q8, void* stream) {
   int32_t chunk = 0, splits = 0;
   int st = fp8kv_decode_plan(cache, batch, gqa_group, max_seq_len, &chunk, &splits);
   if (st != FP8KV_OK) return st;
+  if (q8 && cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16)
+    return FP8KV_ERR_UNSUPPORTED;
   if (batch == 0) return FP8KV_OK;
   const size_t acc_floats = (size_t)batch * cache->num_kv_heads * splits * gqa_group *
                             cache->head_dim;
@@ -257,7 +262,7 @@ int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new
   if (splits > 0 && (!q || !seq_lens || !aligned(q, 16) || !aligned(seq_lens, 4)))
     return FP8KV_ERR_INVALID;
   st = decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
-                           sm_scale, chunk, splits, part_acc, part_ml, stream);
+                           sm_scale, chunk, splits, part_acc, part_ml, q8, stream);
   if (st != FP8KV_OK) return st;
   return fp8kv_decode_merge(batch, cache->num_kv_heads, gqa_group, cache->head_dim, splits,
                             part_acc, part_ml, out, stream);
@@ -269,7 +274,14 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
                  const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
                  float* out, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch, max_seq_len,
-                     sm_scale, out, workspace, workspace_bytes, stream);
+                     sm_scale, out, workspace, workspace_bytes, false, stream);
+}
+
+int fp8kv_decode_q8(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
+                    const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float sm_scale,
+                    float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, true, stream);
 }
 
 int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new, const float* v_new,
@@ -278,7 +290,16 @@ int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new, const floa
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (batch > 0 && max_seq_len > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
   return decode_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
-                     sm_scale, out, workspace, workspace_bytes, stream);
+                     sm_scale, out, workspace, workspace_bytes, false, stream);
+}
+
+int fp8kv_decode_append_q8(const fp8kv_cache* cache, const float* k_new, const float* v_new,
+                           const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens,
+                           int32_t batch, int32_t max_seq_len, float sm_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && max_seq_len > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
+  return decode_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
+                     sm_scale, out, workspace, workspace_bytes, true, stream);
 }
 
 int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst, void* stream) {

@@ -193,9 +193,17 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
 // cache slot (the only write of that slot) and substitutes it for the slot's
 // previous bytes in the registers of the tile being attended, so the append
 // costs no kernel of its own and no extra memory round trip.
-template <int MODE, int D, bool APPEND>
+//
+// Q8 (narrow QK, e4m3 K only): the work-group quantises its G query rows
+// once, by the cache-row rule (fp32 scale amax / 448 per row, e4m3 codes),
+// and QK runs on the fp8 matrix instruction straight from the K codes as
+// loaded, with no conversion; the row's scale multiplies the score ("FP8 KV
+// attention: hardware paths and tile preparation", "Operating model" path 2
+// and "AMD CDNA 3": a per-row scale moves outside the dot product).
+template <int MODE, int D, bool APPEND, bool Q8>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
+  static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
   using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
@@ -206,7 +214,11 @@ void decode_partial_kernel(DecodeArgs a) {
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][4][kMaxGroup];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kMaxGroup][D];
-  __shared__ u32x4_t s_q[KC][64];
+  __shared__ u32x4_t s_q[Q8 ? 1 : KC][64];
+  // Q8: lane (g4, c)'s 32 code bytes of head c (the d of its K bytes) and
+  // the query rows' scales
+  __shared__ u32x4_t s_q8[Q8 ? 2 : 1][64];
+  __shared__ float s_qs[Q8 ? kMaxGroup : 1];
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
   __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
@@ -253,14 +265,47 @@ void decode_partial_kernel(DecodeArgs a) {
   const int tab = a.table[(int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1)];
   // Q^T, the B operand of QK, in LDS in operand order: s_q[kc][lane] is lane
   // (g4, c)'s 16 bytes of head c for k-chunk kc.  Each wave loads a share.
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
+  const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
+  if constexpr (!Q8) {
 #pragma unroll
     for (int kc = wave; kc < KC; kc += kWaves) {
       const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + d0);
       s_q[kc][lane] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
+  } else if (wave == 0) {
+    // Q8: lane (g4, c) takes head c's values at d = 64 p + 16 g4 + i
+    // (i < 16), the d of its K bytes, so byte i of piece p is the same
+    // contraction index in both operands.  amax over the row is the max over
+    // the four lane groups.
+    float4 xq[T::KP][4];
+    float m = 0.0f;
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + 64 * p + 16 * g4 + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float4 f = make_float4(__uint_as_float(w[2 * e] << 16),
+                                       __uint_as_float(w[2 * e] & 0xffff0000u),
+                                       __uint_as_float(w[2 * e + 1] << 16),
+                                       __uint_as_float(w[2 * e + 1] & 0xffff0000u));
+          xq[p][2 * j + e] = f;
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        }
+      }
+    const float q_scale = max_over_groups(m) / kE4M3Max;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x4_t codes = {0u, 0u, 0u, 0u};  // D = 64: the upper 16 k-slots are zero
+      if (p < T::KP) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) codes[e] = e4m3_codes4(xq[p < T::KP ? p : 0][e], q_scale);
+      }
+      s_q8[p][lane] = (c < G) ? codes : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (g4 == 0 && c < G) s_qs[c] = q_scale;
   }
   // Fused append: lanes [0, D/4) hold four values of the K row, lanes
   // [D/4, D/2) four of the V row, loaded with the first round trip.  Every
@@ -407,6 +452,7 @@ void decode_partial_kernel(DecodeArgs a) {
     }
   };
 
+  float q_scale_c = 1.0f;   // Q8: set once s_qs is complete
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
   float l_run = 0.0f;       // this lane's share of the normaliser of head c
   f32x4_t acc[DPR];
@@ -436,18 +482,32 @@ void decode_partial_kernel(DecodeArgs a) {
       for (int hb = 0; hb < 2; ++hb) {
         const int kb = 2 * kp + hb;
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Q8) {
+          // the K codes as loaded: one fp8 instruction per 16 keys
+          const u32x4_t k0 = cur.k[kb][0];
+          const u32x4_t k1 = T::KP == 2 ? cur.k[kb][T::KP - 1] : u32x4_t{0u, 0u, 0u, 0u};
+          const u32x4_t q0 = s_q8[0][lane], q1 = s_q8[1][lane];
+          // (built with a shuffle: element-wise construction with the zero
+          // half of head_dim 64 sends the operand through scratch memory)
+          const i32x8_t av =
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+          const i32x8_t bq =
+              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+          s = mfma_16x16x128_e4m3(av, bq, s);
+        } else {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          u32x4_t av;
-          if (kK8) {
-            const u32x4_t w = cur.k[kb][kc >> 1];
-            const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
-            av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
-                         e4m3x2_to_bf16x2<false>(hi32), e4m3x2_to_bf16x2<true>(hi32)};
-          } else {
-            av = cur.k[kb][kc];
+          for (int kc = 0; kc < KC; ++kc) {
+            u32x4_t av;
+            if (kK8) {
+              const u32x4_t w = cur.k[kb][kc >> 1];
+              const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
+              av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
+                           e4m3x2_to_bf16x2<false>(hi32), e4m3x2_to_bf16x2<true>(hi32)};
+            } else {
+              av = cur.k[kb][kc];
+            }
+            s = mfma_16x16x32_bf16(av, s_q[kc][lane], s);
           }
-          s = mfma_16x16x32_bf16(av, s_q[kc][lane], s);
         }
         sacc[hb] = s;
       }
@@ -466,7 +526,7 @@ void decode_partial_kernel(DecodeArgs a) {
         if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = sacc[hb][i] * ksv[i];
+          float s = (Q8 ? sacc[hb][i] * q_scale_c : sacc[hb][i]) * ksv[i];
           if (!cur.full) {
             const bool ok = (t0 + base + i < t_end) && cur.blk_ok[kb];
             s = ok ? s : -INFINITY;
@@ -557,6 +617,9 @@ void decode_partial_kernel(DecodeArgs a) {
                      e_base, h, lane);
   if (APPEND && pos_n >= 0) append_new();
   __syncthreads();  // s_q complete (after the first tile's loads are in flight)
+  // Q8: the query row's scale of head c (0 for the padding heads c >= G,
+  // whose B columns are zero)
+  if constexpr (Q8) q_scale_c = (c < G) ? s_qs[c] : 0.0f;
   for (int tile = wave; tile < n_tiles; tile += 2 * kWaves) {
     const int t0 = t_begin + tile * kTile;
     if (tile + kWaves < n_tiles)
@@ -677,25 +740,32 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
-template <int MODE, bool APPEND>
+template <int MODE, bool APPEND, bool Q8>
 static void launch_partial_mode(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                                 hipStream_t stream) {
   if (c.d == 128)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND>), dim3(n_wg),
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8>), dim3(n_wg),
                        dim3(64 * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND>), dim3(n_wg),
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8>), dim3(n_wg),
                        dim3(64 * kWaves), 0, stream, a);
 }
 
 template <bool APPEND>
 static void launch_partial_append(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
-                                  hipStream_t stream) {
+                                  bool q8, hipStream_t stream) {
+  if (q8) {  // e4m3 K only (checked by the caller)
+    if (c.mode == kK8V8)
+      launch_partial_mode<kK8V8, APPEND, true>(c, a, n_wg, stream);
+    else
+      launch_partial_mode<kK8V16, APPEND, true>(c, a, n_wg, stream);
+    return;
+  }
   switch (c.mode) {
-    case kK8V8: launch_partial_mode<kK8V8, APPEND>(c, a, n_wg, stream); break;
-    case kK16V8: launch_partial_mode<kK16V8, APPEND>(c, a, n_wg, stream); break;
-    case kK8V16: launch_partial_mode<kK8V16, APPEND>(c, a, n_wg, stream); break;
-    default: launch_partial_mode<kBF16, APPEND>(c, a, n_wg, stream); break;
+    case kK8V8: launch_partial_mode<kK8V8, APPEND, false>(c, a, n_wg, stream); break;
+    case kK16V8: launch_partial_mode<kK16V8, APPEND, false>(c, a, n_wg, stream); break;
+    case kK8V16: launch_partial_mode<kK8V16, APPEND, false>(c, a, n_wg, stream); break;
+    default: launch_partial_mode<kBF16, APPEND, false>(c, a, n_wg, stream); break;
   }
 }
 
@@ -703,14 +773,14 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  const int32_t* seq_lens, int batch, float c_scale,
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
-                                 hipStream_t stream) {
+                                 bool q8, hipStream_t stream) {
   DecodeArgs a{c.k, c.v, c.ks, c.vs, c.table, q, seq_lens, part_acc, part_ml, k_new, v_new,
                c_scale, c.hkv, group, c.bs, c.mbps, chunk, n_splits, c.num_blocks};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
-    launch_partial_append<true>(c, a, n_wg, stream);
+    launch_partial_append<true>(c, a, n_wg, q8, stream);
   else
-    launch_partial_append<false>(c, a, n_wg, stream);
+    launch_partial_append<false>(c, a, n_wg, q8, stream);
   return hipGetLastError();
 }
 

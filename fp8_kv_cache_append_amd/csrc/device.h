@@ -12,6 +12,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 
 constexpr float kE4M3Max = 448.0f;
@@ -51,6 +52,16 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t src0, uint32_t src1, uint
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D(16x16 fp32) += A(16x128 e4m3) * B(128x16 e4m3), block scales 2^0 (E8M0
+// 127): the plain fp8 product.  Lane l holds row / column l % 16 of A / B
+// and 32 of the 128 k-slots (32 bytes); byte p of lane l is the same k-slot
+// in A and in B, so any assignment of the contraction index to (lane group,
+// byte) that A and B share gives the same result.  Output layout as above:
+// rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma_16x16x128_e4m3(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

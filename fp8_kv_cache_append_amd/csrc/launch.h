@@ -42,11 +42,12 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
 // sm_scale * log2(e) rounded to fp32.  With k_new / v_new (fp32
 // [batch][hkv][D]) the kernel first appends each sequence's new token at
 // position seq_lens[b] - 1 (fused append); null pointers: plain decode.
+// q8: narrow QK (Q quantised to e4m3 in the kernel; e4m3 K modes only).
 hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int group,
                                  const int32_t* seq_lens, int batch, float c_scale,
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
-                                 hipStream_t stream);
+                                 bool q8, hipStream_t stream);
 
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,
                                const float* part_acc, const float* part_ml, float* out,

@@ -31,9 +31,12 @@
  *           programs; fp32 partials merged by a second kernel).
  *   [HW]    "FP8 KV attention: hardware paths and tile preparation":
  *           "Operating model" (reconstruct only the active tile, online
- *           softmax tile by tile), "NVIDIA Hopper" path 3 (K16/V8, the
- *           no-K-transform control), "Collect the profiler evidence" (dtype
- *           controls including K16/V16).
+ *           softmax tile by tile; path 2, quantise Q and use FP8 QK),
+ *           "NVIDIA Hopper" path 3 (K16/V8, the no-K-transform control),
+ *           "AMD CDNA 3" (FP8-by-FP8 matrix instruction, a per-row scale
+ *           applied outside the dot product), "Use a native narrow QK path"
+ *           (quantise Q once per decode step), "Collect the profiler
+ *           evidence" (dtype controls including K16/V16).
  *   [FQ]    "Fused KV-cache quantization": "Latency analysis" (the
  *           separate cache-write kernel is one part of the decode gap).
  *   [FA]    "03 . 8n - FA-style tiled prefill attention": sections 2.1
@@ -210,6 +213,33 @@ int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new,
                         int32_t batch, int32_t max_seq_len, float sm_scale,
                         float* out, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * Narrow QK ([HW] "Operating model" path 2, "Use a native narrow QK path",
+ * "AMD CDNA 3"): fp8kv_decode and fp8kv_decode_append with the query rows
+ * quantised once per call, inside the split kernel, by the cache-row rule
+ * (per query row of head_dim values: q_scale = fp32(amax / 448), codes =
+ * e4m3 sat-RNE of fp32(q / q_scale)), and QK computed by the fp8 matrix
+ * instruction directly on the stored K codes:
+ *   s_t = (sum_d value(qc_d) * value(kc_t,d)) * q_scale * k_scale_t
+ *         * sm_scale * log2(e)
+ * Everything after the score is unchanged.  The Q rounding is an extra
+ * error source (a few percent relative L2 against bf16 Q on N(0,1) data),
+ * which the caller accepts by choosing these entry points.  Arguments,
+ * workspace and guards as for fp8kv_decode / fp8kv_decode_append; caches
+ * whose K is not e4m3 (K16V8, BF16) give FP8KV_ERR_UNSUPPORTED.
+ */
+int fp8kv_decode_q8(const fp8kv_cache* cache, const uint16_t* q,
+                    int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
+                    int32_t max_seq_len, float sm_scale, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+int fp8kv_decode_append_q8(const fp8kv_cache* cache, const float* k_new,
+                           const float* v_new, const uint16_t* q,
+                           int32_t gqa_group, const int32_t* seq_lens,
+                           int32_t batch, int32_t max_seq_len, float sm_scale,
+                           float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * The first kernel of fp8kv_decode_append on its own: the fused append and

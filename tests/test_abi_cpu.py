@@ -23,7 +23,7 @@ FAKE = 0x10000  # aligned host-side stand-in; never dereferenced by these calls
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(fp8kv_[a-z_]+)\s*\(", text))
+    return set(re.findall(r"\b(fp8kv_[a-z0-9_]+)\s*\(", text))
 
 
 def test_header_declares_binding_exports():
@@ -171,6 +171,23 @@ def test_decode_append_rejects_bad_arguments():
                                    FAKE, FAKE, 16, None) == -2                  # workspace
     assert lib.fp8kv_decode_append(ctypes.byref(d), None, None, FAKE, 8, FAKE, 0, 0, 0.1,
                                    FAKE, None, 0, None) == 0                    # empty batch
+
+
+def test_narrow_qk_entries_validate_like_the_bf16_ones():
+    lib = binding.lib()
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    # workspace too small, misaligned output, missing rows for the append
+    assert lib.fp8kv_decode_q8(ctypes.byref(d), FAKE, 8, FAKE, 16, 2048, 0.1, FAKE,
+                               FAKE, 16, None) == -2
+    assert lib.fp8kv_decode_q8(ctypes.byref(d), FAKE, 8, FAKE, 16, 2048, 0.1, FAKE + 4,
+                               FAKE, 10 ** 9, None) == -1
+    assert lib.fp8kv_decode_q8(ctypes.byref(d), FAKE, 17, FAKE, 16, 2048, 0.1, FAKE,
+                               FAKE, 10 ** 9, None) == -4   # group > 16
+    args = (FAKE, 8, FAKE, 16, 2048, 0.1, FAKE, FAKE, 10 ** 9, None)
+    assert lib.fp8kv_decode_append_q8(ctypes.byref(d), None, FAKE, *args) == -1
+    assert lib.fp8kv_decode_append_q8(ctypes.byref(d), FAKE + 4, FAKE, *args) == -1
+    assert lib.fp8kv_decode_append_q8(ctypes.byref(d), None, None, FAKE, 8, FAKE, 0, 0, 0.1,
+                                      FAKE, None, 0, None) == 0   # empty batch
 
 
 def test_prefill_rejects_bad_arguments():
