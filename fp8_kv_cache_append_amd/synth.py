@@ -122,6 +122,23 @@ def kv_sequence(w: Workload, b: int, n: int | None = None):
     return k, v
 
 
+def kv_sequence_prebias(w: Workload, b: int):
+    """The ``bias`` workload split into its parts: the token-varying
+    residual of K (the N(0, 1) draw of kv_sequence, before the bias is
+    added), V, and the fixed K bias, fp32 [kv_heads, head_dim] (20 on the 8
+    seeded channels of every head, 0 elsewhere).  kv_sequence's K is the
+    fp32 sum of the first and the last."""
+    if w.dist != "bias":
+        raise ValueError("pre-bias parts exist for the bias workload only")
+    n = int(w.lens[b])
+    shape = (n, w.kv_heads, w.head_dim)
+    k = rng(w.seed, "k", b).standard_normal(size=shape, dtype=np.float32)
+    v = rng(w.seed, "v", b).standard_normal(size=shape, dtype=np.float32)
+    bias = np.zeros((w.kv_heads, w.head_dim), np.float32)
+    bias[:, bias_channels(w.seed, w.head_dim)] = np.float32(20.0)
+    return k, v, bias
+
+
 def block_layout(w: Workload, capacity: int | None = None):
     """Block size, block table [batch, max_blocks] int32 and block count.
 

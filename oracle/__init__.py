@@ -65,6 +65,15 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
             P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, P, P, P, P]
+        L.orc_attend_rows_ex.restype = None
+        L.orc_attend_rows_ex.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P]
+        L.orc_attend_rows_online_ex.restype = None
+        L.orc_attend_rows_online_ex.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, P, P, P, P]
         L.orc_attend_rows_q8.restype = None
         L.orc_attend_rows_q8.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int,
@@ -197,7 +206,7 @@ def _kv_args(kv: dict):
 
 
 def attend_rows(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
-                round_p: bool = True, bounds: bool = False, q8=None):
+                round_p: bool = True, bounds: bool = False, q8=None, k_bias=None):
     """Two-pass attention of query rows q_bits [R, D] against one KV head.
 
     kv holds the stores of that head ([T, D] and [T]); n_valid[r] keys are
@@ -205,43 +214,48 @@ def attend_rows(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     (out, lo, hi) where [lo, hi] holds every output reachable by rounding an
     ambiguous P (one within fp32 noise of a bf16 midpoint) either way.
     q8 = (codes uint8 [R, D], q_scale fp32 [R]): narrow QK on these query
-    codes instead of q_bits (which may then be None).
+    codes instead of q_bits (which may then be None).  k_bias (fp32 [D]):
+    the head's exact K bias; kv then holds the pre-bias residual rows.
     """
-    if q8 is None:
-        q_bits = _c(q_bits, np.uint16)
-        r, d = q_bits.shape
-    else:
-        qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
-        r, d = qc.shape
-        assert qs.shape == (r,)
+    q16, qc, qs, r, d = _query_args(q_bits, q8)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
+    kb = _bias_arg(k_bias, d)
     out = np.empty((r, d), dtype=np.float64)
     lo = np.empty((r, d), dtype=np.float64) if bounds else None
     hi = np.empty((r, d), dtype=np.float64) if bounds else None
-    tail = (_ptr(n_valid), float(sm_scale), int(bool(round_p)), _ptr(out), _ptr(lo), _ptr(hi))
-    if q8 is None:
-        lib().orc_attend_rows(MODES[mode], d, r, _ptr(q_bits), n_keys, *_kv_args(kv), *tail)
-    else:
-        lib().orc_attend_rows_q8(MODES[mode], d, r, _ptr(qc), _ptr(qs), n_keys, *_kv_args(kv),
-                                 *tail)
+    lib().orc_attend_rows_ex(MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(kb), n_keys,
+                             *_kv_args(kv), _ptr(n_valid), float(sm_scale), int(bool(round_p)),
+                             _ptr(out), _ptr(lo), _ptr(hi))
     return (out, lo, hi) if bounds else out
 
 
+def _query_args(q_bits, q8):
+    if q8 is None:
+        q16 = _c(q_bits, np.uint16)
+        return (q16, None, None) + q16.shape
+    qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
+    assert qs.shape == qc.shape[:1]
+    return (None, qc, qs) + qc.shape
+
+
+def _bias_arg(k_bias, d):
+    if k_bias is None:
+        return None
+    kb = _c(k_bias, np.float32)
+    assert kb.shape == (d,), kb.shape
+    return kb
+
+
 def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
-                       tile: int, split: int, round_p: bool = True, q8=None):
+                       tile: int, split: int, round_p: bool = True, q8=None, k_bias=None):
     """Online (tiled, split, merged) attention; see orc_attend_rows_online.
 
     Returns (out [R, D], part_acc [S, R, D], part_l [S, R], part_m [S, R]).
-    q8 as for attend_rows.
+    q8 and k_bias as for attend_rows.
     """
-    if q8 is None:
-        q_bits = _c(q_bits, np.uint16)
-        r, d = q_bits.shape
-    else:
-        qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
-        r, d = qc.shape
-        assert qs.shape == (r,)
+    q16, qc, qs, r, d = _query_args(q_bits, q8)
+    kb = _bias_arg(k_bias, d)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
     n_splits = -(-n_keys // split) if n_keys else 0
@@ -249,14 +263,10 @@ def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     pacc = np.empty((max(n_splits, 1), r, d), dtype=np.float64)
     pl = np.empty((max(n_splits, 1), r), dtype=np.float64)
     pm = np.empty((max(n_splits, 1), r), dtype=np.float64)
-    tail = (_ptr(n_valid), float(sm_scale), int(bool(round_p)), int(tile), int(split),
-            _ptr(pacc), _ptr(pl), _ptr(pm), _ptr(out))
-    if q8 is None:
-        lib().orc_attend_rows_online(MODES[mode], d, r, _ptr(q_bits), n_keys, *_kv_args(kv),
-                                     *tail)
-    else:
-        lib().orc_attend_rows_online_q8(MODES[mode], d, r, _ptr(qc), _ptr(qs), n_keys,
-                                        *_kv_args(kv), *tail)
+    lib().orc_attend_rows_online_ex(
+        MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(kb), n_keys, *_kv_args(kv),
+        _ptr(n_valid), float(sm_scale), int(bool(round_p)), int(tile), int(split),
+        _ptr(pacc), _ptr(pl), _ptr(pm), _ptr(out))
     return out, pacc[:n_splits], pl[:n_splits], pm[:n_splits]
 
 
@@ -268,13 +278,16 @@ def _n_keys(kv: dict) -> int:
 
 
 def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
-           pairs=None, round_p: bool = True, bounds: bool = False, q8: bool = False):
+           pairs=None, round_p: bool = True, bounds: bool = False, q8: bool = False,
+           k_bias=None):
     """Decode attention from the fp32 K/V of each sequence.
 
     q_bits  bf16 bits [B, Hq, D]
     k_seqs  list of B fp32 arrays [len_b, Hkv, D] (v_seqs alike)
     pairs   optional iterable of (b, kv_head) to compute; other rows are NaN
     q8      narrow QK: Q quantised once (quantize_q), scores on its codes
+    k_bias  exact K bias fp32 [Hkv, D]: k_seqs are then the pre-bias
+            residuals (stored quantised) and each key is residual + bias
     Returns fp64 [B, Hq, D] (with bounds=True: (out, lo, hi), see
     attend_rows).  The oracle quantises each sequence itself.
     """
@@ -300,7 +313,7 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
             sl = slice(h * g, (h + 1) * g)
             rq8 = (qc[b, sl], qs[b, sl]) if q8 else None
             res = attend_rows(mode, rows, _head_view(store, h), n, sm_scale, round_p, bounds,
-                              q8=rq8)
+                              q8=rq8, k_bias=None if k_bias is None else k_bias[h])
             if bounds:
                 out[b, sl], lo[b, sl], hi[b, sl] = res
             else:

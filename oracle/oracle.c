@@ -144,6 +144,7 @@ typedef struct {
   const uint8_t *k8, *v8;
   const uint16_t *k16, *v16;
   const float *ks, *vs;
+  const float* kb; /* exact K bias [d] (pre-bias residual cache), or NULL */
 } kv_view;
 
 /* Which side of the cache holds e4m3 codes with a scale (else bf16). */
@@ -168,14 +169,27 @@ static double v_scale(const kv_view* kv, int t) {
   return v_is_e4m3(kv->mode) ? (double)kv->vs[t] : 1.0;
 }
 
+/* q . b for the exact K bias (0 without one). */
+static double bias_dot(const kv_view* kv, const double* qv) {
+  double dot = 0.0;
+  int j;
+  if (!kv->kb) return 0.0;
+  for (j = 0; j < kv->d; ++j) dot += qv[j] * (double)kv->kb[j];
+  return dot;
+}
+
 /* Score in log2 units: (q . K_t) * k_scale_t * sm_scale * log2(e).
  * The K scale sits outside the dot product (CDNA 3 section of the hardware
- * notes; "Math" section of the fp8-kv-cache page). */
-static double score(const kv_view* kv, const double* qv, int t, double c) {
+ * notes; "Math" section of the fp8-kv-cache page).  With an exact K bias the
+ * stored rows are the pre-bias residual and the key is residual + bias, so
+ * the score gains q . b ("Treat numerical safety and kernel speed as
+ * separate gates": keep the fixed bias exact, correct in score space);
+ * qb is that dot product for the row. */
+static double score(const kv_view* kv, const double* qv, int t, double c, double qb) {
   double dot = 0.0;
   int j;
   for (j = 0; j < kv->d; ++j) dot += qv[j] * k_elem(kv, t, j);
-  return dot * k_scale(kv, t) * c;
+  return (dot * k_scale(kv, t) + qb) * c;
 }
 
 /* P with the V scale folded in, rounded to bf16 when round_p is set. */
@@ -202,10 +216,12 @@ static int clamp_valid(int nv, int n_keys) {
  * instruction's sum error above), as a relative window on p = 2^(s - M)
  * with 2^-20 added for an fp32 exp2 within a few ulp. */
 static double p_window(const kv_view* kv, const double* qv, int t, double c, int narrow) {
-  double sabs = 0.0;
+  double sabs = 0.0, babs = 0.0;
   int j;
   for (j = 0; j < kv->d; ++j) sabs += fabs(qv[j] * k_elem(kv, t, j));
-  sabs *= fabs(k_scale(kv, t) * c);
+  if (kv->kb)
+    for (j = 0; j < kv->d; ++j) babs += fabs(qv[j] * (double)kv->kb[j]);
+  sabs = (sabs * fabs(k_scale(kv, t)) + babs) * fabs(c);
   return 0.6931471805599453 *
              (2.0 * (double)(kv->d + 4) * ldexp(1.0, -24) +
               (narrow ? ORC_NARROW_SUM_ERR : 0.0)) * sabs +
@@ -228,12 +244,12 @@ static double query_row(int d, int r, const uint16_t* q16, const uint8_t* q8,
 }
 
 static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
-                        const uint8_t* q8, const float* q_scale, int n_keys,
+                        const uint8_t* q8, const float* q_scale, const float* k_bias, int n_keys,
                         const uint8_t* k8, const uint16_t* k16, const float* ks,
                         const uint8_t* v8, const uint16_t* v16, const float* vs,
                         const int32_t* n_valid, float sm_scale, int round_p,
                         double* out, double* out_lo, double* out_hi) {
-  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias};
   const double c0 = (double)sm_scale * ORC_LOG2E;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
   double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
@@ -247,6 +263,7 @@ static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
     double smax = -INFINITY, m, l = 0.0;
     double* o = out + (size_t)r * d;
     const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
+    const double qb = bias_dot(&kv, qv);
     if (nv == 0) { /* no visible key: the row outputs 0 */
       for (j = 0; j < d; ++j) o[j] = 0.0;
       if (bounds)
@@ -255,7 +272,7 @@ static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
     }
     /* pass 1: scores and their maximum */
     for (t = 0; t < nv; ++t) {
-      s[t] = score(&kv, qv, t, c);
+      s[t] = score(&kv, qv, t, c, qb);
       if (s[t] > smax) smax = s[t];
     }
     m = ceil(smax);
@@ -298,7 +315,7 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
                      const float* ks, const uint8_t* v8, const uint16_t* v16,
                      const float* vs, const int32_t* n_valid, float sm_scale,
                      int round_p, double* out, double* out_lo, double* out_hi) {
-  attend_rows(mode, d, n_rows, q, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+  attend_rows(mode, d, n_rows, q, NULL, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
               sm_scale, round_p, out, out_lo, out_hi);
 }
 
@@ -308,18 +325,19 @@ void orc_attend_rows_q8(int mode, int d, int n_rows, const uint8_t* q8,
                         const uint16_t* v16, const float* vs,
                         const int32_t* n_valid, float sm_scale, int round_p,
                         double* out, double* out_lo, double* out_hi) {
-  attend_rows(mode, d, n_rows, NULL, q8, q_scale, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+  attend_rows(mode, d, n_rows, NULL, q8, q_scale, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
               sm_scale, round_p, out, out_lo, out_hi);
 }
 
 static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
-                               const uint8_t* q8, const float* q_scale, int n_keys,
+                               const uint8_t* q8, const float* q_scale, const float* k_bias,
+                               int n_keys,
                                const uint8_t* k8, const uint16_t* k16, const float* ks,
                                const uint8_t* v8, const uint16_t* v16, const float* vs,
                                const int32_t* n_valid, float sm_scale, int round_p,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out) {
-  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs};
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias};
   const double c0 = (double)sm_scale * ORC_LOG2E;
   int n_splits = n_keys > 0 ? (n_keys + split - 1) / split : 0;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
@@ -333,6 +351,7 @@ static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
     int nv = clamp_valid(n_valid[r], n_keys);
     double mstar = -INFINITY, lsum = 0.0;
     const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
+    const double qb = bias_dot(&kv, qv);
     for (sp = 0; sp < n_splits; ++sp) {
       int k_lo = sp * split;
       int k_hi = k_lo + split < n_keys ? k_lo + split : n_keys;
@@ -344,7 +363,7 @@ static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
         /* scores of the visible keys of this tile */
         for (t = t0; t < t1; ++t) {
           if (t >= nv) break;
-          s[t - t0] = score(&kv, qv, t, c);
+          s[t - t0] = score(&kv, qv, t, c, qb);
           if (s[t - t0] > tmax) tmax = s[t - t0];
         }
         if (tmax == -INFINITY) continue; /* fully masked tile: keep state */
@@ -397,7 +416,7 @@ void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
                             int round_p, int tile, int split,
                             double* part_acc, double* part_l, double* part_m,
                             double* out) {
-  attend_rows_online(mode, d, n_rows, q, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs,
+  attend_rows_online(mode, d, n_rows, q, NULL, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs,
                      n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
 }
 
@@ -408,6 +427,28 @@ void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
                                const int32_t* n_valid, float sm_scale, int round_p,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out) {
-  attend_rows_online(mode, d, n_rows, NULL, q8, q_scale, n_keys, k8, k16, ks, v8, v16, vs,
+  attend_rows_online(mode, d, n_rows, NULL, q8, q_scale, NULL, n_keys, k8, k16, ks, v8, v16, vs,
                      n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
+}
+
+void orc_attend_rows_ex(int mode, int d, int n_rows, const uint16_t* q16, const uint8_t* q8,
+                        const float* q_scale, const float* k_bias, int n_keys,
+                        const uint8_t* k8, const uint16_t* k16, const float* ks,
+                        const uint8_t* v8, const uint16_t* v16, const float* vs,
+                        const int32_t* n_valid, float sm_scale, int round_p, double* out,
+                        double* out_lo, double* out_hi) {
+  attend_rows(mode, d, n_rows, q16, q8, q_scale, k_bias, n_keys, k8, k16, ks, v8, v16, vs,
+              n_valid, sm_scale, round_p, out, out_lo, out_hi);
+}
+
+void orc_attend_rows_online_ex(int mode, int d, int n_rows, const uint16_t* q16,
+                               const uint8_t* q8, const float* q_scale, const float* k_bias,
+                               int n_keys, const uint8_t* k8, const uint16_t* k16,
+                               const float* ks, const uint8_t* v8, const uint16_t* v16,
+                               const float* vs, const int32_t* n_valid, float sm_scale,
+                               int round_p, int tile, int split, double* part_acc,
+                               double* part_l, double* part_m, double* out) {
+  attend_rows_online(mode, d, n_rows, q16, q8, q_scale, k_bias, n_keys, k8, k16, ks, v8, v16,
+                     vs, n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m,
+                     out);
 }

@@ -164,6 +164,32 @@ void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out);
 
+/*
+ * Every form above in one entry, with the options together: bf16 rows (q16)
+ * or narrow rows (q8 + q_scale, q16 NULL), and an optional exact K bias
+ * (k_bias, fp32 [d], NULL for none).  With a bias the stored K rows are the
+ * pre-bias residual and the key is residual + bias ("Treat numerical safety
+ * and kernel speed as separate gates" in the hardware notes; "Bias-aware
+ * symmetric FP8" in the fused-quantisation README: quantise the pre-bias
+ * residual, keep the fixed bias exact, apply the equivalent score-space
+ * correction):
+ *   s_t = ((sum_d q_d * K_td) * ks_t + sum_d q_d * b_d) * sm_scale * log2(e)
+ */
+void orc_attend_rows_ex(int mode, int d, int n_rows, const uint16_t* q16, const uint8_t* q8,
+                        const float* q_scale, const float* k_bias, int n_keys,
+                        const uint8_t* k8, const uint16_t* k16, const float* ks,
+                        const uint8_t* v8, const uint16_t* v16, const float* vs,
+                        const int32_t* n_valid, float sm_scale, int round_p, double* out,
+                        double* out_lo, double* out_hi);
+
+void orc_attend_rows_online_ex(int mode, int d, int n_rows, const uint16_t* q16,
+                               const uint8_t* q8, const float* q_scale, const float* k_bias,
+                               int n_keys, const uint8_t* k8, const uint16_t* k16,
+                               const float* ks, const uint8_t* v8, const uint16_t* v16,
+                               const float* vs, const int32_t* n_valid, float sm_scale,
+                               int round_p, int tile, int split, double* part_acc,
+                               double* part_l, double* part_m, double* out);
+
 #ifdef __cplusplus
 }
 #endif
