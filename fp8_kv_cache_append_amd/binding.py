@@ -46,7 +46,7 @@ class CacheDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("k_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -125,7 +125,9 @@ class KVCache:
     k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
     k_scale, v_scale: float32 [num_blocks, block_size, Hkv] for an e4m3 side,
     else None;
-    block_table: int32 [batch, max_blocks_per_seq].
+    block_table: int32 [batch, max_blocks_per_seq];
+    k_bias: float32 [Hkv, D] for a pre-bias residual cache (the stored K rows
+    are residuals, the key is residual + k_bias), else None.
     """
     mode: str
     k: torch.Tensor
@@ -133,6 +135,7 @@ class KVCache:
     k_scale: torch.Tensor | None
     v_scale: torch.Tensor | None
     block_table: torch.Tensor
+    k_bias: torch.Tensor | None = None
 
     @classmethod
     def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
@@ -159,7 +162,8 @@ class KVCache:
                          int(self.k.shape[2]), int(self.k.shape[3]),
                          int(self.block_table.shape[1]), int(self.block_table.shape[0]),
                          _ptr(self.k), _ptr(self.v),
-                         _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table))
+                         _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table),
+                         _ptr(self.k_bias))
 
 
 def fp8kv_append(cache: KVCache, k_new, v_new, seq_idx, pos, stream=None) -> None:

@@ -60,13 +60,14 @@ int validate_cache(const fp8kv_cache* c) {
   if (need_vs != (c->v_scale != nullptr)) return FP8KV_ERR_INVALID;
   if (c->k_scale && !aligned(c->k_scale, 4)) return FP8KV_ERR_INVALID;
   if (c->v_scale && !aligned(c->v_scale, 4)) return FP8KV_ERR_INVALID;
+  if (c->k_bias && !aligned(c->k_bias, 16)) return FP8KV_ERR_INVALID;
   return FP8KV_OK;
 }
 
 fp8kv::CacheView view_of(const fp8kv_cache* c) {
   return fp8kv::CacheView{c->mode, c->block_size, c->num_kv_heads, c->head_dim,
                           c->max_blocks_per_seq, c->num_seqs, c->num_blocks, c->k, c->v,
-                          c->k_scale, c->v_scale, c->block_table};
+                          c->k_scale, c->v_scale, c->block_table, c->k_bias};
 }
 
 int launch_status(hipError_t e) {
@@ -181,8 +182,8 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
                         void* stream) {
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
-  if (q8 && cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16)
-    return FP8KV_ERR_UNSUPPORTED;  // narrow QK takes the K codes as they are
+  if (q8 && ((cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16) || cache->k_bias))
+    return FP8KV_ERR_UNSUPPORTED;  // narrow QK takes the K codes as they are, no bias
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
   if (!split_fits_table_window(chunk_tokens, cache->block_size)) return FP8KV_ERR_INVALID;
   if ((int64_t)n_splits * chunk_tokens < max_seq_len) return FP8KV_ERR_INVALID;
@@ -248,7 +249,7 @@ int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new
   int32_t chunk = 0, splits = 0;
   int st = fp8kv_decode_plan(cache, batch, gqa_group, max_seq_len, &chunk, &splits);
   if (st != FP8KV_OK) return st;
-  if (q8 && cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16)
+  if (q8 && ((cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16) || cache->k_bias))
     return FP8KV_ERR_UNSUPPORTED;
   if (batch == 0) return FP8KV_OK;
   const size_t acc_floats = (size_t)batch * cache->num_kv_heads * splits * gqa_group *
@@ -325,6 +326,7 @@ int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group
   if (gqa_group < 1 || batch < 0 || max_q_len < 0 || total_q < 0 || batch > cache->num_seqs)
     return FP8KV_ERR_INVALID;
   if (gqa_group > kMaxGroup) return FP8KV_ERR_UNSUPPORTED;
+  if (cache->k_bias) return FP8KV_ERR_UNSUPPORTED;  // pre-bias caches: decode only
   if (batch == 0 || max_q_len == 0 || total_q == 0) return FP8KV_OK;
   if (!q || !cu_q || !q_pos0 || !seq_lens || !out) return FP8KV_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(cu_q, 4) || !aligned(q_pos0, 4) ||

@@ -54,6 +54,7 @@ struct DecodeArgs {
   float* part_ml;
   const float* k_new;  // fused append: the step's new K/V rows, fp32
   const float* v_new;  //   [batch][hkv][D]; unused by the plain decode
+  const float* kbias;  // pre-bias residual cache: exact K bias [hkv][D], else null
   float c_scale;  // sm_scale * log2(e)
   int hkv;
   int group;
@@ -200,10 +201,17 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
 // loaded, with no conversion; the row's scale multiplies the score ("FP8 KV
 // attention: hardware paths and tile preparation", "Operating model" path 2
 // and "AMD CDNA 3": a per-row scale moves outside the dot product).
-template <int MODE, int D, bool APPEND, bool Q8>
+//
+// KB (pre-bias residual cache): the stored K rows are residuals r and the
+// key is r + b with the bias b exact; every score of query row q gains
+// (q . b) * sm_scale * log2(e), computed once per work-group ("Treat
+// numerical safety and kernel speed as separate gates": keep the fixed bias
+// exact, correct in score space).
+template <int MODE, int D, bool APPEND, bool Q8, bool KB>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
+  static_assert(!(Q8 && KB), "narrow QK takes no K bias");
   using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
@@ -318,6 +326,31 @@ void decode_partial_kernel(DecodeArgs a) {
     const int l2 = lane & (2 * kLR - 1);
     xnew = *reinterpret_cast<const float4*>((l2 < kLR ? a.k_new : a.v_new) +
                                             ((int64_t)b * a.hkv + h) * D + 4 * (l2 % kLR));
+  }
+  // KB: (q . b) of head c, in log2 units of the score.  Lane (g4, c) takes
+  // d = 64 p + 16 g4 + i (i < 16) and the four lane groups are summed; the
+  // loads follow the first round trip's, so waiting for them costs no extra
+  // round trip (the block ids are needed before any tile load anyway).
+  float qb_c = 0.0f;
+  if constexpr (KB) {
+    const float* brow = a.kbias + (int64_t)h * D;
+    float part = 0.0f;
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int d0 = 64 * p + 16 * g4 + 8 * j;
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(brow + d0);
+        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(brow + d0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4_t& bb = e < 2 ? b0 : b1;
+          part += __uint_as_float(w[e] << 16) * bb[2 * (e & 1)];
+          part += __uint_as_float(w[e] & 0xffff0000u) * bb[2 * (e & 1) + 1];
+        }
+      }
+    qb_c = sum_over_groups(part) * a.c_scale;
   }
   const int t_end = min(min(max(len, 0), a.mbps * a.bs), t_begin + a.chunk);
 
@@ -527,6 +560,7 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float s = (Q8 ? sacc[hb][i] * q_scale_c : sacc[hb][i]) * ksv[i];
+          if (KB) s += qb_c;
           if (!cur.full) {
             const bool ok = (t0 + base + i < t_end) && cur.blk_ok[kb];
             s = ok ? s : -INFINITY;
@@ -740,15 +774,27 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
+template <int MODE, bool APPEND, bool Q8, bool KB>
+static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
+                             hipStream_t stream) {
+  if (c.d == 128)
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB>), dim3(n_wg),
+                       dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB>), dim3(n_wg),
+                       dim3(64 * kWaves), 0, stream, a);
+}
+
 template <int MODE, bool APPEND, bool Q8>
 static void launch_partial_mode(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                                 hipStream_t stream) {
-  if (c.d == 128)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8>), dim3(n_wg),
-                       dim3(64 * kWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8>), dim3(n_wg),
-                       dim3(64 * kWaves), 0, stream, a);
+  if constexpr (!Q8) {
+    if (c.kbias) {
+      launch_partial_d<MODE, APPEND, false, true>(c, a, n_wg, stream);
+      return;
+    }
+  }
+  launch_partial_d<MODE, APPEND, Q8, false>(c, a, n_wg, stream);
 }
 
 template <bool APPEND>
@@ -774,8 +820,9 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
                                  bool q8, hipStream_t stream) {
-  DecodeArgs a{c.k, c.v, c.ks, c.vs, c.table, q, seq_lens, part_acc, part_ml, k_new, v_new,
-               c_scale, c.hkv, group, c.bs, c.mbps, chunk, n_splits, c.num_blocks};
+  DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,     seq_lens,
+               part_acc, part_ml,  k_new,   v_new,   c.kbias,  c_scale, c.hkv,
+               group,   c.bs,      c.mbps,  chunk,   n_splits, c.num_blocks};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);

@@ -76,6 +76,13 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+__device__ __forceinline__ float sum_over_groups(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Storage rule of a (token, KV head) row ("kadirnar/kernel-agent/fp8-kv-cache",
 // section "Storage"), for a row of D values held four per lane by D/4
 // consecutive, aligned lanes.

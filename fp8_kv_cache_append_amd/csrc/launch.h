@@ -26,6 +26,7 @@ struct CacheView {
   float* ks;
   float* vs;
   const int32_t* table;
+  const float* kbias;  // exact K bias [hkv][d] of a pre-bias residual cache, or null
 };
 
 // Work-groups of the split kernel one compute unit holds at once: two where a

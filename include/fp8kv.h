@@ -38,7 +38,8 @@
  *           (quantise Q once per decode step), "Collect the profiler
  *           evidence" (dtype controls including K16/V16).
  *   [FQ]    "Fused KV-cache quantization": "Latency analysis" (the
- *           separate cache-write kernel is one part of the decode gap).
+ *           separate cache-write kernel is one part of the decode gap),
+ *           "Bias-aware symmetric FP8" (pre-bias residual, exact bias).
  *   [FA]    "03 . 8n - FA-style tiled prefill attention": sections 2.1
  *           (online softmax), 3.1 (64-token query tiles, GQA slicing,
  *           positions are data, causal mask) and 3.2/3.3 (a row with no
@@ -88,6 +89,17 @@ typedef enum {
  *                   b is slot t % block_size of block
  *                   block_table[b * max_blocks_per_seq + t / block_size]
  * A contiguous cache [B][T][Hkv][D] is block_size = T with block_table[b] = b.
+ *   k_bias          NULL, or fp32 [num_kv_heads][head_dim], 16-byte aligned:
+ *                   a pre-bias residual cache ([HW] "Treat numerical safety
+ *                   and kernel speed as separate gates"; [FQ] "Bias-aware
+ *                   symmetric FP8").  The stored K rows are the residual r
+ *                   (the caller appends r, e.g. the key projection before its
+ *                   bias); the key is r + b with b kept exact, and decode
+ *                   applies the equivalent score correction: the score of
+ *                   query row q gains (q . b) * sm_scale * log2(e).
+ *                   fp8kv_decode, fp8kv_decode_append and their partials
+ *                   support it; narrow QK and prefill give
+ *                   FP8KV_ERR_UNSUPPORTED for such a cache.
  * Requirements: head_dim 64 or 128; block_size a multiple of 16; k, v 16-byte
  * aligned; k_scale, v_scale, block_table 4-byte aligned.
  */
@@ -104,6 +116,7 @@ typedef struct fp8kv_cache {
   float* k_scale;
   float* v_scale;
   const int32_t* block_table;
+  const float* k_bias;         /* exact fixed K bias, or NULL (see above) */
 } fp8kv_cache;
 
 /*

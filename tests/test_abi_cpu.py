@@ -50,7 +50,7 @@ def test_strerror():
 def _desc(**kw):
     base = dict(mode=0, num_blocks=4, block_size=16, num_kv_heads=2, head_dim=128,
                 max_blocks_per_seq=4, num_seqs=16, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
-                block_table=FAKE)
+                block_table=FAKE, k_bias=None)
     base.update(kw)
     return CacheDesc(**base)
 
@@ -70,6 +70,7 @@ BAD_CACHES = [
     (dict(mode=1), -1),              # K16V8 must not carry a K scale
     (dict(mode=2, k_scale=None), -1),  # BF16 must not carry a V scale
     (dict(block_table=FAKE + 2), -1),
+    (dict(k_bias=FAKE + 4), -1),        # the bias is read 16 bytes at a time
 ]
 
 
@@ -188,6 +189,19 @@ def test_narrow_qk_entries_validate_like_the_bf16_ones():
     assert lib.fp8kv_decode_append_q8(ctypes.byref(d), FAKE + 4, FAKE, *args) == -1
     assert lib.fp8kv_decode_append_q8(ctypes.byref(d), None, None, FAKE, 8, FAKE, 0, 0, 0.1,
                                       FAKE, None, 0, None) == 0   # empty batch
+
+
+def test_pre_bias_cache_is_decode_only():
+    lib = binding.lib()
+    d = _desc(k_bias=FAKE)
+    # prefill and narrow QK reject a cache with a K bias before any launch
+    assert lib.fp8kv_prefill(ctypes.byref(d), FAKE, 8, FAKE, FAKE, FAKE, 1, 64, 64, 0.1,
+                             FAKE, None) == -4
+    assert lib.fp8kv_decode_q8(ctypes.byref(d), FAKE, 8, FAKE, 4, 64, 0.1, FAKE, FAKE,
+                               10 ** 9, None) == -4
+    # decode validates it like any cache (workspace check reached)
+    assert lib.fp8kv_decode(ctypes.byref(d), FAKE, 8, FAKE, 4, 64, 0.1, FAKE, None, 0,
+                            None) == -2
 
 
 def test_prefill_rejects_bad_arguments():
