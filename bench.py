@@ -29,7 +29,8 @@ rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
 the context sweep of the same shape at 77/512/2048/8192 keys in all four
 modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
 per-side savings against BF16, the ragged batch-64 paged workload
-(32q/8kv, lengths 1024..32768, K8V8 and K16V8), the roofline of the split
+(32q/8kv, lengths 1024..32768, K8V8, K16V8 and K8V8 as a pre-bias residual
+cache with the exact key bias), the roofline of the split
 kernel and the CPU oracle as a baseline.
 """
 from __future__ import annotations
@@ -334,11 +335,13 @@ def bench_sweep(steps, warmup, copies, head):
     return {"tokens": table, "k8v8_vs_k16v8_break_even_tokens": be}
 
 
-def bench_ragged(mode, replays=20, steps=8):
+def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
     """Batch 64, 32q/8kv, D128, lengths uniform in [1024, 32768], paged
     16-token blocks behind a shuffled table, biased keys.  The cache (2.3 GB
     K8V8, 3.4 GB K16V8) is far larger than the Infinity Cache, so one copy is
-    HBM-cold.  Filled from device-generated K/V of the same distributions."""
+    HBM-cold.  Filled from device-generated K/V of the same distributions.
+    pre_bias: the cache stores the keys' pre-bias residuals with the exact
+    bias in the descriptor (decode adds q . b to the scores)."""
     import torch
     from fp8_kv_cache_append_amd import binding, synth
     from fp8_kv_cache_append_amd.binding import KVCache
@@ -347,10 +350,12 @@ def bench_ragged(mode, replays=20, steps=8):
     w = synth.decode_b64_gqa4_ragged_paged()
     bs, table, n_blocks = synth.block_layout(w)
     cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+    if pre_bias:
+        cache.k_bias = torch.from_numpy(synth.kv_sequence_prebias(w, 0)[2]).to(dev)
     k_last, v_last = [], []
     for b in range(w.batch):
         n = int(w.lens[b])
-        k, v = synth.kv_sequence_device(w, b, dev)
+        k, v = synth.kv_sequence_device(w, b, dev, residual=pre_bias)
         seq = torch.full((n,), b, dtype=torch.int32, device=dev)
         pos = torch.arange(n, dtype=torch.int32, device=dev)
         binding.fp8kv_append(cache, k, v, seq, pos)
@@ -397,7 +402,8 @@ def bench_ragged(mode, replays=20, steps=8):
 
     step_us, split_us = timed(step), timed(split)
     kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](w.head_dim)
-    return {"workload": w.name, "mode": mode, "us_per_step": step_us, "split_us": split_us,
+    return {"workload": w.name, "mode": mode + ("_pre_bias" if pre_bias else ""),
+            "us_per_step": step_us, "split_us": split_us,
             "kv_bytes": kv_bytes, "kv_gbs": kv_bytes / (step_us * 1e-6) / 1e9,
             "split_kv_gbs": kv_bytes / (split_us * 1e-6) / 1e9,
             "pct_roofline": 100.0 * kv_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -538,6 +544,7 @@ def main():
         extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
                                       args.copies, head)
         extras["ragged"] = {m: bench_ragged(m) for m in ("K8V8", "K16V8")}
+        extras["ragged"]["K8V8_pre_bias"] = bench_ragged("K8V8", pre_bias=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     rec = {

@@ -168,10 +168,12 @@ def block_layout(w: Workload, capacity: int | None = None):
     return bs, table, n_blocks
 
 
-def kv_sequence_device(w: Workload, b: int, device="cuda"):
+def kv_sequence_device(w: Workload, b: int, device="cuda", residual: bool = False):
     """fp32 K and V of sequence ``b`` drawn on the device (torch's seeded
     generator): the same distributions as kv_sequence, other values.  For
-    benchmark caches of gigabytes, where host generation would dominate."""
+    benchmark caches of gigabytes, where host generation would dominate.
+    residual=True (bias workload): K without its bias, the rows a pre-bias
+    cache stores; the bias is kv_sequence_prebias's."""
     import torch
     n = int(w.lens[b])
     g = torch.Generator(device=device)
@@ -183,8 +185,9 @@ def kv_sequence_device(w: Workload, b: int, device="cuda"):
         k = torch.where(torch.rand(shape, generator=g, device=device) < 0.02, k * 10.0, k)
         v = torch.where(torch.rand(shape, generator=g, device=device) < 0.02, v * 10.0, v)
     elif w.dist == "bias":
-        ch = torch.from_numpy(bias_channels(w.seed, w.head_dim)).to(device)
-        k[:, :, ch] += 20.0
+        if not residual:
+            ch = torch.from_numpy(bias_channels(w.seed, w.head_dim)).to(device)
+            k[:, :, ch] += 20.0
     elif w.dist != "normal":
         raise ValueError(w.dist)
     return k, v
