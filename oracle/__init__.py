@@ -24,9 +24,10 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3}
-K_E4M3 = ("K8V8", "K8V16")   # modes whose K side is e4m3 codes + scale
-V_E4M3 = ("K8V8", "K16V8")   # modes whose V side is e4m3 codes + scale
+MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3, "MXK8V8": 4}
+K_E4M3 = ("K8V8", "K8V16", "MXK8V8")   # modes whose K side is e4m3 codes
+V_E4M3 = ("K8V8", "K16V8", "MXK8V8")   # modes whose V side is e4m3 codes + scale
+K_MX = ("MXK8V8",)                       # K codes with one E8M0 scale per 32 values
 
 _lib = None
 
@@ -67,13 +68,17 @@ def lib() -> ctypes.CDLL:
             ctypes.c_int, ctypes.c_int, P, P, P, P]
         L.orc_attend_rows_ex.restype = None
         L.orc_attend_rows_ex.argtypes = [
-            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
-            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P]
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int, P, P, P]
         L.orc_attend_rows_online_ex.restype = None
         L.orc_attend_rows_online_ex.argtypes = [
-            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, ctypes.c_int,
-            P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P, ctypes.c_int,
+            P, P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, P, P, P, P]
+        L.orc_mx_exponent.restype = ctypes.c_int
+        L.orc_mx_exponent.argtypes = [ctypes.c_float]
+        L.orc_quantize_rows_mx.restype = None
+        L.orc_quantize_rows_mx.argtypes = [P, ctypes.c_int64, ctypes.c_int, P, P]
         L.orc_attend_rows_q8.restype = None
         L.orc_attend_rows_q8.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int,
@@ -161,6 +166,30 @@ def dequantize_rows(codes, scales):
     return out
 
 
+def quantize_rows_mx(x):
+    """Block-scaled (MX) quantisation over the last axis (a multiple of 32):
+    returns (codes uint8 [..., D], exps uint8 [..., D/32]) with exps = E + 127,
+    E = ceil(log2(fp32(amax of the block / 448))) clamped to [-126, 127],
+    codes = e4m3(x / 2^E)."""
+    x = _c(x, np.float32)
+    d = x.shape[-1]
+    assert d % 32 == 0
+    n = x.size // d if d else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    exps = np.empty(x.shape[:-1] + (d // 32,), dtype=np.uint8)
+    lib().orc_quantize_rows_mx(_ptr(x), n, d, _ptr(codes), _ptr(exps))
+    return codes, exps
+
+
+def mx_exponent(amax: float) -> int:
+    return int(lib().orc_mx_exponent(float(amax)))
+
+
+def quantize_q_mx(q_bits):
+    """Block-scaled QK: the bf16 query rows quantised by the MX rule."""
+    return quantize_rows_mx(bf16_value(q_bits).astype(np.float32))
+
+
 def quantize_q(q_bits):
     """Narrow QK: the bf16 query rows quantised once per decode step like
     cache rows (hardware notes, "Operating model" path 2).  q_bits uint16
@@ -172,13 +201,15 @@ def quantize_q(q_bits):
 def store_rows(mode: str, k, v) -> dict:
     """What the cache holds for fp32 K and V rows in the given mode.
 
-    Keys: k8/ks (K8V8, K8V16), k16 (K16V8, BF16), v8/vs (K8V8, K16V8),
-    v16 (BF16, K8V16).
+    Keys: k8/ks (K8V8, K8V16), k8/kx (MXK8V8), k16 (K16V8, BF16), v8/vs
+    (K8V8, K16V8, MXK8V8), v16 (BF16, K8V16).
     """
     if mode not in MODES:
         raise ValueError(mode)
     out = {}
-    if mode in K_E4M3:
+    if mode in K_MX:
+        out["k8"], out["kx"] = quantize_rows_mx(k)
+    elif mode in K_E4M3:
         out["k8"], out["ks"] = quantize_rows(k)
     else:
         out["k16"] = bf16_round_f32(k)
@@ -200,7 +231,8 @@ def _head_view(store: dict, h: int) -> dict:
 
 
 def _kv_args(kv: dict):
-    return (_ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("k16"), np.uint16)),
+    return (_ptr(_c(kv.get("k8"), np.uint8)), _ptr(_c(kv.get("kx"), np.uint8)),
+            _ptr(_c(kv.get("k16"), np.uint16)),
             _ptr(_c(kv.get("ks"), np.float32)), _ptr(_c(kv.get("v8"), np.uint8)),
             _ptr(_c(kv.get("v16"), np.uint16)), _ptr(_c(kv.get("vs"), np.float32)))
 
@@ -214,29 +246,35 @@ def attend_rows(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     (out, lo, hi) where [lo, hi] holds every output reachable by rounding an
     ambiguous P (one within fp32 noise of a bf16 midpoint) either way.
     q8 = (codes uint8 [R, D], q_scale fp32 [R]): narrow QK on these query
-    codes instead of q_bits (which may then be None).  k_bias (fp32 [D]):
+    codes instead of q_bits (which may then be None); (codes, None, exps
+    uint8 [R, D/32]): block-scaled (MX) query rows.  k_bias (fp32 [D]):
     the head's exact K bias; kv then holds the pre-bias residual rows.
     """
-    q16, qc, qs, r, d = _query_args(q_bits, q8)
+    q16, qc, qs, qx, r, d = _query_args(q_bits, q8)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
     kb = _bias_arg(k_bias, d)
     out = np.empty((r, d), dtype=np.float64)
     lo = np.empty((r, d), dtype=np.float64) if bounds else None
     hi = np.empty((r, d), dtype=np.float64) if bounds else None
-    lib().orc_attend_rows_ex(MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(kb), n_keys,
-                             *_kv_args(kv), _ptr(n_valid), float(sm_scale), int(bool(round_p)),
-                             _ptr(out), _ptr(lo), _ptr(hi))
+    lib().orc_attend_rows_ex(MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(qx),
+                             _ptr(kb), n_keys, *_kv_args(kv), _ptr(n_valid), float(sm_scale),
+                             int(bool(round_p)), _ptr(out), _ptr(lo), _ptr(hi))
     return (out, lo, hi) if bounds else out
 
 
 def _query_args(q_bits, q8):
     if q8 is None:
         q16 = _c(q_bits, np.uint16)
-        return (q16, None, None) + q16.shape
-    qc, qs = _c(q8[0], np.uint8), _c(q8[1], np.float32)
+        return (q16, None, None, None) + q16.shape
+    qc = _c(q8[0], np.uint8)
+    if len(q8) == 3 and q8[1] is None:      # block-scaled rows
+        qx = _c(q8[2], np.uint8)
+        assert qx.shape == (qc.shape[0], qc.shape[1] // 32)
+        return (None, qc, None, qx) + qc.shape
+    qs = _c(q8[1], np.float32)
     assert qs.shape == qc.shape[:1]
-    return (None, qc, qs) + qc.shape
+    return (None, qc, qs, None) + qc.shape
 
 
 def _bias_arg(k_bias, d):
@@ -254,7 +292,7 @@ def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     Returns (out [R, D], part_acc [S, R, D], part_l [S, R], part_m [S, R]).
     q8 and k_bias as for attend_rows.
     """
-    q16, qc, qs, r, d = _query_args(q_bits, q8)
+    q16, qc, qs, qx, r, d = _query_args(q_bits, q8)
     kb = _bias_arg(k_bias, d)
     n_valid = _c(np.broadcast_to(np.asarray(n_valid), (r,)), np.int32)
     n_keys = _n_keys(kv)
@@ -264,7 +302,8 @@ def attend_rows_online(mode: str, q_bits, kv: dict, n_valid, sm_scale: float,
     pl = np.empty((max(n_splits, 1), r), dtype=np.float64)
     pm = np.empty((max(n_splits, 1), r), dtype=np.float64)
     lib().orc_attend_rows_online_ex(
-        MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(kb), n_keys, *_kv_args(kv),
+        MODES[mode], d, r, _ptr(q16), _ptr(qc), _ptr(qs), _ptr(qx), _ptr(kb), n_keys,
+        *_kv_args(kv),
         _ptr(n_valid), float(sm_scale), int(bool(round_p)), int(tile), int(split),
         _ptr(pacc), _ptr(pl), _ptr(pm), _ptr(out))
     return out, pacc[:n_splits], pl[:n_splits], pm[:n_splits]
@@ -285,7 +324,8 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
     q_bits  bf16 bits [B, Hq, D]
     k_seqs  list of B fp32 arrays [len_b, Hkv, D] (v_seqs alike)
     pairs   optional iterable of (b, kv_head) to compute; other rows are NaN
-    q8      narrow QK: Q quantised once (quantize_q), scores on its codes
+    q8      narrow QK: Q quantised once (quantize_q; quantize_q_mx for the
+            block-scaled MXK8V8 cache), scores on its codes
     k_bias  exact K bias fp32 [Hkv, D]: k_seqs are then the pre-bias
             residuals (stored quantised) and each key is residual + bias
     Returns fp64 [B, Hq, D] (with bounds=True: (out, lo, hi), see
@@ -293,7 +333,11 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
     """
     q_bits = np.asarray(q_bits, dtype=np.uint16)
     b_n, hq, d = q_bits.shape
-    qc, qs = quantize_q(q_bits) if q8 else (None, None)
+    qc, qs, qx = None, None, None
+    if q8 and mode in K_MX:
+        qc, qx = quantize_q_mx(q_bits)
+    elif q8:
+        qc, qs = quantize_q(q_bits)
     out = np.full((b_n, hq, d), np.nan)
     lo, hi = out.copy(), out.copy()
     if b_n == 0:
@@ -311,7 +355,9 @@ def decode(mode: str, q_bits, k_seqs, v_seqs, sm_scale: float,
         for h in heads:
             rows = q_bits[b, h * g:(h + 1) * g]
             sl = slice(h * g, (h + 1) * g)
-            rq8 = (qc[b, sl], qs[b, sl]) if q8 else None
+            rq8 = None
+            if q8:
+                rq8 = (qc[b, sl], None, qx[b, sl]) if qx is not None else (qc[b, sl], qs[b, sl])
             res = attend_rows(mode, rows, _head_view(store, h), n, sm_scale, round_p, bounds,
                               q8=rq8, k_bias=None if k_bias is None else k_bias[h])
             if bounds:

@@ -124,6 +124,49 @@ void orc_quantize_rows(const float* x, int64_t n_rows, int d, uint8_t* codes,
   }
 }
 
+/* ---- block-scaled (MX) rows ------------------------------------------- */
+
+/* Block-scaled (MX) rows: MXFP8 (OCP Microscaling formats, E4M3 elements,
+ * one power-of-two scale per block of 32 consecutive values) for the
+ * block-scaled QK of the hardware notes ("Measure block-scaled QK", which
+ * leaves the scale policy to be validated).  Reading: the block scale is the
+ * smallest power of two not below the block's storage-rule scale,
+ * 2^E with E = ceil(log2(fp32(amax / 448))), so that, as with the per-row
+ * rule, no element needs clamping (OCP's floor(log2(amax)) - 8 maps amax
+ * into [256, 512) and clamps the block's largest values at 448).  E is
+ * clamped to [-126, 127], so every scale is a normal fp32; a block of zeros
+ * (or one whose quotient is an fp32 subnormal) takes E = -126.  Elements are
+ * e4m3(x / 2^E), rounded to nearest even and saturated at 448.  exps holds
+ * E + 127 (the E8M0 byte). */
+int orc_mx_exponent(float amax) {
+  const float s = amax / 448.0f; /* fp32 division, correctly rounded */
+  int ex, e;
+  float m;
+  if (!(s >= 0x1p-126f)) return -126;
+  m = frexpf(s, &ex); /* s = m * 2^ex, m in [0.5, 1) */
+  e = (m == 0.5f) ? ex - 1 : ex;
+  return e > 127 ? 127 : e;
+}
+
+void orc_quantize_rows_mx(const float* x, int64_t n_rows, int d, uint8_t* codes,
+                          uint8_t* exps) {
+  int64_t r;
+  int blk, j;
+  for (r = 0; r < n_rows; ++r)
+    for (blk = 0; blk < d / 32; ++blk) {
+      const float* v = x + r * d + 32 * blk;
+      float amax = 0.0f, scale;
+      int e;
+      for (j = 0; j < 32; ++j)
+        if (fabsf(v[j]) > amax) amax = fabsf(v[j]);
+      e = orc_mx_exponent(amax);
+      exps[r * (d / 32) + blk] = (uint8_t)(e + 127);
+      scale = ldexpf(1.0f, e);
+      for (j = 0; j < 32; ++j)
+        codes[r * d + 32 * blk + j] = orc_e4m3_encode(v[j] / scale); /* exact quotient */
+    }
+}
+
 void orc_dequantize_rows(const uint8_t* codes, const float* scales, int64_t n_rows,
                          int d, uint16_t* out) {
   int64_t r;
@@ -145,13 +188,21 @@ typedef struct {
   const uint16_t *k16, *v16;
   const float *ks, *vs;
   const float* kb; /* exact K bias [d] (pre-bias residual cache), or NULL */
+  const uint8_t* kx; /* MXK8V8: E8M0 byte of each 32-element K block [n_keys][d/32] */
 } kv_view;
 
 /* Which side of the cache holds e4m3 codes with a scale (else bf16). */
-static int k_is_e4m3(int mode) { return mode == ORC_K8V8 || mode == ORC_K8V16; }
-static int v_is_e4m3(int mode) { return mode == ORC_K8V8 || mode == ORC_K16V8; }
+static int k_is_e4m3(int mode) {
+  return mode == ORC_K8V8 || mode == ORC_K8V16 || mode == ORC_MXK8V8;
+}
+static int v_is_e4m3(int mode) {
+  return mode == ORC_K8V8 || mode == ORC_K16V8 || mode == ORC_MXK8V8;
+}
 
 static double k_elem(const kv_view* kv, int t, int j) {
+  if (kv->mode == ORC_MXK8V8) /* code value times its block's scale 2^E */
+    return orc_e4m3_value(kv->k8[(size_t)t * kv->d + j]) *
+           ldexp(1.0, (int)kv->kx[(size_t)t * (kv->d / 32) + j / 32] - 127);
   if (k_is_e4m3(kv->mode)) return orc_e4m3_value(kv->k8[(size_t)t * kv->d + j]);
   return orc_bf16_value(kv->k16[(size_t)t * kv->d + j]);
 }
@@ -162,6 +213,7 @@ static double v_elem(const kv_view* kv, int t, int j) {
 }
 
 static double k_scale(const kv_view* kv, int t) {
+  if (kv->mode == ORC_MXK8V8) return 1.0; /* the block scales are in k_elem */
   return k_is_e4m3(kv->mode) ? (double)kv->ks[t] : 1.0;
 }
 
@@ -233,8 +285,14 @@ static double p_window(const kv_view* kv, const double* qv, int t, double c, int
  * code values, and the row's scale joins the constant outside the dot
  * product (CDNA 3 section of the hardware notes). */
 static double query_row(int d, int r, const uint16_t* q16, const uint8_t* q8,
-                        const float* q_scale, double c, double* qv) {
+                        const float* q_scale, const uint8_t* q_exp, double c, double* qv) {
   int j;
+  if (q8 && q_exp) { /* block-scaled (MX) rows: code value times 2^E of its block */
+    for (j = 0; j < d; ++j)
+      qv[j] = orc_e4m3_value(q8[(size_t)r * d + j]) *
+              ldexp(1.0, (int)q_exp[(size_t)r * (d / 32) + j / 32] - 127);
+    return c;
+  }
   if (q8) {
     for (j = 0; j < d; ++j) qv[j] = orc_e4m3_value(q8[(size_t)r * d + j]);
     return c * (double)q_scale[r];
@@ -244,12 +302,13 @@ static double query_row(int d, int r, const uint16_t* q16, const uint8_t* q8,
 }
 
 static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
-                        const uint8_t* q8, const float* q_scale, const float* k_bias, int n_keys,
-                        const uint8_t* k8, const uint16_t* k16, const float* ks,
+                        const uint8_t* q8, const float* q_scale, const uint8_t* q_exp,
+                        const float* k_bias, int n_keys, const uint8_t* k8,
+                        const uint8_t* kx, const uint16_t* k16, const float* ks,
                         const uint8_t* v8, const uint16_t* v16, const float* vs,
                         const int32_t* n_valid, float sm_scale, int round_p,
                         double* out, double* out_lo, double* out_hi) {
-  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias};
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias, kx};
   const double c0 = (double)sm_scale * ORC_LOG2E;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
   double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
@@ -262,7 +321,7 @@ static void attend_rows(int mode, int d, int n_rows, const uint16_t* q16,
     int nv = clamp_valid(n_valid[r], n_keys);
     double smax = -INFINITY, m, l = 0.0;
     double* o = out + (size_t)r * d;
-    const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
+    const double c = query_row(d, r, q16, q8, q_scale, q_exp, c0, qv);
     const double qb = bias_dot(&kv, qv);
     if (nv == 0) { /* no visible key: the row outputs 0 */
       for (j = 0; j < d; ++j) o[j] = 0.0;
@@ -315,7 +374,8 @@ void orc_attend_rows(int mode, int d, int n_rows, const uint16_t* q,
                      const float* ks, const uint8_t* v8, const uint16_t* v16,
                      const float* vs, const int32_t* n_valid, float sm_scale,
                      int round_p, double* out, double* out_lo, double* out_hi) {
-  attend_rows(mode, d, n_rows, q, NULL, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+  attend_rows(mode, d, n_rows, q, NULL, NULL, NULL, NULL, n_keys, k8, NULL, k16, ks, v8, v16, vs,
+              n_valid,
               sm_scale, round_p, out, out_lo, out_hi);
 }
 
@@ -325,19 +385,20 @@ void orc_attend_rows_q8(int mode, int d, int n_rows, const uint8_t* q8,
                         const uint16_t* v16, const float* vs,
                         const int32_t* n_valid, float sm_scale, int round_p,
                         double* out, double* out_lo, double* out_hi) {
-  attend_rows(mode, d, n_rows, NULL, q8, q_scale, NULL, n_keys, k8, k16, ks, v8, v16, vs, n_valid,
+  attend_rows(mode, d, n_rows, NULL, q8, q_scale, NULL, NULL, n_keys, k8, NULL, k16, ks, v8, v16,
+              vs, n_valid,
               sm_scale, round_p, out, out_lo, out_hi);
 }
 
 static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
-                               const uint8_t* q8, const float* q_scale, const float* k_bias,
-                               int n_keys,
-                               const uint8_t* k8, const uint16_t* k16, const float* ks,
+                               const uint8_t* q8, const float* q_scale, const uint8_t* q_exp,
+                               const float* k_bias, int n_keys, const uint8_t* k8,
+                               const uint8_t* kx, const uint16_t* k16, const float* ks,
                                const uint8_t* v8, const uint16_t* v16, const float* vs,
                                const int32_t* n_valid, float sm_scale, int round_p,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out) {
-  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias};
+  kv_view kv = {mode, d, n_keys, k8, v8, k16, v16, ks, vs, k_bias, kx};
   const double c0 = (double)sm_scale * ORC_LOG2E;
   int n_splits = n_keys > 0 ? (n_keys + split - 1) / split : 0;
   double* qv = (double*)malloc(sizeof(double) * (size_t)d);
@@ -350,7 +411,7 @@ static void attend_rows_online(int mode, int d, int n_rows, const uint16_t* q16,
   for (r = 0; r < n_rows; ++r) {
     int nv = clamp_valid(n_valid[r], n_keys);
     double mstar = -INFINITY, lsum = 0.0;
-    const double c = query_row(d, r, q16, q8, q_scale, c0, qv);
+    const double c = query_row(d, r, q16, q8, q_scale, q_exp, c0, qv);
     const double qb = bias_dot(&kv, qv);
     for (sp = 0; sp < n_splits; ++sp) {
       int k_lo = sp * split;
@@ -416,7 +477,8 @@ void orc_attend_rows_online(int mode, int d, int n_rows, const uint16_t* q,
                             int round_p, int tile, int split,
                             double* part_acc, double* part_l, double* part_m,
                             double* out) {
-  attend_rows_online(mode, d, n_rows, q, NULL, NULL, NULL, n_keys, k8, k16, ks, v8, v16, vs,
+  attend_rows_online(mode, d, n_rows, q, NULL, NULL, NULL, NULL, n_keys, k8, NULL, k16, ks, v8,
+                     v16, vs,
                      n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
 }
 
@@ -427,28 +489,30 @@ void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
                                const int32_t* n_valid, float sm_scale, int round_p,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out) {
-  attend_rows_online(mode, d, n_rows, NULL, q8, q_scale, NULL, n_keys, k8, k16, ks, v8, v16, vs,
+  attend_rows_online(mode, d, n_rows, NULL, q8, q_scale, NULL, NULL, n_keys, k8, NULL, k16, ks,
+                     v8, v16, vs,
                      n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m, out);
 }
 
 void orc_attend_rows_ex(int mode, int d, int n_rows, const uint16_t* q16, const uint8_t* q8,
-                        const float* q_scale, const float* k_bias, int n_keys,
-                        const uint8_t* k8, const uint16_t* k16, const float* ks,
-                        const uint8_t* v8, const uint16_t* v16, const float* vs,
-                        const int32_t* n_valid, float sm_scale, int round_p, double* out,
-                        double* out_lo, double* out_hi) {
-  attend_rows(mode, d, n_rows, q16, q8, q_scale, k_bias, n_keys, k8, k16, ks, v8, v16, vs,
-              n_valid, sm_scale, round_p, out, out_lo, out_hi);
+                        const float* q_scale, const uint8_t* q_exp, const float* k_bias,
+                        int n_keys, const uint8_t* k8, const uint8_t* kx, const uint16_t* k16,
+                        const float* ks, const uint8_t* v8, const uint16_t* v16,
+                        const float* vs, const int32_t* n_valid, float sm_scale, int round_p,
+                        double* out, double* out_lo, double* out_hi) {
+  attend_rows(mode, d, n_rows, q16, q8, q_scale, q_exp, k_bias, n_keys, k8, kx, k16, ks, v8,
+              v16, vs, n_valid, sm_scale, round_p, out, out_lo, out_hi);
 }
 
 void orc_attend_rows_online_ex(int mode, int d, int n_rows, const uint16_t* q16,
-                               const uint8_t* q8, const float* q_scale, const float* k_bias,
-                               int n_keys, const uint8_t* k8, const uint16_t* k16,
-                               const float* ks, const uint8_t* v8, const uint16_t* v16,
-                               const float* vs, const int32_t* n_valid, float sm_scale,
-                               int round_p, int tile, int split, double* part_acc,
-                               double* part_l, double* part_m, double* out) {
-  attend_rows_online(mode, d, n_rows, q16, q8, q_scale, k_bias, n_keys, k8, k16, ks, v8, v16,
-                     vs, n_valid, sm_scale, round_p, tile, split, part_acc, part_l, part_m,
-                     out);
+                               const uint8_t* q8, const float* q_scale, const uint8_t* q_exp,
+                               const float* k_bias, int n_keys, const uint8_t* k8,
+                               const uint8_t* kx, const uint16_t* k16, const float* ks,
+                               const uint8_t* v8, const uint16_t* v16, const float* vs,
+                               const int32_t* n_valid, float sm_scale, int round_p, int tile,
+                               int split, double* part_acc, double* part_l, double* part_m,
+                               double* out) {
+  attend_rows_online(mode, d, n_rows, q16, q8, q_scale, q_exp, k_bias, n_keys, k8, kx, k16, ks,
+                     v8, v16, vs, n_valid, sm_scale, round_p, tile, split, part_acc, part_l,
+                     part_m, out);
 }

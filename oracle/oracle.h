@@ -48,8 +48,9 @@ extern "C" {
 #endif
 
 /* Cache formats: K8V8 (both e4m3 + scale), K16V8 (K bf16, V e4m3 + scale),
- * BF16 (both bf16), K8V16 (K e4m3 + scale, V bf16). */
-enum { ORC_K8V8 = 0, ORC_K16V8 = 1, ORC_BF16 = 2, ORC_K8V16 = 3 };
+ * BF16 (both bf16), K8V16 (K e4m3 + scale, V bf16), MXK8V8 (K block-scaled
+ * e4m3, V as in K8V8). */
+enum { ORC_K8V8 = 0, ORC_K16V8 = 1, ORC_BF16 = 2, ORC_K8V16 = 3, ORC_MXK8V8 = 4 };
 
 /* Value of an OCP e4m3fn code (NaN for 0x7F / 0xFF). */
 double orc_e4m3_value(uint8_t code);
@@ -164,31 +165,49 @@ void orc_attend_rows_online_q8(int mode, int d, int n_rows, const uint8_t* q8,
                                int tile, int split, double* part_acc, double* part_l,
                                double* part_m, double* out);
 
+/* Block-scaled (MX) rows, MXFP8 (OCP Microscaling: E4M3 elements, one
+ * power-of-two scale per 32 consecutive values; "Measure block-scaled QK" in
+ * the hardware notes): per block E = ceil(log2(fp32(amax / 448))) (the
+ * smallest power of two not below the storage-rule scale, so nothing
+ * clamps; a reading, the pages leave the scale policy open), clamped to
+ * [-126, 127]; codes e4m3(x / 2^E) rounded to nearest even, saturated at 448.
+ * exps: E + 127 per block, [n_rows][d / 32].  orc_mx_exponent gives E. */
+int orc_mx_exponent(float amax);
+void orc_quantize_rows_mx(const float* x, int64_t n_rows, int d, uint8_t* codes,
+                          uint8_t* exps);
+
 /*
- * Every form above in one entry, with the options together: bf16 rows (q16)
- * or narrow rows (q8 + q_scale, q16 NULL), and an optional exact K bias
- * (k_bias, fp32 [d], NULL for none).  With a bias the stored K rows are the
- * pre-bias residual and the key is residual + bias ("Treat numerical safety
- * and kernel speed as separate gates" in the hardware notes; "Bias-aware
- * symmetric FP8" in the fused-quantisation README: quantise the pre-bias
- * residual, keep the fixed bias exact, apply the equivalent score-space
- * correction):
- *   s_t = ((sum_d q_d * K_td) * ks_t + sum_d q_d * b_d) * sm_scale * log2(e)
+ * Every form above in one entry, with the options together:
+ *   q16              bf16 rows, or NULL with
+ *   q8 + q_scale     narrow rows with one fp32 scale per row, or
+ *   q8 + q_exp       block-scaled rows ([n_rows][d/32] E8M0 bytes, q_scale NULL)
+ *   k_bias           optional exact K bias, fp32 [d] (NULL for none).  With a
+ *                    bias the stored K rows are the pre-bias residual and the
+ *                    key is residual + bias ("Treat numerical safety and
+ *                    kernel speed as separate gates" in the hardware notes;
+ *                    "Bias-aware symmetric FP8" in the fused-quantisation
+ *                    README: quantise the pre-bias residual, keep the fixed
+ *                    bias exact, apply the equivalent score-space correction):
+ *                    s_t = ((sum_d q_d K_td) ks_t + sum_d q_d b_d) sm_scale log2(e)
+ *   mode ORC_MXK8V8  K rows are block-scaled (k8 codes + kx E8M0 bytes
+ *                    [n_keys][d/32], ks unused): K_td = value(code) 2^E of
+ *                    its block; V as in K8V8.
  */
 void orc_attend_rows_ex(int mode, int d, int n_rows, const uint16_t* q16, const uint8_t* q8,
-                        const float* q_scale, const float* k_bias, int n_keys,
-                        const uint8_t* k8, const uint16_t* k16, const float* ks,
-                        const uint8_t* v8, const uint16_t* v16, const float* vs,
-                        const int32_t* n_valid, float sm_scale, int round_p, double* out,
-                        double* out_lo, double* out_hi);
+                        const float* q_scale, const uint8_t* q_exp, const float* k_bias,
+                        int n_keys, const uint8_t* k8, const uint8_t* kx, const uint16_t* k16,
+                        const float* ks, const uint8_t* v8, const uint16_t* v16,
+                        const float* vs, const int32_t* n_valid, float sm_scale, int round_p,
+                        double* out, double* out_lo, double* out_hi);
 
 void orc_attend_rows_online_ex(int mode, int d, int n_rows, const uint16_t* q16,
-                               const uint8_t* q8, const float* q_scale, const float* k_bias,
-                               int n_keys, const uint8_t* k8, const uint16_t* k16,
-                               const float* ks, const uint8_t* v8, const uint16_t* v16,
-                               const float* vs, const int32_t* n_valid, float sm_scale,
-                               int round_p, int tile, int split, double* part_acc,
-                               double* part_l, double* part_m, double* out);
+                               const uint8_t* q8, const float* q_scale, const uint8_t* q_exp,
+                               const float* k_bias, int n_keys, const uint8_t* k8,
+                               const uint8_t* kx, const uint16_t* k16, const float* ks,
+                               const uint8_t* v8, const uint16_t* v16, const float* vs,
+                               const int32_t* n_valid, float sm_scale, int round_p, int tile,
+                               int split, double* part_acc, double* part_l, double* part_m,
+                               double* out);
 
 #ifdef __cplusplus
 }
