@@ -30,7 +30,8 @@ the context sweep of the same shape at 77/512/2048/8192 keys in all four
 modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
 per-side savings against BF16, the ragged batch-64 paged workload
 (32q/8kv, lengths 1024..32768, K8V8, K16V8 and K8V8 as a pre-bias residual
-cache with the exact key bias), the roofline of the split
+cache with the exact key bias), block-scaled K (MXK8V8) against per-row
+K8V8 with bf16 Q and with fp8 QK (block_scaled_k), the roofline of the split
 kernel and the CPU oracle as a baseline.
 """
 from __future__ import annotations
@@ -335,6 +336,73 @@ def bench_sweep(steps, warmup, copies, head):
     return {"tokens": table, "k8v8_vs_k16v8_break_even_tokens": be}
 
 
+def bench_block_scaled(steps, copies):
+    """Block-scaled K (MXK8V8) against per-row K8V8 on the B16 T2048 shape,
+    HBM-cold like the headline: fp8kv_decode (bf16 Q) and fp8kv_decode_q8
+    (fp8 QK: per-row Q scale on K8V8, block-scaled QK on MXK8V8), two kernels
+    each (split + merge; block-scaled K takes no fused append).  Errors are
+    each output's relative L2 against the BF16 cache's, GPU against GPU."""
+    import torch
+    from fp8_kv_cache_append_amd import binding, synth
+    from fp8_kv_cache_append_amd.binding import KVCache
+
+    dev = "cuda"
+    w = synth.decode_b16_gqa8_d128(2048)
+    n = int(w.lens[0])
+    bs, table, n_blocks = synth.block_layout(w)
+    q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
+    q = torch.from_numpy(q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    lens = torch.from_numpy(w.lens.astype(np.int32)).to(dev)
+    ref_out = torch.empty((w.batch, w.q_heads, w.head_dim), device=dev)
+    res = {}
+    bases = {}
+    for mode in ("BF16", "K8V8", "MXK8V8"):
+        c = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+        for b in range(w.batch):
+            k, v = synth.kv_sequence(w, b)
+            binding.fp8kv_append(c, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                                 torch.full((n,), b, dtype=torch.int32, device=dev),
+                                 torch.arange(n, dtype=torch.int32, device=dev))
+        bases[mode] = c
+    ws = torch.empty(binding.fp8kv_decode_workspace_bytes(bases["K8V8"], w.batch, w.group, n)
+                     // 4 + 4, device=dev)
+    binding.fp8kv_decode(bases["BF16"], q, w.group, lens, n, w.sm_scale, ref_out, ws)
+    torch.cuda.synchronize()
+    for mode in ("K8V8", "MXK8V8"):
+        base = bases[mode]
+        caches = [base] + [KVCache(mode, base.k.clone(), base.v.clone(),
+                                   None if base.k_scale is None else base.k_scale.clone(),
+                                   base.v_scale.clone(), base.block_table, None,
+                                   None if base.k_exp is None else base.k_exp.clone())
+                           for _ in range(copies - 1)]
+        out = torch.empty_like(ref_out)
+        for name, fn in (("bf16_q", binding.fp8kv_decode), ("fp8_qk", binding.fp8kv_decode_q8)):
+            def step(i):
+                fn(caches[i % copies], q, w.group, lens, n, w.sm_scale, out, ws)
+            step(0)
+            torch.cuda.synchronize()
+            err = float(((out.double() - ref_out.double()).norm() / ref_out.double().norm()).item())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(copies):
+                    step(i)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, math.ceil(steps / copies))
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            res[f"{mode}_{name}"] = {"us_per_step": t0.elapsed_time(t1) * 1e3 / (reps * copies),
+                                     "rel_l2_vs_bf16_cache": err}
+        del caches
+        torch.cuda.empty_cache()
+    return {"workload": w.name + " (decode without append)", **res}
+
+
 def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
     """Batch 64, 32q/8kv, D128, lengths uniform in [1024, 32768], paged
     16-token blocks behind a shuffled table, biased keys.  The cache (2.3 GB
@@ -545,6 +613,7 @@ def main():
                                       args.copies, head)
         extras["ragged"] = {m: bench_ragged(m) for m in ("K8V8", "K16V8")}
         extras["ragged"]["K8V8_pre_bias"] = bench_ragged("K8V8", pre_bias=True)
+        extras["block_scaled"] = bench_block_scaled(max(640, args.steps // 4), args.copies)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     rec = {
@@ -595,6 +664,7 @@ def main():
         rec["prefill"] = extras["prefill"]
         rec["context_sweep"] = extras["sweep"]
         rec["ragged_b64_paged"] = extras["ragged"]
+        rec["block_scaled_k"] = extras["block_scaled"]
     print(json.dumps(rec), flush=True)
 
 

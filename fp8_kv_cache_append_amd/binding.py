@@ -16,9 +16,10 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfp8kv.so")
 
-MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3}
-K_E4M3 = ("K8V8", "K8V16")   # K side: uint8 e4m3 codes + fp32 scale (else bf16)
-V_E4M3 = ("K8V8", "K16V8")   # V side: uint8 e4m3 codes + fp32 scale (else bf16)
+MODES = {"K8V8": 0, "K16V8": 1, "BF16": 2, "K8V16": 3, "MXK8V8": 4}
+K_E4M3 = ("K8V8", "K8V16", "MXK8V8")  # K side: uint8 e4m3 codes (else bf16)
+V_E4M3 = ("K8V8", "K16V8", "MXK8V8")  # V side: uint8 e4m3 codes + fp32 scale (else bf16)
+K_MX = ("MXK8V8",)                     # K codes with an E8M0 byte per 32 values (k_exp)
 
 FP8KV_OK = 0
 FP8KV_ERR_INVALID = -1
@@ -46,7 +47,8 @@ class CacheDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_seqs", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("block_table", ctypes.c_void_p), ("k_bias", ctypes.c_void_p)]
+                ("block_table", ctypes.c_void_p), ("k_bias", ctypes.c_void_p),
+                ("k_exp", ctypes.c_void_p)]
 
 
 _lib = None
@@ -136,18 +138,21 @@ class KVCache:
     v_scale: torch.Tensor | None
     block_table: torch.Tensor
     k_bias: torch.Tensor | None = None
+    k_exp: torch.Tensor | None = None
 
     @classmethod
     def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
                  head_dim: int, block_table, device="cuda") -> "KVCache":
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
-        k8, v8 = mode in K_E4M3, mode in V_E4M3
+        k8, v8, kmx = mode in K_E4M3, mode in V_E4M3, mode in K_MX
         k = torch.zeros(shape, dtype=torch.uint8 if k8 else torch.bfloat16, device=device)
         v = torch.zeros(shape, dtype=torch.uint8 if v8 else torch.bfloat16, device=device)
-        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if k8 else None
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if k8 and not kmx else None
         vs = torch.zeros(shape[:3], dtype=torch.float32, device=device) if v8 else None
+        kx = torch.zeros(shape[:3] + (head_dim // 32,), dtype=torch.uint8,
+                         device=device) if kmx else None
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
-        return cls(mode, k, v, ks, vs, bt)
+        return cls(mode, k, v, ks, vs, bt, None, kx)
 
     @property
     def head_dim(self) -> int:
@@ -163,7 +168,7 @@ class KVCache:
                          int(self.block_table.shape[1]), int(self.block_table.shape[0]),
                          _ptr(self.k), _ptr(self.v),
                          _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table),
-                         _ptr(self.k_bias))
+                         _ptr(self.k_bias), _ptr(self.k_exp))
 
 
 def fp8kv_append(cache: KVCache, k_new, v_new, seq_idx, pos, stream=None) -> None:

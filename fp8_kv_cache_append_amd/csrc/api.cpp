@@ -41,7 +41,7 @@ int check_device() {
 int validate_cache(const fp8kv_cache* c) {
   if (!c) return FP8KV_ERR_INVALID;
   if (c->mode != FP8KV_K8V8 && c->mode != FP8KV_K16V8 && c->mode != FP8KV_BF16 &&
-      c->mode != FP8KV_K8V16)
+      c->mode != FP8KV_K8V16 && c->mode != FP8KV_MXK8V8)
     return FP8KV_ERR_INVALID;
   if (c->head_dim != 64 && c->head_dim != 128) return FP8KV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->max_blocks_per_seq <= 0 ||
@@ -52,8 +52,9 @@ int validate_cache(const fp8kv_cache* c) {
   if (!c->k || !c->v || !c->block_table) return FP8KV_ERR_INVALID;
   if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->block_table, 4))
     return FP8KV_ERR_INVALID;
-  const bool need_ks = fp8kv::k_is_e4m3(c->mode);
+  const bool need_ks = fp8kv::k_has_row_scale(c->mode);
   const bool need_vs = fp8kv::v_is_e4m3(c->mode);
+  const bool need_kx = fp8kv::k_is_mx(c->mode);
   // A scale pointer must be present exactly when the mode stores that scale:
   // a mismatch means the caller and the cache disagree about the format.
   if (need_ks != (c->k_scale != nullptr)) return FP8KV_ERR_INVALID;
@@ -61,13 +62,16 @@ int validate_cache(const fp8kv_cache* c) {
   if (c->k_scale && !aligned(c->k_scale, 4)) return FP8KV_ERR_INVALID;
   if (c->v_scale && !aligned(c->v_scale, 4)) return FP8KV_ERR_INVALID;
   if (c->k_bias && !aligned(c->k_bias, 16)) return FP8KV_ERR_INVALID;
+  if (need_kx != (c->k_exp != nullptr)) return FP8KV_ERR_INVALID;
+  if (c->k_exp && !aligned(c->k_exp, 4)) return FP8KV_ERR_INVALID;
+  if (need_kx && c->k_bias) return FP8KV_ERR_UNSUPPORTED;  // no bias on block-scaled K
   return FP8KV_OK;
 }
 
 fp8kv::CacheView view_of(const fp8kv_cache* c) {
   return fp8kv::CacheView{c->mode, c->block_size, c->num_kv_heads, c->head_dim,
                           c->max_blocks_per_seq, c->num_seqs, c->num_blocks, c->k, c->v,
-                          c->k_scale, c->v_scale, c->block_table, c->k_bias};
+                          c->k_scale, c->v_scale, c->block_table, c->k_bias, c->k_exp};
 }
 
 int launch_status(hipError_t e) {
@@ -182,8 +186,10 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
                         void* stream) {
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
-  if (q8 && ((cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16) || cache->k_bias))
+  if (q8 && (!fp8kv::k_is_e4m3(cache->mode) || cache->k_bias))
     return FP8KV_ERR_UNSUPPORTED;  // narrow QK takes the K codes as they are, no bias
+  if (k_new && fp8kv::k_is_mx(cache->mode))
+    return FP8KV_ERR_UNSUPPORTED;  // no fused append into block-scaled K
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
   if (!split_fits_table_window(chunk_tokens, cache->block_size)) return FP8KV_ERR_INVALID;
   if ((int64_t)n_splits * chunk_tokens < max_seq_len) return FP8KV_ERR_INVALID;
@@ -249,8 +255,8 @@ int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new
   int32_t chunk = 0, splits = 0;
   int st = fp8kv_decode_plan(cache, batch, gqa_group, max_seq_len, &chunk, &splits);
   if (st != FP8KV_OK) return st;
-  if (q8 && ((cache->mode != FP8KV_K8V8 && cache->mode != FP8KV_K8V16) || cache->k_bias))
-    return FP8KV_ERR_UNSUPPORTED;
+  if (q8 && (!fp8kv::k_is_e4m3(cache->mode) || cache->k_bias)) return FP8KV_ERR_UNSUPPORTED;
+  if (k_new && fp8kv::k_is_mx(cache->mode)) return FP8KV_ERR_UNSUPPORTED;
   if (batch == 0) return FP8KV_OK;
   const size_t acc_floats = (size_t)batch * cache->num_kv_heads * splits * gqa_group *
                             cache->head_dim;
@@ -312,6 +318,7 @@ int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst, void* strea
       dst->head_dim != src->head_dim)
     return FP8KV_ERR_INVALID;
   if (dst->k == src->k || dst->v == src->v) return FP8KV_ERR_INVALID;  // no in-place
+  if (fp8kv::k_is_mx(src->mode)) return FP8KV_ERR_UNSUPPORTED;
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(
       fp8kv::launch_dequantize(view_of(src), view_of(dst), static_cast<hipStream_t>(stream)));
@@ -326,7 +333,8 @@ int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group
   if (gqa_group < 1 || batch < 0 || max_q_len < 0 || total_q < 0 || batch > cache->num_seqs)
     return FP8KV_ERR_INVALID;
   if (gqa_group > kMaxGroup) return FP8KV_ERR_UNSUPPORTED;
-  if (cache->k_bias) return FP8KV_ERR_UNSUPPORTED;  // pre-bias caches: decode only
+  if (cache->k_bias || fp8kv::k_is_mx(cache->mode))
+    return FP8KV_ERR_UNSUPPORTED;  // pre-bias and block-scaled caches: decode only
   if (batch == 0 || max_q_len == 0 || total_q == 0) return FP8KV_OK;
   if (!q || !cu_q || !q_pos0 || !seq_lens || !out) return FP8KV_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(cu_q, 4) || !aligned(q_pos0, 4) ||

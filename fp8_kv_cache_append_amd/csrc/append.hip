@@ -25,6 +25,7 @@ struct AppendArgs {
   void* v;
   float* ks;
   float* vs;
+  uint8_t* kexp;   // kMXK8V8: E8M0 byte per 32-value K block
   int64_t n_rows;  // 2 * n_tok * hkv: K and V rows interleaved per (token, head)
   int hkv;
   int bs;
@@ -58,7 +59,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const float4 x = *reinterpret_cast<const float4*>(src);
 
   const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
-  if (quantise) {
+  if (k_is_mx(MODE) && !is_v) {
+    // block-scaled K: eight lanes hold a block of 32 values
+    const int e = mx_exponent(row_amax<8>(x));
+    uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
+    *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x, e8m0_value((uint32_t)(e + 127)));
+    if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
+  } else if (quantise) {
     const float scale = row_amax<kLanesPerRow>(x) / kE4M3Max;  // correctly rounded
     uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
     *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x, scale);
@@ -84,12 +91,13 @@ static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStrea
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
                          const int32_t* seq_idx, const int32_t* pos, int n_tok,
                          hipStream_t stream) {
-  AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs,
+  AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs, c.kexp,
                2 * (int64_t)n_tok * c.hkv, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
   switch (c.mode) {
     case kK8V8: return append_for_d<kK8V8>(c, a, stream);
     case kK16V8: return append_for_d<kK16V8>(c, a, stream);
     case kK8V16: return append_for_d<kK8V16>(c, a, stream);
+    case kMXK8V8: return append_for_d<kMXK8V8>(c, a, stream);
     default: return append_for_d<kBF16>(c, a, stream);
   }
 }

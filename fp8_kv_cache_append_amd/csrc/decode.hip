@@ -55,6 +55,7 @@ struct DecodeArgs {
   const float* k_new;  // fused append: the step's new K/V rows, fp32
   const float* v_new;  //   [batch][hkv][D]; unused by the plain decode
   const float* kbias;  // pre-bias residual cache: exact K bias [hkv][D], else null
+  const uint8_t* kexp; // block-scaled K: E8M0 byte per 32-value block [..][hkv][D/32]
   float c_scale;  // sm_scale * log2(e)
   int hkv;
   int group;
@@ -77,7 +78,14 @@ template <int MODE, int D>
 struct TileRegs {
   static constexpr bool K8 = k_is_e4m3(MODE);
   static constexpr bool V8 = v_is_e4m3(MODE);
+  static constexpr bool MX = k_is_mx(MODE);               // block-scaled K
+  static constexpr bool KS = k_has_row_scale(MODE);       // fp32 K scale per row
   static constexpr int KP = D / 64;                      // 16-element pieces
+  // d of a lane's K bytes: piece p, byte i of lane group g4 holds
+  // d = KPIECE * p + KLANE * g4 + i (in the 32-value blocks of block-scaled
+  // K: piece p of lane group g4 lies in block 2p + g4 / 2)
+  static constexpr int KLANE = 16;
+  static constexpr int KPIECE = 64;
   static constexpr int KRAW = K8 ? KP : 2 * KP;          // 16-byte K loads per sub-block
   static constexpr int DPR = D / 16;
   static constexpr int VW = V8 ? DPR / 4 : DPR / 2;      // dwords of V per token
@@ -85,6 +93,7 @@ struct TileRegs {
   static constexpr int VE = V8 ? 1 : 2;                  // bytes per V element
   u32x4_t k[4][KRAW];
   uint32_t v[2][8][VW];
+  uint32_t kxw;  // block-scaled K: the E8M0 bytes of token t0 + lane (like ks)
   float ks, vs;
   bool tok_ok;     // this lane's own token is before t_end in a valid block
   bool blk_ok[4];  // block id of each 16-token sub-block is a valid block
@@ -139,7 +148,10 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
                                                                                : r.blk_ok[3];
     r.tok_ok = t0 + lane < t_end && bok;
     const int64_t rr = base + (int64_t)((lane & 15) * a.hkv);
-    r.ks = T::K8 ? a.ks[rr] : 1.0f;
+    r.ks = T::KS ? a.ks[rr] : 1.0f;
+    if constexpr (T::MX)  // the row's E8M0 bytes (D / 32 of them)
+      r.kxw = D == 128 ? *reinterpret_cast<const uint32_t*>(a.kexp + rr * 4)
+                       : (uint32_t)*reinterpret_cast<const uint16_t*>(a.kexp + rr * 2);
     r.vs = T::V8 ? a.vs[rr] : 1.0f;
   }
   // Loads half by half (K then V of keys 0-31, then of keys 32-63), so the
@@ -151,7 +163,7 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
       const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + row0[kb] * (D * T::KE) + lo.k;
 #pragma unroll
       for (int p = 0; p < T::KP; ++p) {
-        const uint8_t* src = kbase + 64 * T::KE * p;
+        const uint8_t* src = kbase + T::KPIECE * T::KE * p;
         if (T::K8) {
           r.k[kb][p] = *reinterpret_cast<const u32x4_t*>(src);
         } else {
@@ -212,6 +224,7 @@ __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
   static_assert(!(Q8 && KB), "narrow QK takes no K bias");
+  static_assert(!(k_is_mx(MODE) && (KB || APPEND)), "block-scaled K: no bias, no fused append");
   using T = TileRegs<MODE, D>;
   constexpr int KC = D / 32;         // MFMA k-chunks for QK
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
@@ -219,6 +232,7 @@ void decode_partial_kernel(DecodeArgs a) {
   constexpr bool kV8 = T::V8;
 
   __shared__ float s_scale[kWaves][2][kTile];
+  __shared__ uint32_t s_kx[k_is_mx(MODE) ? kWaves : 1][kTile];  // block-scaled K: E8M0 words
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_l[kWaves][4][kMaxGroup];
   __shared__ __attribute__((aligned(16))) float s_acc[kWaves][kMaxGroup][D];
@@ -227,6 +241,9 @@ void decode_partial_kernel(DecodeArgs a) {
   // the query rows' scales
   __shared__ u32x4_t s_q8[Q8 ? 2 : 1][64];
   __shared__ float s_qs[Q8 ? kMaxGroup : 1];
+  // block-scaled Q: E8M0 byte of block b of head c (the instruction takes the
+  // scale of block b from lane group b)
+  __shared__ uint32_t s_qx[Q8 && k_is_mx(MODE) ? 16 : 1][4];
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
   __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
@@ -277,7 +294,8 @@ void decode_partial_kernel(DecodeArgs a) {
   if constexpr (!Q8) {
 #pragma unroll
     for (int kc = wave; kc < KC; kc += kWaves) {
-      const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
+      // the d of the K bytes the lane converts for k-chunk kc
+      const int d0 = T::KPIECE * (kc >> 1) + T::KLANE * g4 + 8 * (kc & 1);
       const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + d0);
       s_q[kc][lane] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -292,7 +310,8 @@ void decode_partial_kernel(DecodeArgs a) {
     for (int p = 0; p < T::KP; ++p)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + 64 * p + 16 * g4 + 8 * j);
+        const u32x4_t w =
+            *reinterpret_cast<const u32x4_t*>(qrow + T::KPIECE * p + T::KLANE * g4 + 8 * j);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const float4 f = make_float4(__uint_as_float(w[2 * e] << 16),
@@ -303,17 +322,39 @@ void decode_partial_kernel(DecodeArgs a) {
           m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
         }
       }
-    const float q_scale = max_over_groups(m) / kE4M3Max;
+    // per-row rule: the row's scale (max over the four lane groups); block
+    // rule: piece p of lane group g4 lies in block 2p + g4 / 2, shared with
+    // lane group g4 ^ 1 (a 16-lane swap)
+    float q_scale = 0.0f;
+    float piece_scale[2] = {0.0f, 0.0f};
+    if constexpr (T::MX) {
+#pragma unroll
+      for (int p = 0; p < T::KP; ++p) {
+        float mp = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mp = fmaxf(mp, fmaxf(fmaxf(fabsf(xq[p][e].x), fabsf(xq[p][e].y)),
+                               fmaxf(fabsf(xq[p][e].z), fabsf(xq[p][e].w))));
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mp), __float_as_uint(mp),
+                                                  false, false);
+        const int ep = mx_exponent(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+        piece_scale[p] = e8m0_value((uint32_t)(ep + 127));
+        if ((g4 & 1) == 0 && c < G) s_qx[c][2 * p + (g4 >> 1)] = (uint32_t)(ep + 127);
+      }
+    } else {
+      q_scale = max_over_groups(m) / kE4M3Max;
+    }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       u32x4_t codes = {0u, 0u, 0u, 0u};  // D = 64: the upper 16 k-slots are zero
       if (p < T::KP) {
+        const float sc = T::MX ? piece_scale[p < T::KP ? p : 0] : q_scale;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) codes[e] = e4m3_codes4(xq[p < T::KP ? p : 0][e], q_scale);
+        for (int e = 0; e < 4; ++e) codes[e] = e4m3_codes4(xq[p < T::KP ? p : 0][e], sc);
       }
       s_q8[p][lane] = (c < G) ? codes : u32x4_t{0u, 0u, 0u, 0u};
     }
-    if (g4 == 0 && c < G) s_qs[c] = q_scale;
+    if (g4 == 0 && c < G) s_qs[c] = T::MX ? 1.0f : q_scale;
   }
   // Fused append: lanes [0, D/4) hold four values of the K row, lanes
   // [D/4, D/2) four of the V row, loaded with the first round trip.  Every
@@ -370,7 +411,7 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 
   LaneOffsets lo;
-  lo.k = (uint32_t)(c * a.hkv) * (D * T::KE) + 16 * T::KE * g4;
+  lo.k = (uint32_t)(c * a.hkv) * (D * T::KE) + T::KLANE * T::KE * g4;
   lo.v = (uint32_t)(4 * g4 * a.hkv) * (D * T::VE) + DPR * T::VE * c;
   lo.v_token = (uint32_t)wave_uniform(a.hkv * D * T::VE);
 
@@ -445,7 +486,7 @@ void decode_partial_kernel(DecodeArgs a) {
   // move them to scratch memory.
   auto patch_scales = [&](T& r, int t0) __attribute__((always_inline)) {
     const int tn = pos_n - t0;
-    if (kK8) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
+    if (T::KS) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
     if (kV8) r.vs = (lane == tn) ? __uint_as_float(s_new[D + 1]) : r.vs;
   };
   auto patch_half = [&](T& r, int t0, int kp) __attribute__((always_inline)) {
@@ -486,6 +527,7 @@ void decode_partial_kernel(DecodeArgs a) {
   };
 
   float q_scale_c = 1.0f;   // Q8: set once s_qs is complete
+  int q_exp_c = 127;        // Q8, block-scaled: this lane's Q block E8M0 byte
   float m_run = -INFINITY;  // integer reference (log2 units) of head c
   float l_run = 0.0f;       // this lane's share of the normaliser of head c
   f32x4_t acc[DPR];
@@ -503,7 +545,8 @@ void decode_partial_kernel(DecodeArgs a) {
     if (has_new) patch_scales(cur, t0);
     // K scale with sm_scale * log2(e) folded in (one product per token),
     // V scale as is.
-    if (kK8) s_scale[wave][0][lane] = cur.ks * a.c_scale;
+    if (T::KS) s_scale[wave][0][lane] = cur.ks * a.c_scale;
+    if constexpr (T::MX) s_kx[wave][lane] = cur.kxw;
     if (kV8) s_scale[wave][1][lane] = cur.tok_ok ? cur.vs : 0.0f;
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -526,12 +569,31 @@ void decode_partial_kernel(DecodeArgs a) {
               __builtin_bit_cast(i32x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
           const i32x8_t bq =
               __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-          s = mfma_16x16x128_e4m3(av, bq, s);
+          if constexpr (T::MX) {
+            // the lane's K block: head_dim 128 block g4, 64 block g4 / 2
+            // the instruction takes the scale of K block g4 from lane group g4
+            const int kexp =
+                g4 < D / 32 ? (int)((s_kx[wave][16 * kb + c] >> (8 * g4)) & 0xffu) : 127;
+            s = mfma_16x16x128_e4m3_scaled(av, bq, s, kexp, q_exp_c);
+          } else {
+            s = mfma_16x16x128_e4m3(av, bq, s);
+          }
         } else {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
             u32x4_t av;
-            if (kK8) {
+            if (T::MX) {
+              // codes times the lane's block scale (exact in bf16)
+              // piece kc / 2 of lane group g4 lies in block 2 (kc / 2) + g4 / 2
+              const float ksc = e8m0_value(
+                  (s_kx[wave][16 * kb + c] >> (8 * (2 * (kc >> 1) + (g4 >> 1)))) & 0xffu);
+              const u32x4_t w = cur.k[kb][kc >> 1];
+              const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
+              av = u32x4_t{e4m3x2_to_bf16x2_scaled(lo32, ksc, false),
+                           e4m3x2_to_bf16x2_scaled(lo32, ksc, true),
+                           e4m3x2_to_bf16x2_scaled(hi32, ksc, false),
+                           e4m3x2_to_bf16x2_scaled(hi32, ksc, true)};
+            } else if (kK8) {
               const u32x4_t w = cur.k[kb][kc >> 1];
               const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
               av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
@@ -555,7 +617,7 @@ void decode_partial_kernel(DecodeArgs a) {
         const int base = 16 * kb + 4 * g4;
         f32x4_t ksv = {a.c_scale, a.c_scale, a.c_scale, a.c_scale};
         f32x4_t vsv = {1.f, 1.f, 1.f, 1.f};
-        if (kK8) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
+        if (T::KS) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
         if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -654,6 +716,9 @@ void decode_partial_kernel(DecodeArgs a) {
   // Q8: the query row's scale of head c (0 for the padding heads c >= G,
   // whose B columns are zero)
   if constexpr (Q8) q_scale_c = (c < G) ? s_qs[c] : 0.0f;
+  // block-scaled: this lane group supplies the scale of block g4 (head_dim
+  // 64 has blocks 0 and 1; the zero k-slots of blocks 2 and 3 take 2^0)
+  if constexpr (Q8 && T::MX) q_exp_c = (c < G && g4 < D / 32) ? (int)s_qx[c][g4] : 127;
   for (int tile = wave; tile < n_tiles; tile += 2 * kWaves) {
     const int t0 = t_begin + tile * kTile;
     if (tile + kWaves < n_tiles)
@@ -788,7 +853,7 @@ static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n
 template <int MODE, bool APPEND, bool Q8>
 static void launch_partial_mode(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                                 hipStream_t stream) {
-  if constexpr (!Q8) {
+  if constexpr (!Q8 && !k_is_mx(MODE)) {
     if (c.kbias) {
       launch_partial_d<MODE, APPEND, false, true>(c, a, n_wg, stream);
       return;
@@ -800,6 +865,15 @@ static void launch_partial_mode(const CacheView& c, const DecodeArgs& a, unsigne
 template <bool APPEND>
 static void launch_partial_append(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                                   bool q8, hipStream_t stream) {
+  if constexpr (!APPEND) {  // block-scaled K: no fused append (checked by the caller)
+    if (c.mode == kMXK8V8) {
+      if (q8)
+        launch_partial_mode<kMXK8V8, false, true>(c, a, n_wg, stream);
+      else
+        launch_partial_mode<kMXK8V8, false, false>(c, a, n_wg, stream);
+      return;
+    }
+  }
   if (q8) {  // e4m3 K only (checked by the caller)
     if (c.mode == kK8V8)
       launch_partial_mode<kK8V8, APPEND, true>(c, a, n_wg, stream);
@@ -811,7 +885,8 @@ static void launch_partial_append(const CacheView& c, const DecodeArgs& a, unsig
     case kK8V8: launch_partial_mode<kK8V8, APPEND, false>(c, a, n_wg, stream); break;
     case kK16V8: launch_partial_mode<kK16V8, APPEND, false>(c, a, n_wg, stream); break;
     case kK8V16: launch_partial_mode<kK8V16, APPEND, false>(c, a, n_wg, stream); break;
-    default: launch_partial_mode<kBF16, APPEND, false>(c, a, n_wg, stream); break;
+    case kBF16: launch_partial_mode<kBF16, APPEND, false>(c, a, n_wg, stream); break;
+    default: break;  // block-scaled K with the fused append: rejected by the caller
   }
 }
 
@@ -820,9 +895,9 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
                                  bool q8, hipStream_t stream) {
-  DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,     seq_lens,
-               part_acc, part_ml,  k_new,   v_new,   c.kbias,  c_scale, c.hkv,
-               group,   c.bs,      c.mbps,  chunk,   n_splits, c.num_blocks};
+  DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,       seq_lens,
+               part_acc, part_ml,  k_new,   v_new,   c.kbias,  c.kexp,  c_scale,
+               c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);

@@ -71,7 +71,8 @@ hipError_t launch_dequantize(const CacheView& src, const CacheView& dst, hipStre
     case kK8V8: return dequant_for_d<kK8V8>(src.d, a, stream);
     case kK16V8: return dequant_for_d<kK16V8>(src.d, a, stream);
     case kK8V16: return dequant_for_d<kK8V16>(src.d, a, stream);
-    default: return dequant_for_d<kBF16>(src.d, a, stream);
+    case kBF16: return dequant_for_d<kBF16>(src.d, a, stream);
+    default: return hipErrorInvalidValue;  // block-scaled K: rejected by the caller
   }
 }
 

@@ -110,6 +110,36 @@ __device__ __forceinline__ uint32_t e4m3_codes4(float4 x, float scale) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
 }
 
+// Block-scaled (MX) rule for a block of 32 values: the scale is 2^E, the
+// smallest power of two not below the storage rule's amax / 448 (so no code
+// clamps), E clamped to [-126, 127] (a zero or tiny block takes -126).  The
+// fp32 quotient is rounded like the per-row scale; E is read from its bits.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const float s = amax / kE4M3Max;  // correctly rounded
+  if (!(s >= 0x1p-126f)) return -126;
+  const uint32_t bits = __float_as_uint(s);
+  const int e = (int)((bits >> 23) & 0xff) - 127;
+  return min((bits & 0x7fffffu) ? e + 1 : e, 127);
+}
+
+// 2^E as fp32 (normal for E in [-126, 127]) from the E8M0 byte E + 127.
+__device__ __forceinline__ float e8m0_value(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// Two e4m3 codes times a power-of-two scale -> two bf16 (exact while the
+// products stay in the normal range).
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2_scaled(uint32_t w, float scale, bool hi) {
+  bf16x2_t v = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// D += A * B with per-lane block scales 2^(sa - 127), 2^(sb - 127) (E8M0
+// bytes) applied by the instruction to the lane's 32 k-slots.
+__device__ __forceinline__ f32x4_t mfma_16x16x128_e4m3_scaled(i32x8_t a, i32x8_t b, f32x4_t c,
+                                                              int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // Four values rounded to bf16 (nearest even): the K row of the K16V8 control
 // and both rows of the BF16 control.
 __device__ __forceinline__ u32x2_t bf16x4(float4 x) {

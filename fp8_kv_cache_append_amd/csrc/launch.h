@@ -9,12 +9,17 @@ namespace fp8kv {
 
 // Cache formats: which side holds e4m3 codes + an fp32 scale per (token,
 // KV head); the other side, if any, holds bf16.
-enum { kK8V8 = 0, kK16V8 = 1, kBF16 = 2, kK8V16 = 3 };
-constexpr bool k_is_e4m3(int mode) { return mode == kK8V8 || mode == kK8V16; }
-constexpr bool v_is_e4m3(int mode) { return mode == kK8V8 || mode == kK16V8; }
+// kMXK8V8: K as e4m3 codes with one power-of-two (E8M0) scale per 32
+// consecutive values of a row (block-scaled, MXFP8), V as in kK8V8.
+enum { kK8V8 = 0, kK16V8 = 1, kBF16 = 2, kK8V16 = 3, kMXK8V8 = 4 };
+constexpr bool k_is_e4m3(int mode) { return mode == kK8V8 || mode == kK8V16 || mode == kMXK8V8; }
+constexpr bool v_is_e4m3(int mode) { return mode == kK8V8 || mode == kK16V8 || mode == kMXK8V8; }
+constexpr bool k_is_mx(int mode) { return mode == kMXK8V8; }
+// an fp32 scale per (token, KV head) on the K side
+constexpr bool k_has_row_scale(int mode) { return k_is_e4m3(mode) && !k_is_mx(mode); }
 
 struct CacheView {
-  int mode;   // kK8V8 / kK16V8 / kBF16 / kK8V16
+  int mode;   // kK8V8 / kK16V8 / kBF16 / kK8V16 / kMXK8V8
   int bs;     // tokens per block (multiple of 16)
   int hkv;    // KV heads
   int d;      // head_dim, 64 or 128
@@ -27,12 +32,15 @@ struct CacheView {
   float* vs;
   const int32_t* table;
   const float* kbias;  // exact K bias [hkv][d] of a pre-bias residual cache, or null
+  uint8_t* kexp;       // kMXK8V8: E8M0 byte per 32-value K block [..][hkv][d/32]
 };
 
 // Work-groups of the split kernel one compute unit holds at once: two where a
 // lane's registers fit in 256 (the e4m3 K tile of K8V8, and every D = 64
 // tile), else one.  The kernel's launch bounds and the split plan both use it.
-constexpr int split_wgs_per_cu(int mode, int d) { return (mode == kK8V8 || d == 64) ? 2 : 1; }
+constexpr int split_wgs_per_cu(int mode, int d) {
+  return (mode == kK8V8 || mode == kMXK8V8 || d == 64) ? 2 : 1;
+}
 constexpr int kComputeUnits = 256;  // MI355X
 
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,

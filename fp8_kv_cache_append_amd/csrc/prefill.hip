@@ -440,7 +440,8 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
     case kK8V8: launch_prefill_mode<kK8V8>(c.d, a, (unsigned)n_wg, stream); break;
     case kK16V8: launch_prefill_mode<kK16V8>(c.d, a, (unsigned)n_wg, stream); break;
     case kK8V16: launch_prefill_mode<kK8V16>(c.d, a, (unsigned)n_wg, stream); break;
-    default: launch_prefill_mode<kBF16>(c.d, a, (unsigned)n_wg, stream); break;
+    case kBF16: launch_prefill_mode<kBF16>(c.d, a, (unsigned)n_wg, stream); break;
+    default: break;  // block-scaled K: rejected by the caller
   }
   return hipGetLastError();
 }

@@ -60,12 +60,17 @@ extern "C" {
  *   FP8KV_K8V8   K and V: uint8 e4m3 codes + fp32 scale per (token, KV head)
  *   FP8KV_K16V8  K: bf16; V: e4m3 codes + fp32 scale (no K preparation)
  *   FP8KV_BF16   K and V: bf16 (no scales)
- *   FP8KV_K8V16  K: e4m3 codes + fp32 scale; V: bf16 (no V preparation) */
+ *   FP8KV_K8V16  K: e4m3 codes + fp32 scale; V: bf16 (no V preparation)
+ *   FP8KV_MXK8V8 K: block-scaled e4m3 (MXFP8, [HW] "Measure block-scaled
+ *                QK"): one power-of-two scale 2^E per 32 consecutive values
+ *                of a row, E = ceil(log2(fp32(amax / 448))) clamped to
+ *                [-126, 127], codes e4m3(x / 2^E); V as in K8V8 */
 typedef enum {
   FP8KV_K8V8 = 0,
   FP8KV_K16V8 = 1,
   FP8KV_BF16 = 2,
-  FP8KV_K8V16 = 3
+  FP8KV_K8V16 = 3,
+  FP8KV_MXK8V8 = 4
 } fp8kv_mode;
 
 typedef enum {
@@ -84,6 +89,14 @@ typedef enum {
  *                   BF16: bf16 for both; K8V16: k uint8, v bf16
  *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 and
  *                   K8V16 (NULL otherwise)
+ *   k_exp           MXK8V8 only (NULL otherwise): uint8
+ *                   [num_blocks][block_size][num_kv_heads][head_dim / 32], the
+ *                   byte E + 127 of each 32-value K block, 4-byte aligned.
+ *                   Decode reads it with bf16 Q (codes converted by their
+ *                   block's scale) or with block-scaled Q through the q8
+ *                   entries (the matrix instruction applies both operands'
+ *                   block scales); the fused append, prefill, dequantize and
+ *                   a K bias give FP8KV_ERR_UNSUPPORTED for such a cache.
  *   v_scale         same shape, K8V8 and K16V8 (NULL otherwise)
  *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
  *                   b is slot t % block_size of block
@@ -117,6 +130,7 @@ typedef struct fp8kv_cache {
   float* v_scale;
   const int32_t* block_table;
   const float* k_bias;         /* exact fixed K bias, or NULL (see above) */
+  uint8_t* k_exp;              /* FP8KV_MXK8V8: K block exponents (see above) */
 } fp8kv_cache;
 
 /*
@@ -236,11 +250,17 @@ int fp8kv_decode_append(const fp8kv_cache* cache, const float* k_new,
  * instruction directly on the stored K codes:
  *   s_t = (sum_d value(qc_d) * value(kc_t,d)) * q_scale * k_scale_t
  *         * sm_scale * log2(e)
- * Everything after the score is unchanged.  The Q rounding is an extra
- * error source (a few percent relative L2 against bf16 Q on N(0,1) data),
- * which the caller accepts by choosing these entry points.  Arguments,
- * workspace and guards as for fp8kv_decode / fp8kv_decode_append; caches
- * whose K is not e4m3 (K16V8, BF16) give FP8KV_ERR_UNSUPPORTED.
+ * Everything after the score is unchanged.  On an MXK8V8 cache this is
+ * block-scaled QK ([HW] "Measure block-scaled QK"): each 32-value block of a
+ * query row gets its own power-of-two scale by the MXK8V8 rule, and the
+ * matrix instruction applies the Q and K block scales itself:
+ *   s_t = sum_blocks 2^(Eq + Ek) (sum_{d in block} value(qc_d) value(kc_t,d))
+ *         * sm_scale * log2(e)
+ * The Q rounding is an extra error source (a few percent relative L2 against
+ * bf16 Q on N(0,1) data), which the caller accepts by choosing these entry
+ * points.  Arguments, workspace and guards as for fp8kv_decode /
+ * fp8kv_decode_append; caches whose K is not e4m3 (K16V8, BF16), or that
+ * carry a K bias, give FP8KV_ERR_UNSUPPORTED.
  */
 int fp8kv_decode_q8(const fp8kv_cache* cache, const uint16_t* q,
                     int32_t gqa_group, const int32_t* seq_lens, int32_t batch,

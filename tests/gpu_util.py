@@ -49,7 +49,10 @@ def read_rows(cache: KVCache, b: int, n: int) -> dict:
     def grab(x):
         return x[blk, slot].cpu()
 
-    if cache.mode in binding.K_E4M3:
+    if cache.mode in binding.K_MX:
+        out["k8"] = grab(cache.k).numpy()
+        out["kx"] = grab(cache.k_exp).numpy()
+    elif cache.mode in binding.K_E4M3:
         out["k8"] = grab(cache.k).numpy()
         out["ks"] = grab(cache.k_scale).numpy()
     else:

@@ -50,13 +50,13 @@ def test_strerror():
 def _desc(**kw):
     base = dict(mode=0, num_blocks=4, block_size=16, num_kv_heads=2, head_dim=128,
                 max_blocks_per_seq=4, num_seqs=16, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
-                block_table=FAKE, k_bias=None)
+                block_table=FAKE, k_bias=None, k_exp=None)
     base.update(kw)
     return CacheDesc(**base)
 
 
 BAD_CACHES = [
-    (dict(mode=4), -1),
+    (dict(mode=5), -1),
     (dict(mode=3), -1),                 # K8V16 stores no V scale: v_scale must be NULL
     (dict(mode=3, v_scale=None, k_scale=None), -1),   # ... but a K scale
     (dict(head_dim=96), -4),
@@ -71,6 +71,11 @@ BAD_CACHES = [
     (dict(mode=2, k_scale=None), -1),  # BF16 must not carry a V scale
     (dict(block_table=FAKE + 2), -1),
     (dict(k_bias=FAKE + 4), -1),        # the bias is read 16 bytes at a time
+    (dict(mode=4), -1),                 # block-scaled K: no K row scale, but k_exp
+    (dict(mode=4, k_scale=None), -1),   # ... k_exp missing
+    (dict(k_exp=FAKE), -1),             # k_exp only with block-scaled K
+    (dict(mode=4, k_scale=None, k_exp=FAKE + 2), -1),   # misaligned
+    (dict(mode=4, k_scale=None, k_exp=FAKE, k_bias=FAKE), -4),  # no bias on block scales
 ]
 
 
