@@ -64,6 +64,8 @@ struct DecodeArgs {
   int chunk;
   int n_splits;
   int num_blocks;
+  uint64_t k_bytes;  // bytes of the K and V arrays (hardware bound of the tile loads)
+  uint64_t v_bytes;
 };
 
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
@@ -122,10 +124,23 @@ struct LaneOffsets {
 // neutralised where they are used (score -inf, V and v_scale 0).  A fixed
 // number of loads in a fixed order lets the compiler wait for exactly the
 // loads each step needs instead of for all of them.
+//
+// The K/V loads are buffer loads on a resource per sub-block whose extent
+// ends where the cache ends.  A tile that is not live (no tile left for this
+// wave) is issued all the same with an empty extent: its loads return zeros
+// without a memory access, but they are counted like the others, so every
+// path into a compute step has the same loads outstanding and the waits
+// before it stay exact.  (Issued under a branch instead, they would leave
+// the compiler two counts to reconcile where the paths join, and it keeps
+// the smaller: the wait for the current tile then also waits for the whole
+// next one.)  Empty loads are not free (each still passes through the
+// load pipeline; measured at about 3 us per launch when every wave of the
+// B16, 8192-key step issued two empty tiles), so the tile loop is shaped to
+// need them only at a wave's odd last tile.
 template <int MODE, int D>
 __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a,
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
-                                          int e_base, int h, int lane) {
+                                          int e_base, int h, int lane, bool live) {
   using T = TileRegs<MODE, D>;
   int64_t row0[4];
   bool all_ok = t0 + 64 <= t_end;
@@ -147,7 +162,8 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     const bool bok = kb == 0 ? r.blk_ok[0] : kb == 1 ? r.blk_ok[1] : kb == 2 ? r.blk_ok[2]
                                                                                : r.blk_ok[3];
     r.tok_ok = t0 + lane < t_end && bok;
-    const int64_t rr = base + (int64_t)((lane & 15) * a.hkv);
+    // (a tile that is not live reads the scales of row h, in block 0)
+    const int64_t rr = live ? base + (int64_t)((lane & 15) * a.hkv) : (int64_t)h;
     r.ks = T::KS ? a.ks[rr] : 1.0f;
     if constexpr (T::MX)  // the row's E8M0 bytes (D / 32 of them)
       r.kxw = D == 128 ? *reinterpret_cast<const uint32_t*>(a.kexp + rr * 4)
@@ -156,37 +172,50 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
   }
   // Loads half by half (K then V of keys 0-31, then of keys 32-63), so the
   // first half can be computed while the second is in flight.
+  // A sub-block's resource (scalar: the row bases are uniform) covers the
+  // bytes from its first row to the end of the array, saturated to 32 bits.
+  auto rsrc = [&](const void* arr, uint64_t arr_bytes, int kb, int elem_bytes)
+      __attribute__((always_inline)) {
+    const uint64_t off = (uint64_t)row0[kb] * (uint64_t)(D * elem_bytes);
+    const uint64_t rem = arr_bytes - off;
+    const uint32_t n = (rem >> 32) ? 0xffffffffu : (uint32_t)rem;
+    return buffer_rsrc(static_cast<const uint8_t*>(arr) + off, live ? n : 0u);
+  };
 #pragma unroll
   for (int kp = 0; kp < 2; ++kp) {
 #pragma unroll
     for (int kb = 2 * kp; kb < 2 * kp + 2; ++kb) {
-      const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + row0[kb] * (D * T::KE) + lo.k;
+      const __amdgpu_buffer_rsrc_t krs = rsrc(a.k, a.k_bytes, kb, T::KE);
 #pragma unroll
       for (int p = 0; p < T::KP; ++p) {
-        const uint8_t* src = kbase + T::KPIECE * T::KE * p;
+        const int off = (int)lo.k + T::KPIECE * T::KE * p;
         if (T::K8) {
-          r.k[kb][p] = *reinterpret_cast<const u32x4_t*>(src);
+          r.k[kb][p] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
         } else {
-          r.k[kb][2 * p] = *reinterpret_cast<const u32x4_t*>(src);
-          r.k[kb][2 * p + 1] = *reinterpret_cast<const u32x4_t*>(src + 16);
+          r.k[kb][2 * p] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+          r.k[kb][2 * p + 1] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kb = 2 * kp + (j >> 2);
-      const uint8_t* src = static_cast<const uint8_t*>(a.v) + row0[kb] * (D * T::VE) +
-                           (j & 3) * lo.v_token + lo.v;
-      if constexpr (T::VW == 4) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+    for (int hb = 0; hb < 2; ++hb) {
+      const int kb = 2 * kp + hb;
+      const __amdgpu_buffer_rsrc_t vrs = rsrc(a.v, a.v_bytes, kb, T::VE);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r.v[kp][j][e] = w[e];
-      } else if constexpr (T::VW == 2) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(src);
-        r.v[kp][j][0] = w[0];
-        r.v[kp][j][1] = w[1];
-      } else {
-        r.v[kp][j][0] = *reinterpret_cast<const uint32_t*>(src);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * hb + jj;
+        const int soff = jj * (int)lo.v_token;  // uniform: token row within the 4
+        if constexpr (T::VW == 4) {
+          const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)lo.v, soff, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r.v[kp][j][e] = w[e];
+        } else if constexpr (T::VW == 2) {
+          const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vrs, (int)lo.v, soff, 0);
+          r.v[kp][j][0] = w[0];
+          r.v[kp][j][1] = w[1];
+        } else {
+          r.v[kp][j][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (int)lo.v, soff, 0);
+        }
       }
     }
   }
@@ -219,7 +248,13 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
 // (q . b) * sm_scale * log2(e), computed once per work-group ("Treat
 // numerical safety and kernel speed as separate gates": keep the fixed bias
 // exact, correct in score space).
-template <int MODE, int D, bool APPEND, bool Q8, bool KB>
+//
+// MULTI: the split holds more than one tile per wave (chunk > 4 tiles), so
+// the waves stream their tiles through two register buffers.  Without it
+// (chunk <= 4 tiles) each wave computes at most one tile and the kernel holds
+// one buffer: a function of its own, so that its register allocation is not
+// shaped by the loop's.
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
@@ -429,6 +464,7 @@ void decode_partial_kernel(DecodeArgs a) {
   }
   pos_n = wave_uniform(pos_n);
   auto append_new = [&]() __attribute__((always_inline)) {
+    if constexpr (!APPEND) return;  // (s_new is a placeholder then)
     const int p = pos_n;
     const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
     const bool is_v = lane >= kLR;
@@ -459,6 +495,7 @@ void decode_partial_kernel(DecodeArgs a) {
   // consumed, because on gfx9 stores share the load counter: a store among
   // the tile loads would make every wait for tile data wait for it too.
   auto store_new = [&]() __attribute__((always_inline)) {
+    if constexpr (!APPEND) return;
     const int64_t row =
         (int64_t)(((uint64_t)s_new[D + 3] << 32) | (uint64_t)s_new[D + 2]);
     if (row < 0 || lane >= 2 * kLR) return;  // invalid block: key excluded
@@ -485,11 +522,13 @@ void decode_partial_kernel(DecodeArgs a) {
   // one matching element would index the arrays with a runtime value and
   // move them to scratch memory.
   auto patch_scales = [&](T& r, int t0) __attribute__((always_inline)) {
+    if constexpr (!APPEND) return;
     const int tn = pos_n - t0;
     if (T::KS) r.ks = (lane == tn) ? __uint_as_float(s_new[D]) : r.ks;
     if (kV8) r.vs = (lane == tn) ? __uint_as_float(s_new[D + 1]) : r.vs;
   };
   auto patch_half = [&](T& r, int t0, int kp) __attribute__((always_inline)) {
+    if constexpr (!APPEND) return;
     const int tn = pos_n - t0, kbn = tn >> 4, cn = tn & 15;
     if ((kbn >> 1) != kp) return;  // wave-uniform
     const uint8_t* img = reinterpret_cast<const uint8_t*>(s_new);
@@ -700,34 +739,51 @@ void decode_partial_kernel(DecodeArgs a) {
     }
   };
 
-  // Tiles are dealt round-robin to the waves.  Two register buffers
-  // alternate (no copy between them, so no wait is forced on the prefetch):
-  // the loads of the next tile are in flight while the current one is
-  // computed.
+  // Tiles are dealt round-robin to the waves: wave w takes tiles w, w + 4,
+  // ...  Every load is issued unconditionally (a tile that does not exist is
+  // issued empty, see load_tile), because loads under a branch make the
+  // compiler wait for all of them wherever a value loaded before the branch
+  // is used.  Both buffers' first loads go out before the barrier, so its
+  // wait overlaps them.
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
   T buf0, buf1;
-  // Unconditional (a wave without a tile reloads the split's first one, an
-  // L2 hit it never uses): loads under a branch make the compiler wait for
-  // all of them wherever a value loaded before the branch is used.
-  load_tile<MODE, D>(buf0, a, lo, t_begin + (wave < n_tiles ? wave * kTile : 0), t_end, tab,
-                     e_base, h, lane);
+  load_tile<MODE, D>(buf0, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
+                     wave < n_tiles);
+  if constexpr (MULTI)
+    load_tile<MODE, D>(buf1, a, lo, t_begin + (wave + kWaves) * kTile, t_end, tab, e_base, h,
+                       lane, wave + kWaves < n_tiles);
   if (APPEND && pos_n >= 0) append_new();
-  __syncthreads();  // s_q complete (after the first tile's loads are in flight)
+  __syncthreads();  // s_q complete (after the first tiles' loads are in flight)
   // Q8: the query row's scale of head c (0 for the padding heads c >= G,
   // whose B columns are zero)
   if constexpr (Q8) q_scale_c = (c < G) ? s_qs[c] : 0.0f;
   // block-scaled: this lane group supplies the scale of block g4 (head_dim
   // 64 has blocks 0 and 1; the zero k-slots of blocks 2 and 3 take 2^0)
   if constexpr (Q8 && T::MX) q_exp_c = (c < G && g4 < D / 32) ? (int)s_qx[c][g4] : 127;
-  for (int tile = wave; tile < n_tiles; tile += 2 * kWaves) {
-    const int t0 = t_begin + tile * kTile;
-    if (tile + kWaves < n_tiles)
-      load_tile<MODE, D>(buf1, a, lo, t0 + kWaves * kTile, t_end, tab, e_base, h, lane);
-    compute(buf0, t0);
-    if (tile + kWaves >= n_tiles) break;
-    if (tile + 2 * kWaves < n_tiles)
-      load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane);
-    compute(buf1, t0 + kWaves * kTile);
+  if constexpr (!MULTI) {
+    if (wave < n_tiles) compute(buf0, t_begin + wave * kTile);
+  } else if (wave < n_tiles) {
+    // Two buffers alternate (no copy between them): the loads of the next
+    // tile are in flight while the current one is computed.  The wave's
+    // tiles go in pairs (buf0, buf1); every pass but the last computes both
+    // and refills both, and the last pair is computed after the loop with
+    // nothing left to load.  Each compute step in the loop is thus entered
+    // with the same loads outstanding behind its own (the other buffer's,
+    // issued unconditionally), and waits for its own tile only.
+    const int m = (n_tiles - wave + kWaves - 1) / kWaves;  // tiles of this wave
+    const int last = (m - 1) / 2;                           // passes before the last pair
+    int tile = wave;
+    for (int i = 0; i < last; ++i, tile += 2 * kWaves) {
+      const int t0 = t_begin + tile * kTile;
+      compute(buf0, t0);
+      load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane,
+                         true);
+      compute(buf1, t0 + kWaves * kTile);
+      load_tile<MODE, D>(buf1, a, lo, t0 + 3 * kWaves * kTile, t_end, tab, e_base, h, lane,
+                         tile + 3 * kWaves < n_tiles);
+    }
+    compute(buf0, t_begin + tile * kTile);
+    if (tile + kWaves < n_tiles) compute(buf1, t_begin + (tile + kWaves) * kTile);
   }
   if (APPEND && pos_n >= 0) store_new();
 
@@ -842,12 +898,23 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
 template <int MODE, bool APPEND, bool Q8, bool KB>
 static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                              hipStream_t stream) {
-  if (c.d == 128)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB>), dim3(n_wg),
-                       dim3(64 * kWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB>), dim3(n_wg),
-                       dim3(64 * kWaves), 0, stream, a);
+  const bool multi = a.chunk > kWaves * kTile;
+  const dim3 grid(n_wg), block(64 * kWaves);
+  if (c.d == 128) {
+    if (multi)
+      hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB, true>), grid, block,
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB, false>), grid,
+                         block, 0, stream, a);
+  } else {
+    if (multi)
+      hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB, true>), grid, block,
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB, false>), grid, block,
+                         0, stream, a);
+  }
 }
 
 template <int MODE, bool APPEND, bool Q8>
@@ -895,9 +962,13 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
                                  bool q8, hipStream_t stream) {
+  const uint64_t rows = (uint64_t)c.num_blocks * c.bs * c.hkv;
+  const uint64_t k_bytes = rows * c.d * (k_is_e4m3(c.mode) ? 1 : 2);
+  const uint64_t v_bytes = rows * c.d * (v_is_e4m3(c.mode) ? 1 : 2);
   DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,       seq_lens,
                part_acc, part_ml,  k_new,   v_new,   c.kbias,  c.kexp,  c_scale,
-               c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks};
+               c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks,
+               k_bytes, v_bytes};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);

