@@ -647,7 +647,7 @@ def main():
         "narrow_qk_vs_bf16q_rel_l2": head["narrow_qk_vs_bf16q_rel_l2"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "decode_partial_kernel<K8V8,128,append>",
+                     "kernel": "decode_partial_kernel<K8V8,128,append,one tile per wave>",
                      "bytes_per_launch": head["kv_bytes"],
                      "kernel_source_hash": khash},
         "cpu_baseline": cpu,
