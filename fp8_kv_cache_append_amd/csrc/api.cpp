@@ -234,7 +234,7 @@ int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
                        const float* part_ml, float* out, void* stream) {
   if (batch < 0 || num_kv_heads <= 0 || gqa_group < 1 || n_splits < 0) return FP8KV_ERR_INVALID;
   if (gqa_group > kMaxGroup || (head_dim != 64 && head_dim != 128)) return FP8KV_ERR_UNSUPPORTED;
-  if ((int64_t)batch * num_kv_heads > INT32_MAX) return FP8KV_ERR_INVALID;
+  if ((int64_t)batch * num_kv_heads * gqa_group > INT32_MAX) return FP8KV_ERR_INVALID;
   if (batch == 0) return FP8KV_OK;
   if (!out || !aligned(out, 16)) return FP8KV_ERR_INVALID;
   if (n_splits > 0 && (!part_acc || !part_ml || !aligned(part_acc, 16) || !aligned(part_ml, 8)))

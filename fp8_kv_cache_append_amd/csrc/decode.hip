@@ -839,41 +839,61 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// Second kernel: merge the splits of each (sequence, query head).  The splits
-// are consumed in batches of kMergeBatch whose loads are all issued before
-// any is used, and the batches are combined online with power-of-two weights
-// (one memory round trip per batch, not per split).
-constexpr int kMergeBatch = 8;
-
-template <int D>
-__global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, int n_splits,
-                                                           const float* __restrict__ part_acc,
-                                                           const float* __restrict__ part_ml,
-                                                           float* __restrict__ out) {
-  constexpr int L = D / 4;  // lanes per head, four values each
-  const int pi = blockIdx.x;  // pair index, mapped as in the split kernel
+// Second kernel: merge the splits of each (sequence, query head).  One
+// single-wave work-group per query head, so a step's merge spreads over
+// B * Hkv * G work-groups (the partials of a (sequence, KV head) pair are
+// G * (D + 2) * 4 bytes per split; with one work-group per pair, 32 pairs
+// would leave the reads to 32 compute units).  The wave's lanes form
+// 64 / (D/4) split groups; lane (sg, d4) owns the head's values 4*d4 ..
+// 4*d4+3 of the splits sg, sg + NG, sg + 2 NG, ...  Each group consumes its
+// splits in batches of MB whose loads are all issued before any is used
+// (MB = 4, 8 or 16, the smallest that takes a group's splits in one batch),
+// combined online with power-of-two weights; the groups then meet through
+// lane swaps, again with power-of-two weights.
+template <int D, int MB>
+__global__ __launch_bounds__(64) void decode_merge_kernel(int hkv, int group, int n_splits,
+                                                          const float* __restrict__ part_acc,
+                                                          const float* __restrict__ part_ml,
+                                                          float* __restrict__ out) {
+  constexpr int L = D / 4;    // lanes per split group, four values each
+  constexpr int NG = 64 / L;  // split groups of the wave
+  // Work-group -> (pair, head).  As in the split kernel, when the pairs come
+  // in multiples of eight, pair pi = 8k + x runs on XCD x (work-group
+  // w = 8q + x), which holds its partials in L2.
+  const int w = blockIdx.x;
+  const int pairs = gridDim.x / group;
+  int pi, g;
+  if ((pairs & 7) == 0) {
+    const int q = w >> 3;
+    pi = (q / group) * 8 + (w & 7);
+    g = q % group;
+  } else {
+    pi = w / group;
+    g = w % group;
+  }
   const int bh = (pi / hkv) * hkv + rotated_head(pi, hkv);
-  const int g = threadIdx.x / L;
-  const int d4 = threadIdx.x % L;
-  if (g >= group) return;
+  const int lane = threadIdx.x;
+  const int sg = lane / L;
+  const int d4 = lane % L;
   const float* ml = part_ml + (int64_t)bh * n_splits * group * 2;
   const float* pa = part_acc + (int64_t)bh * n_splits * group * D;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch];
-    f32x4_t x[kMergeBatch];
+  for (int s0 = sg; s0 < n_splits; s0 += NG * MB) {
+    float m[MB], l[MB];
+    f32x4_t x[MB];
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
-      const int s = min(s0 + i, n_splits - 1);
+    for (int i = 0; i < MB; ++i) {
+      const int si = s0 + NG * i;
+      const int s = si < n_splits ? si : s0;  // s0 < n_splits: in range
       const f32x2_t v = *reinterpret_cast<const f32x2_t*>(ml + ((int64_t)s * group + g) * 2);
-      m[i] = (s0 + i < n_splits) ? v[0] : -INFINITY;
+      m[i] = si < n_splits ? v[0] : -INFINITY;
       l[i] = v[1];
       x[i] = *reinterpret_cast<const f32x4_t*>(pa + ((int64_t)s * group + g) * D + 4 * d4);
     }
     float mb = m_run;
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) mb = fmaxf(mb, m[i]);
+    for (int i = 0; i < MB; ++i) mb = fmaxf(mb, m[i]);
     if (mb == -INFINITY) continue;  // nothing yet
     if (m_run != -INFINITY && mb != m_run) {
       const float alpha = ldexpf(1.0f, (int)(m_run - mb));
@@ -882,13 +902,31 @@ __global__ __launch_bounds__(512) void decode_merge_kernel(int hkv, int group, i
     }
     m_run = mb;
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
+    for (int i = 0; i < MB; ++i) {
       if (m[i] == -INFINITY) continue;  // empty split: weight 0
-      const float w = ldexpf(1.0f, (int)(m[i] - m_run));
-      l_run += w * l[i];
-      acc += w * x[i];
+      const float wt = ldexpf(1.0f, (int)(m[i] - m_run));
+      l_run += wt * l[i];
+      acc += wt * x[i];
     }
   }
+  // combine the split groups: lanes L, 2L, ... apart hold the same values
+#pragma unroll
+  for (int off = L; off < 64; off *= 2) {
+    const float m2 = __shfl_xor(m_run, off);
+    const float l2 = __shfl_xor(l_run, off);
+    f32x4_t a2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = __shfl_xor(acc[e], off);
+    const float mm = fmaxf(m_run, m2);
+    if (mm != -INFINITY) {  // otherwise both are empty and stay so
+      const float w1 = m_run == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m_run - mm));
+      const float w2 = m2 == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m2 - mm));
+      l_run = w1 * l_run + w2 * l2;
+      acc = w1 * acc + w2 * a2;
+      m_run = mm;
+    }
+  }
+  if (sg != 0) return;
   f32x4_t o = {0.f, 0.f, 0.f, 0.f};
   if (l_run > 0.0f) o = acc / l_run;
   // bh = b * hkv + h, output head h * group + g
@@ -977,17 +1015,31 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
   return hipGetLastError();
 }
 
+template <int D>
+static void launch_merge_d(unsigned n_wg, int hkv, int group, int n_splits,
+                           const float* part_acc, const float* part_ml, float* out,
+                           hipStream_t stream) {
+  constexpr int NG = 64 / (D / 4);  // split groups per wave
+  const int per_group = (n_splits + NG - 1) / NG;
+  if (per_group <= 4)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(n_wg), dim3(64), 0, stream, hkv,
+                       group, n_splits, part_acc, part_ml, out);
+  else if (per_group <= 8)
+    hipLaunchKernelGGL((decode_merge_kernel<D, 8>), dim3(n_wg), dim3(64), 0, stream, hkv,
+                       group, n_splits, part_acc, part_ml, out);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, 16>), dim3(n_wg), dim3(64), 0, stream, hkv,
+                       group, n_splits, part_acc, part_ml, out);
+}
+
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,
                                const float* part_acc, const float* part_ml, float* out,
                                hipStream_t stream) {
-  const unsigned n_wg = (unsigned)((int64_t)batch * hkv);
-  const unsigned threads = (unsigned)(group * (d / 4));
+  const unsigned n_wg = (unsigned)((int64_t)batch * hkv * group);
   if (d == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(n_wg), dim3(threads), 0, stream, hkv,
-                       group, n_splits, part_acc, part_ml, out);
+    launch_merge_d<128>(n_wg, hkv, group, n_splits, part_acc, part_ml, out, stream);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(n_wg), dim3(threads), 0, stream, hkv,
-                       group, n_splits, part_acc, part_ml, out);
+    launch_merge_d<64>(n_wg, hkv, group, n_splits, part_acc, part_ml, out, stream);
   return hipGetLastError();
 }
 
