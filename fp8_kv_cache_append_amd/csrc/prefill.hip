@@ -10,14 +10,22 @@
 // "kadirnar/kernel-agent/fp8-kv-cache" ("Math"): k_scale multiplies the
 // QK product, v_scale is folded into P before its bf16 rounding.
 //
-// gfx950 mapping.  Four waves; wave w owns query rows 32w .. 32w+31 of the
-// tile as two 16-row MFMA column blocks, so every operand read from LDS
-// feeds two matrix instructions (LDS bandwidth, not the matrix cores, is
-// what limits a one-block-per-wave layout).  Each 64-key tile is loaded once
-// per work-group, converted e4m3 -> bf16 with the packed gfx950 convert and
-// written to LDS: K row-major (rows padded by 16 bytes), V transposed (V^T,
-// keys permuted so each lane's eight PV keys are contiguous), so both MFMA
-// A operands are single 16-byte conflict-free LDS reads.  QK and PV use
+// gfx950 mapping.  Eight waves in two key groups of four.  Group p computes
+// the key tiles p, p + 2, p + 4, ... of the work-group's query tile, and
+// within a group wave r owns query rows 32r .. 32r+31 as two 16-row MFMA
+// column blocks, so every operand read from LDS feeds two matrix
+// instructions.  The two groups run the same online softmax on alternate
+// tiles and meet once at the end, where group 1's state (integer reference,
+// row sum, accumulator) is merged into group 0's with exact power-of-two
+// weights.  So the longest work-group of a causal launch (the last query
+// tile, which sees every key) walks half as many tiles in sequence, and each
+// SIMD holds two waves whose softmax and matrix work interleave.
+//
+// Each group stages its own tiles: a 64-key tile is loaded once per group,
+// converted e4m3 -> bf16 with the packed gfx950 convert and written to LDS:
+// K row-major (rows padded by 16 bytes), V transposed (V^T, keys permuted so
+// each lane's eight PV keys are contiguous), so both MFMA A operands are
+// single 16-byte conflict-free LDS reads.  QK and PV use
 // v_mfma_f32_16x16x32_bf16 in the transposed form of the decode kernel:
 // S^T = K Q^T (lane (g4, c) holds query row c, keys 4*g4 + i of each 16-key
 // block) and O^T = V^T P^T, so P goes from the QK result straight into the
@@ -27,12 +35,20 @@
 // exact power of two and rare.  Tiles whose keys every row of a wave sees
 // skip the masks.
 //
+// Memory pipeline, per group: the block ids of tile n + 3 are fetched while
+// tile n + 2's codes are loaded, tile n + 1 is staged to LDS and tile n is
+// computed.  Every load is issued unconditionally from an address inside the
+// cache (a key that does not exist reads row 0 and is neutralised when
+// staged), so the only wait per tile is for loads issued a whole tile
+// earlier.  Each lane follows one 16-key sub-block through the sequence with
+// a (block index, offset) cursor: no division per tile.
+//
 // LDS reuse: iteration j computes on buffer j & 1 and meanwhile stages tile
 // j + 1 into buffer (j + 1) & 1, which was last read by the compute of
 // iteration j - 1; the barrier that ends iteration j - 1 separates that read
 // from this write, and the barrier that ends iteration j separates this write
 // from the reads of iteration j + 1.  One barrier per tile is therefore
-// enough.
+// enough.  The final merge reuses the tile buffers after the last barrier.
 #include "device.h"
 #include "launch.h"
 
@@ -59,9 +75,11 @@ struct PrefillArgs {
   int num_blocks;
 };
 
-constexpr int kPWaves = 4;
+constexpr int kPGroups = 2;                   // key groups (alternate tiles)
+constexpr int kPRowWaves = 4;                 // waves per key group
+constexpr int kPWaves = kPGroups * kPRowWaves;
 constexpr int kCB = 2;    // MFMA column blocks (16 query rows each) per wave
-constexpr int kQT = 16 * kCB * kPWaves;  // queries per tile (128)
+constexpr int kQT = 16 * kCB * kPRowWaves;  // queries per tile (128)
 constexpr int kKT = 64;   // keys per tile
 constexpr float kPLazy = 8.0f;  // log2 units the scores may exceed the reference by
 
@@ -76,6 +94,20 @@ struct PrefillShape {
   static constexpr int DG = D / 16;                          // d values per V staging thread
   static constexpr int VE = V8 ? 1 : 2;                      // bytes per V element
   static constexpr int VWORDS = DG * VE / 4;                 // dwords of V per key per thread
+  static constexpr int NDB = D / 16;                         // PV column blocks of 16 d
+  static constexpr int MF = 2 * kCB + 4 * kCB * NDB;         // merged floats per lane
+};
+
+// One staged 64-key tile.
+template <int MODE, int D>
+struct __attribute__((aligned(16))) PrefillTile {
+  using S = PrefillShape<MODE, D>;
+  __bf16 k[kKT][S::LDK];
+  __bf16 vt[D][S::LDV];
+  float ks[kKT];   // k_scale * sm_scale * log2 e
+  float vs[kKT];
+  float ok[kKT];   // 1: key exists (inside the sequence, valid block), 0: masked
+  uint32_t allok[kPRowWaves];  // per staging wave: all 16 keys exist
 };
 
 // Position of key k of a 64-key tile in an LDS V^T row.  Key
@@ -101,20 +133,18 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t r[4], uint32_t
 }
 
 template <int MODE, int D>
-__global__ __launch_bounds__(64 * kPWaves, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a) {
   using S = PrefillShape<MODE, D>;
+  using Tile = PrefillTile<MODE, D>;
   constexpr int KC = D / 32;
-  constexpr int NDB = D / 16;  // PV MFMAs per 32-key chunk: d in [16 db, 16 db + 16)
+  constexpr int NDB = S::NDB;  // PV MFMAs per 32-key chunk: d in [16 db, 16 db + 16)
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_k[2][kKT][S::LDK];
-  __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][D][S::LDV];
-  __shared__ __attribute__((aligned(16))) float s_ks[2][kKT];  // k_scale * sm_scale * log2 e
-  __shared__ __attribute__((aligned(16))) float s_vs[2][kKT];
-  __shared__ __attribute__((aligned(16))) float s_ok[2][kKT];  // 1: block id valid, 0: key not read
-  __shared__ uint32_t s_allok[2][kPWaves];                    // per staging wave: all 16 keys valid
+  __shared__ Tile s_t[kPGroups][2];
 
   const int tid = threadIdx.x;
   const int wave = wave_uniform(tid >> 6);
+  const int grp = wave / kPRowWaves;   // key group: tiles grp, grp + 2, ...
+  const int rw = wave % kPRowWaves;    // row group inside the query tile
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int c = lane & 15;
@@ -143,11 +173,11 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_kernel(PrefillArgs a)
   int qrow[kCB], qpos[kCB];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    qrow[cb] = qt * kQT + 16 * (kCB * wave + cb) + c;
+    qrow[cb] = qt * kQT + 16 * (kCB * rw + cb) + c;
     qpos[cb] = (qrow[cb] < n_q) ? pos0 + qrow[cb] : -1;
   }
   // every key t <= first_pos is visible to every row of this wave
-  const int first_pos = pos0 + qt * kQT + 16 * kCB * wave;
+  const int first_pos = pos0 + qt * kQT + 16 * kCB * rw;
 
   // Q^T as the B operand of QK, per column block
   u32x4_t qb[kCB][KC];
@@ -172,63 +202,98 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_kernel(PrefillArgs a)
     for (int j = 0; j < NDB; ++j) acc[cb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int n_kt = (kv_end + kKT - 1) / kKT;
+  const int n_kt = (kv_end + kKT - 1) / kKT;   // key tiles of the query tile
+  const int n_it = (n_kt + kPGroups - 1) / kPGroups;  // tiles of key group 0
   const int64_t tab_row = (int64_t)b * a.mbps;
 
-  // Staging of one tile by the work-group's 256 threads:
-  //   K  thread -> (key tid / 4, quarter tid % 4 of the row), row-major bf16;
-  //   V  thread -> (keys 4*kq .. 4*kq+3 with kq = tid % 16, d in
-  //      [DG*dq, DG*dq + DG) with dq = tid / 16), written transposed (V^T):
+  // Staging of one tile by the group's 256 threads (gt = thread in group):
+  //   K  thread -> (key gt / 4, quarter gt % 4 of the row), row-major bf16;
+  //      its key lies in 16-key sub-block rw of the tile;
+  //   V  thread -> (keys 4*kq .. 4*kq+3 with kq = gt % 16, d in
+  //      [DG*dq, DG*dq + DG) with dq = gt / 16), written transposed (V^T):
   //      the 16 lanes of one d group fill a whole V^T row, so a write
   //      instruction of 64 lanes touches 4 rows (the 2-way minimum).
+  //      Its keys lie in sub-block sbv = kq / 4.
   // A 16-key sub-block lies inside one block (block_size is a multiple of
-  // 16), so a key quad has one block id.
-  const int skey = tid >> 2, spart = tid & 3;
-  const int kq = tid & 15, dq = tid >> 4;
+  // 16), so it has one block id; lane 4*rw follows sub-block rw, which the
+  // wave's K threads read from it.
+  const int gt = tid % (64 * kPRowWaves);
+  const int spart = gt & 3;
+  const int kq = gt & 15, dq = gt >> 4;
+  const int sbv = kq >> 2;
+  const int kin = lane >> 2;  // K thread's key inside sub-block rw
+
+  // Cursor over this lane's sub-block sbv of the group's tiles: first key,
+  // block index in the table row and 16-key offset inside the block.  A
+  // group advances by kPGroups tiles = 8 sub-blocks per tile.
+  const int nsb = a.bs >> 4;
+  const int adv = kPGroups * kKT / 16;
+  const int adv_q = adv / nsb, adv_r = adv % nsb;
+  int cur_t = grp * kKT + 16 * sbv;
+  int cur_b = cur_t / a.bs;
+  int cur_r = (cur_t % a.bs) >> 4;
+
+  // block id fetched for the next tile to load
+  int p_id = 0, p_r = 0, p_t = 0;
+  auto fetch_id = [&]() {
+    p_id = a.table[tab_row + (cur_t < kv_end ? cur_b : 0)];
+    p_r = cur_r;
+    p_t = cur_t;
+    cur_t += kPGroups * kKT;
+    cur_b += adv_q;
+    cur_r += adv_r;
+    if (cur_r >= nsb) {
+      cur_r -= nsb;
+      ++cur_b;
+    }
+  };
+
   u32x4_t kreg[S::KW];
   uint32_t vreg[4][S::VWORDS];
-  float ksreg = 0.0f, vsreg = 0.0f;
-  bool okreg = false;
-  auto load_tile = [&](int t0) {
-    {  // K row and its scale
-      const int t = min(t0 + skey, kv_end - 1);
-      const int blk = a.table[tab_row + t / a.bs];
-      const bool ok = (unsigned)blk < (unsigned)a.num_blocks;  // else: key not read
-      const int64_t row = ((int64_t)(ok ? blk : 0) * a.bs + t % a.bs) * a.hkv + hk;
+  float ksreg = 1.0f, vsreg = 1.0f;
+  bool okk = false;
+  uint32_t okv = 0;  // bit r: key 4*kq + r of the tile exists
+  auto load_tile = [&]() {
+    const bool sb_ok = (p_t < kv_end) && ((unsigned)p_id < (unsigned)a.num_blocks);
+    const int64_t slot_v = sb_ok ? (int64_t)p_id * a.bs + 16 * p_r : 0;
+    {  // K row (sub-block rw, from lane 4*rw) and its scales
+      const int id_k = __builtin_amdgcn_readlane(p_id, 4 * rw);
+      const int r_k = __builtin_amdgcn_readlane(p_r, 4 * rw);
+      const int t_k = __builtin_amdgcn_readlane(p_t, 4 * rw) + kin;
+      okk = (t_k < kv_end) && ((unsigned)id_k < (unsigned)a.num_blocks);
+      const int64_t slot = okk ? (int64_t)id_k * a.bs + 16 * r_k + kin : 0;
+      const int64_t row = slot * a.hkv + hk;
       const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * S::KBYTES + spart * (S::KBYTES / 4);
 #pragma unroll
-      for (int i = 0; i < S::KW; ++i)
-        kreg[i] = ok ? reinterpret_cast<const u32x4_t*>(kp)[i] : u32x4_t{0u, 0u, 0u, 0u};
-      okreg = ok;
-      ksreg = (S::K8 && ok) ? a.ks[row] : 1.0f;
-      vsreg = (S::V8 && ok) ? a.vs[row] : 1.0f;
+      for (int i = 0; i < S::KW; ++i) kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
+      if (S::K8) ksreg = a.ks[row];
+      if (S::V8) vsreg = a.vs[row];
     }
-    {  // V: four rows of a quad, DG values each
-      const int t = min(t0 + 4 * kq, kv_end - 1) & ~3;
-      const int blk = a.table[tab_row + t / a.bs];
-      const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
-      const int64_t row0 = ((int64_t)(ok ? blk : 0) * a.bs + t % a.bs) * a.hkv + hk;
+    okv = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint8_t* vp = static_cast<const uint8_t*>(a.v) + (row0 + (int64_t)r * a.hkv) * (D * S::VE) +
-                            dq * (S::DG * S::VE);
-        if constexpr (S::VWORDS == 4) {
-          const u32x4_t x = ok ? *reinterpret_cast<const u32x4_t*>(vp) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int r = 0; r < 4; ++r) {  // V: four rows of a quad, DG values each
+      const int kk = 4 * (kq & 3) + r;
+      const bool ok = sb_ok && (p_t + kk < kv_end);
+      okv |= ok ? (1u << r) : 0u;
+      const int64_t row = (ok ? slot_v + kk : 0) * a.hkv + hk;
+      const uint8_t* vp = static_cast<const uint8_t*>(a.v) + row * (D * S::VE) + dq * (S::DG * S::VE);
+      if constexpr (S::VWORDS == 4) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vreg[r][e] = x[e];
-        } else if constexpr (S::VWORDS == 2) {
-          const u32x2_t x = ok ? *reinterpret_cast<const u32x2_t*>(vp) : u32x2_t{0u, 0u};
-          vreg[r][0] = x[0];
-          vreg[r][1] = x[1];
-        } else {
-          vreg[r][0] = ok ? *reinterpret_cast<const uint32_t*>(vp) : 0u;
-        }
+        for (int e = 0; e < 4; ++e) vreg[r][e] = x[e];
+      } else if constexpr (S::VWORDS == 2) {
+        const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vp);
+        vreg[r][0] = x[0];
+        vreg[r][1] = x[1];
+      } else {
+        vreg[r][0] = *reinterpret_cast<const uint32_t*>(vp);
       }
     }
   };
-  auto store_tile = [&](int buf, int t0) {
-    // K: bf16 elements [spart * D/4, (spart+1) * D/4) of row skey
-    __bf16* kd = &s_k[buf][skey][spart * (D / 4)];
+  auto store_tile = [&](Tile& T) {
+    // K: bf16 elements [spart * D/4, (spart+1) * D/4) of row gt / 4.  A key
+    // that does not exist keeps whatever row 0 holds: its score is masked.
+    __bf16* kd = &T.k[gt >> 2][spart * (D / 4)];
     if (S::K8) {
 #pragma unroll
       for (int i = 0; i < S::KW; ++i) {
@@ -245,159 +310,199 @@ __global__ __launch_bounds__(64 * kPWaves, 2) void prefill_kernel(PrefillArgs a)
       for (int i = 0; i < S::KW; ++i) reinterpret_cast<u32x4_t*>(kd)[i] = kreg[i];
     }
     if (spart == 0) {
-      s_ks[buf][skey] = ksreg * a.c_scale;
-      s_vs[buf][skey] = vsreg;
-      s_ok[buf][skey] = okreg ? 1.0f : 0.0f;
+      T.ks[gt >> 2] = okk ? ksreg * a.c_scale : 0.0f;
+      T.vs[gt >> 2] = okk ? vsreg : 0.0f;
+      T.ok[gt >> 2] = okk ? 1.0f : 0.0f;
     }
-    {  // the 16 keys of this wave all valid (and inside kv_end)?
-      const bool good = okreg && (t0 + skey < kv_end);
-      const uint64_t m = __builtin_amdgcn_ballot_w64(good);
-      if (lane == 0) s_allok[buf][wave] = (m == ~0ull) ? 1u : 0u;
+    {  // the 16 keys of this wave all exist?
+      const uint64_t m = __builtin_amdgcn_ballot_w64(okk);
+      if (lane == 0) T.allok[rw] = (m == ~0ull) ? 1u : 0u;
     }
     // V^T: for each of this thread's DG d values, its 4 keys' values as
-    // 4 bf16 at the quad's position in the row
+    // 4 bf16 at the quad's position in the row; a key that does not exist
+    // contributes zeros (its P is 0, and row 0 may hold any bytes)
     const int pos = vt_pos_of_quad(kq);
 #pragma unroll
     for (int w = 0; w < S::VWORDS; ++w) {
+      uint32_t rr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rr[r] = ((okv >> r) & 1u) ? vreg[r][w] : 0u;
       if constexpr (S::V8) {
-        uint32_t rr[4] = {vreg[0][w], vreg[1][w], vreg[2][w], vreg[3][w]};
         uint32_t cols[4];
         transpose4x4_bytes(rr, cols);  // cols[j]: code of d = DG*dq + 4w + j, keys 0..3
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const u32x2_t bf = {e4m3x2_to_bf16x2<false>(cols[j]), e4m3x2_to_bf16x2<true>(cols[j])};
-          *reinterpret_cast<u32x2_t*>(&s_vt[buf][S::DG * dq + 4 * w + j][pos]) = bf;
+          *reinterpret_cast<u32x2_t*>(&T.vt[S::DG * dq + 4 * w + j][pos]) = bf;
         }
       } else {
         // dword w holds d = DG*dq + 2w (low half) and + 2w + 1 (high half)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const uint32_t sel = hf ? 0x07060302u : 0x05040100u;
-          const u32x2_t bf = {byte_perm(vreg[1][w], vreg[0][w], sel),
-                              byte_perm(vreg[3][w], vreg[2][w], sel)};
-          *reinterpret_cast<u32x2_t*>(&s_vt[buf][S::DG * dq + 2 * w + hf][pos]) = bf;
+          const u32x2_t bf = {byte_perm(rr[1], rr[0], sel), byte_perm(rr[3], rr[2], sel)};
+          *reinterpret_cast<u32x2_t*>(&T.vt[S::DG * dq + 2 * w + hf][pos]) = bf;
         }
       }
     }
   };
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0, 0);
-    load_tile(kKT);
+  // Prologue: tile 0 staged, tile 1's codes and tile 2's block ids in flight.
+  if (n_it > 0) {
+    fetch_id();
+    load_tile();
+    fetch_id();
+    store_tile(s_t[grp][0]);
+    load_tile();
+    fetch_id();
   }
   __syncthreads();
-  for (int j = 0; j < n_kt; ++j) {
+  for (int j = 0; j < n_it; ++j) {
     const int buf = j & 1;
-    const int t0 = j * kKT;
-    // Stage tile j + 1 into the other buffer (its loads were issued an
-    // iteration ago) and issue tile j + 2's loads while tile j is computed.
-    // Both are unconditional -- past the last tile they are clamped reloads
-    // into a buffer nobody reads -- so they stay in the compute's basic block
-    // and the scheduler can interleave them with the matrix instructions.
-    store_tile(buf ^ 1, t0 + kKT);
-    load_tile(t0 + 2 * kKT);
+    const int t0 = (kPGroups * j + grp) * kKT;
+    // Stage the group's next tile (its loads were issued an iteration ago),
+    // issue the codes of the one after and the block ids of the third.  All
+    // are unconditional -- past the last tile they are reloads of row 0 into
+    // a buffer nobody reads -- so the only wait is for loads a tile old.
+    store_tile(s_t[grp][buf ^ 1]);
+    load_tile();
+    fetch_id();
 
-    // every key of the tile visible to every row of this wave, all inside
-    // the sequence and in valid blocks: no mask needed (wave-uniform)
-    const bool fast = (t0 + kKT - 1 <= first_pos) && (t0 + kKT <= kv_end) &&
-                      (s_allok[buf][0] & s_allok[buf][1] & s_allok[buf][2] & s_allok[buf][3]);
+    if (t0 < kv_end) {
+      const Tile& T = s_t[grp][buf];
+      // every key of the tile visible to every row of this wave, all inside
+      // the sequence and in valid blocks: no mask needed (wave-uniform)
+      const bool fast = (t0 + kKT - 1 <= first_pos) && (t0 + kKT <= kv_end) &&
+                        (T.allok[0] & T.allok[1] & T.allok[2] & T.allok[3]);
 
-    // --- S^T = K Q^T for 4 blocks of 16 keys and the wave's column blocks:
-    //     each K operand read from LDS feeds kCB matrix instructions
-    f32x4_t sacc[kCB][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int cb = 0; cb < kCB; ++cb) sacc[cb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const __bf16* krow = &s_k[buf][16 * kb + c][0];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow + d0);
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          sacc[cb][kb] = mfma_16x16x32_bf16(ka, qb[cb][kc], sacc[cb][kb]);
-      }
-    }
-
-    f32x4_t ksv[4], vsv[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      ksv[kb] = f32x4_t{a.c_scale, a.c_scale, a.c_scale, a.c_scale};
-      if (S::K8) ksv[kb] = *reinterpret_cast<const f32x4_t*>(&s_ks[buf][16 * kb + 4 * g4]);
-      vsv[kb] = f32x4_t{1.f, 1.f, 1.f, 1.f};
-      if (S::V8) vsv[kb] = *reinterpret_cast<const f32x4_t*>(&s_vs[buf][16 * kb + 4 * g4]);
-    }
-
-    u32x4_t pb[kCB][2];
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      // --- scores in log2 units: (q . K) * k_scale * sm_scale * log2 e;
-      //     causal, length and block masks only where some key is hidden
-      float sc[4][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[kb][i] = sacc[cb][kb][i] * ksv[kb][i];
-        if (!fast) {
-          const f32x4_t okv = *reinterpret_cast<const f32x4_t*>(&s_ok[buf][16 * kb + 4 * g4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 16 * kb + 4 * g4 + i;
-            sc[kb][i] = (t <= qpos[cb] && t < kv_end && okv[i] != 0.0f) ? sc[kb][i] : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[kb][i]);
-      }
-      tmax = max_over_groups(tmax);
-
-      // --- online softmax with a lazily moved integer reference; a fully
-      //     masked tile (tmax = -inf) keeps the state
-      const float t_ref = ceilf(tmax);
-      if (m_run[cb] == -INFINITY) {
-        m_run[cb] = t_ref;  // l and acc are still zero: nothing to rescale
-      } else if (t_ref > m_run[cb] + kPLazy) {
-        const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref));
-        l_run[cb] *= alpha;
-#pragma unroll
-        for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
-        m_run[cb] = t_ref;
-      }
-      const float m_ref = (m_run[cb] == -INFINITY) ? 0.0f : m_run[cb];
-
+      // The tile is computed in two 32-key halves kp, each QK -> softmax ->
+      // PV, so only one half's scores and scales are live at a time; the
+      // matrix work of one half can overlap the softmax of the other.
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        float pv[8];
+        // --- S^T = K Q^T for the half's two blocks of 16 keys and the
+        //     wave's column blocks: each K operand read from LDS feeds kCB
+        //     matrix instructions
+        f32x4_t sacc[kCB][2];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int kb = 2 * kp + (jj >> 2), i = jj & 3;
-          const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_ref);
-          l_run[cb] += p;
-          pv[jj] = p * vsv[kb][i];
+        for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) sacc[cb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const __bf16* krow = &T.k[16 * (2 * kp + hb) + c][0];
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
+            const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow + d0);
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb)
+              sacc[cb][hb] = mfma_16x16x32_bf16(ka, qb[cb][kc], sacc[cb][hb]);
+          }
         }
-        pb[cb][kp] = u32x4_t{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
-                             f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
-      }
-    }
 
-    // --- O^T += V^T P^T: MFMA db covers d in [16 db, 16 db + 16); lane
-    //     (g4, r) reads row d = 16 db + r of V^T at its eight keys, once for
-    //     all column blocks
+        f32x4_t ksv[2], vsv[2];
 #pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
+        for (int hb = 0; hb < 2; ++hb) {
+          ksv[hb] = *reinterpret_cast<const f32x4_t*>(&T.ks[16 * (2 * kp + hb) + 4 * g4]);
+          vsv[hb] = *reinterpret_cast<const f32x4_t*>(&T.vs[16 * (2 * kp + hb) + 4 * g4]);
+        }
+
+        u32x4_t pb[kCB];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const u32x4_t av =
-            *reinterpret_cast<const u32x4_t*>(&s_vt[buf][16 * db + c][32 * kp + 8 * g4]);
+        for (int cb = 0; cb < kCB; ++cb) {
+          // --- scores in log2 units: (q . K) * k_scale * sm_scale * log2 e;
+          //     causal, length and block masks only where some key is hidden
+          float sc[2][4];
+          float tmax = -INFINITY;
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-          acc[cb][db] = mfma_16x16x32_bf16(av, pb[cb][kp], acc[cb][db]);
+          for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[hb][i] = sacc[cb][hb][i] * ksv[hb][i];
+            if (!fast) {
+              const int kb = 2 * kp + hb;
+              const f32x4_t okf = *reinterpret_cast<const f32x4_t*>(&T.ok[16 * kb + 4 * g4]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * kb + 4 * g4 + i;
+                sc[hb][i] = (t <= qpos[cb] && okf[i] != 0.0f) ? sc[hb][i] : -INFINITY;
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[hb][i]);
+          }
+          tmax = max_over_groups(tmax);
+
+          // --- online softmax with a lazily moved integer reference; fully
+          //     masked keys (tmax = -inf) keep the state
+          const float t_ref = ceilf(tmax);
+          if (m_run[cb] == -INFINITY) {
+            m_run[cb] = t_ref;  // l and acc are still zero: nothing to rescale
+          } else if (t_ref > m_run[cb] + kPLazy) {
+            const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref));
+            l_run[cb] *= alpha;
+#pragma unroll
+            for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
+            m_run[cb] = t_ref;
+          }
+          const float m_ref = (m_run[cb] == -INFINITY) ? 0.0f : m_run[cb];
+
+          float pv[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int hb = jj >> 2, i = jj & 3;
+            const float p = __builtin_amdgcn_exp2f(sc[hb][i] - m_ref);
+            l_run[cb] += p;
+            pv[jj] = p * vsv[hb][i];
+          }
+          pb[cb] = u32x4_t{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
+                           f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
+        }
+
+        // --- O^T += V^T P^T: MFMA db covers d in [16 db, 16 db + 16); lane
+        //     (g4, r) reads row d = 16 db + r of V^T at its eight keys of the
+        //     half, once for all column blocks
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&T.vt[16 * db + c][32 * kp + 8 * g4]);
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) acc[cb][db] = mfma_16x16x32_bf16(av, pb[cb], acc[cb][db]);
+        }
       }
     }
     __syncthreads();
+  }
+
+  // --- merge key group 1 into group 0 through LDS (the tile buffers are free
+  //     after the loop's last barrier): exact power-of-two weights 2^(M - M*),
+  //     a group that saw no key (M = -inf) weighs 0
+  float* s_m = reinterpret_cast<float*>(&s_t[0][0]);  // [rw][MF][64 lanes]
+  static_assert(sizeof(float) * kPRowWaves * S::MF * 64 <= sizeof(s_t), "merge area");
+  float* mine = s_m + rw * S::MF * 64 + lane;
+  if (grp == 1) {
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      mine[(2 * cb) * 64] = m_run[cb];
+      mine[(2 * cb + 1) * 64] = l_run[cb];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mine[(2 * kCB + 4 * (NDB * cb + db) + i) * 64] = acc[cb][db][i];
+    }
+  }
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const float m1 = mine[(2 * cb) * 64];
+    const float l1 = mine[(2 * cb + 1) * 64];
+    const float ms = fmaxf(m_run[cb], m1);
+    const float w0 = (m_run[cb] == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run[cb] - ms));
+    const float w1 = (m1 == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m1 - ms));
+    l_run[cb] = l_run[cb] * w0 + l1 * w1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[cb][db][i] = acc[cb][db][i] * w0 + mine[(2 * kCB + 4 * (NDB * cb + db) + i) * 64] * w1;
   }
 
   // --- normalise and write: lane (g4, c) holds d = 16 db + 4 g4 + i of row c

@@ -8,9 +8,14 @@ are only defined to fp32 accuracy) and they can differ by 2^-8 |V| in the
 output of a short or peaked row.  The oracle therefore also returns the
 interval [lo, hi] of outputs reachable by rounding such P either way; the
 max-abs gate is applied to the distance from that interval, and every
-element must lie within it up to fp32 accumulation error.  The relative L2
-is taken against the nominal oracle output: the contract's 1e-3, and 1e-4 as
-a bug detector (the observed error is ~1e-6 to 1e-5).
+element must lie within it up to fp32 accumulation error.  The contract's
+relative L2 (1e-3) is taken against the nominal oracle output.  The bug
+detector (1e-4; the observed error is ~1e-6 to 1e-5) is the relative L2 of
+the distance outside the interval: a one-pass kernel's integer softmax
+reference may lie below the two-pass maximum the oracle uses, which changes
+the fp32 rounding of the exp2 argument s - M and can move P across a bf16
+midpoint; in a row with few keys one such valid flip alone exceeds 1e-4 of
+the nominal output.
 """
 import math
 
@@ -36,10 +41,13 @@ def _gate(got, ref, lo, hi, ctx, expect_rel=EXPECT_REL, gate_rel=GATE_REL):
     dist = np.abs(got - np.clip(got, lo, hi))
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     print(f"{ctx}: rel_l2={rel:.3e} max_abs={raw:.3e} "
-          f"max_abs_outside_rounding_interval={dist.max() if dist.size else 0:.3e}", flush=True)
+          f"max_abs_outside_rounding_interval={dist.max() if dist.size else 0:.3e} "
+          f"rel_l2_outside_rounding_interval={float(np.linalg.norm(dist)) / max(float(np.linalg.norm(ref)), 1e-30):.3e}",
+          flush=True)
+    rel_out = float(np.linalg.norm(dist) / np.linalg.norm(ref)) if rms > 0 else 0.0
     assert rel <= gate_rel, (ctx, rel)
     assert dist.size == 0 or dist.max() <= GATE_ABS, (ctx, dist.max())
-    assert rel <= expect_rel, (ctx, rel)
+    assert rel_out <= expect_rel, (ctx, rel_out)
     assert np.all(dist <= 1e-4 * (np.abs(ref) + rms)), (ctx, float(dist.max()))
     return rel
 
@@ -220,3 +228,25 @@ def test_decode_repeat_bitwise_identical():
     for _ in range(200):
         again = decode(cache, q_bits, w.lens, w.group, w.sm_scale)
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
+def test_decode_unwritten_slots_hold_nan(mode):
+    """Every byte of the cache is 0xFF (NaN in e4m3, bf16 and fp32) before the
+    keys are appended, so slots past each sequence's last key hold NaN: keys
+    that do not exist must not reach any output."""
+    lens = np.array([1, 37, 300, 1000], np.int32)
+    w = synth.Workload("t", len(lens), 16, 2, 128, lens, "outliers", block_size=48,
+                       shuffle_blocks=True, seed=23)
+    cache = make_cache(mode, w, capacity=1056)
+    for x in (cache.k, cache.v, cache.k_scale, cache.v_scale):
+        if x is not None:
+            x.view(torch.uint8).fill_(0xFF)
+    seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
+    _fill(cache, w, seqs)
+    q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
+    got = decode(cache, q_bits, w.lens, w.group, w.sm_scale)
+    assert np.all(np.isfinite(got))
+    ref, lo, hi = oracle.decode(mode, q_bits, [s[0] for s in seqs], [s[1] for s in seqs],
+                                w.sm_scale, bounds=True)
+    _gate(got, ref, lo, hi, (mode, "nan-filled"))

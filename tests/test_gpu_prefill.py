@@ -64,6 +64,9 @@ CASES = [
     (16, 2, 128, [1, 64, 65, 130], [0, 10, 0, 3], [1, 74, 65, 133], 16),
     (2, 2, 64, [129], [0], [129], 64),                      # MHA
     (16, 1, 64, [90], [5], [95], 0),                        # GQA 16
+    (8, 2, 128, [150], [0], [150], 48),                     # 3 sub-blocks per block
+    (4, 1, 64, [40, 200], [100, 0], [140, 200], 80),        # 5 sub-blocks per block
+    (4, 1, 128, [300], [0], [300], 256),                    # 16 sub-blocks per block
 ]
 
 
@@ -89,6 +92,32 @@ def test_prefill_t2048_gqa7_sampled_rows(mode):
                              seed=w.seed, rows=rows)
     _gate(got[rows], ref[rows], lo[rows], hi[rows], (w.name, mode))
     assert not np.any(np.isnan(got))
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "BF16", "K8V16"])
+def test_prefill_unwritten_slots_hold_nan(mode):
+    """Every byte of the cache is 0xFF (NaN in e4m3, bf16 and fp32) before the
+    keys are appended, so slots past each sequence's last key hold NaN: keys
+    that do not exist must not reach any output."""
+    hq, hkv, d, bs = 8, 2, 128, 48
+    n_q, q_pos0, lens = [37, 100], [0, 29], [37, 129]
+    seq_lens = np.asarray(lens, np.int32)
+    w = synth.Workload("t", 2, hq, hkv, d, seq_lens, "outliers", block_size=bs,
+                       shuffle_blocks=True, seed=11)
+    cache = make_cache(mode, w, capacity=192)
+    for x in (cache.k, cache.v, cache.k_scale, cache.v_scale):
+        if x is not None:
+            x.view(torch.uint8).fill_(0xFF)
+    seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
+    for b, (k, v) in enumerate(seqs):
+        append_seq(cache, b, k, v)
+    q_bits = synth.q_bf16_bits(11, (int(np.sum(n_q)), hq, d))
+    got, cu = gpu_prefill(cache, q_bits, n_q, q_pos0, lens, hq // hkv, w.sm_scale)
+    assert np.all(np.isfinite(got))
+    refs = [oracle.prefill(mode, q_bits[cu[b]:cu[b + 1]], seqs[b][0], seqs[b][1],
+                           int(q_pos0[b]), w.sm_scale, bounds=True) for b in range(2)]
+    ref, lo, hi = (np.concatenate([x[i] for x in refs]) for i in range(3))
+    _gate(got, ref, lo, hi, (mode, "nan-filled"))
 
 
 def test_prefill_repeat_bitwise_identical():
