@@ -135,8 +135,8 @@ struct LaneOffsets {
 // the smaller: the wait for the current tile then also waits for the whole
 // next one.)  Empty loads are not free (each still passes through the
 // load pipeline; measured at about 3 us per launch when every wave of the
-// B16, 8192-key step issued two empty tiles), so the tile loop is shaped to
-// need them only at a wave's odd last tile.
+// B16, 8192-key step issued two empty tiles), so a wave issues one only when
+// it has no tile at all.
 template <int MODE, int D>
 __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a,
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
@@ -250,10 +250,9 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
 // exact, correct in score space).
 //
 // MULTI: the split holds more than one tile per wave (chunk > 4 tiles), so
-// the waves stream their tiles through two register buffers.  Without it
-// (chunk <= 4 tiles) each wave computes at most one tile and the kernel holds
-// one buffer: a function of its own, so that its register allocation is not
-// shaped by the loop's.
+// the waves loop over their tiles.  Without it (chunk <= 4 tiles) each wave
+// computes at most one tile and there is no loop: a function of its own, so
+// that its register allocation is not shaped by the loop's.
 template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
@@ -740,18 +739,22 @@ void decode_partial_kernel(DecodeArgs a) {
   };
 
   // Tiles are dealt round-robin to the waves: wave w takes tiles w, w + 4,
-  // ...  Every load is issued unconditionally (a tile that does not exist is
-  // issued empty, see load_tile), because loads under a branch make the
-  // compiler wait for all of them wherever a value loaded before the branch
-  // is used.  Both buffers' first loads go out before the barrier, so its
-  // wait overlaps them.
+  // ...  The first tile's loads go out before the barrier, so its wait
+  // overlaps them.  A wave with several tiles streams them through one
+  // register buffer: load, compute, load the next, ...  Its own load latency
+  // is not hidden behind its own compute; the other waves on the same SIMD
+  // hide it (one buffer leaves room for three work-groups per compute unit).
+  // Two alternating buffers were measured slower (8192 keys: split 18.3
+  // against 17.9 us; ragged 64-sequence step 431 against 406 us): a wave's
+  // loads issue in order, and with the memory pipeline full the issue of the
+  // second tile's loads held back the compute of the first until late in the
+  // stream.  Every load is issued unconditionally (a tile that does not exist
+  // is issued empty, see load_tile), so the waits before each compute step
+  // are exact.
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-  T buf0, buf1;
-  load_tile<MODE, D>(buf0, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
+  T buf;
+  load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
                      wave < n_tiles);
-  if constexpr (MULTI)
-    load_tile<MODE, D>(buf1, a, lo, t_begin + (wave + kWaves) * kTile, t_end, tab, e_base, h,
-                       lane, wave + kWaves < n_tiles);
   if (APPEND && pos_n >= 0) append_new();
   __syncthreads();  // s_q complete (after the first tiles' loads are in flight)
   // Q8: the query row's scale of head c (0 for the padding heads c >= G,
@@ -761,29 +764,16 @@ void decode_partial_kernel(DecodeArgs a) {
   // 64 has blocks 0 and 1; the zero k-slots of blocks 2 and 3 take 2^0)
   if constexpr (Q8 && T::MX) q_exp_c = (c < G && g4 < D / 32) ? (int)s_qx[c][g4] : 127;
   if constexpr (!MULTI) {
-    if (wave < n_tiles) compute(buf0, t_begin + wave * kTile);
+    if (wave < n_tiles) compute(buf, t_begin + wave * kTile);
   } else if (wave < n_tiles) {
-    // Two buffers alternate (no copy between them): the loads of the next
-    // tile are in flight while the current one is computed.  The wave's
-    // tiles go in pairs (buf0, buf1); every pass but the last computes both
-    // and refills both, and the last pair is computed after the loop with
-    // nothing left to load.  Each compute step in the loop is thus entered
-    // with the same loads outstanding behind its own (the other buffer's,
-    // issued unconditionally), and waits for its own tile only.
     const int m = (n_tiles - wave + kWaves - 1) / kWaves;  // tiles of this wave
-    const int last = (m - 1) / 2;                           // passes before the last pair
     int tile = wave;
-    for (int i = 0; i < last; ++i, tile += 2 * kWaves) {
-      const int t0 = t_begin + tile * kTile;
-      compute(buf0, t0);
-      load_tile<MODE, D>(buf0, a, lo, t0 + 2 * kWaves * kTile, t_end, tab, e_base, h, lane,
-                         true);
-      compute(buf1, t0 + kWaves * kTile);
-      load_tile<MODE, D>(buf1, a, lo, t0 + 3 * kWaves * kTile, t_end, tab, e_base, h, lane,
-                         tile + 3 * kWaves < n_tiles);
+    compute(buf, t_begin + tile * kTile);
+    for (int i = 1; i < m; ++i) {
+      tile += kWaves;
+      load_tile<MODE, D>(buf, a, lo, t_begin + tile * kTile, t_end, tab, e_base, h, lane, true);
+      compute(buf, t_begin + tile * kTile);
     }
-    compute(buf0, t_begin + tile * kTile);
-    if (tile + kWaves < n_tiles) compute(buf1, t_begin + (tile + kWaves) * kTile);
   }
   if (APPEND && pos_n >= 0) store_new();
 

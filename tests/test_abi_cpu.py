@@ -118,11 +118,17 @@ def test_decode_plan():
     assert _plan(d, 64, 4, 32768 + 1)[0] == -1   # beyond the block table
     assert _plan(d, 0, 4, 0) == (0, 256, 0)
     # contiguous B16 x 2 KV heads x 8192 tokens: the grid must fit the units
-    # at once (512 work-groups for K8V8, 256 for K16V8/BF16 at head_dim 128)
+    # at once (768 work-groups for K8V8 and every head_dim 64 cache, 512 for
+    # K16V8/BF16/K8V16 at head_dim 128)
     d = _desc(num_blocks=16, block_size=8192, max_blocks_per_seq=1)
     assert _plan(d, 16, 8, 8192) == (0, 512, 16)
     d16 = _desc(mode=1, num_blocks=16, block_size=8192, max_blocks_per_seq=1, k_scale=None)
-    assert _plan(d16, 16, 8, 8192) == (0, 1024, 8)
+    assert _plan(d16, 16, 8, 8192) == (0, 512, 16)
+    big = dict(num_blocks=24, block_size=16384, max_blocks_per_seq=1, num_seqs=24)
+    assert _plan(_desc(mode=1, k_scale=None, **big), 16, 8, 16384) == (0, 1024, 16)
+    assert _plan(_desc(**big), 16, 8, 16384) == (0, 1024, 16)
+    assert _plan(_desc(**big), 24, 8, 8192) == (0, 512, 16)   # 768 work-groups: one round
+    assert _plan(_desc(mode=1, k_scale=None, **big), 24, 8, 8192) == (0, 1024, 8)
     d64 = _desc(mode=2, num_blocks=16, block_size=8192, max_blocks_per_seq=1, head_dim=64,
                 k_scale=None, v_scale=None)
     assert _plan(d64, 16, 8, 8192) == (0, 512, 16)
