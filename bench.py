@@ -595,7 +595,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="K8V8 decode only (for profiling runs)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the causal prefill of 2048 tokens (for profiling runs)")
     args = ap.parse_args()
+    if args.prefill_only:
+        import torch
+        from fp8_kv_cache_append_amd import binding
+
+        binding.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps({"prefill": bench_prefill()}), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has one, and the decode path "
               "has no cross-GPU step.", file=sys.stderr)
