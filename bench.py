@@ -24,7 +24,9 @@ fp8 QK) is timed on the same rotation for the e4m3-K modes
 (narrow_qk_step_us), with its output's relative L2 against the bf16-Q step
 (narrow_qk_vs_bf16q_rel_l2: the Q rounding's cost).
 
-Extra fields: the K16V8 and BF16 controls (same protocol), the L2/MALL-warm
+Extra fields: the K16V8 and BF16 controls (same protocol), the op-level error
+of each quantised cache (fp8_vs_bf16_rel_l2: the step's output against the
+BF16-cache step's on the same inputs), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
 the context sweep of the same shape at 77/512/2048/8192 keys in all four
 modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
@@ -252,6 +254,14 @@ class DecodeBench:
         spl = [ev[i][0].elapsed_time(ev[i][1]) for i in range(self.copies)]
         mrg = [ev[i][1].elapsed_time(ev[i][2]) for i in range(self.copies)]
         return float(np.mean(spl)), float(np.mean(mrg))
+
+
+def step_output(bench):
+    """The output of one decode step on the bench's first cache copy (fp64,
+    on the device): every mode's bench holds the same seeded inputs."""
+    bench.step(0)
+    bench.torch.cuda.synchronize()
+    return bench.out.double().clone()
 
 
 def bench_decode(mode, w, steps, warmup, copies):
@@ -624,9 +634,15 @@ def main():
     traffic = traffic_for(khash)
     extras = {}
     if not args.no_extras:
+        outs = {"K8V8": step_output(hb)}
         for mode in ("K16V8", "BF16"):
-            r, _ = bench_decode(mode, w, args.steps, args.warmup, args.copies)
+            r, bb = bench_decode(mode, w, args.steps, args.warmup, args.copies)
             extras[mode] = r
+            outs[mode] = step_output(bb)
+            del bb
+        ref = outs["BF16"]
+        extras["fp8_vs_bf16"] = {
+            m: float(((outs[m] - ref).norm() / ref.norm()).item()) for m in ("K8V8", "K16V8")}
         extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
         extras["prefill"] = bench_prefill()
         extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
@@ -680,6 +696,9 @@ def main():
             rec["modes"][mode] = {k: extras[mode][k] for k in keys}
         rec["speedup_vs_bf16"] = extras["BF16"]["ms_per_step"] / head["ms_per_step"]
         rec["speedup_vs_k16v8"] = extras["K16V8"]["ms_per_step"] / head["ms_per_step"]
+        # op-level error of the quantised caches: the GPU step's output
+        # against the BF16-cache step's on the same inputs (relative L2)
+        rec["fp8_vs_bf16_rel_l2"] = extras["fp8_vs_bf16"]
         rec["warm_l2_mall"] = extras["K8V8_warm"]
         rec["prefill"] = extras["prefill"]
         rec["context_sweep"] = extras["sweep"]
