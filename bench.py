@@ -425,6 +425,11 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
     from fp8_kv_cache_append_amd.binding import KVCache
 
     dev = "cuda"
+    # the earlier legs' rotating copies go back to the device first, so the
+    # 2-3 GB cache is allocated fresh rather than from fragmented cached blocks
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
     w = synth.decode_b64_gqa4_ragged_paged()
     bs, table, n_blocks = synth.block_layout(w)
     cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
