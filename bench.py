@@ -24,7 +24,9 @@ fp8 QK) is timed on the same rotation for the e4m3-K modes
 (narrow_qk_step_us), with its output's relative L2 against the bf16-Q step
 (narrow_qk_vs_bf16q_rel_l2: the Q rounding's cost).
 
-Extra fields: the K16V8 and BF16 controls (same protocol), the op-level error
+Extra fields: the K16V8 and BF16 controls (same protocol), a device copy of
+the step's KV bytes under the same protocol (copy_floor_same_bytes: what one
+launch moving this many bytes costs here), the op-level error
 of each quantised cache (fp8_vs_bf16_rel_l2: the step's output against the
 BF16-cache step's on the same inputs), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
@@ -506,6 +508,37 @@ def bench_warm(mode, w, steps, copies):
             "split_us": bench.split_avg_ms(reps) * 1e3}
 
 
+def bench_copy_floor(nbytes: int, copies: int = 64, replays: int = 20):
+    """Context for the roofline at this size: a device-to-device copy of
+    nbytes (the step's KV bytes), one per buffer pair of a 64-pair rotation
+    (HBM-cold like the headline), back to back in a HIP graph.  It reads and
+    writes nbytes each, so it bounds from below what one launch moving this
+    many bytes costs on this stack (launch, ramp and drain included)."""
+    import torch
+
+    n = int(nbytes)
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i % 251) for i in range(copies)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            dst[i].copy_(src[i])
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * copies)
+    ok = all(torch.equal(dst[i][:4096], src[i][:4096]) for i in (0, copies - 1))
+    del src, dst, g
+    return {"bytes_read": n, "bytes_written": n, "us_per_copy": us,
+            "read_plus_write_gbs": 2 * n / (us * 1e-6) / 1e9, "checked": ok}
+
+
 def bench_prefill(reps=200):
     import torch
     from fp8_kv_cache_append_amd import binding, synth
@@ -676,6 +709,7 @@ def main():
         extras["fp8_vs_bf16"] = {
             m: float(((outs[m] - ref).norm() / ref.norm()).item()) for m in ("K8V8", "K16V8")}
         extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
+        extras["copy_floor"] = bench_copy_floor(head["kv_bytes"])
         extras["prefill"] = bench_prefill()
         extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
                                       args.copies, head)
@@ -732,6 +766,7 @@ def main():
         # against the BF16-cache step's on the same inputs (relative L2)
         rec["fp8_vs_bf16_rel_l2"] = extras["fp8_vs_bf16"]
         rec["warm_l2_mall"] = extras["K8V8_warm"]
+        rec["copy_floor_same_bytes"] = extras["copy_floor"]
         rec["prefill"] = extras["prefill"]
         rec["context_sweep"] = extras["sweep"]
         rec["ragged_b64_paged"] = extras["ragged"]
