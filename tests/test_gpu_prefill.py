@@ -67,6 +67,7 @@ CASES = [
     (8, 2, 128, [150], [0], [150], 48),                     # 3 sub-blocks per block
     (4, 1, 64, [40, 200], [100, 0], [140, 200], 80),        # 5 sub-blocks per block
     (4, 1, 128, [300], [0], [300], 256),                    # 16 sub-blocks per block
+    (8, 2, 128, [100], [4900], [5000], 16),                 # chunk of a long context
 ]
 
 
