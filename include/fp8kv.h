@@ -115,6 +115,9 @@ typedef enum {
  *                   FP8KV_ERR_UNSUPPORTED for such a cache.
  * Requirements: head_dim 64 or 128; block_size a multiple of 16; k, v 16-byte
  * aligned; k_scale, v_scale, block_table 4-byte aligned.
+ * Slots at or past a sequence's length (and slots of blocks it does not
+ * hold) may contain any bytes, NaN codes included: attention reads whole
+ * 16-token sub-blocks but no such key reaches an output.
  */
 typedef struct fp8kv_cache {
   int32_t mode;                /* fp8kv_mode */
