@@ -230,7 +230,7 @@ def test_decode_repeat_bitwise_identical():
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
 
 
-@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16", "MXK8V8"])
 def test_decode_unwritten_slots_hold_nan(mode):
     """Every byte of the cache is 0xFF (NaN in e4m3, bf16 and fp32) before the
     keys are appended, so slots past each sequence's last key hold NaN: keys
@@ -239,7 +239,7 @@ def test_decode_unwritten_slots_hold_nan(mode):
     w = synth.Workload("t", len(lens), 16, 2, 128, lens, "outliers", block_size=48,
                        shuffle_blocks=True, seed=23)
     cache = make_cache(mode, w, capacity=1056)
-    for x in (cache.k, cache.v, cache.k_scale, cache.v_scale):
+    for x in (cache.k, cache.v, cache.k_scale, cache.v_scale, cache.k_exp):
         if x is not None:
             x.view(torch.uint8).fill_(0xFF)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
