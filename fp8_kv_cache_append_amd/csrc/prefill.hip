@@ -406,50 +406,71 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
           vsv[hb] = *reinterpret_cast<const f32x4_t*>(&T.vs[16 * (2 * kp + hb) + 4 * g4]);
         }
 
-        u32x4_t pb[kCB];
+        // --- scores in log2 units: (q . K) * k_scale * sm_scale * log2 e,
+        //     for both column blocks at once (two independent chains); the
+        //     causal, length and block masks only where some key is hidden
+        float sc[kCB][2][4];
 #pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          // --- scores in log2 units: (q . K) * k_scale * sm_scale * log2 e;
-          //     causal, length and block masks only where some key is hidden
-          float sc[2][4];
-          float tmax = -INFINITY;
+        for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[cb][hb][i] = sacc[cb][hb][i] * ksv[hb][i];
+        if (!fast) {
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
+            const int kb = 2 * kp + hb;
+            const f32x4_t okf = *reinterpret_cast<const f32x4_t*>(&T.ok[16 * kb + 4 * g4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[hb][i] = sacc[cb][hb][i] * ksv[hb][i];
-            if (!fast) {
-              const int kb = 2 * kp + hb;
-              const f32x4_t okf = *reinterpret_cast<const f32x4_t*>(&T.ok[16 * kb + 4 * g4]);
+            for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int t = t0 + 16 * kb + 4 * g4 + i;
-                sc[hb][i] = (t <= qpos[cb] && okf[i] != 0.0f) ? sc[hb][i] : -INFINITY;
+                sc[cb][hb][i] = (t <= qpos[cb] && okf[i] != 0.0f) ? sc[cb][hb][i] : -INFINITY;
               }
+          }
+        }
+        float t_ref[kCB];
+        bool grow = false;
+#pragma unroll
+        for (int cb = 0; cb < kCB; ++cb) {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[cb][hb][i]);
+          t_ref[cb] = ceilf(max_over_groups(tmax));
+          grow = grow || (m_run[cb] != -INFINITY && t_ref[cb] > m_run[cb] + kPLazy);
+        }
+
+        // --- online softmax with a lazily moved integer reference: set by
+        //     the row's first visible key, moved (exact power-of-two rescale)
+        //     only when a score exceeds it by more than kPLazy, which is rare:
+        //     one branch for both column blocks; fully masked keys
+        //     (t_ref = -inf) keep the state
+        if (grow) {
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) {
+            if (m_run[cb] != -INFINITY && t_ref[cb] > m_run[cb] + kPLazy) {
+              const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref[cb]));
+              l_run[cb] *= alpha;
+#pragma unroll
+              for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
+              m_run[cb] = t_ref[cb];
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[hb][i]);
           }
-          tmax = max_over_groups(tmax);
-
-          // --- online softmax with a lazily moved integer reference; fully
-          //     masked keys (tmax = -inf) keep the state
-          const float t_ref = ceilf(tmax);
-          if (m_run[cb] == -INFINITY) {
-            m_run[cb] = t_ref;  // l and acc are still zero: nothing to rescale
-          } else if (t_ref > m_run[cb] + kPLazy) {
-            const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref));
-            l_run[cb] *= alpha;
+        }
+        u32x4_t pb[kCB];
 #pragma unroll
-            for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
-            m_run[cb] = t_ref;
-          }
+        for (int cb = 0; cb < kCB; ++cb) {
+          // l and acc are still zero before the first visible key: nothing to rescale
+          m_run[cb] = (m_run[cb] == -INFINITY) ? t_ref[cb] : m_run[cb];
           const float m_ref = (m_run[cb] == -INFINITY) ? 0.0f : m_run[cb];
-
           float pv[8];
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) {
             const int hb = jj >> 2, i = jj & 3;
-            const float p = __builtin_amdgcn_exp2f(sc[hb][i] - m_ref);
+            const float p = __builtin_amdgcn_exp2f(sc[cb][hb][i] - m_ref);
             l_run[cb] += p;
             pv[jj] = p * vsv[hb][i];
           }
