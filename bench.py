@@ -26,7 +26,8 @@ fp8 QK) is timed on the same rotation for the e4m3-K modes
 
 Extra fields: the K16V8 and BF16 controls (same protocol), a device copy of
 the step's KV bytes under the same protocol (copy_floor_same_bytes: what one
-launch moving this many bytes costs here), the op-level error
+launch moving this many bytes costs here), the bulk append kernel's rate
+(append_bulk: 1M rows into a paged K8V8 cache), the op-level error
 of each quantised cache (fp8_vs_bf16_rel_l2: the step's output against the
 BF16-cache step's on the same inputs), the L2/MALL-warm
 rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
@@ -539,6 +540,54 @@ def bench_copy_floor(nbytes: int, copies: int = 64, replays: int = 20):
             "read_plus_write_gbs": 2 * n / (us * 1e-6) / 1e9, "checked": ok}
 
 
+def bench_append_bulk(n_tok: int = 131072, replays: int = 10):
+    """Bulk append (fp8kv_append) of n_tok new tokens x 8 KV heads x head_dim
+    128 into a paged K8V8 cache with 16-token blocks behind a shuffled table
+    (the ragged batch's cache format): per (token, KV head) row the kernel
+    reads 8 * 128 B of fp32 K and V and writes 264 B of codes and scales.
+    Eight calls on rotating inputs and caches, back to back in a graph."""
+    import torch
+    from fp8_kv_cache_append_amd import binding
+    from fp8_kv_cache_append_amd.binding import KVCache
+
+    hkv, d, bs, copies = 8, 128, 16, 8
+    n_blocks = n_tok // bs
+    table = np.random.default_rng(4).permutation(n_blocks).astype(np.int32).reshape(1, -1)
+    caches = [KVCache.allocate("K8V8", n_blocks, bs, hkv, d, table, "cuda") for _ in range(copies)]
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    ks = [torch.randn((n_tok, hkv, d), device="cuda", generator=gen) for _ in range(copies)]
+    vs = [torch.randn((n_tok, hkv, d), device="cuda", generator=gen) for _ in range(copies)]
+    seq = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    pos = torch.arange(n_tok, dtype=torch.int32, device="cuda")
+
+    def call(i):
+        binding.fp8kv_append(caches[i], ks[i], vs[i], seq, pos)
+
+    for i in range(copies):
+        call(i)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(copies):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * copies)
+    rows = n_tok * hkv
+    alg = rows * (8 * d + ROW_BYTES["K8V8"](d))
+    res = {"workload": f"append_k8v8_{n_tok}tok_hkv{hkv}_d{d}_paged{bs}", "rows": rows,
+           "us": us, "algorithmic_bytes": alg, "gbs": alg / (us * 1e-6) / 1e9,
+           "pct_roofline": 100.0 * alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    del caches, ks, vs, g
+    return res
+
+
 def bench_prefill(reps=200):
     import torch
     from fp8_kv_cache_append_amd import binding, synth
@@ -710,6 +759,7 @@ def main():
             m: float(((outs[m] - ref).norm() / ref.norm()).item()) for m in ("K8V8", "K16V8")}
         extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
         extras["copy_floor"] = bench_copy_floor(head["kv_bytes"])
+        extras["append_bulk"] = bench_append_bulk()
         extras["prefill"] = bench_prefill()
         extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
                                       args.copies, head)
@@ -767,6 +817,7 @@ def main():
         rec["fp8_vs_bf16_rel_l2"] = extras["fp8_vs_bf16"]
         rec["warm_l2_mall"] = extras["K8V8_warm"]
         rec["copy_floor_same_bytes"] = extras["copy_floor"]
+        rec["append_bulk"] = extras["append_bulk"]
         rec["prefill"] = extras["prefill"]
         rec["context_sweep"] = extras["sweep"]
         rec["ragged_b64_paged"] = extras["ragged"]

@@ -152,9 +152,8 @@ int fp8kv_append(const fp8kv_cache* cache, const float* k_new, const float* v_ne
   if (!k_new || !v_new || !seq_idx || !pos) return FP8KV_ERR_INVALID;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(seq_idx, 4) || !aligned(pos, 4))
     return FP8KV_ERR_INVALID;
-  // one thread per 4 values of each K and V row
-  const int64_t threads = 2 * (int64_t)n_tok * cache->num_kv_heads * (cache->head_dim / 4);
-  if (ceil_div(threads, 256) > INT32_MAX) return FP8KV_ERR_INVALID;
+  // K and V rows of every (token, KV head): the kernel indexes them in 32 bits
+  if (2 * (int64_t)n_tok * cache->num_kv_heads > INT32_MAX) return FP8KV_ERR_INVALID;
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(fp8kv::launch_append(view_of(cache), k_new, v_new, seq_idx, pos, n_tok,
                                             static_cast<hipStream_t>(stream)));

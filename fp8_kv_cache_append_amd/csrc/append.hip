@@ -26,7 +26,7 @@ struct AppendArgs {
   float* ks;
   float* vs;
   uint8_t* kexp;   // kMXK8V8: E8M0 byte per 32-value K block
-  int64_t n_rows;  // 2 * n_tok * hkv: K and V rows interleaved per (token, head)
+  int n_rows;      // 2 * n_tok * hkv (< 2^31): K and V rows interleaved per (token, head)
   int hkv;
   int bs;
   int mbps;
@@ -34,53 +34,87 @@ struct AppendArgs {
   int num_blocks;
 };
 
+// Rows per thread: each thread handles kRowsPerThread rows one grid-sized
+// stride apart and issues all their loads (the fp32 values, then the token's
+// sequence and position) before it uses any, so a wave keeps 4 KB of input
+// in flight instead of waiting on one dependent chain (indices, block id,
+// values) per kilobyte.
+constexpr int kRowsPerThread = 4;
+
 template <int MODE, int D>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int kLanesPerRow = D / 4;
-  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row_id = gtid / kLanesPerRow;
+  constexpr int R = kRowsPerThread;
+  // Row indices fit in 32 bits (checked on the host), so the per-row
+  // divisions by the head count and the block size are 32-bit.
+  const uint32_t gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t slots = gridDim.x * blockDim.x / kLanesPerRow;  // rows per sweep
+  const uint32_t r0 = gtid / kLanesPerRow;
   const int sub = (int)(gtid % kLanesPerRow);
-  // All lanes of one row leave together, so the butterfly below never reads
-  // an inactive lane.
-  if (row_id >= a.n_rows) return;
-  const int is_v = (int)(row_id & 1);
-  const int64_t pair = row_id >> 1;
-  const int64_t tok = pair / a.hkv;
-  const int h = (int)(pair % a.hkv);
-  const int seq = a.seq_idx[tok];
-  const int p = a.pos[tok];
+  const uint32_t hkv = (uint32_t)a.hkv, bs = (uint32_t)a.bs;
+
+  // Every row's state is uniform over its kLanesPerRow lanes, so the
+  // butterfly below, run under a per-row condition, never reads a lane of
+  // another row or an inactive one.
+  uint32_t pair[R];
+  bool in[R];
+  float4 x[R];
+  int seq[R], p[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t row_id = r0 + k * slots;
+    in[k] = row_id < (uint32_t)a.n_rows;
+    const uint32_t rid = in[k] ? row_id : 0u;  // (a row that does not exist reads row 0)
+    pair[k] = rid >> 1;
+    const float* src = ((rid & 1) ? a.v_new : a.k_new) + (uint64_t)pair[k] * D + 4 * sub;
+    x[k] = *reinterpret_cast<const float4*>(src);
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t tok = pair[k] / hkv;
+    seq[k] = a.seq_idx[tok];
+    p[k] = a.pos[tok];
+  }
   // Out-of-range device data is skipped, never followed (uniform per row).
-  if (seq < 0 || seq >= a.num_seqs || p < 0 || p >= a.mbps * a.bs) return;
-  const int blk = a.table[(int64_t)seq * a.mbps + p / a.bs];
-  if (blk < 0 || blk >= a.num_blocks) return;
-  const int64_t row = ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h;
-
-  const float* src = (is_v ? a.v_new : a.k_new) + pair * D + 4 * sub;
-  const float4 x = *reinterpret_cast<const float4*>(src);
-
-  const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
-  if (k_is_mx(MODE) && !is_v) {
-    // block-scaled K: eight lanes hold a block of 32 values
-    const int e = mx_exponent(row_amax<8>(x));
-    uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
-    *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x, e8m0_value((uint32_t)(e + 127)));
-    if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
-  } else if (quantise) {
-    const float scale = row_amax<kLanesPerRow>(x) / kE4M3Max;  // correctly rounded
-    uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
-    *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x, scale);
-    if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
-  } else {
-    uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
-    *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x);
+  int blk[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    in[k] = in[k] && seq[k] >= 0 && seq[k] < a.num_seqs && p[k] >= 0 && p[k] < a.mbps * a.bs;
+    blk[k] = a.table[in[k] ? (int64_t)seq[k] * a.mbps + (uint32_t)p[k] / bs : 0];
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (!in[k] || blk[k] < 0 || blk[k] >= a.num_blocks) continue;
+    const int is_v = (int)((r0 + k * slots) & 1u);
+    const uint32_t h = pair[k] - (pair[k] / hkv) * hkv;
+    const uint32_t slot = (uint32_t)p[k] - ((uint32_t)p[k] / bs) * bs;
+    const int64_t row = ((int64_t)blk[k] * a.bs + slot) * a.hkv + h;
+    const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
+    if (k_is_mx(MODE) && !is_v) {
+      // block-scaled K: eight lanes hold a block of 32 values
+      const int e = mx_exponent(row_amax<8>(x[k]));
+      uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
+      *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], e8m0_value((uint32_t)(e + 127)));
+      if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
+    } else if (quantise) {
+      const float scale = row_amax<kLanesPerRow>(x[k]) / kE4M3Max;  // correctly rounded
+      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
+      *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], scale);
+      if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
+      *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x[k]);
+    }
   }
 }
 
 template <int MODE>
 static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
   const int lanes = c.d / 4;
-  const int64_t threads = a.n_rows * lanes;
+  const int64_t threads = ((int64_t)a.n_rows + kRowsPerThread - 1) / kRowsPerThread * lanes;
   const int64_t blocks = (threads + 255) / 256;
+  // gtid and the row indices of the last sweep stay below 2^32
+  if (blocks * 256 > UINT32_MAX) return hipErrorInvalidValue;
   if (c.d == 128)
     hipLaunchKernelGGL((append_kernel<MODE, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else
@@ -91,8 +125,10 @@ static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStrea
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
                          const int32_t* seq_idx, const int32_t* pos, int n_tok,
                          hipStream_t stream) {
+  const int64_t n_rows = 2 * (int64_t)n_tok * c.hkv;
+  if (n_rows > INT32_MAX) return hipErrorInvalidValue;
   AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs, c.kexp,
-               2 * (int64_t)n_tok * c.hkv, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
+               (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
   switch (c.mode) {
     case kK8V8: return append_for_d<kK8V8>(c, a, stream);
     case kK16V8: return append_for_d<kK16V8>(c, a, stream);

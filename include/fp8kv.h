@@ -147,7 +147,8 @@ typedef struct fp8kv_cache {
  *   seq_idx, pos   device int32 [n_tok]: token i goes to sequence seq_idx[i]
  *                  at position pos[i]
  * Each (token, head) row is written exactly once per call; two tokens of one
- * call must not target the same slot.  n_tok == 0 is a no-op.
+ * call must not target the same slot.  n_tok == 0 is a no-op; a call with
+ * 2 * n_tok * num_kv_heads >= 2^31 rows gives FP8KV_ERR_INVALID (split it).
  */
 int fp8kv_append(const fp8kv_cache* cache, const float* k_new,
                  const float* v_new, const int32_t* seq_idx,
