@@ -34,17 +34,19 @@ struct AppendArgs {
   int num_blocks;
 };
 
-// Rows per thread: each thread handles kRowsPerThread rows one grid-sized
-// stride apart and issues all their loads (the fp32 values, then the token's
-// sequence and position) before it uses any, so a wave keeps 4 KB of input
-// in flight instead of waiting on one dependent chain (indices, block id,
-// values) per kilobyte.
-constexpr int kRowsPerThread = 4;
+// Rows per thread: for a bulk append each thread handles R = 4 rows one
+// grid-sized stride apart and issues all their loads (the fp32 values, then
+// the token's sequence and position) before it uses any, so a wave keeps
+// 4 KB of input in flight instead of waiting on one dependent chain
+// (indices, block id, values) per kilobyte.  An append too small to fill the
+// GPU (a decode step's rows) takes R = 1: there the per-row vector work, not
+// the memory, sets the time, and it is better spread over more threads.
+constexpr int kBulkRowsPerThread = 4;
+constexpr int64_t kBulkThreads = 256 * 2048;  // threads the compute units hold at once
 
-template <int MODE, int D>
+template <int MODE, int D, int R>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   constexpr int kLanesPerRow = D / 4;
-  constexpr int R = kRowsPerThread;
   // Row indices fit in 32 bits (checked on the host), so the per-row
   // divisions by the head count and the block size are 32-bit.
   const uint32_t gtid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -108,18 +110,25 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-template <int MODE>
+template <int MODE, int R>
 static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
   const int lanes = c.d / 4;
-  const int64_t threads = ((int64_t)a.n_rows + kRowsPerThread - 1) / kRowsPerThread * lanes;
+  const int64_t threads = ((int64_t)a.n_rows + R - 1) / R * lanes;
   const int64_t blocks = (threads + 255) / 256;
   // gtid and the row indices of the last sweep stay below 2^32
   if (blocks * 256 > UINT32_MAX) return hipErrorInvalidValue;
   if (c.d == 128)
-    hipLaunchKernelGGL((append_kernel<MODE, 128>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<MODE, 128, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((append_kernel<MODE, 64>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<MODE, 64, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t append_mode(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
+  if ((int64_t)a.n_rows * (c.d / 4) >= kBulkThreads)
+    return append_for_d<MODE, kBulkRowsPerThread>(c, a, stream);
+  return append_for_d<MODE, 1>(c, a, stream);
 }
 
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
@@ -130,11 +139,11 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
   AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs, c.kexp,
                (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
   switch (c.mode) {
-    case kK8V8: return append_for_d<kK8V8>(c, a, stream);
-    case kK16V8: return append_for_d<kK16V8>(c, a, stream);
-    case kK8V16: return append_for_d<kK8V16>(c, a, stream);
-    case kMXK8V8: return append_for_d<kMXK8V8>(c, a, stream);
-    default: return append_for_d<kBF16>(c, a, stream);
+    case kK8V8: return append_mode<kK8V8>(c, a, stream);
+    case kK16V8: return append_mode<kK16V8>(c, a, stream);
+    case kK8V16: return append_mode<kK8V16>(c, a, stream);
+    case kMXK8V8: return append_mode<kMXK8V8>(c, a, stream);
+    default: return append_mode<kBF16>(c, a, stream);
   }
 }
 

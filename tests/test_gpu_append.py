@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from fp8_kv_cache_append_amd import synth
+from fp8_kv_cache_append_amd import binding, synth
 from fp8_kv_cache_append_amd.binding import KVCache
 from golden_io import e4m3_encode_cases, quantize_cases
 from gpu_util import append_seq, make_cache, read_rows
@@ -189,3 +189,51 @@ def test_append_is_deterministic():
     for _ in range(20):
         append_seq(cache, 0, k, v)
     assert torch.equal(cache.k, ref[0]) and torch.equal(cache.k_scale, ref[1])
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "MXK8V8"])
+@pytest.mark.parametrize("d,hkv", [(128, 4), (64, 1)])
+def test_append_bulk_bit_exact(mode, d, hkv):
+    """A bulk append (more rows than the compute units hold threads at once:
+    the kernel's several-rows-per-thread path) into a paged cache behind a
+    shuffled table, with some tokens carrying out-of-range sequence or
+    position indices: every valid row bit-exact with the oracle, the
+    skipped rows' slots left untouched."""
+    n_seq, per = 4, 5008 if hkv == 4 else 10000
+    lens = np.full(n_seq, per, np.int32)
+    w = synth.Workload("t", n_seq, hkv, hkv, d, lens, block_size=16, shuffle_blocks=True,
+                       seed=9)
+    cache = make_cache(mode, w)
+    n_tok = n_seq * per
+    assert 2 * n_tok * hkv * (d // 4) >= 256 * 2048   # the bulk path
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((n_tok, hkv, d)).astype(np.float32) * 3
+    v = rng.standard_normal((n_tok, hkv, d)).astype(np.float32)
+    seq = np.repeat(np.arange(n_seq, dtype=np.int32), per)
+    pos = np.tile(np.arange(per, dtype=np.int32), n_seq)
+    order = rng.permutation(n_tok)                       # tokens in any order
+    seq, pos, k, v = seq[order], pos[order], k[order], v[order]
+    bad = rng.choice(n_tok, 64, replace=False)           # skipped: out-of-range indices
+    seq_dev, pos_dev = seq.copy(), pos.copy()
+    seq_dev[bad[:32]] = n_seq + 7
+    pos_dev[bad[32:]] = -3
+    binding.fp8kv_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                         torch.from_numpy(seq_dev).cuda(), torch.from_numpy(pos_dev).cuda())
+    torch.cuda.synchronize()
+    skipped = np.zeros(n_tok, bool)
+    skipped[bad] = True
+    for b in range(n_seq):
+        mine = np.flatnonzero((seq == b) & ~skipped)
+        want = _expect(mode, k[mine][np.argsort(pos[mine])], v[mine][np.argsort(pos[mine])])
+        got = read_rows(cache, b, per)
+        kept = np.sort(pos[mine])
+        for key in want:
+            g = got[key][kept]
+            wv = want[key]
+            if key in ("ks", "vs"):
+                assert np.array_equal(g.view(np.uint32), wv.view(np.uint32)), (mode, b, key)
+            else:
+                assert np.array_equal(g, wv), (mode, b, key)
+        lost = np.setdiff1d(np.arange(per), kept)        # slots of skipped tokens: untouched
+        for key, a in got.items():
+            assert not np.any(a[lost]), (mode, b, key, "skipped slot written")
