@@ -237,3 +237,47 @@ def test_append_bulk_bit_exact(mode, d, hkv):
         lost = np.setdiff1d(np.arange(per), kept)        # slots of skipped tokens: untouched
         for key, a in got.items():
             assert not np.any(a[lost]), (mode, b, key, "skipped slot written")
+
+
+def _near_midpoint_rows(seed, d):
+    """Rows [amax, values...] whose values divided by the row's scale
+    (fp32(amax / 448)) land within a few fp32 ulp of an e4m3 rounding
+    midpoint -- every midpoint of the normal binades 2^-6 .. 2^8 and of the
+    subnormal range -- for many non-power-of-two scales."""
+    rng = np.random.default_rng(seed)
+    mids = [(1 + (2 * j + 1) / 16) * 2.0 ** e for e in range(-6, 9) for j in range(8)]
+    mids += [(2 * j + 1) * 2.0 ** -10 for j in range(8)]
+    mids = np.array([m for m in mids if m < 448], np.float64)
+    rows = []
+    for amax in rng.uniform(0.5, 1000, 40).astype(np.float32):
+        scale = np.float32(amax / np.float32(448))
+        base = (mids * np.float64(scale)).astype(np.float32)
+        vals = np.concatenate([(base.view(np.int32) + k).view(np.float32) for k in range(-6, 7)])
+        vals *= np.where(rng.random(vals.size) < 0.5, -1, 1).astype(np.float32)
+        n_row = -(-vals.size // (d - 1))
+        vals = np.concatenate([vals, np.zeros(n_row * (d - 1) - vals.size, np.float32)])
+        block = np.concatenate([np.full((n_row, 1), amax, np.float32),
+                                vals.reshape(n_row, d - 1)], axis=1)
+        rows.append(block)
+    return np.concatenate(rows)
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8"])
+@pytest.mark.parametrize("n_tok", [64, 1200])   # one row per thread / the bulk path
+def test_append_near_midpoint_quotients(mode, n_tok):
+    """The append kernel divides by a reciprocal where that cannot change a
+    code and exactly where it can: quotients next to e4m3 midpoints must
+    still give the correctly rounded codes (bit-exact with the oracle)."""
+    d, hkv = 128, 8
+    base = _near_midpoint_rows(31, d)
+    rng = np.random.default_rng(32)
+    k = base[rng.integers(0, base.shape[0], n_tok * hkv)].reshape(n_tok, hkv, d)
+    v = base[rng.integers(0, base.shape[0], n_tok * hkv)].reshape(n_tok, hkv, d)
+    if n_tok * hkv >= base.shape[0]:   # every constructed row at least once
+        k.reshape(-1, d)[:base.shape[0]] = base
+    lens = np.array([n_tok], np.int32)
+    w = synth.Workload("t", 1, hkv, hkv, d, lens, block_size=16, shuffle_blocks=True, seed=5)
+    cache = make_cache(mode, w)
+    append_seq(cache, 0, k, v)
+    torch.cuda.synchronize()
+    _assert_rows_equal(read_rows(cache, 0, n_tok), _expect(mode, k, v), (mode, n_tok))
