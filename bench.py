@@ -30,7 +30,8 @@ launch moving this many bytes costs here), the bulk append kernel's rate
 (append_bulk: 1M rows into a paged K8V8 cache), the op-level error
 of each quantised cache (fp8_vs_bf16_rel_l2: the step's output against the
 BF16-cache step's on the same inputs), the L2/MALL-warm
-rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads),
+rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads;
+K8V8 and the BF16 cache as its matrix-core control),
 the context sweep of the same shape at 77/512/2048/8192 keys in all four
 modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
 per-side savings against BF16, the ragged batch-64 paged workload
@@ -588,7 +589,7 @@ def bench_append_bulk(n_tok: int = 131072, replays: int = 10):
     return res
 
 
-def bench_prefill(reps=200):
+def bench_prefill(reps=200, mode="K8V8"):
     import torch
     from fp8_kv_cache_append_amd import binding, synth
     from fp8_kv_cache_append_amd.binding import KVCache
@@ -596,7 +597,7 @@ def bench_prefill(reps=200):
     w = synth.prefill_gqa7_d128()
     n = int(w.lens[0])
     bs, table, n_blocks = synth.block_layout(w)
-    cache = KVCache.allocate("K8V8", n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda")
+    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda")
     k, v = synth.kv_sequence(w, 0)
     binding.fp8kv_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                          torch.zeros(n, dtype=torch.int32, device="cuda"),
@@ -633,7 +634,7 @@ def bench_prefill(reps=200):
         samples.append(t0.elapsed_time(t1) / per_graph)
     us = float(np.median(samples)) * 1e3
     flops = 4.0 * w.q_heads * w.head_dim * (n * (n + 1) / 2)
-    return {"workload": w.name, "us": us, "tflops": flops / (us * 1e-6) / 1e12,
+    return {"workload": w.name, "mode": mode, "us": us, "tflops": flops / (us * 1e-6) / 1e12,
             "pct_mfma_peak": 100.0 * flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
             "algorithmic_gflop": flops / 1e9}
 
@@ -761,6 +762,7 @@ def main():
         extras["copy_floor"] = bench_copy_floor(head["kv_bytes"])
         extras["append_bulk"] = bench_append_bulk()
         extras["prefill"] = bench_prefill()
+        extras["prefill_bf16"] = bench_prefill(mode="BF16")
         extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
                                       args.copies, head)
         extras["ragged"] = {m: bench_ragged(m) for m in ("K8V8", "K16V8")}
@@ -819,6 +821,7 @@ def main():
         rec["copy_floor_same_bytes"] = extras["copy_floor"]
         rec["append_bulk"] = extras["append_bulk"]
         rec["prefill"] = extras["prefill"]
+        rec["prefill_bf16_control"] = extras["prefill_bf16"]
         rec["context_sweep"] = extras["sweep"]
         rec["ragged_b64_paged"] = extras["ragged"]
         rec["block_scaled_k"] = extras["block_scaled"]
