@@ -134,3 +134,32 @@ def test_prefill_repeat_bitwise_identical():
     for _ in range(100):
         again, _ = gpu_prefill(cache, q_bits, [n], [0], [n], w.group, w.sm_scale)
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8"])
+def test_prefill_long_paged_two_sequences_sampled_rows(mode):
+    """Two sequences of 3000 and 1700 tokens (28/4 heads, D 128) in a paged
+    cache with 16-token blocks behind a shuffled table, the second a chunk
+    of 900 queries after 800 cached keys: long walks over many tiles in both
+    key groups of each work-group.  The oracle checks sampled query rows of
+    each sequence (tile edges, chunk edges, the last rows) for all heads."""
+    lens = [3000, 1700]
+    n_q, q_pos0 = [3000, 900], [0, 800]
+    w = synth.Workload("t", 2, 28, 4, 128, np.array(lens, np.int32), "outliers", block_size=16,
+                       shuffle_blocks=True, seed=77)
+    cache = make_cache(mode, w)
+    seqs = [synth.kv_sequence(w, b) for b in range(2)]
+    for b, (k, v) in enumerate(seqs):
+        append_seq(cache, b, k, v)
+    total = int(np.sum(n_q))
+    q_bits = synth.q_bf16_bits(77, (total, 28, 128))
+    got, cu = gpu_prefill(cache, q_bits, n_q, q_pos0, lens, 7, w.sm_scale)
+    rng = np.random.default_rng(8)
+    for b in range(2):
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, n_q[b] - 129, n_q[b] - 1],
+                                         rng.integers(0, n_q[b], 12)]))
+        ref, lo, hi = oracle.prefill(mode, q_bits[cu[b]:cu[b + 1]], seqs[b][0], seqs[b][1],
+                                     q_pos0[b], w.sm_scale, rows=rows, bounds=True)
+        g = got[cu[b]:cu[b + 1]]
+        _gate(g[rows], ref[rows], lo[rows], hi[rows], (mode, "long paged", b))
+    assert not np.any(np.isnan(got))
