@@ -137,30 +137,42 @@ struct LaneOffsets {
 // load pipeline; measured at about 3 us per launch when every wave of the
 // B16, 8192-key step issued two empty tiles), so a wave issues one only when
 // it has no tile at all.
-template <int MODE, int D>
+//
+// PART selects what is issued: 2 the whole tile; 0 the tile's flags, its
+// scales and keys 0-31; 1 keys 32-63 only (the flags and scales are left as
+// they are).  A wave that streams several tiles issues the next tile's part
+// 0 once it has computed the current tile's first half (whose registers it
+// overwrites) and part 1 after the second half.
+template <int MODE, int D, int PART = 2>
 __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a,
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
                                           int e_base, int h, int lane, bool live) {
   using T = TileRegs<MODE, D>;
   int64_t row0[4];
+  bool blk_ok[4];
   bool all_ok = t0 + 64 <= t_end;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int tb = t0 + 16 * kb;
     const int eb = tb / a.bs;
     const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
-    r.blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
-    all_ok = all_ok && r.blk_ok[kb];
-    row0[kb] = r.blk_ok[kb] ? ((int64_t)blk * a.bs + (tb - eb * a.bs)) * a.hkv + h : h;
+    blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
+    all_ok = all_ok && blk_ok[kb];
+    row0[kb] = blk_ok[kb] ? ((int64_t)blk * a.bs + (tb - eb * a.bs)) * a.hkv + h : h;
   }
-  r.full = all_ok;
-  {  // scales of token t0 + lane.  The sub-block is lane dependent, so its
-     // values are picked with selects: indexing the arrays with it would
-     // move them to scratch memory.
+  if constexpr (PART != 1) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) r.blk_ok[kb] = blk_ok[kb];
+    r.full = all_ok;
+  }
+  if constexpr (PART != 1) {
+    // scales of token t0 + lane.  The sub-block is lane dependent, so its
+    // values are picked with selects: indexing the arrays with it would
+    // move them to scratch memory.
     const int kb = lane >> 4;
     const int64_t base = kb == 0 ? row0[0] : kb == 1 ? row0[1] : kb == 2 ? row0[2] : row0[3];
-    const bool bok = kb == 0 ? r.blk_ok[0] : kb == 1 ? r.blk_ok[1] : kb == 2 ? r.blk_ok[2]
-                                                                               : r.blk_ok[3];
+    const bool bok = kb == 0 ? blk_ok[0] : kb == 1 ? blk_ok[1] : kb == 2 ? blk_ok[2]
+                                                                         : blk_ok[3];
     r.tok_ok = t0 + lane < t_end && bok;
     // (a tile that is not live reads the scales of row h, in block 0)
     const int64_t rr = live ? base + (int64_t)((lane & 15) * a.hkv) : (int64_t)h;
@@ -183,6 +195,7 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
   };
 #pragma unroll
   for (int kp = 0; kp < 2; ++kp) {
+    if (PART != 2 && kp != PART) continue;
 #pragma unroll
     for (int kb = 2 * kp; kb < 2 * kp + 2; ++kb) {
       const __amdgpu_buffer_rsrc_t krs = rsrc(a.k, a.k_bytes, kb, T::KE);
@@ -578,7 +591,7 @@ void decode_partial_kernel(DecodeArgs a) {
   // wave's slice of LDS (written and read by the same wave; its LDS operations
   // complete in order, and the previous tile's reads precede these writes in
   // program order).
-  auto compute = [&](T& cur, int t0) {
+  auto compute_head = [&](T& cur, int t0) __attribute__((always_inline)) {
     const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
     if (has_new) patch_scales(cur, t0);
     // K scale with sm_scale * log2(e) folded in (one product per token),
@@ -587,8 +600,15 @@ void decode_partial_kernel(DecodeArgs a) {
     if constexpr (T::MX) s_kx[wave][lane] = cur.kxw;
     if (kV8) s_scale[wave][1][lane] = cur.tok_ok ? cur.vs : 0.0f;
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
+  };
+  // Half kp of the tile: its sub-blocks' flags (full: every key of the tile
+  // valid; ok0, ok1: the block ids of sub-blocks 2kp and 2kp+1 valid) are
+  // passed in, so that the next tile's first part may already have replaced
+  // the tile's own while its second half is computed.
+  auto compute_half = [&](T& cur, int t0, int kp, bool full, bool ok0, bool ok1)
+      __attribute__((always_inline)) {
+    {
+      const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
       if (has_new) patch_half(cur, t0, kp);
       // --- QK on the matrix cores for sub-blocks 2kp, 2kp+1
       f32x4_t sacc[2];
@@ -661,8 +681,8 @@ void decode_partial_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
           float s = (Q8 ? sacc[hb][i] * q_scale_c : sacc[hb][i]) * ksv[i];
           if (KB) s += qb_c;
-          if (!cur.full) {
-            const bool ok = (t0 + base + i < t_end) && cur.blk_ok[kb];
+          if (!full) {
+            const bool ok = (t0 + base + i < t_end) && (hb == 0 ? ok0 : ok1);
             s = ok ? s : -INFINITY;
           }
           sc[4 * hb + i] = s;
@@ -702,11 +722,11 @@ void decode_partial_kernel(DecodeArgs a) {
       // --- V of keys outside the sequence may hold any bits (even NaN
       //     codes): zero them in place so that P = 0 contributes exactly 0
       auto& vv = cur.v[kp];
-      if (!cur.full) {
+      if (!full) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int kb = 2 * kp + (j >> 2);
-          const bool ok = (t0 + 16 * kb + 4 * g4 + (j & 3) < t_end) && cur.blk_ok[kb];
+          const bool ok = (t0 + 16 * kb + 4 * g4 + (j & 3) < t_end) && ((j >> 2) == 0 ? ok0 : ok1);
 #pragma unroll
           for (int e = 0; e < T::VW; ++e) vv[j][e] = ok ? vv[j][e] : 0u;
         }
@@ -737,13 +757,20 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
   };
+  auto compute = [&](T& cur, int t0) __attribute__((always_inline)) {
+    compute_head(cur, t0);
+    compute_half(cur, t0, 0, cur.full, cur.blk_ok[0], cur.blk_ok[1]);
+    compute_half(cur, t0, 1, cur.full, cur.blk_ok[2], cur.blk_ok[3]);
+  };
 
   // Tiles are dealt round-robin to the waves: wave w takes tiles w, w + 4,
   // ...  The first tile's loads go out before the barrier, so its wait
   // overlaps them.  A wave with several tiles streams them through one
-  // register buffer: load, compute, load the next, ...  Its own load latency
-  // is not hidden behind its own compute; the other waves on the same SIMD
-  // hide it (one buffer leaves room for three work-groups per compute unit).
+  // register buffer, half by half: the next tile's first half is loaded into
+  // the registers of the half just computed while the second half is
+  // computed, and its second half after that (one buffer leaves room for
+  // three work-groups per compute unit; the other waves on the SIMD cover
+  // the rest of the latency).
   // Two alternating buffers were measured slower (8192 keys: split 18.3
   // against 17.9 us; ragged 64-sequence step 431 against 406 us): a wave's
   // loads issue in order, and with the memory pipeline full the issue of the
@@ -768,12 +795,18 @@ void decode_partial_kernel(DecodeArgs a) {
   } else if (wave < n_tiles) {
     const int m = (n_tiles - wave + kWaves - 1) / kWaves;  // tiles of this wave
     int tile = wave;
-    compute(buf, t_begin + tile * kTile);
-    for (int i = 1; i < m; ++i) {
-      tile += kWaves;
-      load_tile<MODE, D>(buf, a, lo, t_begin + tile * kTile, t_end, tab, e_base, h, lane, true);
-      compute(buf, t_begin + tile * kTile);
+    for (int i = 1; i < m; ++i, tile += kWaves) {
+      // the next tile's first part goes into the registers of the half just
+      // computed, its second part after the second half
+      const int t0 = t_begin + tile * kTile, tn = t0 + kWaves * kTile;
+      compute_head(buf, t0);
+      const bool full = buf.full, ok2 = buf.blk_ok[2], ok3 = buf.blk_ok[3];
+      compute_half(buf, t0, 0, full, buf.blk_ok[0], buf.blk_ok[1]);
+      load_tile<MODE, D, 0>(buf, a, lo, tn, t_end, tab, e_base, h, lane, true);
+      compute_half(buf, t0, 1, full, ok2, ok3);
+      load_tile<MODE, D, 1>(buf, a, lo, tn, t_end, tab, e_base, h, lane, true);
     }
+    compute(buf, t_begin + tile * kTile);
   }
   if (APPEND && pos_n >= 0) store_new();
 
