@@ -103,14 +103,12 @@ bool split_fits_table_window(int64_t chunk, int64_t bs) {
 int plan(const fp8kv_cache* c, int32_t batch, int32_t max_seq_len, int32_t* chunk,
          int32_t* n_splits) {
   // Splits of 256 keys (one 64-key tile per wave of a 4-wave work-group),
-  // doubled (up to 1024) while the grid holds more work-groups than the
-  // 256 compute units run at once, so that each work-group streams several
-  // tiles per wave instead of the grid running in rounds of one tile.
+  // doubled (up to 1024) while the grid still gives every compute unit a
+  // work-group: a wave then streams several tiles, half by half, and fewer
+  // splits make the merge cheaper.
   const int64_t pairs = (int64_t)batch * c->num_kv_heads;
-  const int64_t slots =
-      (int64_t)fp8kv::kComputeUnits * fp8kv::split_wgs_per_cu(c->mode, c->head_dim);
   int64_t ch = 256;
-  while (ch < 1024 && pairs * ceil_div(max_seq_len, ch) > slots) ch *= 2;
+  while (ch < 1024 && pairs * ceil_div(max_seq_len, 2 * ch) >= fp8kv::kComputeUnits) ch *= 2;
   *chunk = (int32_t)ch;
   *n_splits = max_seq_len > 0 ? (int32_t)ceil_div(max_seq_len, ch) : 0;
   return FP8KV_OK;

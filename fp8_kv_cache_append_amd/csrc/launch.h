@@ -38,8 +38,7 @@ struct CacheView {
 // Work-groups of the split kernel one compute unit holds at once (one
 // register buffer per wave): three where a lane's registers fit in 168 (the
 // e4m3 K and V tiles of K8V8 and MXK8V8, and every D = 64 tile), else two
-// (a bf16 side at D = 128 needs up to 240).  The kernel's launch bounds and
-// the split plan both use it.
+// (a bf16 side at D = 128 needs up to 240): the kernel's launch bounds.
 constexpr int split_wgs_per_cu(int mode, int d) {
   return (mode == kK8V8 || mode == kMXK8V8 || d == 64) ? 3 : 2;
 }

@@ -158,10 +158,11 @@ int fp8kv_append(const fp8kv_cache* cache, const float* k_new,
  * Split plan for decode: keys of each (sequence, KV head) are cut into
  * splits of *chunk_tokens keys (a multiple of 64); *n_splits =
  * ceil(max_seq_len / chunk_tokens).  The chunk is 256, 512 or 1024 keys:
- * the smallest whose grid fits in what MI355X's 256 compute units hold at
- * once (two work-groups per unit for K8V8 and head_dim 64, one otherwise),
- * so that the splits feed every unit without queueing in rounds ([SKILL]
- * Speed).  Host-only and deterministic.
+ * the largest whose grid (batch * num_kv_heads * n_splits work-groups)
+ * still gives each of MI355X's 256 compute units a work-group, so that the
+ * splits feed every unit ([SKILL] Speed) while each wave streams as many
+ * tiles as it can and the merge has few splits.  Host-only and
+ * deterministic.
  */
 int fp8kv_decode_plan(const fp8kv_cache* cache, int32_t batch,
                       int32_t gqa_group, int32_t max_seq_len,

@@ -117,21 +117,22 @@ def test_decode_plan():
     assert _plan(d, 64, 0, 32768)[0] == -1
     assert _plan(d, 64, 4, 32768 + 1)[0] == -1   # beyond the block table
     assert _plan(d, 0, 4, 0) == (0, 256, 0)
-    # contiguous B16 x 2 KV heads x 8192 tokens: the grid must fit the units
-    # at once (768 work-groups for K8V8 and every head_dim 64 cache, 512 for
-    # K16V8/BF16/K8V16 at head_dim 128)
+    # contiguous B16 x 2 KV heads: the chunk doubles while every one of the
+    # 256 compute units still gets a work-group
     d = _desc(num_blocks=16, block_size=8192, max_blocks_per_seq=1)
-    assert _plan(d, 16, 8, 8192) == (0, 512, 16)
+    assert _plan(d, 16, 8, 4096) == (0, 512, 8)      # 256 work-groups
+    assert _plan(d, 16, 8, 8192) == (0, 1024, 8)     # 256 work-groups
+    assert _plan(d, 16, 8, 512) == (0, 256, 2)       # 64: no doubling
     d16 = _desc(mode=1, num_blocks=16, block_size=8192, max_blocks_per_seq=1, k_scale=None)
-    assert _plan(d16, 16, 8, 8192) == (0, 512, 16)
+    assert _plan(d16, 16, 8, 8192) == (0, 1024, 8)
     big = dict(num_blocks=24, block_size=16384, max_blocks_per_seq=1, num_seqs=24)
     assert _plan(_desc(mode=1, k_scale=None, **big), 16, 8, 16384) == (0, 1024, 16)
     assert _plan(_desc(**big), 16, 8, 16384) == (0, 1024, 16)
-    assert _plan(_desc(**big), 24, 8, 8192) == (0, 512, 16)   # 768 work-groups: one round
-    assert _plan(_desc(mode=1, k_scale=None, **big), 24, 8, 8192) == (0, 1024, 8)
+    assert _plan(_desc(**big), 1, 8, 16384) == (0, 256, 64)   # 2 pairs: 128 work-groups
+    assert _plan(_desc(**big), 24, 8, 8192) == (0, 1024, 8)
     d64 = _desc(mode=2, num_blocks=16, block_size=8192, max_blocks_per_seq=1, head_dim=64,
                 k_scale=None, v_scale=None)
-    assert _plan(d64, 16, 8, 8192) == (0, 512, 16)
+    assert _plan(d64, 16, 8, 8192) == (0, 1024, 8)
 
 
 def test_workspace_bytes():
