@@ -722,7 +722,18 @@ def main():
                     help="K8V8 decode only (for profiling runs)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the causal prefill of 2048 tokens (for profiling runs)")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="only the ragged batch-64 paged K8V8 decode (for profiling runs)")
     args = ap.parse_args()
+    if args.ragged_only:
+        import torch
+        from fp8_kv_cache_append_amd import binding
+
+        binding.lib()
+        torch.cuda.set_device(0)
+        print(json.dumps({"ragged_b64_paged": bench_ragged("K8V8", replays=4, steps=4)}),
+              flush=True)
+        return
     if args.prefill_only:
         import torch
         from fp8_kv_cache_append_amd import binding
