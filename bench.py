@@ -85,7 +85,10 @@ class DecodeBench:
         dev = "cuda"
         n = int(w.lens[0])
         bs, table, n_blocks = synth.block_layout(w)
-        base = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+        # a contiguous cache is passed without a table (the library computes the ids)
+        mem_table = w.block_size != 0
+        base = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev,
+                                table_in_memory=mem_table)
         last_k, last_v = [], []
         for b in range(w.batch):
             k, v = synth.kv_sequence(w, b)
@@ -98,7 +101,8 @@ class DecodeBench:
         self.caches = [base] + [KVCache(mode, base.k.clone(), base.v.clone(),
                                         None if base.k_scale is None else base.k_scale.clone(),
                                         None if base.v_scale is None else base.v_scale.clone(),
-                                        base.block_table) for _ in range(n_copies - 1)]
+                                        base.block_table, table_in_memory=mem_table)
+                                for _ in range(n_copies - 1)]
         # the new token of each sequence, appended at its last position
         self.k_new = torch.from_numpy(np.stack(last_k)).to(dev)
         self.v_new = torch.from_numpy(np.stack(last_v)).to(dev)
@@ -125,7 +129,8 @@ class DecodeBench:
         if mode == "K8V8":
             # the unfused control: the cache dequantised to bf16 in HBM, then
             # the BF16 kernels on the copy
-            self.dq = KVCache.allocate("BF16", n_blocks, bs, w.kv_heads, d, table, dev)
+            self.dq = KVCache.allocate("BF16", n_blocks, bs, w.kv_heads, d, table, dev,
+                                       table_in_memory=mem_table)
             self.dq_chunk, self.dq_splits = binding.fp8kv_decode_plan(self.dq, w.batch, g, n)
             self.dq_pacc = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, d), device=dev)
             self.dq_pml = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, 2), device=dev)
@@ -371,7 +376,8 @@ def bench_block_scaled(steps, copies):
     res = {}
     bases = {}
     for mode in ("BF16", "K8V8", "MXK8V8"):
-        c = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+        c = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev,
+                             table_in_memory=False)   # contiguous
         for b in range(w.batch):
             k, v = synth.kv_sequence(w, b)
             binding.fp8kv_append(c, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
@@ -387,7 +393,8 @@ def bench_block_scaled(steps, copies):
         caches = [base] + [KVCache(mode, base.k.clone(), base.v.clone(),
                                    None if base.k_scale is None else base.k_scale.clone(),
                                    base.v_scale.clone(), base.block_table, None,
-                                   None if base.k_exp is None else base.k_exp.clone())
+                                   None if base.k_exp is None else base.k_exp.clone(),
+                                   False)
                            for _ in range(copies - 1)]
         out = torch.empty_like(ref_out)
         for name, fn in (("bf16_q", binding.fp8kv_decode), ("fp8_qk", binding.fp8kv_decode_q8)):
@@ -597,7 +604,8 @@ def bench_prefill(reps=200, mode="K8V8"):
     w = synth.prefill_gqa7_d128()
     n = int(w.lens[0])
     bs, table, n_blocks = synth.block_layout(w)
-    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda")
+    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda",
+                             table_in_memory=False)   # contiguous
     k, v = synth.kv_sequence(w, 0)
     binding.fp8kv_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                          torch.zeros(n, dtype=torch.int32, device="cuda"),

@@ -127,7 +127,9 @@ class KVCache:
     k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
     k_scale, v_scale: float32 [num_blocks, block_size, Hkv] for an e4m3 side,
     else None;
-    block_table: int32 [batch, max_blocks_per_seq];
+    block_table: int32 [batch, max_blocks_per_seq]; with table_in_memory False
+    the descriptor passes no table and the library computes the contiguous
+    ids b * max_blocks_per_seq + e (block_table then only gives the shape);
     k_bias: float32 [Hkv, D] for a pre-bias residual cache (the stored K rows
     are residuals, the key is residual + k_bias), else None.
     """
@@ -139,10 +141,12 @@ class KVCache:
     block_table: torch.Tensor
     k_bias: torch.Tensor | None = None
     k_exp: torch.Tensor | None = None
+    table_in_memory: bool = True   # False: pass no table (contiguous layout)
 
     @classmethod
     def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
-                 head_dim: int, block_table, device="cuda") -> "KVCache":
+                 head_dim: int, block_table, device="cuda",
+                 table_in_memory: bool = True) -> "KVCache":
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         k8, v8, kmx = mode in K_E4M3, mode in V_E4M3, mode in K_MX
         k = torch.zeros(shape, dtype=torch.uint8 if k8 else torch.bfloat16, device=device)
@@ -152,7 +156,12 @@ class KVCache:
         kx = torch.zeros(shape[:3] + (head_dim // 32,), dtype=torch.uint8,
                          device=device) if kmx else None
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
-        return cls(mode, k, v, ks, vs, bt, None, kx)
+        if not table_in_memory:
+            # the library then computes block b * max_blocks_per_seq + e itself
+            want = torch.arange(bt.numel(), dtype=torch.int32, device=device).view(bt.shape)
+            if not torch.equal(bt, want):
+                raise ValueError("table_in_memory=False needs the contiguous table")
+        return cls(mode, k, v, ks, vs, bt, None, kx, table_in_memory)
 
     @property
     def head_dim(self) -> int:
@@ -167,7 +176,8 @@ class KVCache:
                          int(self.k.shape[2]), int(self.k.shape[3]),
                          int(self.block_table.shape[1]), int(self.block_table.shape[0]),
                          _ptr(self.k), _ptr(self.v),
-                         _ptr(self.k_scale), _ptr(self.v_scale), _ptr(self.block_table),
+                         _ptr(self.k_scale), _ptr(self.v_scale),
+                         _ptr(self.block_table) if self.table_in_memory else None,
                          _ptr(self.k_bias), _ptr(self.k_exp))
 
 

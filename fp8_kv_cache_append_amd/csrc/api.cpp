@@ -49,8 +49,11 @@ int validate_cache(const fp8kv_cache* c) {
     return FP8KV_ERR_INVALID;
   if ((int64_t)c->max_blocks_per_seq * c->block_size > INT32_MAX) return FP8KV_ERR_INVALID;
   if (c->block_size <= 0 || c->block_size % 16 != 0) return FP8KV_ERR_INVALID;
-  if (!c->k || !c->v || !c->block_table) return FP8KV_ERR_INVALID;
+  if (!c->k || !c->v) return FP8KV_ERR_INVALID;
   if (!aligned(c->k, 16) || !aligned(c->v, 16) || !aligned(c->block_table, 4))
+    return FP8KV_ERR_INVALID;
+  // no table: block e of sequence b is block b * max_blocks_per_seq + e, an int32
+  if (!c->block_table && (int64_t)c->num_seqs * c->max_blocks_per_seq > INT32_MAX)
     return FP8KV_ERR_INVALID;
   const bool need_ks = fp8kv::k_has_row_scale(c->mode);
   const bool need_vs = fp8kv::v_is_e4m3(c->mode);

@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     in[k] = in[k] && seq[k] >= 0 && seq[k] < a.num_seqs && p[k] >= 0 && p[k] < a.mbps * a.bs;
-    blk[k] = a.table[in[k] ? (int64_t)seq[k] * a.mbps + (uint32_t)p[k] / bs : 0];
+    const int64_t ti = in[k] ? (int64_t)seq[k] * a.mbps + (uint32_t)p[k] / bs : 0;
+    blk[k] = a.table ? a.table[ti] : (int)ti;  // no table: contiguous
   }
 #pragma unroll
   for (int k = 0; k < R; ++k) {

@@ -266,7 +266,11 @@ __device__ __forceinline__ int rotated_head(int pi, int hkv) {
 // the waves loop over their tiles.  Without it (chunk <= 4 tiles) each wave
 // computes at most one tile and there is no loop: a function of its own, so
 // that its register allocation is not shaped by the loop's.
-template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI>
+//
+// TB: the cache has a block table in memory; without one (contiguous cache)
+// the block ids are computed, a variant of its own so that no wait for a
+// table load sits in front of the first K/V loads.
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI, bool TB>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
@@ -331,10 +335,14 @@ void decode_partial_kernel(DecodeArgs a) {
 
   // First round trip, all independent: the sequence length, the block ids
   // of this split (lane e: block t_begin / bs + e, index kept inside the
-  // table row; ids past the sequence are never used) and Q.
+  // table row; ids past the sequence are never used) and Q.  Without a
+  // table (contiguous cache) the block ids are computed, and the K/V loads
+  // need not wait for them.
   const int len = a.seq_lens[b];  // clamped below to the block-table capacity
   const int e_base = t_begin / a.bs;
-  const int tab = a.table[(int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1)];
+  const int64_t tab_i = (int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1);
+  int tab = (int)tab_i;  // no table: contiguous
+  if constexpr (TB) tab = a.table[tab_i];
   // Q^T, the B operand of QK, in LDS in operand order: s_q[kc][lane] is lane
   // (g4, c)'s 16 bytes of head c for k-chunk kc.  Each wave loads a share.
   const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
@@ -956,6 +964,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(int hkv, int group, in
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI>
+static void launch_split(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.table)
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, MULTI, true>), grid, block,
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, MULTI, false>), grid,
+                       block, 0, stream, a);
+}
+
 template <int MODE, bool APPEND, bool Q8, bool KB>
 static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                              hipStream_t stream) {
@@ -963,18 +981,14 @@ static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n
   const dim3 grid(n_wg), block(64 * kWaves);
   if (c.d == 128) {
     if (multi)
-      hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB, true>), grid, block,
-                         0, stream, a);
+      launch_split<MODE, 128, APPEND, Q8, KB, true>(a, grid, block, stream);
     else
-      hipLaunchKernelGGL((decode_partial_kernel<MODE, 128, APPEND, Q8, KB, false>), grid,
-                         block, 0, stream, a);
+      launch_split<MODE, 128, APPEND, Q8, KB, false>(a, grid, block, stream);
   } else {
     if (multi)
-      hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB, true>), grid, block,
-                         0, stream, a);
+      launch_split<MODE, 64, APPEND, Q8, KB, true>(a, grid, block, stream);
     else
-      hipLaunchKernelGGL((decode_partial_kernel<MODE, 64, APPEND, Q8, KB, false>), grid, block,
-                         0, stream, a);
+      launch_split<MODE, 64, APPEND, Q8, KB, false>(a, grid, block, stream);
   }
 }
 

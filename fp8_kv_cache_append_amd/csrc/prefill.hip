@@ -236,7 +236,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   // block id fetched for the next tile to load
   int p_id = 0, p_r = 0, p_t = 0;
   auto fetch_id = [&]() {
-    p_id = a.table[tab_row + (cur_t < kv_end ? cur_b : 0)];
+    const int64_t ti = tab_row + (cur_t < kv_end ? cur_b : 0);
+    p_id = a.table ? a.table[ti] : (int)ti;  // no table: contiguous
     p_r = cur_r;
     p_t = cur_t;
     cur_t += kPGroups * kKT;

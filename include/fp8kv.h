@@ -100,8 +100,13 @@ typedef enum {
  *   v_scale         same shape, K8V8 and K16V8 (NULL otherwise)
  *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
  *                   b is slot t % block_size of block
- *                   block_table[b * max_blocks_per_seq + t / block_size]
- * A contiguous cache [B][T][Hkv][D] is block_size = T with block_table[b] = b.
+ *                   block_table[b * max_blocks_per_seq + t / block_size].
+ *                   NULL: a contiguous cache, where that block is
+ *                   b * max_blocks_per_seq + t / block_size (no table is
+ *                   read, so the first K/V loads need not wait for one;
+ *                   num_seqs * max_blocks_per_seq must fit an int32).
+ * A contiguous cache [B][T][Hkv][D] is block_size = T, max_blocks_per_seq = 1
+ * and block_table NULL (or block_table[b] = b).
  *   k_bias          NULL, or fp32 [num_kv_heads][head_dim], 16-byte aligned:
  *                   a pre-bias residual cache ([HW] "Treat numerical safety
  *                   and kernel speed as separate gates"; [FQ] "Bias-aware

@@ -70,6 +70,8 @@ BAD_CACHES = [
     (dict(mode=1), -1),              # K16V8 must not carry a K scale
     (dict(mode=2, k_scale=None), -1),  # BF16 must not carry a V scale
     (dict(block_table=FAKE + 2), -1),
+    # no table: block ids b * max_blocks_per_seq + e must fit an int32
+    (dict(block_table=None, num_seqs=2**20, max_blocks_per_seq=2**12), -1),
     (dict(k_bias=FAKE + 4), -1),        # the bias is read 16 bytes at a time
     (dict(mode=4), -1),                 # block-scaled K: no K row scale, but k_exp
     (dict(mode=4, k_scale=None), -1),   # ... k_exp missing
@@ -107,6 +109,9 @@ def _plan(d, b, g, t):
 def test_decode_plan():
     # contiguous B16 x 2 KV heads x 2048 tokens
     d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    assert _plan(d, 16, 8, 2048) == (0, 256, 8)
+    # the same cache passed with no table (contiguous ids) is valid
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1, block_table=None)
     assert _plan(d, 16, 8, 2048) == (0, 256, 8)
     # paged B64 x 8 KV heads up to 32768 tokens: longer splits, bounded grid
     d = _desc(num_blocks=70000, block_size=16, num_kv_heads=8, max_blocks_per_seq=2048,
