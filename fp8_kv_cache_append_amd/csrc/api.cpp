@@ -55,6 +55,10 @@ int validate_cache(const fp8kv_cache* c) {
   // no table: block e of sequence b is block b * max_blocks_per_seq + e, an int32
   if (!c->block_table && (int64_t)c->num_seqs * c->max_blocks_per_seq > INT32_MAX)
     return FP8KV_ERR_INVALID;
+  // ... and every such id must be a block of the cache: a smaller allocation
+  // would make the kernels drop keys and skip appends without an error
+  if (!c->block_table && (int64_t)c->num_seqs * c->max_blocks_per_seq > c->num_blocks)
+    return FP8KV_ERR_INVALID;
   const bool need_ks = fp8kv::k_has_row_scale(c->mode);
   const bool need_vs = fp8kv::v_is_e4m3(c->mode);
   const bool need_kx = fp8kv::k_is_mx(c->mode);
@@ -193,6 +197,14 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
   if (chunk_tokens <= 0 || chunk_tokens % 64 != 0 || n_splits < 0) return FP8KV_ERR_INVALID;
   if (!split_fits_table_window(chunk_tokens, cache->block_size)) return FP8KV_ERR_INVALID;
   if ((int64_t)n_splits * chunk_tokens < max_seq_len) return FP8KV_ERR_INVALID;
+  // The kernel computes split * chunk_tokens (and that plus chunk_tokens) in
+  // 32 bits; a split that starts at or past the block-table capacity holds
+  // no key, so more splits than the capacity needs are rejected, which also
+  // keeps those values inside an int32.
+  const int64_t capacity = (int64_t)cache->max_blocks_per_seq * cache->block_size;
+  if ((int64_t)n_splits * chunk_tokens > capacity + chunk_tokens - 1 ||
+      (int64_t)n_splits * chunk_tokens > INT32_MAX)
+    return FP8KV_ERR_INVALID;
   const int64_t n_wg = (int64_t)batch * cache->num_kv_heads * n_splits;
   if (n_wg > INT32_MAX) return FP8KV_ERR_INVALID;
   if (n_wg == 0) return FP8KV_OK;

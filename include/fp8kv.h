@@ -104,7 +104,8 @@ typedef enum {
  *                   NULL: a contiguous cache, where that block is
  *                   b * max_blocks_per_seq + t / block_size (no table is
  *                   read, so the first K/V loads need not wait for one;
- *                   num_seqs * max_blocks_per_seq must fit an int32).
+ *                   num_seqs * max_blocks_per_seq must fit an int32 and
+ *                   be at most num_blocks, else FP8KV_ERR_INVALID).
  * A contiguous cache [B][T][Hkv][D] is block_size = T, max_blocks_per_seq = 1
  * and block_table NULL (or block_table[b] = b).
  *   k_bias          NULL, or fp32 [num_kv_heads][head_dim], 16-byte aligned:
@@ -198,7 +199,9 @@ size_t fp8kv_decode_workspace_bytes(const fp8kv_cache* cache, int32_t batch,
  * (block_size - g + chunk_tokens - 16) / block_size <= 63.  This holds for
  * every chunk_tokens <= 64 * block_size that block_size divides or that
  * divides block_size, and for every plan fp8kv_decode_plan returns;
- * otherwise FP8KV_ERR_INVALID.  n_splits >= ceil(max_seq_len / chunk_tokens).
+ * otherwise FP8KV_ERR_INVALID.  n_splits >= ceil(max_seq_len / chunk_tokens),
+ * and no split may start past the block table: n_splits * chunk_tokens <
+ * max_blocks_per_seq * block_size + chunk_tokens (else FP8KV_ERR_INVALID).
  * gqa_group in 1..16.
  */
 int fp8kv_decode_partial(const fp8kv_cache* cache, const uint16_t* q,

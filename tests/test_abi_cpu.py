@@ -72,6 +72,8 @@ BAD_CACHES = [
     (dict(block_table=FAKE + 2), -1),
     # no table: block ids b * max_blocks_per_seq + e must fit an int32
     (dict(block_table=None, num_seqs=2**20, max_blocks_per_seq=2**12), -1),
+    # ... and must all be blocks of the cache (16 sequences x 4 blocks > 63)
+    (dict(block_table=None, num_blocks=63), -1),
     (dict(k_bias=FAKE + 4), -1),        # the bias is read 16 bytes at a time
     (dict(mode=4), -1),                 # block-scaled K: no K row scale, but k_exp
     (dict(mode=4, k_scale=None), -1),   # ... k_exp missing
@@ -79,6 +81,14 @@ BAD_CACHES = [
     (dict(mode=4, k_scale=None, k_exp=FAKE + 2), -1),   # misaligned
     (dict(mode=4, k_scale=None, k_exp=FAKE, k_bias=FAKE), -4),  # no bias on block scales
 ]
+
+
+def test_contiguous_cache_without_table_is_valid():
+    # no table, and exactly num_seqs * max_blocks_per_seq blocks: accepted
+    # (append reaches the device check, which has no GPU here)
+    d = _desc(block_table=None, num_blocks=64)
+    r = binding.lib().fp8kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert r in (0, -4), r
 
 
 @pytest.mark.parametrize("kw,status", BAD_CACHES)
@@ -169,6 +179,17 @@ def test_decode_rejects_bad_arguments():
     odd = _desc(num_blocks=16, block_size=112, max_blocks_per_seq=200)
     assert lib.fp8kv_decode_partial(ctypes.byref(odd), FAKE, 8, FAKE, 16, 14208, 0.1,
                                     7104, 2, FAKE, FAKE, None) == -1
+    # more splits than the capacity needs: split * chunk would pass 2^31 in
+    # the kernel's 32-bit arithmetic (chunk 1024, 2^21 + 1 splits), or merely
+    # start past the block table
+    big = _desc(num_blocks=1, block_size=1024, max_blocks_per_seq=1, num_seqs=1)
+    assert lib.fp8kv_decode_partial(ctypes.byref(big), FAKE, 8, FAKE, 1, 1024, 0.1,
+                                    1024, 2 ** 21 + 1, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_partial(ctypes.byref(big), FAKE, 8, FAKE, 1, 1024, 0.1,
+                                    1024, 2, FAKE, FAKE, None) == -1
+    assert lib.fp8kv_decode_append_partial(ctypes.byref(big), FAKE, FAKE, FAKE, 8, FAKE, 1,
+                                           1024, 0.1, 1024, 2 ** 21 + 1, FAKE, FAKE,
+                                           None) == -1
     assert lib.fp8kv_decode_plan(ctypes.byref(d), 17, 8, 2048, ctypes.byref(ctypes.c_int32()),
                                  ctypes.byref(ctypes.c_int32())) == -1  # batch > table rows
     # merge shape checks
