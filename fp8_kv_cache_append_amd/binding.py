@@ -26,12 +26,14 @@ FP8KV_ERR_INVALID = -1
 FP8KV_ERR_WORKSPACE = -2
 FP8KV_ERR_LAUNCH = -3
 FP8KV_ERR_UNSUPPORTED = -4
+FP8KV_ERR_TOO_LARGE = -5
 
 # Every symbol include/fp8kv.h declares.
 EXPORTS = ("fp8kv_append", "fp8kv_decode_plan", "fp8kv_decode_workspace_bytes",
            "fp8kv_decode_partial", "fp8kv_decode_merge", "fp8kv_decode",
            "fp8kv_decode_append", "fp8kv_decode_append_partial", "fp8kv_decode_q8",
-           "fp8kv_decode_append_q8", "fp8kv_prefill", "fp8kv_dequantize", "fp8kv_strerror")
+           "fp8kv_decode_append_q8", "fp8kv_prefill", "fp8kv_dequantize", "fp8kv_strerror",
+           "fp8kv_decode_noalloc")
 
 
 class Fp8kvError(RuntimeError):
@@ -84,6 +86,7 @@ def lib() -> ctypes.CDLL:
                                                            I32, I32, P, P, P]),
             "fp8kv_prefill": (ctypes.c_int, [C, P, I32, P, P, P, I32, I32, I32, F, P, P]),
             "fp8kv_dequantize": (ctypes.c_int, [C, C, P]),
+            "fp8kv_decode_noalloc": (ctypes.c_int, [C, P, I32, P, I32, I32, F, P, P]),
             "fp8kv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         }
         for name, (res, args) in sig.items():
@@ -229,6 +232,16 @@ def fp8kv_decode(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
     _check(lib().fp8kv_decode(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
                               int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
                               _ptr(workspace), ws_bytes, _stream(stream)), "fp8kv_decode")
+
+
+def fp8kv_decode_noalloc(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,
+                         sm_scale: float, out, stream=None) -> None:
+    """fp8kv_decode with the partials in the library's own device scratch
+    (no workspace; see include/fp8kv.h for the limit)."""
+    d = cache.desc()
+    _check(lib().fp8kv_decode_noalloc(ctypes.byref(d), _ptr(q), gqa_group, _ptr(seq_lens),
+                                      int(seq_lens.shape[0]), max_seq_len, sm_scale, _ptr(out),
+                                      _stream(stream)), "fp8kv_decode_noalloc")
 
 
 def fp8kv_decode_q8(cache: KVCache, q, gqa_group: int, seq_lens, max_seq_len: int,

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfp8kv.so")
-SOURCES = ["append.hip", "decode.hip", "prefill.hip", "dequant.hip", "api.cpp"]
+SOURCES = ["append.hip", "decode.hip", "prefill.hip", "dequant.hip", "scratch.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

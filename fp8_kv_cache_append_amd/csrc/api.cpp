@@ -144,6 +144,7 @@ const char* fp8kv_strerror(int status) {
     case FP8KV_ERR_WORKSPACE: return "workspace too small";
     case FP8KV_ERR_LAUNCH: return "kernel launch failed";
     case FP8KV_ERR_UNSUPPORTED: return "unsupported device or shape";
+    case FP8KV_ERR_TOO_LARGE: return "request exceeds the library's 64 MiB device scratch";
     default: return "unknown status";
   }
 }
@@ -319,6 +320,26 @@ int fp8kv_decode_append_q8(const fp8kv_cache* cache, const float* k_new, const f
   if (batch > 0 && max_seq_len > 0 && (!k_new || !v_new)) return FP8KV_ERR_INVALID;
   return decode_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
                      sm_scale, out, workspace, workspace_bytes, true, stream);
+}
+
+int fp8kv_decode_noalloc(const fp8kv_cache* cache, const uint16_t* q, int32_t gqa_group,
+                         const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                         float sm_scale, float* out, void* stream) {
+  int32_t chunk = 0, splits = 0;
+  int st = fp8kv_decode_plan(cache, batch, gqa_group, max_seq_len, &chunk, &splits);
+  if (st != FP8KV_OK) return st;
+  const size_t need = fp8kv_decode_workspace_bytes(cache, batch, gqa_group, max_seq_len);
+  if (need > fp8kv::kScratchBytes) return FP8KV_ERR_TOO_LARGE;
+  if (batch == 0) return FP8KV_OK;
+  if ((st = check_device()) != FP8KV_OK) return st;
+  void* ws = nullptr;
+  if (fp8kv::scratch_address(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8KV_ERR_LAUNCH;
+  }
+  // the same two kernels as fp8kv_decode, with the partials in the scratch
+  return decode_impl(cache, nullptr, nullptr, q, gqa_group, seq_lens, batch, max_seq_len,
+                     sm_scale, out, ws, fp8kv::kScratchBytes, false, stream);
 }
 
 int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst, void* stream) {

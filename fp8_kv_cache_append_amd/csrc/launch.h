@@ -44,6 +44,12 @@ constexpr int split_wgs_per_cu(int mode, int d) {
 }
 constexpr int kComputeUnits = 256;  // MI355X
 
+// Bytes of the library-owned scratch (one copy per device) that
+// fp8kv_decode_noalloc keeps the split partials in, and its device address
+// on the current device (resolved on the first call per device, then kept).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void** ptr);
+
 hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_new,
                          const int32_t* seq_idx, const int32_t* pos, int n_tok,
                          hipStream_t stream);

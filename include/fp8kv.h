@@ -3,7 +3,8 @@
  *
  * C ABI.  Every pointer argument named as "device" is HIP device memory; the
  * caller owns every buffer.  The library allocates no device memory, keeps
- * no state between calls apart from a per-device architecture check, and
+ * no state between calls apart from a per-device architecture check (and,
+ * for fp8kv_decode_noalloc, the address of its per-device scratch), and
  * never synchronises: each call validates its arguments on the host, enqueues
  * its kernels on `stream` (a hipStream_t; NULL is the default stream) and
  * returns.  Calls are HIP-graph capturable (no allocation, no memset).
@@ -78,7 +79,8 @@ typedef enum {
   FP8KV_ERR_INVALID = -1,     /* bad argument: null pointer, shape, alignment */
   FP8KV_ERR_WORKSPACE = -2,   /* workspace smaller than the size query says  */
   FP8KV_ERR_LAUNCH = -3,      /* the HIP runtime rejected a launch           */
-  FP8KV_ERR_UNSUPPORTED = -4  /* device is not gfx950, or head_dim/G unsupported */
+  FP8KV_ERR_UNSUPPORTED = -4, /* device is not gfx950, or head_dim/G unsupported */
+  FP8KV_ERR_TOO_LARGE = -5    /* fp8kv_decode_noalloc: partials exceed its scratch */
 } fp8kv_status;
 
 /*
@@ -299,6 +301,32 @@ int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
                                 float sm_scale, int32_t chunk_tokens,
                                 int32_t n_splits, float* part_acc,
                                 float* part_ml, void* stream);
+
+/*
+ * fp8kv_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid allocation).  The same two kernels and the same plan as
+ * fp8kv_decode, so the output is bit-identical to fp8kv_decode's; the split
+ * partials live in a device array the library owns instead of a caller
+ * workspace: 64 MiB, one copy per GPU, loaded with the library's code
+ * object and held until the process ends.  No call allocates or frees.
+ *   Limit: fp8kv_decode_workspace_bytes(cache, batch, gqa_group,
+ *   max_seq_len) must be at most 64 MiB (2^26 bytes), else
+ *   FP8KV_ERR_TOO_LARGE and nothing is enqueued (e.g. 64 sequences x 8 KV
+ *   heads x G 4 x D 128 up to 32768 keys take 32.5 MiB).
+ *   Nothing in the array needs clearing between calls: every split writes
+ *   its (M, l) before the merge of the same call reads it, and an empty
+ *   split's accumulator is never read.
+ *   Calls that overlap on one GPU (other streams, other threads) share the
+ *   array and race: serialise them.  The array's address is resolved on the
+ *   first call on each device (hipGetSymbolAddress), a host-side step that
+ *   is best taken before any graph capture.
+ * Arguments, guards and other errors as for fp8kv_decode.
+ */
+int fp8kv_decode_noalloc(const fp8kv_cache* cache, const uint16_t* q,
+                         int32_t gqa_group, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_seq_len, float sm_scale, float* out,
+                         void* stream);
 
 /*
  * Causal prefill attention ([FA] 3.1): queries of sequence b are rows

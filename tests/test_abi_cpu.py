@@ -229,6 +229,25 @@ def test_narrow_qk_entries_validate_like_the_bf16_ones():
                                       FAKE, None, 0, None) == 0   # empty batch
 
 
+def test_noalloc_refuses_beyond_its_scratch_on_the_host():
+    """fp8kv_decode_noalloc refuses partials above its 64 MiB scratch before
+    touching a device, and validates like fp8kv_decode otherwise."""
+    lib = binding.lib()
+    huge = _desc(num_blocks=1, block_size=16, num_kv_heads=8, max_blocks_per_seq=1 << 16,
+                 num_seqs=64)
+    assert lib.fp8kv_decode_workspace_bytes(ctypes.byref(huge), 64, 4, 1 << 20) > 64 << 20
+    assert lib.fp8kv_decode_noalloc(ctypes.byref(huge), FAKE, 4, FAKE, 64, 1 << 20, 0.1,
+                                    FAKE, None) == -5
+    assert "scratch" in binding.strerror(-5)
+    d = _desc(num_blocks=16, block_size=2048, max_blocks_per_seq=1)
+    assert lib.fp8kv_decode_noalloc(ctypes.byref(d), FAKE, 17, FAKE, 16, 2048, 0.1, FAKE,
+                                    None) == -4
+    assert lib.fp8kv_decode_noalloc(ctypes.byref(d), FAKE, 8, FAKE, 17, 2048, 0.1, FAKE,
+                                    None) == -1
+    assert lib.fp8kv_decode_noalloc(ctypes.byref(d), FAKE, 8, FAKE, 0, 0, 0.1, FAKE,
+                                    None) == 0    # empty batch: nothing to do
+
+
 def test_pre_bias_cache_is_decode_only():
     lib = binding.lib()
     d = _desc(k_bias=FAKE)
