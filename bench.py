@@ -11,34 +11,49 @@ fp8kv_decode_merge) is timed too and reported as unfused_step_us, and the
 unfused control -- append, the whole cache dequantised to bf16 in HBM
 (fp8kv_dequantize), BF16 split + merge on the copy -- as
 dequant_then_bf16_step_us.
-The headline value is K8V8 KV bytes per step / time per step, HBM-cold: the
-step rotates over 64 copies of the cache (> 1 GB, larger than the 256 MB
-Infinity Cache), so no copy is cache-resident when it is read.  All steps of
-one rotation are captured in a HIP graph (no host launch cost inside the
-timed region).  Per-kernel durations come from HIP event pairs around each
-kernel of one more rotation, launched on the same stream right behind the
-timed replays (see DecodeBench.run).
+
+Protocol.  The headline value is K8V8 KV bytes per step / time per step,
+HBM-cold: the step rotates over 64 copies of the cache (> 1 GB, larger than
+the 256 MB Infinity Cache), so no copy is cache-resident when it is read.
+Steps are replayed from HIP graphs of one rotation (and of the remainder),
+so exactly --warmup untimed steps run, then exactly --steps timed steps
+between two events with a synchronisation on both sides (no host launch
+cost inside the timed region).  Then each step form (fused step, split
+kernel alone, three-kernel step, narrow QK, unfused control) is replayed a
+number of whole rotations, each between its own events, for the median and
+10th / 90th percentiles of the per-replay means; the roofline's duration is
+the split kernel's median.  Per-kernel durations also come from HIP event
+pairs around each kernel of one eager rotation, enqueued behind a replay.
+Before anything is timed, every timed output is checked on sampled rows
+against a plain torch / numpy fp64 reference computed from the cache bytes
+(reference_rows; parity against the oracle is the test suite's), and the
+headline step's output against the oracle's own output of the same step in
+the CPU-baseline leg.
 
 Narrow QK (fp8kv_decode_append_q8: Q quantised to e4m3 in the split kernel,
 fp8 QK) is timed on the same rotation for the e4m3-K modes
 (narrow_qk_step_us), with its output's relative L2 against the bf16-Q step
 (narrow_qk_vs_bf16q_rel_l2: the Q rounding's cost).
 
-Extra fields: the K16V8 and BF16 controls (same protocol), a device copy of
-the step's KV bytes under the same protocol (copy_floor_same_bytes: what one
-launch moving this many bytes costs here), the bulk append kernel's rate
-(append_bulk: 1M rows into a paged K8V8 cache), the op-level error
-of each quantised cache (fp8_vs_bf16_rel_l2: the step's output against the
-BF16-cache step's on the same inputs), the L2/MALL-warm
-rate (one copy, labelled), the causal prefill of 2048 tokens (28/4 heads;
-K8V8 and the BF16 cache as its matrix-core control),
-the context sweep of the same shape at 77/512/2048/8192 keys in all four
-modes (K8V16 isolates the K side) with the K8V8-vs-K16V8 break-even and the
-per-side savings against BF16, the ragged batch-64 paged workload
-(32q/8kv, lengths 1024..32768, K8V8, K16V8 and K8V8 as a pre-bias residual
-cache with the exact key bias), block-scaled K (MXK8V8) against per-row
-K8V8 with bf16 Q and with fp8 QK (block_scaled_k), the roofline of the split
-kernel and the CPU oracle as a baseline.
+Extra fields: the K16V8 and BF16 controls (same protocol); two floors for
+one launch moving the step's KV bytes under the same rotation -- a device
+copy (read + write, copy_floor_same_bytes) and a plain streaming read
+(read_floor_same_bytes); the bulk append kernel's rate (append_bulk: 1M
+rows into a paged K8V8 cache); the op-level error of each quantised cache
+(fp8_vs_bf16_rel_l2: the step's output against the BF16-cache step's on the
+same inputs); the L2/MALL-warm rate (one copy, labelled); the causal prefill
+of 2048 tokens (28/4 heads; K8V8 and the BF16 cache as its matrix-core
+control); the batch-1 4q/1kv D64 128-key step; the context sweep of the
+headline shape at 77/512/2048/8192 keys in all four modes (K8V16 isolates
+the K side) with the K8V8-vs-K16V8 break-even and the per-side savings
+against BF16; a GQA-group sweep (G 1/4/8/16 at 8192 keys) and a batch sweep
+(1/4/16/64 at 2048 keys), K8V8 against BF16; the ragged batch-64 paged
+workload (32q/8kv, lengths 1024..32768, K8V8, K16V8 and K8V8 as a pre-bias
+residual cache with the exact key bias) and a page-size sweep (16/32/64/256
+tokens) on its first 16 sequences; block-scaled K (MXK8V8) against per-row
+K8V8 with bf16 Q and with fp8 QK (block_scaled_k); the roofline of the split
+kernel and the CPU oracle as a baseline.  Rotations of the sweeps hold at
+least 1 GiB of cache (fewer copies only where a copy is tiny, labelled).
 """
 from __future__ import annotations
 
@@ -70,6 +85,213 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def pctl(samples_ms) -> dict:
+    """Median and 10th / 90th percentiles of per-replay mean times, in us."""
+    x = np.asarray(samples_ms, np.float64) * 1e3
+    return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+            "p90": float(np.percentile(x, 90)), "replays": int(x.size)}
+
+
+class GraphTimer:
+    """HIP graphs of consecutive calls fn(0), fn(1), ... over a rotation of
+    `copies` inputs: one graph of a whole rotation, and one of the remainder,
+    so that exactly n calls can be replayed (no host launch cost inside a
+    timed region; HIP cannot time events recorded inside a graph)."""
+
+    def __init__(self, torch, fn, copies: int):
+        self.torch, self.fn, self.copies = torch, fn, copies
+        self.graphs = {}
+
+    def graph(self, n: int):
+        if n not in self.graphs:
+            torch = self.torch
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n):
+                    self.fn(i)
+            torch.cuda.synchronize()
+            self.graphs[n] = g
+        return self.graphs[n]
+
+    def run(self, n_calls: int) -> None:
+        """Enqueue exactly n_calls calls (whole rotations, then the rest)."""
+        full, rest = divmod(int(n_calls), self.copies)
+        for _ in range(full):
+            self.graph(self.copies).replay()
+        if rest:
+            self.graph(rest).replay()
+
+    def time(self, n_calls: int) -> float:
+        """ms per call over exactly n_calls calls, between two events, with a
+        synchronisation on both sides."""
+        torch = self.torch
+        self.graph(self.copies)
+        if n_calls % self.copies:
+            self.graph(n_calls % self.copies)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        self.run(n_calls)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n_calls
+
+    def samples(self, replays: int) -> list:
+        """Mean ms per call of each of `replays` whole-rotation replays, each
+        between its own pair of events."""
+        torch = self.torch
+        g = self.graph(self.copies)
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / self.copies for a, b in ev]
+
+
+# ---------------------------------------------------------------------------
+# Sanity check of what is timed: a plain torch / numpy fp64 reference of the
+# attention on sampled rows, computed from the cache bytes the kernels read
+# (e4m3 codes decoded through torch's float8_e4m3fn type).  It is independent
+# of the HIP kernels and of the oracle (parity against the oracle is the test
+# suite's job); a timed kernel whose output strays from it beyond the
+# contract's figures is reported as not validated.
+
+LOG2E = 1.4426950408889634
+_E4M3 = None
+
+
+def _e4m3_values():
+    global _E4M3
+    if _E4M3 is None:
+        import torch
+        _E4M3 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(
+            torch.float8_e4m3fn).double().numpy()
+    return _E4M3
+
+
+def _bf16_round(x):
+    """fp64 -> fp32 -> bf16 (nearest even, torch) -> fp64."""
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float64)).float().to(torch.bfloat16).double().numpy()
+
+
+def _e4m3_round(x32):
+    import torch
+    return _e4m3_values()[torch.from_numpy(np.asarray(x32, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)]
+
+
+def _cache_rows(cache, b, h, n):
+    """fp64 K, V [n, D] and the per-token factors ks, vs [n] of (sequence b,
+    KV head h), read back from the cache through its block table."""
+    import torch
+    bs = int(cache.k.shape[1])
+    table = cache.block_table[b].cpu().numpy()
+    t = np.arange(n)
+    blk = torch.from_numpy(table[t // bs].astype(np.int64)).to(cache.k.device)
+    slot = torch.from_numpy((t % bs).astype(np.int64)).to(cache.k.device)
+    tab = _e4m3_values()
+
+    def side(x):
+        r = x[blk, slot, h].cpu()
+        if r.dtype == torch.uint8:
+            return tab[r.numpy().astype(np.int64)]
+        return r.double().numpy()
+
+    k, v = side(cache.k), side(cache.v)
+    # scales and K exponents are head-major within a block: [block][head][slot]
+    if cache.k_exp is not None:   # block-scaled K: 2^(E - 127) per 32 values
+        e = cache.k_exp[blk, h, slot].cpu().numpy().astype(np.float64)
+        k = k * np.repeat(np.exp2(e - 127.0), 32, axis=1)
+    ks = cache.k_scale[blk, h, slot].cpu().double().numpy() if cache.k_scale is not None \
+        else np.ones(n)
+    vs = cache.v_scale[blk, h, slot].cpu().double().numpy() if cache.v_scale is not None \
+        else np.ones(n)
+    return k, v, ks, vs
+
+
+def _query_values(qrows, narrow, mx):
+    """bf16 query rows as fp64 values and their per-row factor; narrow QK:
+    the rows quantised by the cache-row rule (per row, or per 32 values with
+    a power-of-two scale for block-scaled K)."""
+    q = qrows.astype(np.float64)
+    if not narrow:
+        return q, np.ones(q.shape[0])
+    if mx:
+        blocks = q.reshape(q.shape[0], -1, 32)
+        s = (np.abs(blocks).max(axis=2).astype(np.float32) / np.float32(448.0)).astype(np.float64)
+        m, e = np.frexp(np.maximum(s, 2.0 ** -126))
+        e = np.clip(np.where(m == 0.5, e - 1, e), -126, 127).astype(np.float64)
+        codes = _e4m3_round((blocks / np.exp2(e)[..., None]).astype(np.float32))
+        return (codes * np.exp2(e)[..., None]).reshape(q.shape), np.ones(q.shape[0])
+    qs = (np.abs(q).max(axis=1).astype(np.float32) / np.float32(448.0)).astype(np.float64)
+    safe = np.where(qs > 0, qs, 1.0)
+    codes = _e4m3_round((q.astype(np.float32) / safe[:, None].astype(np.float32)))
+    return np.where(qs[:, None] > 0, codes, 0.0), qs
+
+
+def reference_rows(cache, q_bits, group, sm_scale, items, narrow=False):
+    """items: (b, h, n_keys per query row of the head group, output row
+    index); returns fp64 [len(items), G, D] of the two-pass attention with
+    the integer log2 reference and bf16 P (v_scale folded in)."""
+    c = float(np.float32(np.float64(np.float32(sm_scale)) * LOG2E))
+    mx = cache.k_exp is not None
+    out = []
+    for b, h, n_keys, qi in items:
+        n = int(max(n_keys))
+        k, v, ks, vs = _cache_rows(cache, b, h, n)
+        rows = q_bits[qi][h * group:(h + 1) * group].astype(np.uint32) << 16
+        q, qf = _query_values(rows.view(np.float32), narrow, mx)
+        s = (q @ k.T) * ks[None, :] * qf[:, None]
+        if cache.k_bias is not None:
+            s = s + (q @ cache.k_bias[h].cpu().double().numpy())[:, None]
+        s = s * c
+        mask = np.arange(n)[None, :] < np.asarray(n_keys)[:, None]
+        s = np.where(mask, s, -np.inf)
+        m = np.ceil(s.max(axis=1, keepdims=True))
+        p = np.where(mask, np.exp2(s - m), 0.0)
+        w = _bf16_round(p * vs[None, :])
+        out.append((w @ v) / p.sum(axis=1, keepdims=True))
+    return np.stack(out)
+
+
+def check_rows(got_rows, ref_rows, gate_rel=1e-3, gate_abs=5e-3) -> dict:
+    got = np.asarray(got_rows, np.float64)
+    ref = np.asarray(ref_rows, np.float64)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+    mab = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    return {"validated": bool(rel <= gate_rel and mab <= gate_abs and np.all(np.isfinite(got))),
+            "rel_l2": rel, "max_abs": mab, "gate_rel_l2": gate_rel, "gate_max_abs": gate_abs}
+
+
+def validate_decode(cache, q, out, lens, group, sm_scale, pairs, narrow=False):
+    """The decode output `out` (device [B, Hq, D]) of sampled (sequence, KV
+    head) pairs against reference_rows."""
+    q_bits = q.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    lens = np.asarray(lens)
+    items = [(b, h, np.full(group, int(lens[b])), b) for b, h in pairs]
+    ref = reference_rows(cache, q_bits, group, sm_scale, items, narrow)
+    o = out.cpu().numpy()
+    got = np.stack([o[b, h * group:(h + 1) * group] for b, h in pairs])
+    if narrow:
+        # the fp8 matrix instruction sums its products only to ~2^-12 of their
+        # absolute sum, so narrow-QK scores carry that noise, and through
+        # rows that weigh two keys (x10 outlier values) an output can move by
+        # ~0.1; its figure is the relative L2 (the test suite gates it inside
+        # the oracle's rounding interval)
+        r = check_rows(got, ref, gate_rel=5e-3, gate_abs=float("inf"))
+    else:
+        r = check_rows(got, ref)
+    r["sample"] = f"{len(pairs)} (sequence, KV head) pairs, all their query heads"
+    return r
 
 
 class DecodeBench:
@@ -184,85 +406,64 @@ class DecodeBench:
         b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.dq_splits,
                              self.dq_pacc, self.dq_pml, self.out)
 
-    def _graph(self, fn):
-        torch = self.torch
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(self.copies):
-                fn(i)
-        torch.cuda.synchronize()
-        return g
-
     def capture(self):
+        """Eager calls first (the library's one-time device check), then a
+        graph timer per step form; graphs are captured on first use."""
         torch = self.torch
-        self.step(0)  # eager calls first: the library's one-time device check
+        self.step(0)
         self.step_unfused(0)
         torch.cuda.synchronize()
-        self.graph = self._graph(self.step)
-        self.split_graph = self._graph(self.split)
-        self.unfused_graph = self._graph(self.step_unfused)
-        self.q8_graph = None
+        T = lambda fn: GraphTimer(torch, fn, self.copies)
+        self.t_step, self.t_split, self.t_unfused = T(self.step), T(self.split), T(self.step_unfused)
+        self.t_q8 = self.t_dq = None
         if self.narrow:
             self.step_q8(0)
-            torch.cuda.synchronize()
-            self.q8_graph = self._graph(self.step_q8)
-        self.dq_graph = None
+            self.t_q8 = T(self.step_q8)
         if self.dq is not None:
             self.step_unfused_dequant(0)
-            torch.cuda.synchronize()
-            self.dq_graph = self._graph(self.step_unfused_dequant)
+            self.t_dq = T(self.step_unfused_dequant)
+        torch.cuda.synchronize()
 
-    def graph_avg_ms(self, graph, replays: int) -> float:
-        """Average time of one rotation entry of `graph` (ms), back to back."""
+    def kernel_events(self):
+        """One rotation launched eagerly with an event pair around every
+        kernel on the launch stream, enqueued while the GPU is still busy
+        with a whole-rotation replay, so no host launch gap falls inside a
+        pair: each pair brackets exactly one kernel.  Mean durations (ms) of
+        the split kernel (with the fused append) and the merge kernel."""
         torch = self.torch
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        graph.replay()
         torch.cuda.synchronize()
-        t0.record()
-        for _ in range(replays):
-            graph.replay()
-        t1.record()
+        self.t_step.graph(self.copies).replay()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(self.copies)]
+        for i in range(self.copies):
+            self.step(i, ev[i])
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / (replays * self.copies)
-
-    def split_avg_ms(self, replays: int) -> float:
-        """Average duration of one split-kernel launch: the split kernel alone
-        over the rotation, back to back in a graph, between two events."""
-        return self.graph_avg_ms(self.split_graph, replays)
-
-    def run(self, replays: int, kernel_events: bool = False):
-        """Replay the rotation `replays` times between two events (ms).
-
-        With kernel_events, one more rotation is then launched eagerly with an
-        event pair around every kernel on the launch stream.  It is enqueued
-        while the GPU is still busy with the replays, so no host launch gap
-        falls inside a pair: each pair brackets exactly one kernel."""
-        torch = self.torch
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(replays):
-            self.graph.replay()
-        t1.record()
-        ev = None
-        if kernel_events:
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                  for _ in range(self.copies)]
-            for i in range(self.copies):
-                self.step(i, ev[i])
-        torch.cuda.synchronize()
-        self.events = ev
-        return t0.elapsed_time(t1)  # ms
-
-    def kernel_ms(self):
-        """Mean per-launch durations (ms) of the split kernel (with the fused
-        append) and the merge kernel."""
-        ev = self.events
         spl = [ev[i][0].elapsed_time(ev[i][1]) for i in range(self.copies)]
         mrg = [ev[i][1].elapsed_time(ev[i][2]) for i in range(self.copies)]
         return float(np.mean(spl)), float(np.mean(mrg))
+
+    def sample_pairs(self, n=4):
+        """(sequence, KV head) pairs for the sanity check: first, last and
+        spread sequences, every KV head in turn."""
+        bsz, hkv = self.w.batch, self.w.kv_heads
+        seqs = sorted({0, bsz - 1, bsz // 2, bsz // 3})[:n]
+        return [(b, (i * 3 + 1) % hkv) for i, b in enumerate(seqs)] + [(0, 0)]
+
+    def validate(self):
+        """The fused step's output on copy 0 (and the narrow-QK step's)
+        against the torch reference on sampled rows."""
+        w, torch = self.w, self.torch
+        self.step(0)
+        torch.cuda.synchronize()
+        pairs = self.sample_pairs()
+        res = validate_decode(self.caches[0], self.q, self.out, w.lens, w.group, w.sm_scale, pairs)
+        if self.narrow:
+            self.step_q8(0)
+            torch.cuda.synchronize()
+            res["narrow_qk"] = validate_decode(self.caches[0], self.q, self.out_q8, w.lens,
+                                               w.group, w.sm_scale, pairs, narrow=True)
+            res["validated"] = res["validated"] and res["narrow_qk"]["validated"]
+        return res
 
 
 def step_output(bench):
@@ -273,20 +474,31 @@ def step_output(bench):
     return bench.out.double().clone()
 
 
-def bench_decode(mode, w, steps, warmup, copies):
+def cold_copies(mode, w, at_least=64, total=1 << 30, cap=2048) -> int:
+    """Copies in a rotation whose caches total at least 1 GiB (larger than
+    the 256 MB Infinity Cache and the eight 4 MB L2s), so that no copy is
+    resident when it is read again; capped for tiny workloads (then the
+    rotation is cache-resident and the figure is labelled so)."""
+    kv = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](w.head_dim)
+    return int(min(cap, max(at_least, math.ceil(total / max(kv, 1)))))
+
+
+def bench_decode(mode, w, steps, warmup, copies, replays=8):
+    """Warm up with exactly `warmup` steps, time exactly `steps` steps (the
+    headline figures), then `replays` whole-rotation replays of each step
+    form, each between its own events, for the median and 10th / 90th
+    percentiles.  The outputs are checked before any timing."""
     bench = DecodeBench(mode, w, copies)
     bench.capture()
-    reps = max(1, math.ceil(steps / copies))
-    bench.run(max(1, math.ceil(warmup / copies)))
-    ms = bench.run(reps, kernel_events=True)
-    n_steps = reps * copies
-    spl, mrg = bench.kernel_ms()
-    split_avg = bench.split_avg_ms(reps)
-    unfused = bench.graph_avg_ms(bench.unfused_graph, reps)
-    dq = bench.graph_avg_ms(bench.dq_graph, reps) if bench.dq_graph is not None else None
-    q8 = bench.graph_avg_ms(bench.q8_graph, reps) if bench.q8_graph is not None else None
+    valid = bench.validate()
+    bench.t_step.run(warmup)
+    step_ms = bench.t_step.time(steps)
+    spl, mrg = bench.kernel_events()
+    st = {name: pctl(t.samples(replays)) for name, t in
+          (("step", bench.t_step), ("split", bench.t_split), ("unfused", bench.t_unfused),
+           ("narrow_qk", bench.t_q8), ("dequant_then_bf16", bench.t_dq)) if t is not None}
     q8_err = None
-    if q8 is not None:
+    if bench.t_q8 is not None:
         # narrow against bf16-Q outputs of the same step on the same cache
         bench.step(0)
         bench.step_q8(0)
@@ -294,15 +506,18 @@ def bench_decode(mode, w, steps, warmup, copies):
         a = bench.out_q8.double()
         r = bench.out.double()
         q8_err = float(((a - r).norm() / r.norm()).item())
-    step_ms = ms / n_steps
-    res = {"ms_per_step": step_ms, "steps": n_steps, "kv_bytes": bench.kv_bytes,
+    res = {"ms_per_step": step_ms, "steps": int(steps), "warmup": int(warmup),
+           "kv_bytes": bench.kv_bytes,
            "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
            "kernel_us_event_pairs": {"split_with_append": spl * 1e3, "merge": mrg * 1e3},
-           "split_us": split_avg * 1e3,
-           "unfused_step_us": unfused * 1e3,
-           "dequant_then_bf16_step_us": None if dq is None else dq * 1e3,
-           "narrow_qk_step_us": None if q8 is None else q8 * 1e3,
+           "split_us": st["split"]["median"],
+           "step_us_stats": st["step"], "split_us_stats": st["split"],
+           "unfused_step_us": st["unfused"]["median"],
+           "dequant_then_bf16_step_us": st["dequant_then_bf16"]["median"]
+           if "dequant_then_bf16" in st else None,
+           "narrow_qk_step_us": st["narrow_qk"]["median"] if "narrow_qk" in st else None,
            "narrow_qk_vs_bf16q_rel_l2": q8_err,
+           "validation": valid,
            "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
     res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
     return res, bench
@@ -323,11 +538,14 @@ def bench_sweep(steps, warmup, copies, head):
             if tokens == 2048 and mode == "K8V8":
                 r = head
             else:
-                r, _ = bench_decode(mode, w, steps, warmup, copies)
+                r, _ = bench_decode(mode, w, steps, warmup, cold_copies(mode, w, copies))
             row[mode] = {"us_per_step": r["ms_per_step"] * 1e3, "split_us": r["split_us"],
                          "kv_gbs": r["kv_gbs"], "pct_roofline": r["pct_roofline"],
+                         "step_us_p10_p90": [r["step_us_stats"]["p10"], r["step_us_stats"]["p90"]],
                          "unfused_step_us": r["unfused_step_us"],
-                         "narrow_qk_step_us": r["narrow_qk_step_us"]}
+                         "narrow_qk_step_us": r["narrow_qk_step_us"],
+                         "validated": r["validation"]["validated"],
+                         "copies": cold_copies(mode, w, copies)}
         row["K8V8_speedup_vs_K16V8"] = row["K16V8"]["us_per_step"] / row["K8V8"]["us_per_step"]
         row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
         # time the BF16 control saves by storing one side in e4m3 ("Account
@@ -353,6 +571,101 @@ def bench_sweep(steps, warmup, copies, head):
                 be = round(t0 + (t1 - t0) * (-d0) / (d1 - d0))
                 break
     return {"tokens": table, "k8v8_vs_k16v8_break_even_tokens": be}
+
+
+def _row(r):
+    return {"us_per_step": r["ms_per_step"] * 1e3, "split_us": r["split_us"],
+            "kv_gbs": r["kv_gbs"], "pct_roofline": r["pct_roofline"],
+            "step_us_p10_p90": [r["step_us_stats"]["p10"], r["step_us_stats"]["p90"]],
+            "validated": r["validation"]["validated"], "split_plan": r["split_plan"]}
+
+
+def bench_gqa_sweep(steps, warmup, tokens=8192):
+    """GQA group sweep: batch 16, 2 KV heads, head_dim 128, 8192 keys, query
+    heads 2G for G = 1, 4, 8, 16; K8V8 and the BF16 control, HBM-cold."""
+    from fp8_kv_cache_append_amd import synth
+
+    res = {}
+    for g in (1, 4, 8, 16):
+        w = synth.Workload(f"decode_b16_hq{2 * g}_hkv2_d128_t{tokens}", 16, 2 * g, 2, 128,
+                           np.full(16, tokens, np.int32), "outliers", seed=2)
+        row = {}
+        for mode in ("K8V8", "BF16"):
+            r, _ = bench_decode(mode, w, steps, warmup, cold_copies(mode, w))
+            row[mode] = _row(r)
+        row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
+        res[str(g)] = row
+    return {"workload": f"decode_b16_hkv2_d128_t{tokens}, query heads 2G", "group": res}
+
+
+def bench_batch_sweep(steps, warmup, tokens=2048):
+    """Batch sweep of the 16q/2kv D128 shape at 2048 keys: batch 1, 4, 16,
+    64; K8V8 and the BF16 control, HBM-cold."""
+    from fp8_kv_cache_append_amd import synth
+
+    res = {}
+    for bsz in (1, 4, 16, 64):
+        w = synth.Workload(f"decode_b{bsz}_hq16_hkv2_d128_t{tokens}", bsz, 16, 2, 128,
+                           np.full(bsz, tokens, np.int32), "outliers", seed=2)
+        row = {}
+        for mode in ("K8V8", "BF16"):
+            r, _ = bench_decode(mode, w, steps, warmup, cold_copies(mode, w))
+            row[mode] = _row(r)
+        row["K8V8_speedup_vs_BF16"] = row["BF16"]["us_per_step"] / row["K8V8"]["us_per_step"]
+        res[str(bsz)] = row
+    return {"workload": f"decode_hq16_hkv2_d128_t{tokens}", "batch": res}
+
+
+def bench_small(steps, warmup):
+    """Batch 1, 4 query / 1 KV head, head_dim 64, 128 keys, K8V8: 17 KB of
+    cache per step, so even a rotation of 2048 copies (36 MB) stays in the
+    Infinity Cache; the step is launch- and latency-bound."""
+    from fp8_kv_cache_append_amd import synth
+
+    w = synth.decode_b1_gqa4_d64()
+    copies = cold_copies("K8V8", w)
+    r, _ = bench_decode("K8V8", w, steps, warmup, copies)
+    out = _row(r)
+    out.update({"workload": w.name, "copies": copies,
+                "cache_state": f"rotation of {copies} copies ({copies * r['kv_bytes'] / 1e6:.0f} MB)"
+                               ", Infinity-Cache resident"})
+    return out
+
+
+def bench_read_floor(nbytes: int, copies: int = 64, replays: int = 10):
+    """A plain streaming read of nbytes (the step's KV bytes) per launch, one
+    buffer per launch of a 64-buffer rotation (HBM-cold like the headline),
+    back to back in a HIP graph: what a single launch reading this many
+    bytes reaches on this device (launch, ramp and drain included).  The
+    fastest of a few grid sizes is the floor."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "hw", "libstream_read.so"))
+    lib.stream_read_launch.restype = ctypes.c_int
+    lib.stream_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+    n = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i % 251)
+            for i in range(copies)]
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    res = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        def launch(i, blocks=blocks):
+            st = lib.stream_read_launch(bufs[i].data_ptr(), n, sink.data_ptr(), blocks,
+                                        torch.cuda.current_stream().cuda_stream)
+            assert st == 0, st
+        launch(0)
+        t = GraphTimer(torch, launch, copies)
+        t.run(copies)
+        res[str(blocks)] = pctl(t.samples(replays))["median"]
+        del t
+    best = min(res, key=res.get)
+    us = res[best]
+    del bufs
+    return {"bytes_read": n, "us_per_launch": us, "read_gbs": n / (us * 1e-6) / 1e9,
+            "pct_of_8tbs": 100.0 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "work_groups": int(best), "us_by_work_groups": res}
 
 
 def bench_block_scaled(steps, copies):
@@ -403,6 +716,8 @@ def bench_block_scaled(steps, copies):
             step(0)
             torch.cuda.synchronize()
             err = float(((out.double() - ref_out.double()).norm() / ref_out.double().norm()).item())
+            valid = validate_decode(caches[0], q, out, w.lens, w.group, w.sm_scale,
+                                    [(0, 0), (7, 1), (15, 0)], narrow=(name == "fp8_qk"))
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(copies):
@@ -418,19 +733,22 @@ def bench_block_scaled(steps, copies):
             t1.record()
             torch.cuda.synchronize()
             res[f"{mode}_{name}"] = {"us_per_step": t0.elapsed_time(t1) * 1e3 / (reps * copies),
-                                     "rel_l2_vs_bf16_cache": err}
+                                     "rel_l2_vs_bf16_cache": err,
+                                     "validated": valid["validated"]}
         del caches
         torch.cuda.empty_cache()
     return {"workload": w.name + " (decode without append)", **res}
 
 
-def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
+def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None):
     """Batch 64, 32q/8kv, D128, lengths uniform in [1024, 32768], paged
-    16-token blocks behind a shuffled table, biased keys.  The cache (2.3 GB
-    K8V8, 3.4 GB K16V8) is far larger than the Infinity Cache, so one copy is
-    HBM-cold.  Filled from device-generated K/V of the same distributions.
-    pre_bias: the cache stores the keys' pre-bias residuals with the exact
-    bias in the descriptor (decode adds q . b to the scores)."""
+    16-token blocks behind a shuffled table, biased keys (or workload w of
+    that kind).  The cache (2.3 GB K8V8, 3.4 GB K16V8) is far larger than the
+    Infinity Cache, so one copy is HBM-cold.  Filled from device-generated
+    K/V of the same distributions.  pre_bias: the cache stores the keys'
+    pre-bias residuals with the exact bias in the descriptor (decode adds
+    q . b to the scores).  The step's output is checked on sampled pairs
+    before timing."""
     import torch
     from fp8_kv_cache_append_amd import binding, synth
     from fp8_kv_cache_append_amd.binding import KVCache
@@ -441,7 +759,7 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
     import gc
     gc.collect()
     torch.cuda.empty_cache()
-    w = synth.decode_b64_gqa4_ragged_paged()
+    w = synth.decode_b64_gqa4_ragged_paged() if w is None else w
     bs, table, n_blocks = synth.block_layout(w)
     cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
     if pre_bias:
@@ -467,41 +785,54 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False):
     pml = torch.empty((w.batch, w.kv_heads, splits, w.group, 2), device=dev)
     out = torch.empty((w.batch, w.q_heads, w.head_dim), device=dev)
 
-    def split():
+    def split(i=0):
         binding.fp8kv_decode_append_partial(cache, k_new, v_new, q, w.group, lens, max_len,
                                             w.sm_scale, chunk, splits, pacc, pml)
 
-    def step():
+    def step(i=0):
         split()
         binding.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, splits, pacc,
                                    pml, out)
 
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(steps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(replays):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e3 / (replays * steps)
-
-    step_us, split_us = timed(step), timed(split)
+    step()
+    torch.cuda.synchronize()
+    order = np.argsort(w.lens)
+    pairs = [(int(order[0]), 0), (int(order[-1]), w.kv_heads - 1),
+             (int(order[len(order) // 2]), w.kv_heads // 2)]
+    valid = validate_decode(cache, q, out, w.lens, w.group, w.sm_scale, pairs)
+    t_step, t_split = GraphTimer(torch, step, steps), GraphTimer(torch, split, steps)
+    t_step.run(steps)
+    step_st, split_st = pctl(t_step.samples(replays)), pctl(t_split.samples(replays))
+    step_us, split_us = step_st["median"], split_st["median"]
     kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](w.head_dim)
     return {"workload": w.name, "mode": mode + ("_pre_bias" if pre_bias else ""),
             "us_per_step": step_us, "split_us": split_us,
+            "step_us_stats": step_st, "split_us_stats": split_st,
             "kv_bytes": kv_bytes, "kv_gbs": kv_bytes / (step_us * 1e-6) / 1e9,
             "split_kv_gbs": kv_bytes / (split_us * 1e-6) / 1e9,
             "pct_roofline": 100.0 * kv_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "split_pct_roofline": 100.0 * kv_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "validation": valid,
             "split_plan": {"chunk_tokens": chunk, "n_splits": splits}}
+
+
+def bench_page_sizes(replays=10, steps=8):
+    """Page-size sweep on a subset of the ragged workload: its first 16
+    sequences (same lengths, distributions and heads), K8V8, blocks of 16,
+    32, 64 and 256 tokens behind a shuffled table."""
+    from fp8_kv_cache_append_amd import synth
+
+    base = synth.decode_b64_gqa4_ragged_paged()
+    res = {}
+    for bs in (16, 32, 64, 256):
+        w = synth.Workload(f"decode_b16_hq32_hkv8_d128_ragged_paged{bs}", 16, 32, 8, 128,
+                           base.lens[:16].copy(), "bias", block_size=bs, shuffle_blocks=True,
+                           seed=base.seed)
+        r = bench_ragged("K8V8", replays, steps, w=w)
+        res[str(bs)] = {k: r[k] for k in ("us_per_step", "split_us", "kv_gbs", "pct_roofline",
+                                           "split_pct_roofline", "split_plan")}
+        res[str(bs)]["validated"] = r["validation"]["validated"]
+    return {"workload": "first 16 sequences of the ragged batch, K8V8", "block_size": res}
 
 
 def bench_warm(mode, w, steps, copies):
@@ -509,12 +840,11 @@ def bench_warm(mode, w, steps, copies):
     labelled as such (it can exceed the HBM rate)."""
     bench = DecodeBench(mode, w, copies, warm=True)
     bench.capture()
-    bench.run(2)
-    reps = max(1, math.ceil(steps / copies))
-    ms = bench.run(reps)
-    step_ms = ms / (reps * copies)
-    return {"ms_per_step": step_ms, "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
-            "split_us": bench.split_avg_ms(reps) * 1e3}
+    bench.t_step.run(2 * copies)
+    step_ms = bench.t_step.time(steps)
+    return {"ms_per_step": step_ms, "steps": int(steps),
+            "kv_gbs": bench.kv_bytes / (step_ms * 1e-3) / 1e9,
+            "split_us": pctl(bench.t_split.samples(4))["median"]}
 
 
 def bench_copy_floor(nbytes: int, copies: int = 64, replays: int = 20):
@@ -642,9 +972,35 @@ def bench_prefill(reps=200, mode="K8V8"):
         samples.append(t0.elapsed_time(t1) / per_graph)
     us = float(np.median(samples)) * 1e3
     flops = 4.0 * w.q_heads * w.head_dim * (n * (n + 1) / 2)
+    # sanity check of the timed output on sampled query rows, every head
+    call()
+    torch.cuda.synchronize()
+    rows = [0, 63, 64, 1000, 2047]
+    g = w.group
+    items = [(0, hk, np.full(g, i + 1), i) for i in rows for hk in range(w.kv_heads)]
+    ref = reference_rows(cache, q_bits, g, w.sm_scale, items)
+    o = out.cpu().numpy()
+    got = np.stack([o[i, hk * g:(hk + 1) * g] for i in rows for hk in range(w.kv_heads)])
+    valid = check_rows(got, ref)
+    valid["sample"] = f"query rows {rows}, all heads"
     return {"workload": w.name, "mode": mode, "us": us, "tflops": flops / (us * 1e-6) / 1e12,
             "pct_mfma_peak": 100.0 * flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-            "algorithmic_gflop": flops / 1e9}
+            "us_stats": {"median": us, "p10": float(np.percentile(samples, 10)) * 1e3,
+                         "p90": float(np.percentile(samples, 90)) * 1e3,
+                         "replays": len(samples), "launches_per_replay": per_graph},
+            "validation": valid, "algorithmic_gflop": flops / 1e9}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, min_seconds=8.0):
@@ -653,7 +1009,9 @@ def cpu_baseline(w, min_seconds=8.0):
     cache is quantised once beforehand (not timed).  Timed twice: on one
     thread, and with the (sequence, KV head) units spread over the host's
     cores (up to 16, the box's share) by a thread pool -- the oracle's C
-    calls release the interpreter lock, and the units share nothing."""
+    calls release the interpreter lock, and the units share nothing.
+    Returns the record and the oracle's output of the step (fp64 [B, Hq,
+    D]), which the caller compares with the GPU step's."""
     import os
     from concurrent.futures import ThreadPoolExecutor
 
@@ -668,11 +1026,13 @@ def cpu_baseline(w, min_seconds=8.0):
         stores.append(oracle.store_rows("K8V8", k, v))
         news.append((k[-1:], v[-1:]))
     units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    result = np.full((w.batch, w.q_heads, w.head_dim), np.nan)
 
     def unit(bh):
         b, h = bh
         view = {key: np.ascontiguousarray(a[:, h]) for key, a in stores[b].items()}
-        oracle.attend_rows("K8V8", q_bits[b, h * g:(h + 1) * g], view, n, w.sm_scale)
+        result[b, h * g:(h + 1) * g] = oracle.attend_rows(
+            "K8V8", q_bits[b, h * g:(h + 1) * g], view, n, w.sm_scale)
 
     def run(workers):
         steps, t0 = 0, time.perf_counter()
@@ -701,9 +1061,11 @@ def cpu_baseline(w, min_seconds=8.0):
                              f"(16 seqs x 2 KV heads x {n} keys, K8V8), {el:.1f} s on "
                              f"{nw} thread{'s' if nw > 1 else ''}"}
     out = dict(res[workers])
+    out["cpu_model"] = cpu_model()
+    out["host_cpus"] = os.cpu_count()
     if workers > 1:
         out["single_thread"] = res[1]
-    return out
+    return out, result
 
 
 def traffic_for(kernel_hash: str, split_launches_bytes_hint=None):
@@ -719,12 +1081,28 @@ def traffic_for(kernel_hash: str, split_launches_bytes_hint=None):
     return rec.get("bytes_per_launch")
 
 
+def _validated_flags(x):
+    """Every "validated" flag anywhere in the record."""
+    if isinstance(x, dict):
+        for k, v in x.items():
+            if k == "validated" and isinstance(v, bool):
+                yield v
+            else:
+                yield from _validated_flags(v)
+    elif isinstance(x, list):
+        for v in x:
+            yield from _validated_flags(v)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=6400)
-    ap.add_argument("--warmup", type=int, default=640)
-    ap.add_argument("--copies", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=6400,
+                    help="decode steps timed for the headline (exactly this many)")
+    ap.add_argument("--warmup", type=int, default=640,
+                    help="untimed decode steps before them (exactly this many)")
+    ap.add_argument("--copies", type=int, default=64,
+                    help="cache copies in the headline's rotation (64: 1.1 GB, HBM-cold)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="K8V8 decode only (for profiling runs)")
@@ -733,26 +1111,12 @@ def main():
     ap.add_argument("--ragged-only", action="store_true",
                     help="only the ragged batch-64 paged K8V8 decode (for profiling runs)")
     args = ap.parse_args()
-    if args.ragged_only:
-        import torch
-        from fp8_kv_cache_append_amd import binding
-
-        binding.lib()
-        torch.cuda.set_device(0)
-        print(json.dumps({"ragged_b64_paged": bench_ragged("K8V8", replays=4, steps=4)}),
-              flush=True)
-        return
-    if args.prefill_only:
-        import torch
-        from fp8_kv_cache_append_amd import binding
-
-        binding.lib()
-        torch.cuda.set_device(0)
-        print(json.dumps({"prefill": bench_prefill()}), flush=True)
-        return
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has one, and the decode path "
               "has no cross-GPU step.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.copies < 1:
+        print("--steps >= 1, --warmup >= 0, --copies >= 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -760,34 +1124,67 @@ def main():
 
     binding.lib()
     torch.cuda.set_device(0)
+    t_start = time.perf_counter()
+
+    def leg(name, fn, *a, **k):
+        t0 = time.perf_counter()
+        r = fn(*a, **k)
+        print(f"[bench] {name}: {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        return r
+
+    if args.ragged_only:
+        print(json.dumps({"ragged_b64_paged": bench_ragged("K8V8", replays=4, steps=4)}),
+              flush=True)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill()}), flush=True)
+        return
+
     w = synth.decode_b16_gqa8_d128(2048)
-    head, hb = bench_decode("K8V8", w, args.steps, args.warmup, args.copies)
+    head, hb = leg("headline K8V8", bench_decode, "K8V8", w, args.steps, args.warmup,
+                   args.copies, replays=16)
     split_us = head["split_us"]
     achieved = head["kv_bytes"] / (split_us * 1e-6) / 1e9
     khash = kernel_source_hash()
     traffic = traffic_for(khash)
+    gpu_out = step_output(hb)
     extras = {}
     if not args.no_extras:
-        outs = {"K8V8": step_output(hb)}
+        sw, ww = max(640, args.steps // 4), max(64, args.warmup // 4)
+        outs = {"K8V8": gpu_out}
         for mode in ("K16V8", "BF16"):
-            r, bb = bench_decode(mode, w, args.steps, args.warmup, args.copies)
+            r, bb = leg(f"headline {mode}", bench_decode, mode, w, args.steps, args.warmup,
+                        args.copies)
             extras[mode] = r
             outs[mode] = step_output(bb)
             del bb
         ref = outs["BF16"]
         extras["fp8_vs_bf16"] = {
             m: float(((outs[m] - ref).norm() / ref.norm()).item()) for m in ("K8V8", "K16V8")}
-        extras["K8V8_warm"] = bench_warm("K8V8", w, args.steps, args.copies)
-        extras["copy_floor"] = bench_copy_floor(head["kv_bytes"])
-        extras["append_bulk"] = bench_append_bulk()
-        extras["prefill"] = bench_prefill()
-        extras["prefill_bf16"] = bench_prefill(mode="BF16")
-        extras["sweep"] = bench_sweep(max(640, args.steps // 4), max(64, args.warmup // 4),
-                                      args.copies, head)
-        extras["ragged"] = {m: bench_ragged(m) for m in ("K8V8", "K16V8")}
-        extras["ragged"]["K8V8_pre_bias"] = bench_ragged("K8V8", pre_bias=True)
-        extras["block_scaled"] = bench_block_scaled(max(640, args.steps // 4), args.copies)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+        del hb
+        extras["K8V8_warm"] = leg("warm", bench_warm, "K8V8", w, args.steps, args.copies)
+        extras["copy_floor"] = leg("copy floor", bench_copy_floor, head["kv_bytes"])
+        extras["read_floor"] = leg("read floor", bench_read_floor, head["kv_bytes"])
+        extras["append_bulk"] = leg("append bulk", bench_append_bulk)
+        extras["prefill"] = leg("prefill K8V8", bench_prefill)
+        extras["prefill_bf16"] = leg("prefill BF16", bench_prefill, mode="BF16")
+        extras["small"] = leg("config 1", bench_small, sw, ww)
+        extras["sweep"] = leg("context sweep", bench_sweep, sw, ww, args.copies, head)
+        extras["gqa"] = leg("GQA sweep", bench_gqa_sweep, sw, ww)
+        extras["batch"] = leg("batch sweep", bench_batch_sweep, sw, ww)
+        extras["ragged"] = {m: leg(f"ragged {m}", bench_ragged, m) for m in ("K8V8", "K16V8")}
+        extras["ragged"]["K8V8_pre_bias"] = leg("ragged pre-bias", bench_ragged, "K8V8",
+                                                pre_bias=True)
+        extras["page_sizes"] = leg("page sizes", bench_page_sizes)
+        extras["block_scaled"] = leg("block-scaled K", bench_block_scaled, sw, args.copies)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, orc = leg("cpu baseline", cpu_baseline, w)
+        # the oracle's own output of the step (this leg) against the GPU's
+        got = gpu_out.cpu().numpy()
+        cpu["oracle_vs_gpu_step"] = {
+            "rel_l2": float(np.linalg.norm(got - orc) / np.linalg.norm(orc)),
+            "max_abs": float(np.max(np.abs(got - orc)))}
 
     rec = {
         "metric": "KV-cache GB/s (% of 8 TB/s) and us/decode step, K8/V8 vs K16/V8 vs BF16",
@@ -795,7 +1192,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": head["steps"],
-        "warmup": args.warmup,
+        "warmup": head["warmup"],
         "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -812,25 +1209,30 @@ def main():
                    "split_plan": head["split_plan"]},
         "us_per_step": head["ms_per_step"] * 1e3,
         "pct_roofline": head["pct_roofline"],
+        "step_us_stats": head["step_us_stats"],
         "split_us": head["split_us"],
+        "split_us_stats": head["split_us_stats"],
         "kernel_us_event_pairs": head["kernel_us_event_pairs"],
         "unfused_step_us": head["unfused_step_us"],
         "dequant_then_bf16_step_us": head["dequant_then_bf16_step_us"],
         "narrow_qk_step_us": head["narrow_qk_step_us"],
         "narrow_qk_vs_bf16q_rel_l2": head["narrow_qk_vs_bf16q_rel_l2"],
+        "validation": head["validation"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_partial_kernel<K8V8,128,append,one tile per wave>",
                      "bytes_per_launch": head["kv_bytes"],
+                     "duration_us": "median of per-replay means (split_us_stats)",
                      "kernel_source_hash": khash},
         "cpu_baseline": cpu,
     }
     if extras:
         keys = ("ms_per_step", "kv_gbs", "pct_roofline", "split_us", "kernel_us_event_pairs",
-                "unfused_step_us")
+                "unfused_step_us", "step_us_stats")
         rec["modes"] = {"K8V8": {k: head[k] for k in keys}}
         for mode in ("K16V8", "BF16"):
             rec["modes"][mode] = {k: extras[mode][k] for k in keys}
+            rec["modes"][mode]["validated"] = extras[mode]["validation"]["validated"]
         rec["speedup_vs_bf16"] = extras["BF16"]["ms_per_step"] / head["ms_per_step"]
         rec["speedup_vs_k16v8"] = extras["K16V8"]["ms_per_step"] / head["ms_per_step"]
         # op-level error of the quantised caches: the GPU step's output
@@ -838,12 +1240,19 @@ def main():
         rec["fp8_vs_bf16_rel_l2"] = extras["fp8_vs_bf16"]
         rec["warm_l2_mall"] = extras["K8V8_warm"]
         rec["copy_floor_same_bytes"] = extras["copy_floor"]
+        rec["read_floor_same_bytes"] = extras["read_floor"]
         rec["append_bulk"] = extras["append_bulk"]
         rec["prefill"] = extras["prefill"]
         rec["prefill_bf16_control"] = extras["prefill_bf16"]
+        rec["decode_b1_hq4_hkv1_d64_t128"] = extras["small"]
         rec["context_sweep"] = extras["sweep"]
+        rec["gqa_sweep"] = extras["gqa"]
+        rec["batch_sweep"] = extras["batch"]
         rec["ragged_b64_paged"] = extras["ragged"]
+        rec["page_size_sweep"] = extras["page_sizes"]
         rec["block_scaled_k"] = extras["block_scaled"]
+        rec["all_timed_outputs_validated"] = bool(all(_validated_flags(rec)))
+    rec["bench_wall_s"] = time.perf_counter() - t_start
     print(json.dumps(rec), flush=True)
 
 

@@ -128,8 +128,9 @@ class KVCache:
     """A paged cache in device memory plus its C descriptor.
 
     k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
-    k_scale, v_scale: float32 [num_blocks, block_size, Hkv] for an e4m3 side,
-    else None;
+    k_scale, v_scale: float32 [num_blocks, Hkv, block_size] (head-major within
+    a block) for an e4m3 side, else None; k_exp: uint8 [num_blocks, Hkv,
+    block_size, D / 32] for block-scaled K, else None;
     block_table: int32 [batch, max_blocks_per_seq]; with table_in_memory False
     the descriptor passes no table and the library computes the contiguous
     ids b * max_blocks_per_seq + e (block_table then only gives the shape);
@@ -154,9 +155,11 @@ class KVCache:
         k8, v8, kmx = mode in K_E4M3, mode in V_E4M3, mode in K_MX
         k = torch.zeros(shape, dtype=torch.uint8 if k8 else torch.bfloat16, device=device)
         v = torch.zeros(shape, dtype=torch.uint8 if v8 else torch.bfloat16, device=device)
-        ks = torch.zeros(shape[:3], dtype=torch.float32, device=device) if k8 and not kmx else None
-        vs = torch.zeros(shape[:3], dtype=torch.float32, device=device) if v8 else None
-        kx = torch.zeros(shape[:3] + (head_dim // 32,), dtype=torch.uint8,
+        # scales and K exponents are head-major within a block
+        sshape = (num_blocks, num_kv_heads, block_size)
+        ks = torch.zeros(sshape, dtype=torch.float32, device=device) if k8 and not kmx else None
+        vs = torch.zeros(sshape, dtype=torch.float32, device=device) if v8 else None
+        kx = torch.zeros(sshape + (head_dim // 32,), dtype=torch.uint8,
                          device=device) if kmx else None
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
         if not table_in_memory:

@@ -3,6 +3,11 @@
 // Storage rule ("kadirnar/kernel-agent/fp8-kv-cache", section "Storage"):
 // one fp32 scale per (token, KV head) row, scale = amax(|row|) / 448 over the
 // head dimension, codes in e4m3, written at append and never re-quantised.
+// Codes are token-major within a block ([block][slot][head][d]); scales are
+// head-major within a block ([block][head][slot]), so the scales one KV head
+// reads for a run of tokens are contiguous and no cache line of scales is
+// shared by the heads ("FP8 KV attention: hardware paths and tile
+// preparation", "Store the preferred cache layout once").
 //
 // Mapping: a row of D fp32 values is read by D/4 lanes with one 16-byte load
 // each (32 lanes for D = 128, 16 for D = 64), so a wave covers the K row and
@@ -92,18 +97,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const uint32_t h = pair[k] - (pair[k] / hkv) * hkv;
     const uint32_t slot = (uint32_t)p[k] - ((uint32_t)p[k] / bs) * bs;
     const int64_t row = ((int64_t)blk[k] * a.bs + slot) * a.hkv + h;
+    const int64_t srow = ((int64_t)blk[k] * a.hkv + h) * a.bs + slot;  // head-major scales
     const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
     if (k_is_mx(MODE) && !is_v) {
       // block-scaled K: eight lanes hold a block of 32 values
       const int e = mx_exponent(row_amax<8>(x[k]));
       uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], e8m0_value((uint32_t)(e + 127)));
-      if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
+      if ((sub & 7) == 0) a.kexp[srow * (D / 32) + sub / 8] = (uint8_t)(e + 127);
     } else if (quantise) {
       const float scale = row_amax<kLanesPerRow>(x[k]) / kE4M3Max;  // correctly rounded
       uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], scale);
-      if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
+      if (sub == 0) (is_v ? a.vs : a.ks)[srow] = scale;
     } else {
       uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x[k]);

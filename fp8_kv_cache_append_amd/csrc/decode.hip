@@ -148,7 +148,7 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
                                           int e_base, int h, int lane, bool live) {
   using T = TileRegs<MODE, D>;
-  int64_t row0[4];
+  int64_t row0[4], srow0[4];
   bool blk_ok[4];
   bool all_ok = t0 + 64 <= t_end;
 #pragma unroll
@@ -158,7 +158,12 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
     blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
     all_ok = all_ok && blk_ok[kb];
+    // codes: token-major rows (block * bs + slot) * hkv + h; scales:
+    // head-major (block * hkv + h) * bs + slot, so a sub-block's 16 scales
+    // are contiguous and the other heads' lines are never fetched
     row0[kb] = blk_ok[kb] ? ((int64_t)blk * a.bs + (tb - eb * a.bs)) * a.hkv + h : h;
+    srow0[kb] = blk_ok[kb] ? ((int64_t)blk * a.hkv + h) * a.bs + (tb - eb * a.bs)
+                           : (int64_t)h * a.bs;
   }
   if constexpr (PART != 1) {
 #pragma unroll
@@ -170,12 +175,12 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     // values are picked with selects: indexing the arrays with it would
     // move them to scratch memory.
     const int kb = lane >> 4;
-    const int64_t base = kb == 0 ? row0[0] : kb == 1 ? row0[1] : kb == 2 ? row0[2] : row0[3];
+    const int64_t base = kb == 0 ? srow0[0] : kb == 1 ? srow0[1] : kb == 2 ? srow0[2] : srow0[3];
     const bool bok = kb == 0 ? blk_ok[0] : kb == 1 ? blk_ok[1] : kb == 2 ? blk_ok[2]
                                                                          : blk_ok[3];
     r.tok_ok = t0 + lane < t_end && bok;
-    // (a tile that is not live reads the scales of row h, in block 0)
-    const int64_t rr = live ? base + (int64_t)((lane & 15) * a.hkv) : (int64_t)h;
+    // (a tile that is not live reads the scales of head h's slot 0 in block 0)
+    const int64_t rr = live ? base + (int64_t)(lane & 15) : (int64_t)h * a.bs;
     r.ks = T::KS ? a.ks[rr] : 1.0f;
     if constexpr (T::MX)  // the row's E8M0 bytes (D / 32 of them)
       r.kxw = D == 128 ? *reinterpret_cast<const uint32_t*>(a.kexp + rr * 4)
@@ -297,9 +302,10 @@ void decode_partial_kernel(DecodeArgs a) {
   __shared__ uint32_t s_qx[Q8 && k_is_mx(MODE) ? 16 : 1][4];
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
-  __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 6 : 1];
   //   s_new[D], s_new[D+1]: K and V scale; s_new[D+2], s_new[D+3]: the
-  //   slot's cache row (low, high word; high word ~0u: not stored)
+  //   slot's cache row (low, high word; high word ~0u: not stored);
+  //   s_new[D+4], s_new[D+5]: the index of its scales (head-major)
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -497,6 +503,9 @@ void decode_partial_kernel(DecodeArgs a) {
                               : -1;  // invalid block: not stored, key excluded
       s_new[D + 2] = (uint32_t)row;
       s_new[D + 3] = (uint32_t)((uint64_t)row >> 32);
+      const int64_t srow = row < 0 ? -1 : ((int64_t)blk * a.hkv + h) * a.bs + p % a.bs;
+      s_new[D + 4] = (uint32_t)srow;
+      s_new[D + 5] = (uint32_t)((uint64_t)srow >> 32);
     }
     if (lane < 2 * kLR) {
       // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
@@ -527,7 +536,9 @@ void decode_partial_kernel(DecodeArgs a) {
       uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
       *reinterpret_cast<uint32_t*>(dst + 4 * sub) = img[sub];
       if (sub == 0)
-        const_cast<float*>(is_v ? a.vs : a.ks)[row] = __uint_as_float(s_new[D + (is_v ? 1 : 0)]);
+        const_cast<float*>(is_v ? a.vs : a.ks)[(int64_t)(((uint64_t)s_new[D + 5] << 32) |
+                                                          (uint64_t)s_new[D + 4])] =
+            __uint_as_float(s_new[D + (is_v ? 1 : 0)]);
     } else {
       uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
       *reinterpret_cast<u32x2_t*>(dst + 4 * sub) = *reinterpret_cast<const u32x2_t*>(img + 2 * sub);

@@ -264,11 +264,13 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
       okk = (t_k < kv_end) && ((unsigned)id_k < (unsigned)a.num_blocks);
       const int64_t slot = okk ? (int64_t)id_k * a.bs + 16 * r_k + kin : 0;
       const int64_t row = slot * a.hkv + hk;
+      // scales are head-major within a block: [block][head][slot]
+      const int64_t srow = okk ? ((int64_t)id_k * a.hkv + hk) * a.bs + 16 * r_k + kin : 0;
       const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * S::KBYTES + spart * (S::KBYTES / 4);
 #pragma unroll
       for (int i = 0; i < S::KW; ++i) kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
-      if (S::K8) ksreg = a.ks[row];
-      if (S::V8) vsreg = a.vs[row];
+      if (S::K8) ksreg = a.ks[srow];
+      if (S::V8) vsreg = a.vs[srow];
     }
     okv = 0;
 #pragma unroll

@@ -85,21 +85,25 @@ typedef enum {
 
 /*
  * Paged KV cache descriptor (all pointers device memory, owned by the
- * caller).  Layout, token-major within a block:
+ * caller).  Layout: codes token-major within a block, scales head-major
+ * within a block (the scales one KV head reads for a run of tokens are
+ * contiguous, so no cache line of scales is shared by two heads; [HW]
+ * "Store the preferred cache layout once"):
  *   k, v            [num_blocks][block_size][num_kv_heads][head_dim]
  *                   K8V8: uint8 codes for both; K16V8: k bf16, v uint8;
  *                   BF16: bf16 for both; K8V16: k uint8, v bf16
- *   k_scale         [num_blocks][block_size][num_kv_heads] fp32, K8V8 and
+ *   k_scale         [num_blocks][num_kv_heads][block_size] fp32, K8V8 and
  *                   K8V16 (NULL otherwise)
  *   k_exp           MXK8V8 only (NULL otherwise): uint8
- *                   [num_blocks][block_size][num_kv_heads][head_dim / 32], the
+ *                   [num_blocks][num_kv_heads][block_size][head_dim / 32], the
  *                   byte E + 127 of each 32-value K block, 4-byte aligned.
  *                   Decode reads it with bf16 Q (codes converted by their
  *                   block's scale) or with block-scaled Q through the q8
  *                   entries (the matrix instruction applies both operands'
  *                   block scales); the fused append, prefill, dequantize and
  *                   a K bias give FP8KV_ERR_UNSUPPORTED for such a cache.
- *   v_scale         same shape, K8V8 and K16V8 (NULL otherwise)
+ *   v_scale         [num_blocks][num_kv_heads][block_size] fp32, K8V8 and
+ *                   K16V8 (NULL otherwise)
  *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
  *                   b is slot t % block_size of block
  *                   block_table[b * max_blocks_per_seq + t / block_size].
@@ -108,8 +112,8 @@ typedef enum {
  *                   read, so the first K/V loads need not wait for one;
  *                   num_seqs * max_blocks_per_seq must fit an int32 and
  *                   be at most num_blocks, else FP8KV_ERR_INVALID).
- * A contiguous cache [B][T][Hkv][D] is block_size = T, max_blocks_per_seq = 1
- * and block_table NULL (or block_table[b] = b).
+ * A contiguous cache [B][T][Hkv][D] (scales [B][Hkv][T]) is block_size = T,
+ * max_blocks_per_seq = 1 and block_table NULL (or block_table[b] = b).
  *   k_bias          NULL, or fp32 [num_kv_heads][head_dim], 16-byte aligned:
  *                   a pre-bias residual cache ([HW] "Treat numerical safety
  *                   and kernel speed as separate gates"; [FQ] "Bias-aware

@@ -46,20 +46,23 @@ def read_rows(cache: KVCache, b: int, n: int) -> dict:
     slot = torch.from_numpy((t % bs).astype(np.int64)).to(DEV)
     out = {}
 
-    def grab(x):
+    def grab(x):        # codes: [block][slot][head][...]
         return x[blk, slot].cpu()
+
+    def grab_scale(x):  # scales and K exponents: [block][head][slot][...]
+        return x[blk, :, slot].cpu()
 
     if cache.mode in binding.K_MX:
         out["k8"] = grab(cache.k).numpy()
-        out["kx"] = grab(cache.k_exp).numpy()
+        out["kx"] = grab_scale(cache.k_exp).numpy()
     elif cache.mode in binding.K_E4M3:
         out["k8"] = grab(cache.k).numpy()
-        out["ks"] = grab(cache.k_scale).numpy()
+        out["ks"] = grab_scale(cache.k_scale).numpy()
     else:
         out["k16"] = grab(cache.k).view(torch.int16).numpy().view(np.uint16)
     if cache.mode in binding.V_E4M3:
         out["v8"] = grab(cache.v).numpy()
-        out["vs"] = grab(cache.v_scale).numpy()
+        out["vs"] = grab_scale(cache.v_scale).numpy()
     else:
         out["v16"] = grab(cache.v).view(torch.int16).numpy().view(np.uint16)
     return out

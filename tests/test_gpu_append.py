@@ -86,7 +86,8 @@ def test_append_leaves_other_slots_untouched():
         written[table[1, t // 16], t % 16] = True
     kk = cache.k.cpu().numpy()
     assert np.all(kk[~written] == 0)
-    assert np.all(cache.k_scale.cpu().numpy()[~written] == 0)
+    # scales are head-major within a block: [block][head][slot]
+    assert np.all(cache.k_scale.cpu().numpy().transpose(0, 2, 1)[~written] == 0)
     assert np.any(kk[written] != 0)
 
 
@@ -150,7 +151,7 @@ def test_append_exhaustive_e4m3_encoding():
                 x[:, 0, 1:] = xt
                 binding.fp8kv_append(cache, x, x, seq, pos)
                 codes = cache.k[0, :n_rows, 0, 1:].cpu().numpy().reshape(-1)[:n]
-                assert np.all(cache.k_scale[0, :n_rows, 0].cpu().numpy() == 1.0)
+                assert np.all(cache.k_scale[0, 0, :n_rows].cpu().numpy() == 1.0)
                 jobs.append(pool.submit(check, bits, codes))
                 if len(jobs) > 24:
                     bad += sum(j.result() for j in jobs)
