@@ -193,28 +193,28 @@ def _cache_rows(cache, b, h, n):
     """fp64 K, V [n, D] and the per-token factors ks, vs [n] of (sequence b,
     KV head h), read back from the cache through its block table."""
     import torch
-    bs = int(cache.k.shape[1])
+    bs = cache.block_size
     table = cache.block_table[b].cpu().numpy()
     t = np.arange(n)
     blk = torch.from_numpy(table[t // bs].astype(np.int64)).to(cache.k.device)
     slot = torch.from_numpy((t % bs).astype(np.int64)).to(cache.k.device)
     tab = _e4m3_values()
 
+    def row(x):  # rows of a block: [slot][head] or [head][slot]
+        return x[blk, slot, h] if cache.layout == "token" else x[blk, h, slot]
+
     def side(x):
-        r = x[blk, slot, h].cpu()
+        r = row(x).cpu()
         if r.dtype == torch.uint8:
             return tab[r.numpy().astype(np.int64)]
         return r.double().numpy()
 
     k, v = side(cache.k), side(cache.v)
-    # scales and K exponents are head-major within a block: [block][head][slot]
     if cache.k_exp is not None:   # block-scaled K: 2^(E - 127) per 32 values
-        e = cache.k_exp[blk, h, slot].cpu().numpy().astype(np.float64)
+        e = row(cache.k_exp).cpu().numpy().astype(np.float64)
         k = k * np.repeat(np.exp2(e - 127.0), 32, axis=1)
-    ks = cache.k_scale[blk, h, slot].cpu().double().numpy() if cache.k_scale is not None \
-        else np.ones(n)
-    vs = cache.v_scale[blk, h, slot].cpu().double().numpy() if cache.v_scale is not None \
-        else np.ones(n)
+    ks = row(cache.k_scale).cpu().double().numpy() if cache.k_scale is not None else np.ones(n)
+    vs = row(cache.v_scale).cpu().double().numpy() if cache.v_scale is not None else np.ones(n)
     return k, v, ks, vs
 
 
@@ -297,7 +297,7 @@ def validate_decode(cache, q, out, lens, group, sm_scale, pairs, narrow=False):
 class DecodeBench:
     """Rotating copies of one decode workload plus the graph of one rotation."""
 
-    def __init__(self, mode: str, w, copies: int, warm: bool = False):
+    def __init__(self, mode: str, w, copies: int, warm: bool = False, layout: str = "token"):
         import torch
         from fp8_kv_cache_append_amd import binding, synth
         from fp8_kv_cache_append_amd.binding import KVCache
@@ -310,7 +310,7 @@ class DecodeBench:
         # a contiguous cache is passed without a table (the library computes the ids)
         mem_table = w.block_size != 0
         base = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev,
-                                table_in_memory=mem_table)
+                                table_in_memory=mem_table, layout=layout)
         last_k, last_v = [], []
         for b in range(w.batch):
             k, v = synth.kv_sequence(w, b)
@@ -323,7 +323,8 @@ class DecodeBench:
         self.caches = [base] + [KVCache(mode, base.k.clone(), base.v.clone(),
                                         None if base.k_scale is None else base.k_scale.clone(),
                                         None if base.v_scale is None else base.v_scale.clone(),
-                                        base.block_table, table_in_memory=mem_table)
+                                        base.block_table, table_in_memory=mem_table,
+                                        layout=base.layout)
                                 for _ in range(n_copies - 1)]
         # the new token of each sequence, appended at its last position
         self.k_new = torch.from_numpy(np.stack(last_k)).to(dev)
@@ -352,7 +353,7 @@ class DecodeBench:
             # the unfused control: the cache dequantised to bf16 in HBM, then
             # the BF16 kernels on the copy
             self.dq = KVCache.allocate("BF16", n_blocks, bs, w.kv_heads, d, table, dev,
-                                       table_in_memory=mem_table)
+                                       table_in_memory=mem_table, layout=layout)
             self.dq_chunk, self.dq_splits = binding.fp8kv_decode_plan(self.dq, w.batch, g, n)
             self.dq_pacc = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, d), device=dev)
             self.dq_pml = torch.empty((w.batch, w.kv_heads, self.dq_splits, g, 2), device=dev)
@@ -483,12 +484,12 @@ def cold_copies(mode, w, at_least=64, total=1 << 30, cap=2048) -> int:
     return int(min(cap, max(at_least, math.ceil(total / max(kv, 1)))))
 
 
-def bench_decode(mode, w, steps, warmup, copies, replays=8):
+def bench_decode(mode, w, steps, warmup, copies, replays=8, layout="token"):
     """Warm up with exactly `warmup` steps, time exactly `steps` steps (the
     headline figures), then `replays` whole-rotation replays of each step
     form, each between its own events, for the median and 10th / 90th
     percentiles.  The outputs are checked before any timing."""
-    bench = DecodeBench(mode, w, copies)
+    bench = DecodeBench(mode, w, copies, layout=layout)
     bench.capture()
     valid = bench.validate()
     bench.t_step.run(warmup)
@@ -517,7 +518,7 @@ def bench_decode(mode, w, steps, warmup, copies, replays=8):
            if "dequant_then_bf16" in st else None,
            "narrow_qk_step_us": st["narrow_qk"]["median"] if "narrow_qk" in st else None,
            "narrow_qk_vs_bf16q_rel_l2": q8_err,
-           "validation": valid,
+           "validation": valid, "layout": layout,
            "split_plan": {"chunk_tokens": bench.chunk, "n_splits": bench.splits}}
     res["pct_roofline"] = 100.0 * res["kv_gbs"] / HBM_PEAK_GBS
     return res, bench
@@ -707,7 +708,7 @@ def bench_block_scaled(steps, copies):
                                    None if base.k_scale is None else base.k_scale.clone(),
                                    base.v_scale.clone(), base.block_table, None,
                                    None if base.k_exp is None else base.k_exp.clone(),
-                                   False)
+                                   False, base.layout)
                            for _ in range(copies - 1)]
         out = torch.empty_like(ref_out)
         for name, fn in (("bf16_q", binding.fp8kv_decode), ("fp8_qk", binding.fp8kv_decode_q8)):
@@ -740,7 +741,7 @@ def bench_block_scaled(steps, copies):
     return {"workload": w.name + " (decode without append)", **res}
 
 
-def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None):
+def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None, layout="token"):
     """Batch 64, 32q/8kv, D128, lengths uniform in [1024, 32768], paged
     16-token blocks behind a shuffled table, biased keys (or workload w of
     that kind).  The cache (2.3 GB K8V8, 3.4 GB K16V8) is far larger than the
@@ -761,7 +762,8 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None):
     torch.cuda.empty_cache()
     w = synth.decode_b64_gqa4_ragged_paged() if w is None else w
     bs, table, n_blocks = synth.block_layout(w)
-    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev)
+    cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, dev,
+                             layout=layout)
     if pre_bias:
         cache.k_bias = torch.from_numpy(synth.kv_sequence_prebias(w, 0)[2]).to(dev)
     k_last, v_last = [], []
@@ -806,7 +808,7 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None):
     step_us, split_us = step_st["median"], split_st["median"]
     kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](w.head_dim)
     return {"workload": w.name, "mode": mode + ("_pre_bias" if pre_bias else ""),
-            "us_per_step": step_us, "split_us": split_us,
+            "layout": layout, "us_per_step": step_us, "split_us": split_us,
             "step_us_stats": step_st, "split_us_stats": split_st,
             "kv_bytes": kv_bytes, "kv_gbs": kv_bytes / (step_us * 1e-6) / 1e9,
             "split_kv_gbs": kv_bytes / (split_us * 1e-6) / 1e9,
@@ -926,7 +928,7 @@ def bench_append_bulk(n_tok: int = 131072, replays: int = 10):
     return res
 
 
-def bench_prefill(reps=200, mode="K8V8"):
+def bench_prefill(reps=200, mode="K8V8", layout="token"):
     import torch
     from fp8_kv_cache_append_amd import binding, synth
     from fp8_kv_cache_append_amd.binding import KVCache
@@ -935,7 +937,7 @@ def bench_prefill(reps=200, mode="K8V8"):
     n = int(w.lens[0])
     bs, table, n_blocks = synth.block_layout(w)
     cache = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, "cuda",
-                             table_in_memory=False)   # contiguous
+                             table_in_memory=False, layout=layout)   # contiguous
     k, v = synth.kv_sequence(w, 0)
     binding.fp8kv_append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
                          torch.zeros(n, dtype=torch.int32, device="cuda"),

@@ -21,6 +21,8 @@ K_E4M3 = ("K8V8", "K8V16", "MXK8V8")  # K side: uint8 e4m3 codes (else bf16)
 V_E4M3 = ("K8V8", "K16V8", "MXK8V8")  # V side: uint8 e4m3 codes + fp32 scale (else bf16)
 K_MX = ("MXK8V8",)                     # K codes with an E8M0 byte per 32 values (k_exp)
 
+LAYOUTS = {"token": 0, "head": 1}   # row order in a block: [slot][head] or [head][slot]
+
 FP8KV_OK = 0
 FP8KV_ERR_INVALID = -1
 FP8KV_ERR_WORKSPACE = -2
@@ -50,7 +52,7 @@ class CacheDesc(ctypes.Structure):
                 ("num_seqs", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("k_bias", ctypes.c_void_p),
-                ("k_exp", ctypes.c_void_p)]
+                ("k_exp", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -127,10 +129,12 @@ def _stream(stream):
 class KVCache:
     """A paged cache in device memory plus its C descriptor.
 
-    k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, block_size, Hkv, D];
-    k_scale, v_scale: float32 [num_blocks, Hkv, block_size] (head-major within
-    a block) for an e4m3 side, else None; k_exp: uint8 [num_blocks, Hkv,
-    block_size, D / 32] for block-scaled K, else None;
+    layout "token" (rows of a block in [slot][head] order) or "head"
+    ([head][slot]); with R the block's rows in that order, shaped
+    (block_size, Hkv) or (Hkv, block_size):
+    k, v: uint8 (e4m3 codes) or bfloat16 [num_blocks, *R, D];
+    k_scale, v_scale: float32 [num_blocks, *R] for an e4m3 side, else None;
+    k_exp: uint8 [num_blocks, *R, D / 32] for block-scaled K, else None;
     block_table: int32 [batch, max_blocks_per_seq]; with table_in_memory False
     the descriptor passes no table and the library computes the contiguous
     ids b * max_blocks_per_seq + e (block_table then only gives the shape);
@@ -146,17 +150,20 @@ class KVCache:
     k_bias: torch.Tensor | None = None
     k_exp: torch.Tensor | None = None
     table_in_memory: bool = True   # False: pass no table (contiguous layout)
+    layout: str = "token"
 
     @classmethod
     def allocate(cls, mode: str, num_blocks: int, block_size: int, num_kv_heads: int,
                  head_dim: int, block_table, device="cuda",
-                 table_in_memory: bool = True) -> "KVCache":
-        shape = (num_blocks, block_size, num_kv_heads, head_dim)
+                 table_in_memory: bool = True, layout: str = "token") -> "KVCache":
+        if layout not in LAYOUTS:
+            raise ValueError(layout)
+        rows = (block_size, num_kv_heads) if layout == "token" else (num_kv_heads, block_size)
+        shape = (num_blocks, *rows, head_dim)
         k8, v8, kmx = mode in K_E4M3, mode in V_E4M3, mode in K_MX
         k = torch.zeros(shape, dtype=torch.uint8 if k8 else torch.bfloat16, device=device)
         v = torch.zeros(shape, dtype=torch.uint8 if v8 else torch.bfloat16, device=device)
-        # scales and K exponents are head-major within a block
-        sshape = (num_blocks, num_kv_heads, block_size)
+        sshape = (num_blocks, *rows)
         ks = torch.zeros(sshape, dtype=torch.float32, device=device) if k8 and not kmx else None
         vs = torch.zeros(sshape, dtype=torch.float32, device=device) if v8 else None
         kx = torch.zeros(sshape + (head_dim // 32,), dtype=torch.uint8,
@@ -167,7 +174,7 @@ class KVCache:
             want = torch.arange(bt.numel(), dtype=torch.int32, device=device).view(bt.shape)
             if not torch.equal(bt, want):
                 raise ValueError("table_in_memory=False needs the contiguous table")
-        return cls(mode, k, v, ks, vs, bt, None, kx, table_in_memory)
+        return cls(mode, k, v, ks, vs, bt, None, kx, table_in_memory, layout)
 
     @property
     def head_dim(self) -> int:
@@ -175,16 +182,20 @@ class KVCache:
 
     @property
     def num_kv_heads(self) -> int:
-        return int(self.k.shape[2])
+        return int(self.k.shape[2] if self.layout == "token" else self.k.shape[1])
+
+    @property
+    def block_size(self) -> int:
+        return int(self.k.shape[1] if self.layout == "token" else self.k.shape[2])
 
     def desc(self) -> CacheDesc:
-        return CacheDesc(MODES[self.mode], int(self.k.shape[0]), int(self.k.shape[1]),
-                         int(self.k.shape[2]), int(self.k.shape[3]),
+        return CacheDesc(MODES[self.mode], int(self.k.shape[0]), self.block_size,
+                         self.num_kv_heads, self.head_dim,
                          int(self.block_table.shape[1]), int(self.block_table.shape[0]),
                          _ptr(self.k), _ptr(self.v),
                          _ptr(self.k_scale), _ptr(self.v_scale),
                          _ptr(self.block_table) if self.table_in_memory else None,
-                         _ptr(self.k_bias), _ptr(self.k_exp))
+                         _ptr(self.k_bias), _ptr(self.k_exp), LAYOUTS[self.layout])
 
 
 def fp8kv_append(cache: KVCache, k_new, v_new, seq_idx, pos, stream=None) -> None:

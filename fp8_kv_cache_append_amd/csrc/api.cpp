@@ -43,6 +43,7 @@ int validate_cache(const fp8kv_cache* c) {
   if (c->mode != FP8KV_K8V8 && c->mode != FP8KV_K16V8 && c->mode != FP8KV_BF16 &&
       c->mode != FP8KV_K8V16 && c->mode != FP8KV_MXK8V8)
     return FP8KV_ERR_INVALID;
+  if (c->layout != FP8KV_TOKEN_MAJOR && c->layout != FP8KV_HEAD_MAJOR) return FP8KV_ERR_INVALID;
   if (c->head_dim != 64 && c->head_dim != 128) return FP8KV_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->max_blocks_per_seq <= 0 ||
       c->num_seqs <= 0)
@@ -78,7 +79,8 @@ int validate_cache(const fp8kv_cache* c) {
 fp8kv::CacheView view_of(const fp8kv_cache* c) {
   return fp8kv::CacheView{c->mode, c->block_size, c->num_kv_heads, c->head_dim,
                           c->max_blocks_per_seq, c->num_seqs, c->num_blocks, c->k, c->v,
-                          c->k_scale, c->v_scale, c->block_table, c->k_bias, c->k_exp};
+                          c->k_scale, c->v_scale, c->block_table, c->k_bias, c->k_exp,
+                          c->layout};
 }
 
 int launch_status(hipError_t e) {
@@ -348,7 +350,7 @@ int fp8kv_dequantize(const fp8kv_cache* src, const fp8kv_cache* dst, void* strea
   if ((st = validate_cache(dst)) != FP8KV_OK) return st;
   if (dst->mode != FP8KV_BF16 || dst->num_blocks != src->num_blocks ||
       dst->block_size != src->block_size || dst->num_kv_heads != src->num_kv_heads ||
-      dst->head_dim != src->head_dim)
+      dst->head_dim != src->head_dim || dst->layout != src->layout)
     return FP8KV_ERR_INVALID;
   if (dst->k == src->k || dst->v == src->v) return FP8KV_ERR_INVALID;  // no in-place
   if (fp8kv::k_is_mx(src->mode)) return FP8KV_ERR_UNSUPPORTED;

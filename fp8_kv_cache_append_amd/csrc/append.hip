@@ -3,11 +3,9 @@
 // Storage rule ("kadirnar/kernel-agent/fp8-kv-cache", section "Storage"):
 // one fp32 scale per (token, KV head) row, scale = amax(|row|) / 448 over the
 // head dimension, codes in e4m3, written at append and never re-quantised.
-// Codes are token-major within a block ([block][slot][head][d]); scales are
-// head-major within a block ([block][head][slot]), so the scales one KV head
-// reads for a run of tokens are contiguous and no cache line of scales is
-// shared by the heads ("FP8 KV attention: hardware paths and tile
-// preparation", "Store the preferred cache layout once").
+// A row (one (token, KV head) pair) of a block sits at the index the cache's
+// layout gives it (cache_row: token-major [slot][head] or head-major
+// [head][slot]); its codes, scale and K exponents all use that index.
 //
 // Mapping: a row of D fp32 values is read by D/4 lanes with one 16-byte load
 // each (32 lanes for D = 128, 16 for D = 64), so a wave covers the K row and
@@ -37,6 +35,7 @@ struct AppendArgs {
   int mbps;
   int num_seqs;
   int num_blocks;
+  int layout;
 };
 
 // Rows per thread: for a bulk append each thread handles R = 4 rows one
@@ -96,20 +95,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int is_v = (int)((r0 + k * slots) & 1u);
     const uint32_t h = pair[k] - (pair[k] / hkv) * hkv;
     const uint32_t slot = (uint32_t)p[k] - ((uint32_t)p[k] / bs) * bs;
-    const int64_t row = ((int64_t)blk[k] * a.bs + slot) * a.hkv + h;
-    const int64_t srow = ((int64_t)blk[k] * a.hkv + h) * a.bs + slot;  // head-major scales
+    const int64_t row = cache_row(a.layout, blk[k], (int)slot, (int)h, a.bs, a.hkv);
     const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
     if (k_is_mx(MODE) && !is_v) {
       // block-scaled K: eight lanes hold a block of 32 values
       const int e = mx_exponent(row_amax<8>(x[k]));
       uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], e8m0_value((uint32_t)(e + 127)));
-      if ((sub & 7) == 0) a.kexp[srow * (D / 32) + sub / 8] = (uint8_t)(e + 127);
+      if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
     } else if (quantise) {
       const float scale = row_amax<kLanesPerRow>(x[k]) / kE4M3Max;  // correctly rounded
       uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], scale);
-      if (sub == 0) (is_v ? a.vs : a.ks)[srow] = scale;
+      if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
     } else {
       uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x[k]);
@@ -144,7 +142,7 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
   const int64_t n_rows = 2 * (int64_t)n_tok * c.hkv;
   if (n_rows > INT32_MAX) return hipErrorInvalidValue;
   AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs, c.kexp,
-               (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks};
+               (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks, c.layout};
   switch (c.mode) {
     case kK8V8: return append_mode<kK8V8>(c, a, stream);
     case kK16V8: return append_mode<kK16V8>(c, a, stream);

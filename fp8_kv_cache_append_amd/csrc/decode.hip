@@ -64,6 +64,8 @@ struct DecodeArgs {
   int chunk;
   int n_splits;
   int num_blocks;
+  int layout;  // kTokenMajor / kHeadMajor (cache_row)
+  int ss;      // rows from one slot of a head to its next slot (slot_stride)
   uint64_t k_bytes;  // bytes of the K and V arrays (hardware bound of the tile loads)
   uint64_t v_bytes;
 };
@@ -113,9 +115,10 @@ struct LaneOffsets {
 // Issue the loads of the tile starting at token t0.  tab holds, in lane e,
 // the block id of block t_begin / bs + e of the sequence; it is indexed with
 // a wave-uniform lane, so every block id is a scalar.  A 16-token sub-block
-// lies inside one block, so its first row (block * bs + slot) * hkv + h is one
-// scalar per sub-block (four scalar divisions per tile) and every load is a
-// scalar base plus a per-lane offset fixed for the kernel.
+// lies inside one block, so its first row (cache_row of the layout) is one
+// scalar per sub-block (four scalar divisions per tile), its later slots
+// follow every ss rows, and every load is a scalar base plus a per-lane
+// offset fixed for the kernel.
 //
 // Every load is issued unconditionally and stays inside the cache: a
 // sub-block whose block id is out of range reads block 0 instead (block_size
@@ -148,9 +151,10 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
                                           int e_base, int h, int lane, bool live) {
   using T = TileRegs<MODE, D>;
-  int64_t row0[4], srow0[4];
+  int64_t row0[4];
   bool blk_ok[4];
   bool all_ok = t0 + 64 <= t_end;
+  const int64_t row_invalid = cache_row(a.layout, 0, 0, h, a.bs, a.hkv);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int tb = t0 + 16 * kb;
@@ -158,12 +162,10 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
     blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
     all_ok = all_ok && blk_ok[kb];
-    // codes: token-major rows (block * bs + slot) * hkv + h; scales:
-    // head-major (block * hkv + h) * bs + slot, so a sub-block's 16 scales
-    // are contiguous and the other heads' lines are never fetched
-    row0[kb] = blk_ok[kb] ? ((int64_t)blk * a.bs + (tb - eb * a.bs)) * a.hkv + h : h;
-    srow0[kb] = blk_ok[kb] ? ((int64_t)blk * a.hkv + h) * a.bs + (tb - eb * a.bs)
-                           : (int64_t)h * a.bs;
+    // the sub-block's first row (its codes at row * D, its scales at row;
+    // the next slot of the head is ss rows on)
+    row0[kb] = blk_ok[kb] ? cache_row(a.layout, blk, tb - eb * a.bs, h, a.bs, a.hkv)
+                          : row_invalid;
   }
   if constexpr (PART != 1) {
 #pragma unroll
@@ -175,12 +177,12 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     // values are picked with selects: indexing the arrays with it would
     // move them to scratch memory.
     const int kb = lane >> 4;
-    const int64_t base = kb == 0 ? srow0[0] : kb == 1 ? srow0[1] : kb == 2 ? srow0[2] : srow0[3];
+    const int64_t base = kb == 0 ? row0[0] : kb == 1 ? row0[1] : kb == 2 ? row0[2] : row0[3];
     const bool bok = kb == 0 ? blk_ok[0] : kb == 1 ? blk_ok[1] : kb == 2 ? blk_ok[2]
                                                                          : blk_ok[3];
     r.tok_ok = t0 + lane < t_end && bok;
     // (a tile that is not live reads the scales of head h's slot 0 in block 0)
-    const int64_t rr = live ? base + (int64_t)(lane & 15) : (int64_t)h * a.bs;
+    const int64_t rr = live ? base + (int64_t)((lane & 15) * a.ss) : row_invalid;
     r.ks = T::KS ? a.ks[rr] : 1.0f;
     if constexpr (T::MX)  // the row's E8M0 bytes (D / 32 of them)
       r.kxw = D == 128 ? *reinterpret_cast<const uint32_t*>(a.kexp + rr * 4)
@@ -302,10 +304,9 @@ void decode_partial_kernel(DecodeArgs a) {
   __shared__ uint32_t s_qx[Q8 && k_is_mx(MODE) ? 16 : 1][4];
   // fused append: the new token's K bytes, V bytes (each at most 2D) and
   // scales, in cache layout, for the wave that attends it
-  __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 6 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t s_new[APPEND ? D + 4 : 1];
   //   s_new[D], s_new[D+1]: K and V scale; s_new[D+2], s_new[D+3]: the
-  //   slot's cache row (low, high word; high word ~0u: not stored);
-  //   s_new[D+4], s_new[D+5]: the index of its scales (head-major)
+  //   slot's cache row (low, high word; high word ~0u: not stored)
 
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -472,9 +473,9 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 
   LaneOffsets lo;
-  lo.k = (uint32_t)(c * a.hkv) * (D * T::KE) + T::KLANE * T::KE * g4;
-  lo.v = (uint32_t)(4 * g4 * a.hkv) * (D * T::VE) + DPR * T::VE * c;
-  lo.v_token = (uint32_t)wave_uniform(a.hkv * D * T::VE);
+  lo.k = (uint32_t)(c * a.ss) * (D * T::KE) + T::KLANE * T::KE * g4;
+  lo.v = (uint32_t)(4 * g4 * a.ss) * (D * T::VE) + DPR * T::VE * c;
+  lo.v_token = (uint32_t)wave_uniform(a.ss * D * T::VE);
 
   // Fused append: the new token (position len - 1, only if it lies inside
   // the block table) belongs to this split's tiles; the wave that attends it
@@ -499,13 +500,10 @@ void decode_partial_kernel(DecodeArgs a) {
     const int sub = lane % kLR;
     if (lane == 0) {
       const int64_t row = (unsigned)blk < (unsigned)a.num_blocks
-                              ? ((int64_t)blk * a.bs + p % a.bs) * a.hkv + h
+                              ? cache_row(a.layout, blk, p % a.bs, h, a.bs, a.hkv)
                               : -1;  // invalid block: not stored, key excluded
       s_new[D + 2] = (uint32_t)row;
       s_new[D + 3] = (uint32_t)((uint64_t)row >> 32);
-      const int64_t srow = row < 0 ? -1 : ((int64_t)blk * a.hkv + h) * a.bs + p % a.bs;
-      s_new[D + 4] = (uint32_t)srow;
-      s_new[D + 5] = (uint32_t)((uint64_t)srow >> 32);
     }
     if (lane < 2 * kLR) {
       // LDS image: K bytes at dword 0, V bytes at dword D/2, scales at D, D+1
@@ -536,9 +534,7 @@ void decode_partial_kernel(DecodeArgs a) {
       uint8_t* dst = static_cast<uint8_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
       *reinterpret_cast<uint32_t*>(dst + 4 * sub) = img[sub];
       if (sub == 0)
-        const_cast<float*>(is_v ? a.vs : a.ks)[(int64_t)(((uint64_t)s_new[D + 5] << 32) |
-                                                          (uint64_t)s_new[D + 4])] =
-            __uint_as_float(s_new[D + (is_v ? 1 : 0)]);
+        const_cast<float*>(is_v ? a.vs : a.ks)[row] = __uint_as_float(s_new[D + (is_v ? 1 : 0)]);
     } else {
       uint16_t* dst = static_cast<uint16_t*>(const_cast<void*>(is_v ? a.v : a.k)) + row * D;
       *reinterpret_cast<u32x2_t*>(dst + 4 * sub) = *reinterpret_cast<const u32x2_t*>(img + 2 * sub);
@@ -1054,7 +1050,7 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
   DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,       seq_lens,
                part_acc, part_ml,  k_new,   v_new,   c.kbias,  c.kexp,  c_scale,
                c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks,
-               k_bytes, v_bytes};
+               c.layout, slot_stride(c.layout, c.hkv), k_bytes, v_bytes};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);

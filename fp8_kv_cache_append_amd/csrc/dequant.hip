@@ -23,8 +23,6 @@ struct DequantArgs {
   uint16_t* dk;
   uint16_t* dv;
   int64_t n_rows;  // 2 * cache rows (K and V)
-  int bs;          // tokens per block
-  int hkv;         // KV heads
 };
 
 template <int MODE, int D>
@@ -41,13 +39,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
   if (e4m3) {
     const u32x4_t codes = reinterpret_cast<const u32x4_t*>(
         static_cast<const uint8_t*>(is_v ? a.v : a.k) + row * D)[sub];
-    // row = (block * bs + slot) * hkv + head; its scale sits at
-    // (block * hkv + head) * bs + slot (head-major within a block)
-    const int64_t per_blk = (int64_t)a.bs * a.hkv;
-    const int64_t blk = row / per_blk;
-    const int rem = (int)(row - blk * per_blk);
-    const int slot = rem / a.hkv, head = rem - slot * a.hkv;
-    const float s = (is_v ? a.vs : a.ks)[(blk * a.hkv + head) * a.bs + slot];
+    // source and destination share the layout, so row r is the same
+    // (token, head) in both, and its scale is element r
+    const float s = (is_v ? a.vs : a.ks)[row];
     uint32_t out[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -83,7 +77,7 @@ static hipError_t dequant_for_d(int d, const DequantArgs& a, hipStream_t stream)
 hipError_t launch_dequantize(const CacheView& src, const CacheView& dst, hipStream_t stream) {
   DequantArgs a{src.k, src.v, src.ks, src.vs, static_cast<uint16_t*>(dst.k),
                 static_cast<uint16_t*>(dst.v),
-                2 * (int64_t)src.num_blocks * src.bs * src.hkv, src.bs, src.hkv};
+                2 * (int64_t)src.num_blocks * src.bs * src.hkv};
   switch (src.mode) {
     case kK8V8: return dequant_for_d<kK8V8>(src.d, a, stream);
     case kK16V8: return dequant_for_d<kK16V8>(src.d, a, stream);

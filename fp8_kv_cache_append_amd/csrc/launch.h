@@ -18,6 +18,21 @@ constexpr bool k_is_mx(int mode) { return mode == kMXK8V8; }
 // an fp32 scale per (token, KV head) on the K side
 constexpr bool k_has_row_scale(int mode) { return k_is_e4m3(mode) && !k_is_mx(mode); }
 
+// Row order inside a block: token-major [slot][head] or head-major
+// [head][slot]; codes, scales and K exponents of row r sit at r * D, r and
+// r * D / 32 of their arrays.
+enum { kTokenMajor = 0, kHeadMajor = 1 };
+
+__host__ __device__ inline int64_t cache_row(int layout, int64_t blk, int slot, int h, int bs,
+                                             int hkv) {
+  return layout == kHeadMajor ? (blk * hkv + h) * bs + slot : (blk * bs + slot) * hkv + h;
+}
+
+// Rows from one slot of a head to the next slot of the same head.
+__host__ __device__ inline int slot_stride(int layout, int hkv) {
+  return layout == kHeadMajor ? 1 : hkv;
+}
+
 struct CacheView {
   int mode;   // kK8V8 / kK16V8 / kBF16 / kK8V16 / kMXK8V8
   int bs;     // tokens per block (multiple of 16)
@@ -32,7 +47,8 @@ struct CacheView {
   float* vs;
   const int32_t* table;
   const float* kbias;  // exact K bias [hkv][d] of a pre-bias residual cache, or null
-  uint8_t* kexp;       // kMXK8V8: E8M0 byte per 32-value K block [..][hkv][d/32]
+  uint8_t* kexp;       // kMXK8V8: E8M0 byte per 32-value K block [row][d/32]
+  int layout;          // kTokenMajor / kHeadMajor
 };
 
 // Work-groups of the split kernel one compute unit holds at once (one

@@ -73,6 +73,7 @@ struct PrefillArgs {
   int n_qt;  // query tiles per sequence (ceil(max_q_len / 128))
   int total_q;
   int num_blocks;
+  int layout;  // kTokenMajor / kHeadMajor (cache_row)
 };
 
 constexpr int kPGroups = 2;                   // key groups (alternate tiles)
@@ -205,6 +206,9 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   const int n_kt = (kv_end + kKT - 1) / kKT;   // key tiles of the query tile
   const int n_it = (n_kt + kPGroups - 1) / kPGroups;  // tiles of key group 0
   const int64_t tab_row = (int64_t)b * a.mbps;
+  // a key that does not exist reads head hk's slot 0 of block 0 (masked)
+  const int64_t row_invalid = cache_row(a.layout, 0, 0, hk, a.bs, a.hkv);
+  const int ss = slot_stride(a.layout, a.hkv);
 
   // Staging of one tile by the group's 256 threads (gt = thread in group):
   //   K  thread -> (key gt / 4, quarter gt % 4 of the row), row-major bf16;
@@ -256,21 +260,21 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   uint32_t okv = 0;  // bit r: key 4*kq + r of the tile exists
   auto load_tile = [&]() {
     const bool sb_ok = (p_t < kv_end) && ((unsigned)p_id < (unsigned)a.num_blocks);
-    const int64_t slot_v = sb_ok ? (int64_t)p_id * a.bs + 16 * p_r : 0;
+    // first row of this lane's V sub-block; its later slots follow every ss rows
+    const int64_t row_v = sb_ok ? cache_row(a.layout, p_id, 16 * p_r, hk, a.bs, a.hkv)
+                                : row_invalid;
     {  // K row (sub-block rw, from lane 4*rw) and its scales
       const int id_k = __builtin_amdgcn_readlane(p_id, 4 * rw);
       const int r_k = __builtin_amdgcn_readlane(p_r, 4 * rw);
       const int t_k = __builtin_amdgcn_readlane(p_t, 4 * rw) + kin;
       okk = (t_k < kv_end) && ((unsigned)id_k < (unsigned)a.num_blocks);
-      const int64_t slot = okk ? (int64_t)id_k * a.bs + 16 * r_k + kin : 0;
-      const int64_t row = slot * a.hkv + hk;
-      // scales are head-major within a block: [block][head][slot]
-      const int64_t srow = okk ? ((int64_t)id_k * a.hkv + hk) * a.bs + 16 * r_k + kin : 0;
+      const int64_t row = okk ? cache_row(a.layout, id_k, 16 * r_k + kin, hk, a.bs, a.hkv)
+                              : row_invalid;
       const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * S::KBYTES + spart * (S::KBYTES / 4);
 #pragma unroll
       for (int i = 0; i < S::KW; ++i) kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
-      if (S::K8) ksreg = a.ks[srow];
-      if (S::V8) vsreg = a.vs[srow];
+      if (S::K8) ksreg = a.ks[row];
+      if (S::V8) vsreg = a.vs[row];
     }
     okv = 0;
 #pragma unroll
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
       const int kk = 4 * (kq & 3) + r;
       const bool ok = sb_ok && (p_t + kk < kv_end);
       okv |= ok ? (1u << r) : 0u;
-      const int64_t row = (ok ? slot_v + kk : 0) * a.hkv + hk;
+      const int64_t row = ok ? row_v + (int64_t)kk * ss : row_invalid;
       const uint8_t* vp = static_cast<const uint8_t*>(a.v) + row * (D * S::VE) + dq * (S::DG * S::VE);
       if constexpr (S::VWORDS == 4) {
         const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
@@ -562,7 +566,7 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
                           float c_scale, float* out, hipStream_t stream) {
   const int n_qt = (max_q_len + kQT - 1) / kQT;
   PrefillArgs a{c.k, c.v, c.ks, c.vs, c.table, q, cu_q, q_pos0, seq_lens, out,
-                c_scale, c.hkv, group, c.bs, c.mbps, n_qt, total_q, c.num_blocks};
+                c_scale, c.hkv, group, c.bs, c.mbps, n_qt, total_q, c.num_blocks, c.layout};
   const int64_t n_wg = (int64_t)batch * n_qt * c.hkv * group;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   switch (c.mode) {

@@ -83,27 +83,33 @@ typedef enum {
   FP8KV_ERR_TOO_LARGE = -5    /* fp8kv_decode_noalloc: partials exceed its scratch */
 } fp8kv_status;
 
+/* Order of the rows of a block (one row = one (token, KV head) pair):
+ *   FP8KV_TOKEN_MAJOR  [block][slot][head]: a contiguous cache is
+ *                      [B][T][Hkv][D] with scales [B][T][Hkv]
+ *   FP8KV_HEAD_MAJOR   [block][head][slot]: one KV head's rows of a block
+ *                      are contiguous (codes and scales), the order the
+ *                      decode tile reads ([HW] "Store the preferred cache
+ *                      layout once": align pages and scale blocks with the
+ *                      decode tile) */
+typedef enum { FP8KV_TOKEN_MAJOR = 0, FP8KV_HEAD_MAJOR = 1 } fp8kv_layout;
+
 /*
  * Paged KV cache descriptor (all pointers device memory, owned by the
- * caller).  Layout: codes token-major within a block, scales head-major
- * within a block (the scales one KV head reads for a run of tokens are
- * contiguous, so no cache line of scales is shared by two heads; [HW]
- * "Store the preferred cache layout once"):
- *   k, v            [num_blocks][block_size][num_kv_heads][head_dim]
+ * caller).  With R the rows of a block in the order `layout` names
+ * ([slot][head] or [head][slot]):
+ *   k, v            [num_blocks][R][head_dim]
  *                   K8V8: uint8 codes for both; K16V8: k bf16, v uint8;
  *                   BF16: bf16 for both; K8V16: k uint8, v bf16
- *   k_scale         [num_blocks][num_kv_heads][block_size] fp32, K8V8 and
- *                   K8V16 (NULL otherwise)
+ *   k_scale         [num_blocks][R] fp32, K8V8 and K8V16 (NULL otherwise)
  *   k_exp           MXK8V8 only (NULL otherwise): uint8
- *                   [num_blocks][num_kv_heads][block_size][head_dim / 32], the
+ *                   [num_blocks][R][head_dim / 32], the
  *                   byte E + 127 of each 32-value K block, 4-byte aligned.
  *                   Decode reads it with bf16 Q (codes converted by their
  *                   block's scale) or with block-scaled Q through the q8
  *                   entries (the matrix instruction applies both operands'
  *                   block scales); the fused append, prefill, dequantize and
  *                   a K bias give FP8KV_ERR_UNSUPPORTED for such a cache.
- *   v_scale         [num_blocks][num_kv_heads][block_size] fp32, K8V8 and
- *                   K16V8 (NULL otherwise)
+ *   v_scale         [num_blocks][R] fp32, K8V8 and K16V8 (NULL otherwise)
  *   block_table     int32 [num_seqs][max_blocks_per_seq]; token t of sequence
  *                   b is slot t % block_size of block
  *                   block_table[b * max_blocks_per_seq + t / block_size].
@@ -112,8 +118,11 @@ typedef enum {
  *                   read, so the first K/V loads need not wait for one;
  *                   num_seqs * max_blocks_per_seq must fit an int32 and
  *                   be at most num_blocks, else FP8KV_ERR_INVALID).
- * A contiguous cache [B][T][Hkv][D] (scales [B][Hkv][T]) is block_size = T,
- * max_blocks_per_seq = 1 and block_table NULL (or block_table[b] = b).
+ * A contiguous cache ([B][T][Hkv][D] token-major, [B][Hkv][T][D] head-major)
+ * is block_size = T, max_blocks_per_seq = 1 and block_table NULL (or
+ * block_table[b] = b).
+ *   layout          fp8kv_layout of every array above; any other value is
+ *                   FP8KV_ERR_INVALID.
  *   k_bias          NULL, or fp32 [num_kv_heads][head_dim], 16-byte aligned:
  *                   a pre-bias residual cache ([HW] "Treat numerical safety
  *                   and kernel speed as separate gates"; [FQ] "Bias-aware
@@ -146,6 +155,7 @@ typedef struct fp8kv_cache {
   const int32_t* block_table;
   const float* k_bias;         /* exact fixed K bias, or NULL (see above) */
   uint8_t* k_exp;              /* FP8KV_MXK8V8: K block exponents (see above) */
+  int32_t layout;              /* fp8kv_layout */
 } fp8kv_cache;
 
 /*
@@ -355,8 +365,8 @@ int fp8kv_prefill(const fp8kv_cache* cache, const uint16_t* q,
 /*
  * The unfused control ("Fused KV-cache quantization"; [HW] Collect the
  * profiler evidence): every row of src, in any mode, converted into dst, a
- * BF16-mode cache of the same num_blocks, block_size, num_kv_heads and
- * head_dim (its own buffers; block tables are not read).  An e4m3 element
+ * BF16-mode cache of the same num_blocks, block_size, num_kv_heads,
+ * head_dim and layout (its own buffers; block tables are not read).  An e4m3 element
  * becomes bf16(fp32(value(code) * scale)) -- the fp32 product rounded once,
  * then to the nearest-even bf16; a bf16 element is copied.  Attention on dst
  * with the BF16 kernels is then the pipeline that dequantises the cache in

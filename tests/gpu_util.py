@@ -18,10 +18,11 @@ def check_layout(table: np.ndarray, bs: int, lens) -> None:
         assert np.all(table[b, :need] >= 0), (b, n)
 
 
-def make_cache(mode: str, w: synth.Workload, capacity=None) -> KVCache:
+def make_cache(mode: str, w: synth.Workload, capacity=None, layout="token") -> KVCache:
     bs, table, n_blocks = synth.block_layout(w, capacity)
     check_layout(table, bs, w.lens)
-    return KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV)
+    return KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV,
+                            layout=layout)
 
 
 def append_seq(cache: KVCache, b: int, k: np.ndarray, v: np.ndarray, pos0: int = 0) -> None:
@@ -29,7 +30,7 @@ def append_seq(cache: KVCache, b: int, k: np.ndarray, v: np.ndarray, pos0: int =
     if n == 0:
         return
     table = cache.block_table.cpu().numpy()
-    check_layout(table, int(cache.k.shape[1]), [0] * b + [pos0 + n])
+    check_layout(table, cache.block_size, [0] * b + [pos0 + n])
     kt = torch.from_numpy(np.ascontiguousarray(k, np.float32)).to(DEV)
     vt = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(DEV)
     seq = torch.full((n,), b, dtype=torch.int32, device=DEV)
@@ -39,18 +40,17 @@ def append_seq(cache: KVCache, b: int, k: np.ndarray, v: np.ndarray, pos0: int =
 
 def read_rows(cache: KVCache, b: int, n: int) -> dict:
     """Cache contents of tokens 0..n-1 of sequence b, as oracle stores."""
-    bs = int(cache.k.shape[1])
+    bs = cache.block_size
     table = cache.block_table.cpu().numpy()
     t = np.arange(n)
     blk = torch.from_numpy(table[b, t // bs].astype(np.int64)).to(DEV)
     slot = torch.from_numpy((t % bs).astype(np.int64)).to(DEV)
     out = {}
 
-    def grab(x):        # codes: [block][slot][head][...]
-        return x[blk, slot].cpu()
+    def grab(x):  # rows of a block: [slot][head] or [head][slot]; -> [n, Hkv, ...]
+        return (x[blk, slot] if cache.layout == "token" else x[blk, :, slot]).cpu()
 
-    def grab_scale(x):  # scales and K exponents: [block][head][slot][...]
-        return x[blk, :, slot].cpu()
+    grab_scale = grab
 
     if cache.mode in binding.K_MX:
         out["k8"] = grab(cache.k).numpy()
@@ -77,7 +77,7 @@ def decode(cache: KVCache, q_bits: np.ndarray, lens, group: int, sm_scale: float
     lens = np.asarray(lens, np.int32)
     b, hq, d = q_bits.shape
     assert hq == group * cache.num_kv_heads and d == cache.head_dim
-    check_layout(cache.block_table.cpu().numpy(), int(cache.k.shape[1]), lens)
+    check_layout(cache.block_table.cpu().numpy(), cache.block_size, lens)
     max_len = int(lens.max()) if b else 0
     ws_bytes = binding.fp8kv_decode_workspace_bytes(cache, b, group, max_len)
     ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device=DEV)
@@ -90,7 +90,7 @@ def decode(cache: KVCache, q_bits: np.ndarray, lens, group: int, sm_scale: float
 def decode_partial(cache: KVCache, q_bits, lens, group, sm_scale, chunk):
     lens = np.asarray(lens, np.int32)
     b, hq, d = q_bits.shape
-    check_layout(cache.block_table.cpu().numpy(), int(cache.k.shape[1]), lens)
+    check_layout(cache.block_table.cpu().numpy(), cache.block_size, lens)
     max_len = int(lens.max())
     splits = -(-max_len // chunk)
     hkv = cache.num_kv_heads

@@ -50,13 +50,15 @@ def test_strerror():
 def _desc(**kw):
     base = dict(mode=0, num_blocks=4, block_size=16, num_kv_heads=2, head_dim=128,
                 max_blocks_per_seq=4, num_seqs=16, k=FAKE, v=FAKE, k_scale=FAKE, v_scale=FAKE,
-                block_table=FAKE, k_bias=None, k_exp=None)
+                block_table=FAKE, k_bias=None, k_exp=None, layout=0)
     base.update(kw)
     return CacheDesc(**base)
 
 
 BAD_CACHES = [
     (dict(mode=5), -1),
+    (dict(layout=2), -1),               # token-major (0) or head-major (1) only
+    (dict(layout=-1), -1),
     (dict(mode=3), -1),                 # K8V16 stores no V scale: v_scale must be NULL
     (dict(mode=3, v_scale=None, k_scale=None), -1),   # ... but a K scale
     (dict(head_dim=96), -4),
@@ -310,7 +312,9 @@ def test_dequantize_rejects_bad_arguments():
     other_shape = _desc(mode=2, k=FAKE + 4096, v=FAKE + 8192, k_scale=None, v_scale=None,
                         num_blocks=5)
     in_place = _desc(mode=2, k_scale=None, v_scale=None)
-    for dst in (not_bf16, other_shape, in_place):
+    other_layout = _desc(mode=2, k=FAKE + 4096, v=FAKE + 8192, k_scale=None, v_scale=None,
+                         layout=1)
+    for dst in (not_bf16, other_shape, in_place, other_layout):
         assert lib.fp8kv_dequantize(ctypes.byref(src), ctypes.byref(dst), None) == -1
     assert lib.fp8kv_dequantize(None, ctypes.byref(good), None) == -1
     assert lib.fp8kv_dequantize(ctypes.byref(src), None, None) == -1

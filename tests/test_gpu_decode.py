@@ -64,10 +64,10 @@ def _fill(cache, w, seqs):
         append_seq(cache, b, k, v)
 
 
-def _run_case(mode, w, pairs=None):
+def _run_case(mode, w, pairs=None, layout="token"):
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
-    cache = make_cache(mode, w)
+    cache = make_cache(mode, w, layout=layout)
     _fill(cache, w, seqs)
     got = decode(cache, q_bits, w.lens, w.group, w.sm_scale)
     ref, lo, hi = oracle.decode(mode, q_bits, [s[0] for s in seqs], [s[1] for s in seqs],
@@ -86,15 +86,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
-def test_decode_small_shapes(mode, shape):
+def test_decode_small_shapes(mode, shape, layout):
     hq, hkv, d, lens, bs = shape
     lens = np.array(lens, np.int32)
     w = synth.Workload("t", len(lens), hq, hkv, d, lens, "outliers", block_size=bs,
                        shuffle_blocks=bs > 0, seed=hq * 31 + d)
-    got, *ref = _run_case(mode, w)
-    _gate(got, *ref, (mode, shape))
+    got, *ref = _run_case(mode, w, layout=layout)
+    _gate(got, *ref, (mode, shape, layout))
     empty = lens == 0
     assert np.all(got[empty] == 0)
 
@@ -206,15 +207,16 @@ def test_decode_repeat_bitwise_identical():
         assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16", "MXK8V8"])
-def test_decode_unwritten_slots_hold_nan(mode):
+def test_decode_unwritten_slots_hold_nan(mode, layout):
     """Every byte of the cache is 0xFF (NaN in e4m3, bf16 and fp32) before the
     keys are appended, so slots past each sequence's last key hold NaN: keys
     that do not exist must not reach any output."""
     lens = np.array([1, 37, 300, 1000], np.int32)
     w = synth.Workload("t", len(lens), 16, 2, 128, lens, "outliers", block_size=48,
                        shuffle_blocks=True, seed=23)
-    cache = make_cache(mode, w, capacity=1056)
+    cache = make_cache(mode, w, capacity=1056, layout=layout)
     for x in (cache.k, cache.v, cache.k_scale, cache.v_scale, cache.k_exp):
         if x is not None:
             x.view(torch.uint8).fill_(0xFF)

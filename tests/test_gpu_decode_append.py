@@ -44,11 +44,11 @@ def _cache_bytes(cache):
     return [p.cpu().numpy().copy() for p in parts]
 
 
-def _compare(mode, w, lens_attend, news):
+def _compare(mode, w, lens_attend, news, layout="token"):
     """news[b]: index of the token the step appends (the sequence's last)."""
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     q_bits = synth.q_bf16_bits(w.seed + 7, (w.batch, w.q_heads, w.head_dim))
-    fused, plain = make_cache(mode, w), make_cache(mode, w)
+    fused, plain = make_cache(mode, w, layout=layout), make_cache(mode, w, layout=layout)
     k_new = np.zeros((w.batch, w.kv_heads, w.head_dim), np.float32)
     v_new = np.zeros_like(k_new)
     for b, (k, v) in enumerate(seqs):
@@ -75,14 +75,15 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
-def test_fused_append_matches_append_then_decode(mode, shape):
+def test_fused_append_matches_append_then_decode(mode, shape, layout):
     hq, hkv, d, lens, bs = shape
     lens = np.array(lens, np.int32)
     w = synth.Workload("t", len(lens), hq, hkv, d, lens, "outliers", block_size=bs,
                        shuffle_blocks=bs > 0, seed=hq * 13 + d + bs)
-    seqs, q_bits, got = _compare(mode, w, lens, [int(n) - 1 for n in lens])
+    seqs, q_bits, got = _compare(mode, w, lens, [int(n) - 1 for n in lens], layout)
     ref, lo, hi = oracle.decode(mode, q_bits, [s[0] for s in seqs], [s[1] for s in seqs],
                                 w.sm_scale, bounds=True)
     _gate(got, ref, lo, hi, (mode, "fused append", shape))

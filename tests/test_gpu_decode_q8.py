@@ -58,7 +58,7 @@ def _narrow_gate(got, mode, q_bits, k_seqs, v_seqs, sm_scale, ctx, pairs=None):
 def decode_q8(cache, q_bits, lens, group, sm_scale):
     lens = np.asarray(lens, np.int32)
     b, hq, d = q_bits.shape
-    check_layout(cache.block_table.cpu().numpy(), int(cache.k.shape[1]), lens)
+    check_layout(cache.block_table.cpu().numpy(), cache.block_size, lens)
     max_len = int(lens.max()) if b else 0
     ws = torch.empty(max(binding.fp8kv_decode_workspace_bytes(cache, b, group, max_len) // 4, 4),
                      dtype=torch.float32, device=DEV)
@@ -68,24 +68,25 @@ def decode_q8(cache, q_bits, lens, group, sm_scale):
     return out.cpu().numpy()
 
 
-def _case(mode, w, with_cache=False):
+def _case(mode, w, with_cache=False, layout="token"):
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
-    cache = make_cache(mode, w)
+    cache = make_cache(mode, w, layout=layout)
     for b, (k, v) in enumerate(seqs):
         append_seq(cache, b, k, v)
     got = decode_q8(cache, q_bits, w.lens, w.group, w.sm_scale)
     return (got, seqs, q_bits, cache) if with_cache else (got, seqs, q_bits)
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", NARROW_MODES)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
-def test_narrow_decode_small_shapes(mode, shape):
+def test_narrow_decode_small_shapes(mode, shape, layout):
     hq, hkv, d, lens, bs = shape
     lens = np.array(lens, np.int32)
     w = synth.Workload("t", len(lens), hq, hkv, d, lens, "outliers", block_size=bs,
                        shuffle_blocks=bs > 0, seed=hq * 7 + d + bs + 1)
-    got, seqs, q_bits = _case(mode, w)
+    got, seqs, q_bits = _case(mode, w, layout=layout)
     _narrow_gate(got, mode, q_bits, [s[0] for s in seqs], [s[1] for s in seqs], w.sm_scale,
                  (mode, "narrow", shape))
     for b, n in enumerate(lens):

@@ -15,21 +15,23 @@ pytestmark = pytest.mark.gpu
 
 
 def _bf16_cache_like(src: KVCache) -> KVCache:
-    nb, bs, hkv, d = src.k.shape
-    return KVCache.allocate("BF16", nb, bs, hkv, d, src.block_table.cpu().numpy(), DEV)
+    return KVCache.allocate("BF16", int(src.k.shape[0]), src.block_size, src.num_kv_heads,
+                            src.head_dim, src.block_table.cpu().numpy(), DEV,
+                            layout=src.layout)
 
 
 def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "K8V16", "BF16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_dequantize_bit_exact_and_attention(mode, d):
+def test_dequantize_bit_exact_and_attention(mode, d, layout):
     lens = np.array([100, 37], np.int32)
     w = synth.Workload("t", 2, 8, 2, d, lens, "outliers", block_size=16,
                        shuffle_blocks=True, seed=91 + d)
-    src = make_cache(mode, w)
+    src = make_cache(mode, w, layout=layout)
     seqs = [synth.kv_sequence(w, b) for b in range(2)]
     for b, (k, v) in enumerate(seqs):
         append_seq(src, b, k, v)
@@ -40,6 +42,11 @@ def test_dequantize_bit_exact_and_attention(mode, d):
     torch.cuda.synchronize()
     # expected: the oracle's stores of the same rows, converted by the oracle
     table = src.block_table.cpu().numpy()
+
+    def at(x, b, t):  # rows of sequence b's tokens t: [slot][head] or [head][slot]
+        blk, slot = table[b, t // 16], t % 16
+        return (blk, slot) if layout == "token" else (blk, slice(None), slot)
+
     want_k = np.zeros(dst.k.shape, np.uint16)
     want_v = np.zeros(dst.v.shape, np.uint16)
     for b, (k, v) in enumerate(seqs):
@@ -47,8 +54,8 @@ def test_dequantize_bit_exact_and_attention(mode, d):
         kb = oracle.dequantize_rows(st["k8"], st["ks"]) if "k8" in st else st["k16"]
         vb = oracle.dequantize_rows(st["v8"], st["vs"]) if "v8" in st else st["v16"]
         t = np.arange(k.shape[0])
-        want_k[table[b, t // 16], t % 16] = kb
-        want_v[table[b, t // 16], t % 16] = vb
+        want_k[at(want_k, b, t)] = kb
+        want_v[at(want_v, b, t)] = vb
     assert np.array_equal(_bits(dst.k), want_k)
     assert np.array_equal(_bits(dst.v), want_v)
     # attention over the converted cache = the oracle's BF16 mode on those values
@@ -57,7 +64,7 @@ def test_dequantize_bit_exact_and_attention(mode, d):
     keys, vals = [], []
     for b in range(2):
         t = np.arange(int(lens[b]))
-        keys.append(oracle.bf16_value(want_k[table[b, t // 16], t % 16]).astype(np.float32))
-        vals.append(oracle.bf16_value(want_v[table[b, t // 16], t % 16]).astype(np.float32))
+        keys.append(oracle.bf16_value(want_k[at(want_k, b, t)]).astype(np.float32))
+        vals.append(oracle.bf16_value(want_v[at(want_v, b, t)]).astype(np.float32))
     ref, lo, hi = oracle.decode("BF16", q_bits, keys, vals, w.sm_scale, bounds=True)
     _gate(got, ref, lo, hi, (mode, d, "dequantized"))

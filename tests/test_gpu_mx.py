@@ -23,8 +23,9 @@ from test_gpu_decode_q8 import _narrow_gate, decode_q8
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_mx_append_bytes_match_oracle(d):
+def test_mx_append_bytes_match_oracle(d, layout):
     rng = np.random.default_rng(d)
     n, hkv = 300, 2
     k = (rng.standard_normal((n, hkv, d)) * np.exp2(rng.integers(-30, 30, size=(n, hkv, 1)))
@@ -36,7 +37,7 @@ def test_mx_append_bytes_match_oracle(d):
     v = rng.standard_normal((n, hkv, d)).astype(np.float32)
     w = synth.Workload("t", 1, 2 * hkv, hkv, d, np.array([n], np.int32), "normal",
                        block_size=16, shuffle_blocks=True, seed=5)
-    cache = make_cache("MXK8V8", w)
+    cache = make_cache("MXK8V8", w, layout=layout)
     append_seq(cache, 0, k, v)
     got = read_rows(cache, 0, n)
     want = oracle.store_rows("MXK8V8", k, v)
@@ -53,22 +54,23 @@ SHAPES = [
 ]
 
 
-def _filled(w):
+def _filled(w, layout="token"):
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
-    cache = make_cache("MXK8V8", w)
+    cache = make_cache("MXK8V8", w, layout=layout)
     for b, (k, v) in enumerate(seqs):
         append_seq(cache, b, k, v)
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
     return cache, seqs, q_bits
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
-def test_mx_decode_bf16_q(shape):
+def test_mx_decode_bf16_q(shape, layout):
     hq, hkv, d, lens, bs = shape
     lens = np.array(lens, np.int32)
     w = synth.Workload("t", len(lens), hq, hkv, d, lens, "outliers", block_size=bs,
                        shuffle_blocks=bs > 0, seed=hq + d + bs + 9)
-    cache, seqs, q_bits = _filled(w)
+    cache, seqs, q_bits = _filled(w, layout)
     got = decode(cache, q_bits, lens, w.group, w.sm_scale)
     ref, lo, hi = oracle.decode("MXK8V8", q_bits, [s[0] for s in seqs], [s[1] for s in seqs],
                                 w.sm_scale, bounds=True)

@@ -21,12 +21,12 @@ from test_gpu_decode import _gate
 pytestmark = pytest.mark.gpu
 
 
-def _pair(mode, w, capacity):
+def _pair(mode, w, capacity, layout="token"):
     bs, table, n_blocks = synth.block_layout(w, capacity)
     assert np.array_equal(table.ravel(), np.arange(table.size)), "layout is not contiguous"
-    a = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV)
+    a = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV, layout=layout)
     b = KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV,
-                         table_in_memory=False)
+                         table_in_memory=False, layout=layout)
     return a, b
 
 
@@ -43,12 +43,13 @@ def _same_cache(a, b):
 LAYOUTS = [(0, None), (16, 2048)]
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16"])
 @pytest.mark.parametrize("bs,capacity", LAYOUTS)
-def test_decode_append_without_table(mode, bs, capacity):
+def test_decode_append_without_table(mode, bs, capacity, layout):
     lens = np.array([300, 1, 2048, 777], np.int32)
     w = synth.Workload("t", len(lens), 16, 2, 128, lens, "outliers", block_size=bs, seed=43)
-    cache_t, cache_n = _pair(mode, w, capacity)
+    cache_t, cache_n = _pair(mode, w, capacity, layout)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     for cache in (cache_t, cache_n):
         for b, (k, v) in enumerate(seqs):
@@ -77,12 +78,13 @@ def test_decode_append_without_table(mode, bs, capacity):
     _gate(outs[1], ref, lo, hi, (mode, bs, "no table"))
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("bs,capacity", LAYOUTS)
-def test_prefill_without_table(bs, capacity):
+def test_prefill_without_table(bs, capacity, layout):
     lens = np.array([640, 200], np.int32)
     w = synth.Workload("t", len(lens), 28, 4, 128, lens, "normal", block_size=bs,
                        prefill=True, seed=44)
-    cache_t, cache_n = _pair("K8V8", w, capacity)
+    cache_t, cache_n = _pair("K8V8", w, capacity, layout)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     for cache in (cache_t, cache_n):
         for b, (k, v) in enumerate(seqs):

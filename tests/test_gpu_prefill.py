@@ -27,7 +27,7 @@ def gpu_prefill(cache, q_bits, n_q, q_pos0, seq_lens, group, sm_scale):
     q_pos0 = np.asarray(q_pos0, np.int32)
     assert q_bits.shape[0] == cu[-1]
     assert np.all(q_pos0 + n_q <= seq_lens) and np.all(q_pos0 >= 0)
-    check_layout(cache.block_table.cpu().numpy(), int(cache.k.shape[1]), seq_lens)
+    check_layout(cache.block_table.cpu().numpy(), cache.block_size, seq_lens)
     out = torch.full(q_bits.shape, float("nan"), dtype=torch.float32, device="cuda")
     binding.fp8kv_prefill(cache, q_tensor(q_bits), group, torch.from_numpy(cu).cuda(),
                           torch.from_numpy(q_pos0).cuda(), torch.from_numpy(seq_lens).cuda(),
@@ -35,11 +35,12 @@ def gpu_prefill(cache, q_bits, n_q, q_pos0, seq_lens, group, sm_scale):
     return out.cpu().numpy(), cu
 
 
-def _case(mode, hq, hkv, d, n_q, q_pos0, seq_lens, bs, seed, rows=None, dist="outliers"):
+def _case(mode, hq, hkv, d, n_q, q_pos0, seq_lens, bs, seed, rows=None, dist="outliers",
+          layout="token"):
     seq_lens = np.asarray(seq_lens, np.int32)
     w = synth.Workload("t", len(seq_lens), hq, hkv, d, seq_lens, dist, block_size=bs,
                        shuffle_blocks=bs > 0, seed=seed)
-    cache = make_cache(mode, w)
+    cache = make_cache(mode, w, layout=layout)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     for b, (k, v) in enumerate(seqs):
         append_seq(cache, b, k, v)
@@ -73,12 +74,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"hq{c[0]}_hkv{c[1]}_d{c[2]}_n{sum(c[3])}")
-def test_prefill_small(mode, case):
+def test_prefill_small(mode, case, layout):
     hq, hkv, d, n_q, q_pos0, lens, bs = case
-    got, ref, lo, hi = _case(mode, hq, hkv, d, n_q, q_pos0, lens, bs, seed=hq + d)
-    _gate(got, ref, lo, hi, (mode, case))
+    got, ref, lo, hi = _case(mode, hq, hkv, d, n_q, q_pos0, lens, bs, seed=hq + d,
+                             layout=layout)
+    _gate(got, ref, lo, hi, (mode, case, layout))
 
 
 @pytest.mark.timeout(600)

@@ -35,10 +35,10 @@ from test_gpu_decode import _gate
 pytestmark = pytest.mark.gpu
 
 
-def _cache(mode, w, table_in_memory=True):
+def _cache(mode, w, table_in_memory=True, layout="token"):
     bs, table, n_blocks = synth.block_layout(w)
     return KVCache.allocate(mode, n_blocks, bs, w.kv_heads, w.head_dim, table, DEV,
-                            table_in_memory=table_in_memory)
+                            table_in_memory=table_in_memory, layout=layout)
 
 
 def _append(cache, b, k, v):
@@ -113,9 +113,9 @@ def _oracle8192(mode, q8=False):
     return ref, unr
 
 
-def _fused_and_plain(mode, w, seqs, table_in_memory):
-    fused = _cache(mode, w, table_in_memory)
-    plain = _cache(mode, w, table_in_memory)
+def _fused_and_plain(mode, w, seqs, table_in_memory, layout="token"):
+    fused = _cache(mode, w, table_in_memory, layout)
+    plain = _cache(mode, w, table_in_memory, layout)
     for b, (k, v) in enumerate(seqs):
         _append(fused, b, k[:-1], v[:-1])
         _append(plain, b, k, v)
@@ -124,18 +124,19 @@ def _fused_and_plain(mode, w, seqs, table_in_memory):
     return fused, plain, k_new, v_new
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("table_in_memory", [False, True], ids=["no_table", "table"])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
-def test_fused_multi_tile_b16_t8192(mode, table_in_memory):
+def test_fused_multi_tile_b16_t8192(mode, table_in_memory, layout):
     w = W8192
     seqs = _seqs8192()
-    fused, plain, k_new, v_new = _fused_and_plain(mode, w, seqs, table_in_memory)
+    fused, plain, k_new, v_new = _fused_and_plain(mode, w, seqs, table_in_memory, layout)
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
     q = q_tensor(q_bits)
     lens = torch.from_numpy(w.lens).to(DEV)
     got = _bench_step(fused, w, k_new, v_new, q, lens)
     want = _plain_decode(plain, w, q, lens)
-    ctx = (w.name, mode, "table" if table_in_memory else "no table")
+    ctx = (w.name, mode, "table" if table_in_memory else "no table", layout)
     _same_cache(fused, plain, ctx)
     assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (ctx, "output differs")
     # the public fused entry point is the same two kernels
@@ -150,14 +151,15 @@ def test_fused_multi_tile_b16_t8192(mode, table_in_memory):
     _gate(got.cpu().numpy(), ref, lo, hi, ctx, literal=True)
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("mode", ["K8V8", "K8V16"])
-def test_fused_narrow_qk_multi_tile_b16_t8192(mode):
+def test_fused_narrow_qk_multi_tile_b16_t8192(mode, layout):
     """fp8kv_decode_append_q8 (the benchmark's narrow_qk leg) at 8192 keys:
     bit-identical to fp8kv_append + fp8kv_decode_q8, and the narrow-QK gate
     (test_gpu_decode_q8) against the oracle's narrow path in full."""
     w = W8192
     seqs = _seqs8192()
-    fused, plain, k_new, v_new = _fused_and_plain(mode, w, seqs, table_in_memory=False)
+    fused, plain, k_new, v_new = _fused_and_plain(mode, w, seqs, False, layout)
     _plan(fused, w)
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
     q = q_tensor(q_bits)
@@ -168,7 +170,7 @@ def test_fused_narrow_qk_multi_tile_b16_t8192(mode):
     binding.fp8kv_decode_append_q8(fused, k_new, v_new, q, w.group, lens, w.max_len,
                                    w.sm_scale, got, ws)
     want = _plain_decode(plain, w, q, lens, q8=True)
-    ctx = (w.name, mode, "narrow QK")
+    ctx = (w.name, mode, "narrow QK", layout)
     _same_cache(fused, plain, ctx)
     assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (ctx, "output differs")
     (ref, lo, hi), unr = _oracle8192(mode, q8=True)
@@ -180,8 +182,9 @@ def test_fused_narrow_qk_multi_tile_b16_t8192(mode):
 # ------------------------------------------- ragged batch 64, paged 16, full
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("variant", ["K8V8", "K16V8", "K8V8_pre_bias"])
-def test_ragged_b64_paged_fused_full(variant):
+def test_ragged_b64_paged_fused_full(variant, layout):
     """The benchmark's ragged legs: 64 sequences of 1024-32768 keys, 32q/8kv,
     16-token blocks behind a shuffled table, biased keys; the fused split
     kernel with the plan (chunk 1024) and the merge.  Every (sequence, KV
@@ -192,7 +195,7 @@ def test_ragged_b64_paged_fused_full(variant):
     pre_bias = variant.endswith("pre_bias")
     w = synth.decode_b64_gqa4_ragged_paged()
     q_bits = synth.q_bf16_bits(w.seed, (w.batch, w.q_heads, w.head_dim))
-    fused, plain = _cache(mode, w), _cache(mode, w)
+    fused, plain = _cache(mode, w, layout=layout), _cache(mode, w, layout=layout)
     bias = None
     if pre_bias:
         bias = synth.kv_sequence_prebias(w, 0)[2]
@@ -216,7 +219,7 @@ def test_ragged_b64_paged_fused_full(variant):
     got = _bench_step(fused, w, torch.from_numpy(k_new).to(DEV), torch.from_numpy(v_new).to(DEV),
                       q, lens)
     want = _plain_decode(plain, w, q, lens)
-    ctx = (w.name, variant)
+    ctx = (w.name, variant, layout)
     _same_cache(fused, plain, ctx)
     assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (ctx, "output differs")
     del fused, plain
