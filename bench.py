@@ -49,8 +49,9 @@ the K side) with the K8V8-vs-K16V8 break-even and the per-side savings
 against BF16; a GQA-group sweep (G 1/4/8/16 at 8192 keys) and a batch sweep
 (1/4/16/64 at 2048 keys), K8V8 against BF16; the ragged batch-64 paged
 workload (32q/8kv, lengths 1024..32768, K8V8, K16V8 and K8V8 as a pre-bias
-residual cache with the exact key bias) and a page-size sweep (16/32/64/256
-tokens) on its first 16 sequences; block-scaled K (MXK8V8) against per-row
+residual cache with the exact key bias, in the head-major layout, and K8V8
+token-major beside them) and a page-size sweep (16/32/64/256 tokens) on its
+first 16 sequences; block-scaled K (MXK8V8) against per-row
 K8V8 with bf16 Q and with fp8 QK (block_scaled_k); the roofline of the split
 kernel and the CPU oracle as a baseline.  Rotations of the sweeps hold at
 least 1 GiB of cache (fewer copies only where a copy is tiny, labelled).
@@ -820,8 +821,8 @@ def bench_ragged(mode, replays=20, steps=8, pre_bias=False, w=None, layout="toke
 
 def bench_page_sizes(replays=10, steps=8):
     """Page-size sweep on a subset of the ragged workload: its first 16
-    sequences (same lengths, distributions and heads), K8V8, blocks of 16,
-    32, 64 and 256 tokens behind a shuffled table."""
+    sequences (same lengths, distributions and heads), K8V8, head-major
+    blocks of 16, 32, 64 and 256 tokens behind a shuffled table."""
     from fp8_kv_cache_append_amd import synth
 
     base = synth.decode_b64_gqa4_ragged_paged()
@@ -830,7 +831,7 @@ def bench_page_sizes(replays=10, steps=8):
         w = synth.Workload(f"decode_b16_hq32_hkv8_d128_ragged_paged{bs}", 16, 32, 8, 128,
                            base.lens[:16].copy(), "bias", block_size=bs, shuffle_blocks=True,
                            seed=base.seed)
-        r = bench_ragged("K8V8", replays, steps, w=w)
+        r = bench_ragged("K8V8", replays, steps, w=w, layout="head")
         res[str(bs)] = {k: r[k] for k in ("us_per_step", "split_us", "kv_gbs", "pct_roofline",
                                            "split_pct_roofline", "split_plan")}
         res[str(bs)]["validated"] = r["validation"]["validated"]
@@ -1135,8 +1136,8 @@ def main():
         return r
 
     if args.ragged_only:
-        print(json.dumps({"ragged_b64_paged": bench_ragged("K8V8", replays=4, steps=4)}),
-              flush=True)
+        print(json.dumps({"ragged_b64_paged": bench_ragged("K8V8", replays=4, steps=4,
+                                                           layout="head")}), flush=True)
         return
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill()}), flush=True)
@@ -1174,9 +1175,14 @@ def main():
         extras["sweep"] = leg("context sweep", bench_sweep, sw, ww, args.copies, head)
         extras["gqa"] = leg("GQA sweep", bench_gqa_sweep, sw, ww)
         extras["batch"] = leg("batch sweep", bench_batch_sweep, sw, ww)
-        extras["ragged"] = {m: leg(f"ragged {m}", bench_ragged, m) for m in ("K8V8", "K16V8")}
+        # the paged batch's page-internal order is free: head-major, the order
+        # the split kernel reads; token-major reported beside it
+        extras["ragged"] = {m: leg(f"ragged {m}", bench_ragged, m, layout="head")
+                            for m in ("K8V8", "K16V8")}
         extras["ragged"]["K8V8_pre_bias"] = leg("ragged pre-bias", bench_ragged, "K8V8",
-                                                pre_bias=True)
+                                                pre_bias=True, layout="head")
+        extras["ragged"]["K8V8_token_major"] = leg("ragged token-major", bench_ragged, "K8V8",
+                                                   layout="token")
         extras["page_sizes"] = leg("page sizes", bench_page_sizes)
         extras["block_scaled"] = leg("block-scaled K", bench_block_scaled, sw, args.copies)
     cpu = None
