@@ -37,6 +37,8 @@
 //
 // No LDS traffic on the K/V path; LDS holds the tile's per-token scales (so
 // each lane can read the four it needs) and the work-group merge.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -68,12 +70,17 @@ struct DecodeArgs {
   int ss;      // rows from one slot of a head to its next slot (slot_stride)
   uint64_t k_bytes;  // bytes of the K and V arrays (hardware bound of the tile loads)
   uint64_t v_bytes;
+  FastDiv div_hkv;     // by hkv
+  FastDiv div_bs;      // by bs
+  FastDiv div_splits;  // by n_splits
+  FastDiv div_pairs;   // by the (sequence, KV head) pairs of the grid
 };
 
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kMaxGroup = 16; // query heads per KV head (one MFMA column block)
 constexpr float kLazy = 8.0f; // log2 units the scores may exceed the reference by
+constexpr float kLazyP = 256.0f;  // 2^kLazy: the largest p = 2^(s - M) the reference allows
 
 // Raw (still compressed) K/V of one 64-token tile in the registers of one
 // lane, the scales of the lane's own token (token t0 + lane) and the
@@ -158,7 +165,7 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     const int tb = t0 + 16 * kb;
-    const int eb = tb / a.bs;
+    const int eb = a.div_bs.div(tb);
     const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
     blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
     all_ok = all_ok && blk_ok[kb];
@@ -241,11 +248,12 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
   }
 }
 
-// KV head of pair index pi (sequence pi / hkv): rotated by the sequence, so
-// that pairs 8k + x (one XCD) cover every head.
-__device__ __forceinline__ int rotated_head(int pi, int hkv) {
-  const int b = pi / hkv;
-  return (pi % hkv + hkv - b % hkv) % hkv;
+// KV head of pair index pi (sequence b = pi / hkv): rotated by the
+// sequence, h = (pi mod hkv - b mod hkv) mod hkv, so that pairs 8k + x (one
+// XCD) cover every head.
+__device__ __forceinline__ int rotated_head(int pi, int b, const FastDiv& div_hkv) {
+  const int h = (pi - b * div_hkv.d) - div_hkv.mod(b);
+  return h < 0 ? h + div_hkv.d : h;
 }
 
 
@@ -288,6 +296,8 @@ void decode_partial_kernel(DecodeArgs a) {
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
   constexpr bool kK8 = T::K8;
   constexpr bool kV8 = T::V8;
+  // the first tile's loads go out before the sequence length is known
+  constexpr bool kEarly = !TB && !MULTI;
 
   __shared__ float s_scale[kWaves][2][kTile];
   __shared__ uint32_t s_kx[k_is_mx(MODE) ? kWaves : 1][kTile];  // block-scaled K: E8M0 words
@@ -324,105 +334,72 @@ void decode_partial_kernel(DecodeArgs a) {
   // confined to one head's rows of the cache.  The merge kernel maps pair
   // pi to the same XCD and finds the partials in that L2.
   const int wg = blockIdx.x;
-  const int pairs = gridDim.x / a.n_splits;
+  const int pairs = a.div_pairs.d;
   int pi, split;
   if ((pairs & 7) == 0) {
     const int q = wg >> 3;
-    pi = (q / a.n_splits) * 8 + (wg & 7);
-    split = q % a.n_splits;
+    const int qd = a.div_splits.div(q);
+    pi = qd * 8 + (wg & 7);
+    split = q - qd * a.n_splits;
   } else {
-    pi = wg % pairs;
-    split = wg / pairs;
+    split = a.div_pairs.div(wg);
+    pi = wg - split * pairs;
   }
-  const int b = pi / a.hkv;
-  const int h = rotated_head(pi, a.hkv);
+  const int b = a.div_hkv.div(pi);
+  const int h = rotated_head(pi, b, a.div_hkv);
   const int bh = b * a.hkv + h;
   const int G = a.group;
   const int t_begin = split * a.chunk;
 
-  // First round trip, all independent: the sequence length, the block ids
-  // of this split (lane e: block t_begin / bs + e, index kept inside the
-  // table row; ids past the sequence are never used) and Q.  Without a
-  // table (contiguous cache) the block ids are computed, and the K/V loads
-  // need not wait for them.
-  const int len = a.seq_lens[b];  // clamped below to the block-table capacity
-  const int e_base = t_begin / a.bs;
+  // First round trip, all independent and issued in this order: the
+  // sequence length, the block ids of this split (lane e: block
+  // t_begin / bs + e, index kept inside the table row; ids past the
+  // sequence are never used), Q, the step's new K/V rows and the K bias.
+  // Nothing is written to LDS before the first tile's loads are out: a
+  // write of loaded data waits for its load, and the wait would sit in
+  // front of them.
+  //
+  // kEarly: the early tile's base addresses and bounds are read from the
+  // kernel arguments with the first ones.  Loaded only where they are used,
+  // they would come after the length's scalar load, and the wait for them
+  // (scalar loads return out of order: a wait for one is a wait for all)
+  // would wait for the length too.  After this statement the length is
+  // read with a vector load, whose wait counts in order.
+  if constexpr (kEarly)
+    asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.ks), "s"(a.vs), "s"(a.k_bytes), "s"(a.v_bytes));
+  int len = a.seq_lens[b];  // clamped below to the block-table capacity
+  const int e_base = a.div_bs.div(t_begin);
   const int64_t tab_i = (int64_t)b * a.mbps + min(e_base + lane, a.mbps - 1);
   int tab = (int)tab_i;  // no table: contiguous
   if constexpr (TB) tab = a.table[tab_i];
-  // Q^T, the B operand of QK, in LDS in operand order: s_q[kc][lane] is lane
-  // (g4, c)'s 16 bytes of head c for k-chunk kc.  Each wave loads a share.
+  // Q^T, the B operand of QK, goes to LDS in operand order: s_q[kc][lane] is
+  // lane (g4, c)'s 16 bytes of head c for k-chunk kc; wave kc loads chunk kc.
+  static_assert(KC <= kWaves, "one Q k-chunk per wave");
   const uint16_t* qrow = a.q + ((int64_t)b * a.hkv * G + (int64_t)h * G + min(c, G - 1)) * D;
+  u32x4_t qx = {0u, 0u, 0u, 0u};
   if constexpr (!Q8) {
-#pragma unroll
-    for (int kc = wave; kc < KC; kc += kWaves) {
-      // the d of the K bytes the lane converts for k-chunk kc
-      const int d0 = T::KPIECE * (kc >> 1) + T::KLANE * g4 + 8 * (kc & 1);
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      s_q[kc][lane] = (c < G) ? x : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  } else if (wave == 0) {
-    // Q8: lane (g4, c) takes head c's values at d = 64 p + 16 g4 + i
-    // (i < 16), the d of its K bytes, so byte i of piece p is the same
-    // contraction index in both operands.  amax over the row is the max over
-    // the four lane groups.
-    float4 xq[T::KP][4];
-    float m = 0.0f;
+    const int kc = min(wave, KC - 1);
+    // the d of the K bytes the lane converts for k-chunk kc
+    const int d0 = T::KPIECE * (kc >> 1) + T::KLANE * g4 + 8 * (kc & 1);
+    qx = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+  }
+  // Q8 and KB: lane (g4, c) takes head c's values at d = KPIECE p + KLANE g4
+  // + i (i < 16), the d of its K bytes (every wave loads them; wave 0
+  // quantises them for Q8).
+  constexpr int kQW = (Q8 || KB) ? T::KP : 1;
+  u32x4_t qw[kQW][2];
+  if constexpr (Q8 || KB) {
 #pragma unroll
     for (int p = 0; p < T::KP; ++p)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4_t w =
-            *reinterpret_cast<const u32x4_t*>(qrow + T::KPIECE * p + T::KLANE * g4 + 8 * j);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float4 f = make_float4(__uint_as_float(w[2 * e] << 16),
-                                       __uint_as_float(w[2 * e] & 0xffff0000u),
-                                       __uint_as_float(w[2 * e + 1] << 16),
-                                       __uint_as_float(w[2 * e + 1] & 0xffff0000u));
-          xq[p][2 * j + e] = f;
-          m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
-        }
-      }
-    // per-row rule: the row's scale (max over the four lane groups); block
-    // rule: piece p of lane group g4 lies in block 2p + g4 / 2, shared with
-    // lane group g4 ^ 1 (a 16-lane swap)
-    float q_scale = 0.0f;
-    float piece_scale[2] = {0.0f, 0.0f};
-    if constexpr (T::MX) {
-#pragma unroll
-      for (int p = 0; p < T::KP; ++p) {
-        float mp = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          mp = fmaxf(mp, fmaxf(fmaxf(fabsf(xq[p][e].x), fabsf(xq[p][e].y)),
-                               fmaxf(fabsf(xq[p][e].z), fabsf(xq[p][e].w))));
-        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mp), __float_as_uint(mp),
-                                                  false, false);
-        const int ep = mx_exponent(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-        piece_scale[p] = e8m0_value((uint32_t)(ep + 127));
-        if ((g4 & 1) == 0 && c < G) s_qx[c][2 * p + (g4 >> 1)] = (uint32_t)(ep + 127);
-      }
-    } else {
-      q_scale = max_over_groups(m) / kE4M3Max;
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      u32x4_t codes = {0u, 0u, 0u, 0u};  // D = 64: the upper 16 k-slots are zero
-      if (p < T::KP) {
-        const float sc = T::MX ? piece_scale[p < T::KP ? p : 0] : q_scale;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) codes[e] = e4m3_codes4(xq[p < T::KP ? p : 0][e], sc);
-      }
-      s_q8[p][lane] = (c < G) ? codes : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (g4 == 0 && c < G) s_qs[c] = T::MX ? 1.0f : q_scale;
+      for (int j = 0; j < 2; ++j)
+        qw[p][j] = *reinterpret_cast<const u32x4_t*>(qrow + T::KPIECE * p + T::KLANE * g4 + 8 * j);
   }
   // Fused append: lanes [0, D/4) hold four values of the K row, lanes
-  // [D/4, D/2) four of the V row, loaded with the first round trip.  Every
-  // lane loads (the lanes past D/2 repeat the first ones): a load under a
-  // lane condition would make the compiler wait for all later loads, tile
-  // data included, before the values can be used.
+  // [D/4, D/2) four of the V row.  Every lane loads (the lanes past D/2
+  // repeat the first ones): a load under a lane condition would make the
+  // compiler wait for all later loads, tile data included, before the
+  // values can be used.
   constexpr int kLR = D / 4;  // lanes per row
   float4 xnew = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (APPEND) {
@@ -430,52 +407,69 @@ void decode_partial_kernel(DecodeArgs a) {
     xnew = *reinterpret_cast<const float4*>((l2 < kLR ? a.k_new : a.v_new) +
                                             ((int64_t)b * a.hkv + h) * D + 4 * (l2 % kLR));
   }
-  // KB: (q . b) of head c, in log2 units of the score.  Lane (g4, c) takes
-  // d = 64 p + 16 g4 + i (i < 16) and the four lane groups are summed; the
-  // loads follow the first round trip's, so waiting for them costs no extra
-  // round trip (the block ids are needed before any tile load anyway).
-  float qb_c = 0.0f;
+  // KB: the bias values at the same d as qw
+  constexpr int kBW = KB ? T::KP : 1;
+  f32x4_t bw[kBW][2][2];
   if constexpr (KB) {
     const float* brow = a.kbias + (int64_t)h * D;
-    float part = 0.0f;
 #pragma unroll
     for (int p = 0; p < T::KP; ++p)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int d0 = 64 * p + 16 * g4 + 8 * j;
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-        const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(brow + d0);
-        const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(brow + d0 + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x4_t& bb = e < 2 ? b0 : b1;
-          part += __uint_as_float(w[e] << 16) * bb[2 * (e & 1)];
-          part += __uint_as_float(w[e] & 0xffff0000u) * bb[2 * (e & 1) + 1];
-        }
+        const int d0 = T::KPIECE * p + T::KLANE * g4 + 8 * j;
+        bw[p][j][0] = *reinterpret_cast<const f32x4_t*>(brow + d0);
+        bw[p][j][1] = *reinterpret_cast<const f32x4_t*>(brow + d0 + 4);
       }
-    qb_c = sum_over_groups(part) * a.c_scale;
   }
-  const int t_end = min(min(max(len, 0), a.mbps * a.bs), t_begin + a.chunk);
-
-  float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
-  float* pml = a.part_ml + ((int64_t)bh * a.n_splits + split) * G * 2;
-  // The test below reads both the length and the block ids (no block id is
-  // INT_MIN, so the second term is always true).  Without it the compiler
-  // sinks the table load below the branch on the length, adding a whole
-  // memory round trip before the first K/V load.
-  const bool empty = (t_begin >= t_end) & (__builtin_amdgcn_readfirstlane(tab) != INT_MIN);
-  if (empty) {  // no key in this split
-    for (int i = threadIdx.x; i < G; i += blockDim.x) {
-      pml[2 * i] = -INFINITY;
-      pml[2 * i + 1] = 0.0f;
-    }
-    return;
-  }
+  float qb_c = 0.0f;  // KB: (q . b) of head c, in log2 units of the score
 
   LaneOffsets lo;
   lo.k = (uint32_t)(c * a.ss) * (D * T::KE) + T::KLANE * T::KE * g4;
   lo.v = (uint32_t)(4 * g4 * a.ss) * (D * T::VE) + DPR * T::VE * c;
   lo.v_token = (uint32_t)wave_uniform(a.ss * D * T::VE);
+
+  // kEarly (no block table, one tile per wave): the first tile's addresses
+  // depend on nothing in memory, so its loads go out now, with the first
+  // round trip, as if the split held every key up to its end or the
+  // block-table capacity (t_cap): every row they read lies inside the cache.
+  // Once the length is known the tile's flags are narrowed to it, and a
+  // wave whose tile turns out to lie past the length does not compute it.
+  // A split with no key at all leaves only after the barrier below: a
+  // return before it would let the compiler move these loads after the
+  // test, behind the length.  Otherwise the loads wait for the length, and
+  // with a table for the block ids.  (The split kernel that streams several
+  // tiles per wave issues its first tile after the length: with the early
+  // tile's registers live from the start it runs out of scalar registers.)
+  const int t_cap = min(a.mbps * a.bs, t_begin + a.chunk);
+  T buf;
+  if constexpr (kEarly) {
+    load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_cap, tab, e_base, h, lane,
+                       t_begin + wave * kTile < t_cap);
+    // (the length, loaded before the tile, is used only from here on: the
+    // compiler would otherwise move its wait in front of the tile's loads)
+    asm volatile("" : "+v"(len));
+    len = __builtin_amdgcn_readfirstlane(len);
+  }
+  const int t_end = min(max(len, 0), t_cap);
+
+  float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
+  float* pml = a.part_ml + ((int64_t)bh * a.n_splits + split) * G * 2;
+  const bool empty = t_begin >= t_end;  // no key in this split
+  auto leave_empty = [&]() __attribute__((always_inline)) {
+    for (int i = threadIdx.x; i < G; i += blockDim.x) {
+      pml[2 * i] = -INFINITY;
+      pml[2 * i + 1] = 0.0f;
+    }
+  };
+  if constexpr (!kEarly) {
+    // The test reads the block ids too (no block id is INT_MIN, so the
+    // second term is always true): without it the compiler sinks the table
+    // load below the branch, a whole round trip before the first K/V load.
+    if (empty & (__builtin_amdgcn_readfirstlane(tab) != INT_MIN)) {
+      leave_empty();
+      return;
+    }
+  }
 
   // Fused append: the new token (position len - 1, only if it lies inside
   // the block table) belongs to this split's tiles; the wave that attends it
@@ -493,14 +487,15 @@ void decode_partial_kernel(DecodeArgs a) {
   auto append_new = [&]() __attribute__((always_inline)) {
     if constexpr (!APPEND) return;  // (s_new is a placeholder then)
     const int p = pos_n;
-    const int blk = __builtin_amdgcn_readlane(tab, p / a.bs - e_base);
+    const int pb = a.div_bs.div(p);
+    const int blk = __builtin_amdgcn_readlane(tab, pb - e_base);
     const bool is_v = lane >= kLR;
     const bool quantise = is_v ? kV8 : kK8;
     const float scale = row_amax<kLR>(xnew) / kE4M3Max;
     const int sub = lane % kLR;
     if (lane == 0) {
       const int64_t row = (unsigned)blk < (unsigned)a.num_blocks
-                              ? cache_row(a.layout, blk, p % a.bs, h, a.bs, a.hkv)
+                              ? cache_row(a.layout, blk, p - pb * a.bs, h, a.bs, a.hkv)
                               : -1;  // invalid block: not stored, key excluded
       s_new[D + 2] = (uint32_t)row;
       s_new[D + 3] = (uint32_t)((uint64_t)row >> 32);
@@ -600,12 +595,13 @@ void decode_partial_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < DPR; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // One tile, in two halves of 32 keys (sub-blocks 2kp and 2kp+1, PV chunk
-  // kp): QK, an online-softmax step, PV.  The second half's data may still be
-  // arriving while the first is computed.  The scales are staged through this
-  // wave's slice of LDS (written and read by the same wave; its LDS operations
-  // complete in order, and the previous tile's reads precede these writes in
-  // program order).
+  // A tile is computed whole (QK of its four sub-blocks, one online-softmax
+  // step, PV) or, in the streaming loop, in two halves of 32 keys (sub-blocks
+  // 2kp and 2kp+1, PV chunk kp), so that the second half's data may still be
+  // arriving while the first is computed.  Its scales are staged through this
+  // wave's slice of LDS first (written and read by the same wave; its LDS
+  // operations complete in order, and the previous tile's reads precede these
+  // writes in program order).
   auto compute_head = [&](T& cur, int t0) __attribute__((always_inline)) {
     const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
     if (has_new) patch_scales(cur, t0);
@@ -616,99 +612,130 @@ void decode_partial_kernel(DecodeArgs a) {
     if (kV8) s_scale[wave][1][lane] = cur.tok_ok ? cur.vs : 0.0f;
     __builtin_amdgcn_wave_barrier();
   };
-  // Half kp of the tile: its sub-blocks' flags (full: every key of the tile
-  // valid; ok0, ok1: the block ids of sub-blocks 2kp and 2kp+1 valid) are
-  // passed in, so that the next tile's first part may already have replaced
-  // the tile's own while its second half is computed.
-  auto compute_half = [&](T& cur, int t0, int kp, bool full, bool ok0, bool ok1)
-      __attribute__((always_inline)) {
-    {
-      const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
-      if (has_new) patch_half(cur, t0, kp);
-      // --- QK on the matrix cores for sub-blocks 2kp, 2kp+1
-      f32x4_t sacc[2];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int kb = 2 * kp + hb;
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Q8) {
-          // the K codes as loaded: one fp8 instruction per 16 keys
-          const u32x4_t k0 = cur.k[kb][0];
-          const u32x4_t k1 = T::KP == 2 ? cur.k[kb][T::KP - 1] : u32x4_t{0u, 0u, 0u, 0u};
-          const u32x4_t q0 = s_q8[0][lane], q1 = s_q8[1][lane];
-          // (built with a shuffle: element-wise construction with the zero
-          // half of head_dim 64 sends the operand through scratch memory)
-          const i32x8_t av =
-              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
-          const i32x8_t bq =
-              __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-          if constexpr (T::MX) {
-            // the lane's K block: head_dim 128 block g4, 64 block g4 / 2
-            // the instruction takes the scale of K block g4 from lane group g4
-            const int kexp =
-                g4 < D / 32 ? (int)((s_kx[wave][16 * kb + c] >> (8 * g4)) & 0xffu) : 127;
-            s = mfma_16x16x128_e4m3_scaled(av, bq, s, kexp, q_exp_c);
-          } else {
-            s = mfma_16x16x128_e4m3(av, bq, s);
-          }
-        } else {
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            u32x4_t av;
-            if (T::MX) {
-              // codes times the lane's block scale (exact in bf16)
-              // piece kc / 2 of lane group g4 lies in block 2 (kc / 2) + g4 / 2
-              const float ksc = e8m0_value(
-                  (s_kx[wave][16 * kb + c] >> (8 * (2 * (kc >> 1) + (g4 >> 1)))) & 0xffu);
-              const u32x4_t w = cur.k[kb][kc >> 1];
-              const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
-              av = u32x4_t{e4m3x2_to_bf16x2_scaled(lo32, ksc, false),
-                           e4m3x2_to_bf16x2_scaled(lo32, ksc, true),
-                           e4m3x2_to_bf16x2_scaled(hi32, ksc, false),
-                           e4m3x2_to_bf16x2_scaled(hi32, ksc, true)};
-            } else if (kK8) {
-              const u32x4_t w = cur.k[kb][kc >> 1];
-              const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
-              av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
-                           e4m3x2_to_bf16x2<false>(hi32), e4m3x2_to_bf16x2<true>(hi32)};
-            } else {
-              av = cur.k[kb][kc];
-            }
-            s = mfma_16x16x32_bf16(av, s_q[kc][lane], s);
-          }
-        }
-        sacc[hb] = s;
+  // QK of sub-block kb on the matrix cores: S^T for its 16 keys (rows) and
+  // the 16 query-head columns.
+  auto qk_block = [&](T& cur, int kb) __attribute__((always_inline)) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (Q8) {
+      // the K codes as loaded: one fp8 instruction per 16 keys
+      const u32x4_t k0 = cur.k[kb][0];
+      const u32x4_t k1 = T::KP == 2 ? cur.k[kb][T::KP - 1] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t q0 = s_q8[0][lane], q1 = s_q8[1][lane];
+      // (built with a shuffle: element-wise construction with the zero
+      // half of head_dim 64 sends the operand through scratch memory)
+      const i32x8_t av =
+          __builtin_bit_cast(i32x8_t, __builtin_shufflevector(k0, k1, 0, 1, 2, 3, 4, 5, 6, 7));
+      const i32x8_t bq =
+          __builtin_bit_cast(i32x8_t, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
+      if constexpr (T::MX) {
+        // the lane's K block: head_dim 128 block g4, 64 block g4 / 2
+        // the instruction takes the scale of K block g4 from lane group g4
+        const int kexp = g4 < D / 32 ? (int)((s_kx[wave][16 * kb + c] >> (8 * g4)) & 0xffu) : 127;
+        s = mfma_16x16x128_e4m3_scaled(av, bq, s, kexp, q_exp_c);
+      } else {
+        s = mfma_16x16x128_e4m3(av, bq, s);
       }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        u32x4_t av;
+        if (T::MX) {
+          // codes times the lane's block scale (exact in bf16)
+          // piece kc / 2 of lane group g4 lies in block 2 (kc / 2) + g4 / 2
+          const float ksc = e8m0_value(
+              (s_kx[wave][16 * kb + c] >> (8 * (2 * (kc >> 1) + (g4 >> 1)))) & 0xffu);
+          const u32x4_t w = cur.k[kb][kc >> 1];
+          const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
+          av = u32x4_t{e4m3x2_to_bf16x2_scaled(lo32, ksc, false),
+                       e4m3x2_to_bf16x2_scaled(lo32, ksc, true),
+                       e4m3x2_to_bf16x2_scaled(hi32, ksc, false),
+                       e4m3x2_to_bf16x2_scaled(hi32, ksc, true)};
+        } else if (kK8) {
+          const u32x4_t w = cur.k[kb][kc >> 1];
+          const uint32_t lo32 = w[2 * (kc & 1)], hi32 = w[2 * (kc & 1) + 1];
+          av = u32x4_t{e4m3x2_to_bf16x2<false>(lo32), e4m3x2_to_bf16x2<true>(lo32),
+                       e4m3x2_to_bf16x2<false>(hi32), e4m3x2_to_bf16x2<true>(hi32)};
+        } else {
+          av = cur.k[kb][kc];
+        }
+        s = mfma_16x16x32_bf16(av, s_q[kc][lane], s);
+      }
+    }
+    return s;
+  };
 
-      // --- scores in log2 units: (q . K) * (k_scale * sm_scale * log2 e);
-      //     k-slot j of the PV chunk is token 16*(2kp + j/4) + 4*g4 + j%4
-      float sc[8], vsc[8];
+  // One online-softmax step over the NB sub-blocks kb0 .. kb0 + NB - 1 of a
+  // tile (NB 2: one 32-key half, NB 4: the whole tile), then their PV chunks
+  // kb0 / 2 .. (kb0 + NB) / 2 - 1.  okb[kb]: the block id of sub-block kb is
+  // valid; full: every key of the tile is valid.  The flags come in as
+  // values, so that the next tile's first part may already have replaced the
+  // tile's own while its second half is computed.
+  //
+  // Scores: s = (q . K) * mult + add in log2 units, mult = k_scale * sm_scale
+  // * log2(e) (times the query row's scale on the narrow path), add = (q . b)
+  // * sm_scale * log2(e) for a K bias.  p = 2^(s - M) against the integer
+  // reference M, computed as one fma into the exp2.  M moves (lazily) only
+  // when a score exceeds it by more than kLazy; such a score makes its p
+  // exceed 2^kLazy and with it its lane's sum of p, so only then (or while
+  // no reference is set) is the row maximum taken and the step redone with
+  // the exact rule.  That is the decision of comparing every row maximum
+  // with M + kLazy, without the maximum on the common path.
+  auto attend = [&](T& cur, int t0, auto nb_c, int kb0, bool full, const bool (&okb)[4])
+      __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_c)::value;
+    constexpr int NS = 4 * NB;  // scores per lane
+    const bool has_new = APPEND && pos_n >= t0 && pos_n < t0 + kTile;  // wave-uniform
+    if (has_new) {
+#pragma unroll
+      for (int kp = kb0 / 2; kp < (kb0 + NB) / 2; ++kp) patch_half(cur, t0, kp);
+    }
+    f32x4_t sacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sacc[nb] = qk_block(cur, kb0 + nb);
+
+    // per key: mult, v_scale, validity; score j is token
+    // 16 * (kb0 + j / 4) + 4 * g4 + j % 4 (k-slot j % 8 of its PV chunk)
+    float mult[NS], vsc[NS];
+    bool okk[NS];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int kb = kb0 + nb;
+      const int base = 16 * kb + 4 * g4;
+      f32x4_t ksv = {a.c_scale, a.c_scale, a.c_scale, a.c_scale};
+      f32x4_t vsv = {1.f, 1.f, 1.f, 1.f};
+      if (T::KS) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
+      if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mult[4 * nb + i] = Q8 ? ksv[i] * q_scale_c : ksv[i];
+        vsc[4 * nb + i] = vsv[i];
+        okk[4 * nb + i] = full || ((t0 + base + i < t_end) && okb[kb]);
+      }
+    }
+    const float add = KB ? qb_c : 0.0f;
+
+    float p[NS];
+    float psum = 0.0f;
+    {
+      const float off = add - (m_run == -INFINITY ? 0.0f : m_run);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float arg = okk[j] ? __builtin_fmaf(sacc[j >> 2][j & 3], mult[j], off) : -INFINITY;
+        p[j] = __builtin_amdgcn_exp2f(arg);
+        psum += p[j];
+      }
+    }
+    const bool redo = (m_run == -INFINITY) || !(psum <= kLazyP);
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {  // wave-uniform, rare
+      float sc[NS];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int kb = 2 * kp + hb;
-        const int base = 16 * kb + 4 * g4;
-        f32x4_t ksv = {a.c_scale, a.c_scale, a.c_scale, a.c_scale};
-        f32x4_t vsv = {1.f, 1.f, 1.f, 1.f};
-        if (T::KS) ksv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][0][base]);
-        if (kV8) vsv = *reinterpret_cast<const f32x4_t*>(&s_scale[wave][1][base]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = (Q8 ? sacc[hb][i] * q_scale_c : sacc[hb][i]) * ksv[i];
-          if (KB) s += qb_c;
-          if (!full) {
-            const bool ok = (t0 + base + i < t_end) && (hb == 0 ? ok0 : ok1);
-            s = ok ? s : -INFINITY;
-          }
-          sc[4 * hb + i] = s;
-          vsc[4 * hb + i] = vsv[i];
-          tmax = fmaxf(tmax, s);
-        }
+      for (int j = 0; j < NS; ++j) {
+        sc[j] = okk[j] ? __builtin_fmaf(sacc[j >> 2][j & 3], mult[j], add) : -INFINITY;
+        tmax = fmaxf(tmax, sc[j]);
       }
       tmax = max_over_groups(tmax);
-
-      // --- online softmax step with a lazily moved integer reference; a
-      //     half with no valid key (tmax = -inf) leaves the state unchanged
+      // a step with no valid key (tmax = -inf) leaves the state unchanged
       const float t_ref = ceilf(tmax);
       if (m_run == -INFINITY) {
         m_run = t_ref;  // l and acc are still zero: nothing to rescale
@@ -722,15 +749,22 @@ void decode_partial_kernel(DecodeArgs a) {
       // exp2(-inf - m) is 0 for finite m; m is -inf only while every score
       // so far is -inf, and then the reference 0 avoids -inf - -inf.
       const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+      psum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(sc[j] - m_ref);
+        psum += p[j];
+      }
+    }
+    l_run += psum;
 
+#pragma unroll
+    for (int ch = 0; ch < NB / 2; ++ch) {
+      const int kp = kb0 / 2 + ch;
       // --- P with the V scale folded in, rounded to bf16: B operand of PV
       float pv[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(sc[j] - m_ref);
-        l_run += p;
-        pv[j] = p * vsc[j];
-      }
+      for (int j = 0; j < 8; ++j) pv[j] = p[8 * ch + j] * vsc[8 * ch + j];
       const u32x4_t pb = {f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
                           f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
 
@@ -740,8 +774,7 @@ void decode_partial_kernel(DecodeArgs a) {
       if (!full) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int kb = 2 * kp + (j >> 2);
-          const bool ok = (t0 + 16 * kb + 4 * g4 + (j & 3) < t_end) && ((j >> 2) == 0 ? ok0 : ok1);
+          const bool ok = okk[8 * ch + j];
 #pragma unroll
           for (int e = 0; e < T::VW; ++e) vv[j][e] = ok ? vv[j][e] : 0u;
         }
@@ -772,10 +805,17 @@ void decode_partial_kernel(DecodeArgs a) {
       }
     }
   };
+  using Half = std::integral_constant<int, 2>;
+  using Whole = std::integral_constant<int, 4>;
+  // Half kp of the tile (the streaming loop).
+  auto compute_half = [&](T& cur, int t0, int kp, bool full, const bool (&okb)[4])
+      __attribute__((always_inline)) { attend(cur, t0, Half{}, 2 * kp, full, okb); };
+  // The whole tile in one step: its four sub-blocks' QK, one online-softmax
+  // step, both PV chunks, so the scheduler has four independent chains.
   auto compute = [&](T& cur, int t0) __attribute__((always_inline)) {
     compute_head(cur, t0);
-    compute_half(cur, t0, 0, cur.full, cur.blk_ok[0], cur.blk_ok[1]);
-    compute_half(cur, t0, 1, cur.full, cur.blk_ok[2], cur.blk_ok[3]);
+    const bool okb[4] = {cur.blk_ok[0], cur.blk_ok[1], cur.blk_ok[2], cur.blk_ok[3]};
+    attend(cur, t0, Whole{}, 0, cur.full, okb);
   };
 
   // Tiles are dealt round-robin to the waves: wave w takes tiles w, w + 4,
@@ -794,11 +834,97 @@ void decode_partial_kernel(DecodeArgs a) {
   // is issued empty, see load_tile), so the waits before each compute step
   // are exact.
   const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
-  T buf;
-  load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
-                     wave < n_tiles);
+  if constexpr (!kEarly)
+    load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
+                       wave < n_tiles);
+  // The first round trip's data, now that the tile loads are out: Q to LDS
+  // (narrow QK: quantised first), the K bias product.
+  if constexpr (!Q8) {
+    if (wave < KC) s_q[wave][lane] = (c < G) ? qx : u32x4_t{0u, 0u, 0u, 0u};
+  } else if (wave == 0) {
+    // Q8: byte i of piece p is the same contraction index in the Q codes
+    // and the lane's K bytes.  amax over the row is the max over
+    // the four lane groups.
+    float4 xq[T::KP][4];
+    float m = 0.0f;
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t w = qw[p][j];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float4 f = make_float4(__uint_as_float(w[2 * e] << 16),
+                                       __uint_as_float(w[2 * e] & 0xffff0000u),
+                                       __uint_as_float(w[2 * e + 1] << 16),
+                                       __uint_as_float(w[2 * e + 1] & 0xffff0000u));
+          xq[p][2 * j + e] = f;
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        }
+      }
+    // per-row rule: the row's scale (max over the four lane groups); block
+    // rule: piece p of lane group g4 lies in block 2p + g4 / 2, shared with
+    // lane group g4 ^ 1 (a 16-lane swap)
+    float q_scale = 0.0f;
+    float piece_scale[2] = {0.0f, 0.0f};
+    if constexpr (T::MX) {
+#pragma unroll
+      for (int p = 0; p < T::KP; ++p) {
+        float mp = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          mp = fmaxf(mp, fmaxf(fmaxf(fabsf(xq[p][e].x), fabsf(xq[p][e].y)),
+                               fmaxf(fabsf(xq[p][e].z), fabsf(xq[p][e].w))));
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mp), __float_as_uint(mp),
+                                                  false, false);
+        const int ep = mx_exponent(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+        piece_scale[p] = e8m0_value((uint32_t)(ep + 127));
+        if ((g4 & 1) == 0 && c < G) s_qx[c][2 * p + (g4 >> 1)] = (uint32_t)(ep + 127);
+      }
+    } else {
+      q_scale = max_over_groups(m) / kE4M3Max;
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x4_t codes = {0u, 0u, 0u, 0u};  // D = 64: the upper 16 k-slots are zero
+      if (p < T::KP) {
+        const float sc = T::MX ? piece_scale[p < T::KP ? p : 0] : q_scale;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) codes[e] = e4m3_codes4(xq[p < T::KP ? p : 0][e], sc);
+      }
+      s_q8[p][lane] = (c < G) ? codes : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (g4 == 0 && c < G) s_qs[c] = T::MX ? 1.0f : q_scale;
+  }
+  // KB: (q . b) of head c, in log2 units of the score; the lane's products
+  // at its d, summed over the four lane groups.
+  if constexpr (KB) {
+    float part = 0.0f;
+#pragma unroll
+    for (int p = 0; p < T::KP; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4_t& bb = bw[p][j][e >> 1];
+          part += __uint_as_float(qw[p][j][e] << 16) * bb[2 * (e & 1)];
+          part += __uint_as_float(qw[p][j][e] & 0xffff0000u) * bb[2 * (e & 1) + 1];
+        }
+    qb_c = sum_over_groups(part) * a.c_scale;
+  }
+  if constexpr (kEarly) {  // narrow the early tile's flags to the length
+    const int t0 = t_begin + wave * kTile;
+    buf.full = buf.full && t0 + kTile <= t_end;
+    buf.tok_ok = buf.tok_ok && t0 + lane < t_end;
+  }
   if (APPEND && pos_n >= 0) append_new();
   __syncthreads();  // s_q complete (after the first tiles' loads are in flight)
+  if constexpr (kEarly) {
+    if (empty) {
+      leave_empty();
+      return;
+    }
+  }
   // Q8: the query row's scale of head c (0 for the padding heads c >= G,
   // whose B columns are zero)
   if constexpr (Q8) q_scale_c = (c < G) ? s_qs[c] : 0.0f;
@@ -815,10 +941,11 @@ void decode_partial_kernel(DecodeArgs a) {
       // computed, its second part after the second half
       const int t0 = t_begin + tile * kTile, tn = t0 + kWaves * kTile;
       compute_head(buf, t0);
-      const bool full = buf.full, ok2 = buf.blk_ok[2], ok3 = buf.blk_ok[3];
-      compute_half(buf, t0, 0, full, buf.blk_ok[0], buf.blk_ok[1]);
+      const bool full = buf.full;
+      const bool okb[4] = {buf.blk_ok[0], buf.blk_ok[1], buf.blk_ok[2], buf.blk_ok[3]};
+      compute_half(buf, t0, 0, full, okb);
       load_tile<MODE, D, 0>(buf, a, lo, tn, t_end, tab, e_base, h, lane, true);
-      compute_half(buf, t0, 1, full, ok2, ok3);
+      compute_half(buf, t0, 1, full, okb);
       load_tile<MODE, D, 1>(buf, a, lo, tn, t_end, tab, e_base, h, lane, true);
     }
     compute(buf, t_begin + tile * kTile);
@@ -889,27 +1016,31 @@ void decode_partial_kernel(DecodeArgs a) {
 // combined online with power-of-two weights; the groups then meet through
 // lane swaps, again with power-of-two weights.
 template <int D, int MB>
-__global__ __launch_bounds__(64) void decode_merge_kernel(int hkv, int group, int n_splits,
+__global__ __launch_bounds__(64) void decode_merge_kernel(FastDiv div_hkv, FastDiv div_group,
+                                                          int n_splits,
                                                           const float* __restrict__ part_acc,
                                                           const float* __restrict__ part_ml,
                                                           float* __restrict__ out) {
+  const int hkv = div_hkv.d, group = div_group.d;
   constexpr int L = D / 4;    // lanes per split group, four values each
   constexpr int NG = 64 / L;  // split groups of the wave
   // Work-group -> (pair, head).  As in the split kernel, when the pairs come
   // in multiples of eight, pair pi = 8k + x runs on XCD x (work-group
   // w = 8q + x), which holds its partials in L2.
   const int w = blockIdx.x;
-  const int pairs = gridDim.x / group;
+  const int pairs = div_group.div(gridDim.x);
   int pi, g;
   if ((pairs & 7) == 0) {
     const int q = w >> 3;
-    pi = (q / group) * 8 + (w & 7);
-    g = q % group;
+    const int qd = div_group.div(q);
+    pi = qd * 8 + (w & 7);
+    g = q - qd * group;
   } else {
-    pi = w / group;
-    g = w % group;
+    pi = div_group.div(w);
+    g = w - pi * group;
   }
-  const int bh = (pi / hkv) * hkv + rotated_head(pi, hkv);
+  const int b = div_hkv.div(pi);
+  const int bh = b * hkv + rotated_head(pi, b, div_hkv);
   const int lane = threadIdx.x;
   const int sg = lane / L;
   const int d4 = lane % L;
@@ -1050,7 +1181,9 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
   DecodeArgs a{c.k,     c.v,       c.ks,    c.vs,    c.table,  q,       seq_lens,
                part_acc, part_ml,  k_new,   v_new,   c.kbias,  c.kexp,  c_scale,
                c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks,
-               c.layout, slot_stride(c.layout, c.hkv), k_bytes, v_bytes};
+               c.layout, slot_stride(c.layout, c.hkv), k_bytes, v_bytes,
+               FastDiv::of(c.hkv), FastDiv::of(c.bs), FastDiv::of(n_splits),
+               FastDiv::of(batch * c.hkv)};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);
@@ -1066,14 +1199,14 @@ static void launch_merge_d(unsigned n_wg, int hkv, int group, int n_splits,
   constexpr int NG = 64 / (D / 4);  // split groups per wave
   const int per_group = (n_splits + NG - 1) / NG;
   if (per_group <= 4)
-    hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(n_wg), dim3(64), 0, stream, hkv,
-                       group, n_splits, part_acc, part_ml, out);
+    hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(n_wg), dim3(64), 0, stream,
+                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
   else if (per_group <= 8)
-    hipLaunchKernelGGL((decode_merge_kernel<D, 8>), dim3(n_wg), dim3(64), 0, stream, hkv,
-                       group, n_splits, part_acc, part_ml, out);
+    hipLaunchKernelGGL((decode_merge_kernel<D, 8>), dim3(n_wg), dim3(64), 0, stream,
+                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<D, 16>), dim3(n_wg), dim3(64), 0, stream, hkv,
-                       group, n_splits, part_acc, part_ml, out);
+    hipLaunchKernelGGL((decode_merge_kernel<D, 16>), dim3(n_wg), dim3(64), 0, stream,
+                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
 }
 
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,

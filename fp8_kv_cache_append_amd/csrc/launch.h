@@ -33,6 +33,30 @@ __host__ __device__ inline int slot_stride(int layout, int hkv) {
   return layout == kHeadMajor ? 1 : hkv;
 }
 
+// Division by a divisor fixed for a launch (head count, block size, split
+// count) as a multiply-high, an add and a shift instead of the ~20
+// instructions of a general integer division: the round-up method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication" (PLDI 1994), section 4.  With l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1 (below 2^32 for every d >= 1),
+// floor(n / d) = (mulhi(m, n) + n) >> l for every n < 2^32; the sum needs a
+// 33rd bit only for n >= 2^31, so dividends are kept below 2^31.
+struct FastDiv {
+  uint32_t m;
+  uint32_t l;
+  int d;
+  static FastDiv of(int d) {  // d >= 1
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < (uint64_t)d) ++l;
+    const uint64_t m = (((uint64_t(1) << l) - (uint64_t)d) << 32) / (uint64_t)d + 1;
+    return FastDiv{(uint32_t)m, l, d};
+  }
+  __device__ __forceinline__ int div(int n) const {  // 0 <= n < 2^31
+    return (int)((__umulhi(m, (uint32_t)n) + (uint32_t)n) >> l);
+  }
+  __device__ __forceinline__ int mod(int n) const { return n - div(n) * d; }
+};
+
 struct CacheView {
   int mode;   // kK8V8 / kK16V8 / kBF16 / kK8V16 / kMXK8V8
   int bs;     // tokens per block (multiple of 16)
