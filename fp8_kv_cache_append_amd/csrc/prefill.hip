@@ -37,10 +37,11 @@
 //
 // Memory pipeline, per group: the block ids of tile n + 3 are fetched while
 // tile n + 2's codes are loaded, tile n + 1 is staged to LDS and tile n is
-// computed.  Every load is issued unconditionally from an address inside the
-// cache (a key that does not exist reads row 0 and is neutralised when
-// staged), so the only wait per tile is for loads issued a whole tile
-// earlier.  Each lane follows one 16-key sub-block through the sequence with
+// computed.  Every load of a tile that exists is issued, for every lane,
+// from an address inside the cache (a key that does not exist reads row 0
+// and is neutralised when staged), so the only wait per tile is for loads
+// issued a whole tile earlier; past the group's last tile nothing is
+// loaded.  Each lane follows one 16-key sub-block through the sequence with
 // a (block index, offset) cursor: no division per tile.
 //
 // LDS reuse: iteration j computes on buffer j & 1 and meanwhile stages tile
@@ -74,6 +75,10 @@ struct PrefillArgs {
   int total_q;
   int num_blocks;
   int layout;  // kTokenMajor / kHeadMajor (cache_row)
+  FastDiv div_hq;     // by the query heads hkv * group
+  FastDiv div_nqt;    // by n_qt
+  FastDiv div_group;  // by group
+  FastDiv div_bs;     // by bs
 };
 
 constexpr int kPGroups = 2;                   // key groups (alternate tiles)
@@ -83,6 +88,7 @@ constexpr int kCB = 2;    // MFMA column blocks (16 query rows each) per wave
 constexpr int kQT = 16 * kCB * kPRowWaves;  // queries per tile (128)
 constexpr int kKT = 64;   // keys per tile
 constexpr float kPLazy = 8.0f;  // log2 units the scores may exceed the reference by
+constexpr float kPLazyP = 256.0f;  // 2^kPLazy: the largest p = 2^(s - M) the reference allows
 
 template <int MODE, int D>
 struct PrefillShape {
@@ -133,7 +139,10 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t r[4], uint32_t
   out[3] = byte_perm(p23h, p01h, 0x07060302u);
 }
 
-template <int MODE, int D>
+// TB: the cache has a block table in memory; without one (contiguous cache)
+// the block ids are computed, a variant of its own so that no wait for a
+// table load joins the paths of the loads.
+template <int MODE, int D, bool TB>
 __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a) {
   using S = PrefillShape<MODE, D>;
   using Tile = PrefillTile<MODE, D>;
@@ -151,21 +160,29 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   const int c = lane & 15;
 
   // Largest query tiles first: causal work grows with the tile index.
-  const int hq = a.hkv * a.group;
-  const int h = blockIdx.x % hq;
-  const int rest = blockIdx.x / hq;
-  const int qt = a.n_qt - 1 - (rest % a.n_qt);
-  const int b = rest / a.n_qt;
-  const int hk = h / a.group;
+  const int hq = a.div_hq.d;
+  const int rest = a.div_hq.div(blockIdx.x);
+  const int h = blockIdx.x - rest * hq;
+  const int b = a.div_nqt.div(rest);
+  const int qt = a.n_qt - 1 - (rest - b * a.n_qt);
+  const int hk = a.div_group.div(h);
 
   // Device data is clamped so that no access leaves the buffers: query rows
-  // stay inside [0, total_q), lengths inside the block-table capacity.
-  const int q_begin = min(max(a.cu_q[b], 0), a.total_q);
-  const int q_end = min(max(a.cu_q[b + 1], q_begin), a.total_q);
+  // stay inside [0, total_q), lengths inside the block-table capacity.  The
+  // sequence's four values are read together, in one round trip.
+  const int cu0 = a.cu_q[b], cu1 = a.cu_q[b + 1];
+  const int pos0 = a.q_pos0[b];
+  const int seq_len_raw = a.seq_lens[b];
+  // (used here, so that the compiler loads them with the query offsets
+  // rather than after the test below, a round trip later; likewise the
+  // cache's base addresses, read from the kernel arguments with the first)
+  asm volatile("" ::"s"(cu0), "s"(cu1), "s"(pos0), "s"(seq_len_raw), "s"(a.k), "s"(a.v),
+               "s"(a.ks), "s"(a.vs));
+  const int q_begin = min(max(cu0, 0), a.total_q);
+  const int q_end = min(max(cu1, q_begin), a.total_q);
   const int n_q = min(q_end - q_begin, a.n_qt * kQT);
   if (qt * kQT >= n_q) return;
-  const int pos0 = a.q_pos0[b];
-  const int seq_len = min(max(a.seq_lens[b], 0), a.mbps * a.bs);
+  const int seq_len = min(max(seq_len_raw, 0), a.mbps * a.bs);
   const int last_q = min(qt * kQT + kQT, n_q) - 1;
   const int kv_end = max(0, min(seq_len, pos0 + last_q + 1));  // keys past the last query: skipped
 
@@ -187,11 +204,18 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     const uint16_t* qp = a.q + ((int64_t)(q_begin + min(qrow[cb], n_q - 1)) * hq + h) * D;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
+      // loaded for every lane (a padding row reads the last row) and zeroed
+      // after: a load under a lane condition would join two paths, and the
+      // wait where they meet would wait for every load before it
       const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
-      qb[cb][kc] = (qrow[cb] < n_q) ? *reinterpret_cast<const u32x4_t*>(qp + d0)
-                                     : u32x4_t{0u, 0u, 0u, 0u};
+      qb[cb][kc] = *reinterpret_cast<const u32x4_t*>(qp + d0);
     }
   }
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      if (qrow[cb] >= n_q) qb[cb][kc] = u32x4_t{0u, 0u, 0u, 0u};
 
   float m_run[kCB], l_run[kCB];
   f32x4_t acc[kCB][NDB];
@@ -234,16 +258,20 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   const int adv = kPGroups * kKT / 16;
   const int adv_q = adv / nsb, adv_r = adv % nsb;
   int cur_t = grp * kKT + 16 * sbv;
-  int cur_b = cur_t / a.bs;
-  int cur_r = (cur_t % a.bs) >> 4;
+  int cur_b = a.div_bs.div(cur_t);
+  int cur_r = (cur_t - cur_b * a.bs) >> 4;
 
-  // block id fetched for the next tile to load
-  int p_id = 0, p_r = 0, p_t = 0;
+  // A tile's block id (this lane's sub-block), its 16-key offset inside the
+  // block and its first key, fetched ahead of the tile's loads.
+  struct Pend {
+    int id, r, t;
+  };
   auto fetch_id = [&]() {
     const int64_t ti = tab_row + (cur_t < kv_end ? cur_b : 0);
-    p_id = a.table ? a.table[ti] : (int)ti;  // no table: contiguous
-    p_r = cur_r;
-    p_t = cur_t;
+    Pend pd;
+    pd.id = TB ? a.table[ti] : (int)ti;  // no table: contiguous
+    pd.r = cur_r;
+    pd.t = cur_t;
     cur_t += kPGroups * kKT;
     cur_b += adv_q;
     cur_r += adv_r;
@@ -251,14 +279,19 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
       cur_r -= nsb;
       ++cur_b;
     }
+    return pd;
   };
 
-  u32x4_t kreg[S::KW];
-  uint32_t vreg[4][S::VWORDS];
-  float ksreg = 1.0f, vsreg = 1.0f;
-  bool okk = false;
-  uint32_t okv = 0;  // bit r: key 4*kq + r of the tile exists
-  auto load_tile = [&]() {
+  // One tile's codes and scales in flight to this thread's registers.
+  struct StageRegs {
+    u32x4_t kreg[S::KW];
+    uint32_t vreg[4][S::VWORDS];
+    float ksreg = 1.0f, vsreg = 1.0f;
+    bool okk = false;
+    uint32_t okv = 0;  // bit r: key 4*kq + r of the tile exists
+  };
+  auto load_tile = [&](StageRegs& R, const Pend& pd) {
+    const int p_id = pd.id, p_r = pd.r, p_t = pd.t;
     const bool sb_ok = (p_t < kv_end) && ((unsigned)p_id < (unsigned)a.num_blocks);
     // first row of this lane's V sub-block; its later slots follow every ss rows
     const int64_t row_v = sb_ok ? cache_row(a.layout, p_id, 16 * p_r, hk, a.bs, a.hkv)
@@ -267,44 +300,44 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
       const int id_k = __builtin_amdgcn_readlane(p_id, 4 * rw);
       const int r_k = __builtin_amdgcn_readlane(p_r, 4 * rw);
       const int t_k = __builtin_amdgcn_readlane(p_t, 4 * rw) + kin;
-      okk = (t_k < kv_end) && ((unsigned)id_k < (unsigned)a.num_blocks);
-      const int64_t row = okk ? cache_row(a.layout, id_k, 16 * r_k + kin, hk, a.bs, a.hkv)
+      R.okk = (t_k < kv_end) && ((unsigned)id_k < (unsigned)a.num_blocks);
+      const int64_t row = R.okk ? cache_row(a.layout, id_k, 16 * r_k + kin, hk, a.bs, a.hkv)
                               : row_invalid;
       const uint8_t* kp = static_cast<const uint8_t*>(a.k) + row * S::KBYTES + spart * (S::KBYTES / 4);
 #pragma unroll
-      for (int i = 0; i < S::KW; ++i) kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
-      if (S::K8) ksreg = a.ks[row];
-      if (S::V8) vsreg = a.vs[row];
+      for (int i = 0; i < S::KW; ++i) R.kreg[i] = reinterpret_cast<const u32x4_t*>(kp)[i];
+      if (S::K8) R.ksreg = a.ks[row];
+      if (S::V8) R.vsreg = a.vs[row];
     }
-    okv = 0;
+    R.okv = 0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // V: four rows of a quad, DG values each
       const int kk = 4 * (kq & 3) + r;
       const bool ok = sb_ok && (p_t + kk < kv_end);
-      okv |= ok ? (1u << r) : 0u;
+      R.okv |= ok ? (1u << r) : 0u;
       const int64_t row = ok ? row_v + (int64_t)kk * ss : row_invalid;
       const uint8_t* vp = static_cast<const uint8_t*>(a.v) + row * (D * S::VE) + dq * (S::DG * S::VE);
       if constexpr (S::VWORDS == 4) {
         const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[r][e] = x[e];
+        for (int e = 0; e < 4; ++e) R.vreg[r][e] = x[e];
       } else if constexpr (S::VWORDS == 2) {
         const u32x2_t x = *reinterpret_cast<const u32x2_t*>(vp);
-        vreg[r][0] = x[0];
-        vreg[r][1] = x[1];
+        R.vreg[r][0] = x[0];
+        R.vreg[r][1] = x[1];
       } else {
-        vreg[r][0] = *reinterpret_cast<const uint32_t*>(vp);
+        R.vreg[r][0] = *reinterpret_cast<const uint32_t*>(vp);
       }
     }
   };
-  auto store_tile = [&](Tile& T) {
+  auto store_tile = [&](Tile& T, const StageRegs& R) {
     // K: bf16 elements [spart * D/4, (spart+1) * D/4) of row gt / 4.  A key
     // that does not exist keeps whatever row 0 holds: its score is masked.
     __bf16* kd = &T.k[gt >> 2][spart * (D / 4)];
     if (S::K8) {
 #pragma unroll
       for (int i = 0; i < S::KW; ++i) {
-        const u32x4_t w = kreg[i];
+        const u32x4_t w = R.kreg[i];
         u32x4_t lo = {e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
                       e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
         u32x4_t hi = {e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
@@ -314,15 +347,15 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < S::KW; ++i) reinterpret_cast<u32x4_t*>(kd)[i] = kreg[i];
+      for (int i = 0; i < S::KW; ++i) reinterpret_cast<u32x4_t*>(kd)[i] = R.kreg[i];
     }
     if (spart == 0) {
-      T.ks[gt >> 2] = okk ? ksreg * a.c_scale : 0.0f;
-      T.vs[gt >> 2] = okk ? vsreg : 0.0f;
-      T.ok[gt >> 2] = okk ? 1.0f : 0.0f;
+      T.ks[gt >> 2] = R.okk ? R.ksreg * a.c_scale : 0.0f;
+      T.vs[gt >> 2] = R.okk ? R.vsreg : 0.0f;
+      T.ok[gt >> 2] = R.okk ? 1.0f : 0.0f;
     }
     {  // the 16 keys of this wave all exist?
-      const uint64_t m = __builtin_amdgcn_ballot_w64(okk);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(R.okk);
       if (lane == 0) T.allok[rw] = (m == ~0ull) ? 1u : 0u;
     }
     // V^T: for each of this thread's DG d values, its 4 keys' values as
@@ -333,7 +366,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     for (int w = 0; w < S::VWORDS; ++w) {
       uint32_t rr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rr[r] = ((okv >> r) & 1u) ? vreg[r][w] : 0u;
+      for (int r = 0; r < 4; ++r) rr[r] = ((R.okv >> r) & 1u) ? R.vreg[r][w] : 0u;
       if constexpr (S::V8) {
         uint32_t cols[4];
         transpose4x4_bytes(rr, cols);  // cols[j]: code of d = DG*dq + 4w + j, keys 0..3
@@ -354,183 +387,226 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     }
   };
 
-  // Prologue: tile 0 staged, tile 1's codes and tile 2's block ids in flight.
+  // Prologue: tile 0 staged, tile 1's codes and tile 2's block ids in flight
+  // (tile 1's loads issued before tile 0 is waited for, into registers of
+  // their own, so the two round trips overlap).
+  StageRegs R;
+  Pend pn{0, 0, 0};  // block id of the next tile to load
   if (n_it > 0) {
-    fetch_id();
-    load_tile();
-    fetch_id();
-    store_tile(s_t[grp][0]);
-    load_tile();
-    fetch_id();
+    StageRegs R0;
+    const Pend p0 = fetch_id();
+    const Pend p1 = fetch_id();
+    pn = fetch_id();
+    load_tile(R0, p0);
+    load_tile(R, p1);
+    store_tile(s_t[grp][0], R0);
   }
   __syncthreads();
   for (int j = 0; j < n_it; ++j) {
     const int buf = j & 1;
     const int t0 = (kPGroups * j + grp) * kKT;
     // Stage the group's next tile (its loads were issued an iteration ago),
-    // issue the codes of the one after and the block ids of the third.  All
-    // are unconditional -- past the last tile they are reloads of row 0 into
-    // a buffer nobody reads -- so the only wait is for loads a tile old.
-    store_tile(s_t[grp][buf ^ 1]);
-    load_tile();
-    fetch_id();
+    // issue the codes of the one after and the block ids of the third, so
+    // the only wait is for loads a tile old.  Past the group's last tile
+    // nothing is loaded (the registers keep stale bytes, staged into a buffer
+    // that is never computed), so no load is left in flight when the loop
+    // ends.
+    const bool more = (kPGroups * (j + 2) + grp) * kKT < kv_end;  // wave-uniform
+    auto stage = [&]() __attribute__((always_inline)) {
+      store_tile(s_t[grp][buf ^ 1], R);
+      if (more) {
+        load_tile(R, pn);
+        pn = fetch_id();
+      }
+    };
+    auto compute_tile = [&]() __attribute__((always_inline)) {
+      if (t0 < kv_end) {
+        const Tile& T = s_t[grp][buf];
+        // every key of the tile visible to every row of this wave, all inside
+        // the sequence and in valid blocks: no mask needed (wave-uniform)
+        const bool fast = (t0 + kKT - 1 <= first_pos) && (t0 + kKT <= kv_end) &&
+                          (T.allok[0] & T.allok[1] & T.allok[2] & T.allok[3]);
 
-    if (t0 < kv_end) {
-      const Tile& T = s_t[grp][buf];
-      // every key of the tile visible to every row of this wave, all inside
-      // the sequence and in valid blocks: no mask needed (wave-uniform)
-      const bool fast = (t0 + kKT - 1 <= first_pos) && (t0 + kKT <= kv_end) &&
-                        (T.allok[0] & T.allok[1] & T.allok[2] & T.allok[3]);
-
-      // The tile is computed in two 32-key halves kp, each QK -> softmax ->
-      // PV, so only one half's scores and scales are live at a time; the
-      // matrix work of one half can overlap the softmax of the other.
+        // The tile is computed in two 32-key halves kp, each QK -> softmax ->
+        // PV, so only one half's scores and scales are live at a time; the
+        // matrix work of one half can overlap the softmax of the other.
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        // --- S^T = K Q^T for the half's two blocks of 16 keys and the
-        //     wave's column blocks: each K operand read from LDS feeds kCB
-        //     matrix instructions
-        f32x4_t sacc[kCB][2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) sacc[cb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const __bf16* krow = &T.k[16 * (2 * kp + hb) + c][0];
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
-            const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow + d0);
-#pragma unroll
-            for (int cb = 0; cb < kCB; ++cb)
-              sacc[cb][hb] = mfma_16x16x32_bf16(ka, qb[cb][kc], sacc[cb][hb]);
-          }
-        }
-
-        f32x4_t ksv[2], vsv[2];
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          ksv[hb] = *reinterpret_cast<const f32x4_t*>(&T.ks[16 * (2 * kp + hb) + 4 * g4]);
-          vsv[hb] = *reinterpret_cast<const f32x4_t*>(&T.vs[16 * (2 * kp + hb) + 4 * g4]);
-        }
-
-        // --- scores in log2 units: (q . K) * k_scale * sm_scale * log2 e,
-        //     for both column blocks at once (two independent chains); the
-        //     causal, length and block masks only where some key is hidden
-        float sc[kCB][2][4];
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[cb][hb][i] = sacc[cb][hb][i] * ksv[hb][i];
-        if (!fast) {
+        for (int kp = 0; kp < 2; ++kp) {
+          // --- S^T = K Q^T for the half's two blocks of 16 keys and the
+          //     wave's column blocks: each K operand read from LDS feeds kCB
+          //     matrix instructions
+          f32x4_t sacc[kCB][2];
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
-            const int kb = 2 * kp + hb;
-            const f32x4_t okf = *reinterpret_cast<const f32x4_t*>(&T.ok[16 * kb + 4 * g4]);
 #pragma unroll
-            for (int cb = 0; cb < kCB; ++cb)
+            for (int cb = 0; cb < kCB; ++cb) sacc[cb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const __bf16* krow = &T.k[16 * (2 * kp + hb) + c][0];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+              const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
+              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow + d0);
+#pragma unroll
+              for (int cb = 0; cb < kCB; ++cb)
+                sacc[cb][hb] = mfma_16x16x32_bf16(ka, qb[cb][kc], sacc[cb][hb]);
+            }
+          }
+
+          f32x4_t ksv[2], vsv[2];
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            ksv[hb] = *reinterpret_cast<const f32x4_t*>(&T.ks[16 * (2 * kp + hb) + 4 * g4]);
+            vsv[hb] = *reinterpret_cast<const f32x4_t*>(&T.vs[16 * (2 * kp + hb) + 4 * g4]);
+          }
+          // visibility of the lane's eight keys to its rows: causal, length and
+          // block masks, only where some key is hidden
+          bool vis[kCB][8];
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) vis[cb][jj] = true;
+          if (!fast) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              const int kb = 2 * kp + hb;
+              const f32x4_t okf = *reinterpret_cast<const f32x4_t*>(&T.ok[16 * kb + 4 * g4]);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int t = t0 + 16 * kb + 4 * g4 + i;
-                sc[cb][hb][i] = (t <= qpos[cb] && okf[i] != 0.0f) ? sc[cb][hb][i] : -INFINITY;
+#pragma unroll
+                for (int cb = 0; cb < kCB; ++cb)
+                  vis[cb][4 * hb + i] = t <= qpos[cb] && okf[i] != 0.0f;
               }
-          }
-        }
-        float t_ref[kCB];
-        bool grow = false;
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          float tmax = -INFINITY;
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[cb][hb][i]);
-          t_ref[cb] = ceilf(max_over_groups(tmax));
-          grow = grow || (m_run[cb] != -INFINITY && t_ref[cb] > m_run[cb] + kPLazy);
-        }
-
-        // --- online softmax with a lazily moved integer reference: set by
-        //     the row's first visible key, moved (exact power-of-two rescale)
-        //     only when a score exceeds it by more than kPLazy, which is rare:
-        //     one branch for both column blocks; fully masked keys
-        //     (t_ref = -inf) keep the state
-        if (grow) {
-#pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) {
-            if (m_run[cb] != -INFINITY && t_ref[cb] > m_run[cb] + kPLazy) {
-              const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref[cb]));
-              l_run[cb] *= alpha;
-#pragma unroll
-              for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
-              m_run[cb] = t_ref[cb];
             }
           }
-        }
-        u32x4_t pb[kCB];
-#pragma unroll
-        for (int cb = 0; cb < kCB; ++cb) {
-          // l and acc are still zero before the first visible key: nothing to rescale
-          m_run[cb] = (m_run[cb] == -INFINITY) ? t_ref[cb] : m_run[cb];
-          const float m_ref = (m_run[cb] == -INFINITY) ? 0.0f : m_run[cb];
-          float pv[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int hb = jj >> 2, i = jj & 3;
-            const float p = __builtin_amdgcn_exp2f(sc[cb][hb][i] - m_ref);
-            l_run[cb] += p;
-            pv[jj] = p * vsv[hb][i];
-          }
-          pb[cb] = u32x4_t{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
-                           f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
-        }
 
-        // --- O^T += V^T P^T: MFMA db covers d in [16 db, 16 db + 16); lane
-        //     (g4, r) reads row d = 16 db + r of V^T at its eight keys of the
-        //     half, once for all column blocks
+          // --- online softmax against the row's integer reference M (log2
+          //     units of the score): p = 2^(s - M) with s = (q . K) * k_scale *
+          //     sm_scale * log2 e, one fma into the exp2.  M moves (an exact
+          //     power-of-two rescale) only when a score exceeds it by more than
+          //     kPLazy; such a score makes its p, and so the lane's sum of p,
+          //     exceed 2^kPLazy.  Only then, or while the row has no reference,
+          //     is the row maximum taken and the step redone with the exact
+          //     rule (wave-uniform branch, rare).  Fully masked keys keep the
+          //     state.
+          float p[kCB][8], psum[kCB];
+          bool redo = false;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&T.vt[16 * db + c][32 * kp + 8 * g4]);
+          for (int cb = 0; cb < kCB; ++cb) {
+            const float off = (m_run[cb] == -INFINITY) ? 0.0f : -m_run[cb];
+            psum[cb] = 0.0f;
 #pragma unroll
-          for (int cb = 0; cb < kCB; ++cb) acc[cb][db] = mfma_16x16x32_bf16(av, pb[cb], acc[cb][db]);
+            for (int jj = 0; jj < 8; ++jj) {
+              const int hb = jj >> 2, i = jj & 3;
+              const float arg = vis[cb][jj] ? __builtin_fmaf(sacc[cb][hb][i], ksv[hb][i], off)
+                                            : -INFINITY;
+              p[cb][jj] = __builtin_amdgcn_exp2f(arg);
+              psum[cb] += p[cb][jj];
+            }
+            redo = redo || (m_run[cb] == -INFINITY) || !(psum[cb] <= kPLazyP);
+          }
+          if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) {
+              float tmax = -INFINITY;
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const int hb = jj >> 2, i = jj & 3;
+                tmax = fmaxf(tmax, vis[cb][jj] ? sacc[cb][hb][i] * ksv[hb][i] : -INFINITY);
+              }
+              const float t_ref = ceilf(max_over_groups(tmax));
+              if (m_run[cb] == -INFINITY) {
+                m_run[cb] = t_ref;  // l and acc are still zero: nothing to rescale
+              } else if (t_ref > m_run[cb] + kPLazy) {
+                const float alpha = ldexpf(1.0f, (int)(m_run[cb] - t_ref));
+                l_run[cb] *= alpha;
+#pragma unroll
+                for (int jj = 0; jj < NDB; ++jj) acc[cb][jj] *= alpha;
+                m_run[cb] = t_ref;
+              }
+              // exp2(-inf - M) is 0 for finite M; M is -inf only while every
+              // key so far is masked, and then the reference 0 avoids -inf - -inf
+              const float off = (m_run[cb] == -INFINITY) ? 0.0f : -m_run[cb];
+              psum[cb] = 0.0f;
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const int hb = jj >> 2, i = jj & 3;
+                const float arg = vis[cb][jj] ? __builtin_fmaf(sacc[cb][hb][i], ksv[hb][i], off)
+                                              : -INFINITY;
+                p[cb][jj] = __builtin_amdgcn_exp2f(arg);
+                psum[cb] += p[cb][jj];
+              }
+            }
+          }
+          u32x4_t pb[kCB];
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) {
+            l_run[cb] += psum[cb];
+            float pv[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) pv[jj] = p[cb][jj] * vsv[jj >> 2][jj & 3];
+            pb[cb] = u32x4_t{f32x2_to_bf16x2(pv[0], pv[1]), f32x2_to_bf16x2(pv[2], pv[3]),
+                             f32x2_to_bf16x2(pv[4], pv[5]), f32x2_to_bf16x2(pv[6], pv[7])};
+          }
+
+          // --- O^T += V^T P^T: MFMA db covers d in [16 db, 16 db + 16); lane
+          //     (g4, r) reads row d = 16 db + r of V^T at its eight keys of the
+          //     half, once for all column blocks
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&T.vt[16 * db + c][32 * kp + 8 * g4]);
+#pragma unroll
+            for (int cb = 0; cb < kCB; ++cb) acc[cb][db] = mfma_16x16x32_bf16(av, pb[cb], acc[cb][db]);
+          }
         }
       }
-    }
+    };
+    // The two groups take the iteration's halves in opposite order (group 0
+    // stages then computes, group 1 computes then stages), so the two waves
+    // that share a SIMD, one of each group, run vector work and matrix work
+    // side by side instead of in step.  Both orders are safe: group 1's
+    // compute reads buffer buf, staged an iteration ago, and its staging
+    // writes buffer buf ^ 1, last read before the previous barrier.
+    if (grp == 0) stage();
+    compute_tile();
+    if (grp != 0) stage();
     __syncthreads();
   }
 
   // --- merge key group 1 into group 0 through LDS (the tile buffers are free
   //     after the loop's last barrier): exact power-of-two weights 2^(M - M*),
   //     a group that saw no key (M = -inf) weighs 0
-  float* s_m = reinterpret_cast<float*>(&s_t[0][0]);  // [rw][MF][64 lanes]
+  //     Each lane's state is contiguous ([rw][lane][MF]: M and l of both
+  //     column blocks, then the accumulators), written and read with 16-byte
+  //     LDS operations; the lane stride of MF floats keeps each group of 16
+  //     lanes on distinct banks.
+  static_assert(kCB == 2 && S::MF == 4 + 4 * kCB * NDB, "merge layout");
   static_assert(sizeof(float) * kPRowWaves * S::MF * 64 <= sizeof(s_t), "merge area");
-  float* mine = s_m + rw * S::MF * 64 + lane;
+  f32x4_t* mine = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(&s_t[0][0]) +
+                                             (rw * 64 + lane) * S::MF);
   if (grp == 1) {
+    mine[0] = f32x4_t{m_run[0], l_run[0], m_run[1], l_run[1]};
 #pragma unroll
-    for (int cb = 0; cb < kCB; ++cb) {
-      mine[(2 * cb) * 64] = m_run[cb];
-      mine[(2 * cb + 1) * 64] = l_run[cb];
+    for (int cb = 0; cb < kCB; ++cb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mine[(2 * kCB + 4 * (NDB * cb + db) + i) * 64] = acc[cb][db][i];
-    }
+      for (int db = 0; db < NDB; ++db) mine[1 + NDB * cb + db] = acc[cb][db];
   }
   __syncthreads();
   if (grp != 0) return;
+  const f32x4_t ml1 = mine[0];
 #pragma unroll
   for (int cb = 0; cb < kCB; ++cb) {
-    const float m1 = mine[(2 * cb) * 64];
-    const float l1 = mine[(2 * cb + 1) * 64];
+    const float m1 = ml1[2 * cb];
+    const float l1 = ml1[2 * cb + 1];
     const float ms = fmaxf(m_run[cb], m1);
     const float w0 = (m_run[cb] == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m_run[cb] - ms));
     const float w1 = (m1 == -INFINITY) ? 0.0f : ldexpf(1.0f, (int)(m1 - ms));
     l_run[cb] = l_run[cb] * w0 + l1 * w1;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
+      const f32x4_t a1 = mine[1 + NDB * cb + db];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[cb][db][i] = acc[cb][db][i] * w0 + mine[(2 * kCB + 4 * (NDB * cb + db) + i) * 64] * w1;
+      for (int i = 0; i < 4; ++i) acc[cb][db][i] = acc[cb][db][i] * w0 + a1[i] * w1;
+    }
   }
 
   // --- normalise and write: lane (g4, c) holds d = 16 db + 4 g4 + i of row c
@@ -541,23 +617,34 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     l += __shfl_xor(l, 32);
     if (qrow[cb] < n_q) {
       float* orow = a.out + ((int64_t)(q_begin + qrow[cb]) * hq + h) * D;
+      const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;  // a row that sees no key: 0
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         f32x4_t o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (l > 0.0f) ? acc[cb][db][i] / l : 0.0f;
+        for (int i = 0; i < 4; ++i) o[i] = acc[cb][db][i] * inv_l;
         *reinterpret_cast<f32x4_t*>(orow + 16 * db + 4 * g4) = o;
       }
     }
   }
 }
 
+template <int MODE, int D>
+static void launch_prefill_d(const PrefillArgs& a, unsigned n_wg, hipStream_t stream) {
+  if (a.table)
+    hipLaunchKernelGGL((prefill_kernel<MODE, D, true>), dim3(n_wg), dim3(64 * kPWaves), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<MODE, D, false>), dim3(n_wg), dim3(64 * kPWaves), 0,
+                       stream, a);
+}
+
 template <int MODE>
 static void launch_prefill_mode(int d, const PrefillArgs& a, unsigned n_wg, hipStream_t stream) {
   if (d == 128)
-    hipLaunchKernelGGL((prefill_kernel<MODE, 128>), dim3(n_wg), dim3(64 * kPWaves), 0, stream, a);
+    launch_prefill_d<MODE, 128>(a, n_wg, stream);
   else
-    hipLaunchKernelGGL((prefill_kernel<MODE, 64>), dim3(n_wg), dim3(64 * kPWaves), 0, stream, a);
+    launch_prefill_d<MODE, 64>(a, n_wg, stream);
 }
 
 hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
@@ -565,10 +652,13 @@ hipError_t launch_prefill(const CacheView& c, const uint16_t* q, int group,
                           const int32_t* seq_lens, int batch, int total_q, int max_q_len,
                           float c_scale, float* out, hipStream_t stream) {
   const int n_qt = (max_q_len + kQT - 1) / kQT;
-  PrefillArgs a{c.k, c.v, c.ks, c.vs, c.table, q, cu_q, q_pos0, seq_lens, out,
-                c_scale, c.hkv, group, c.bs, c.mbps, n_qt, total_q, c.num_blocks, c.layout};
   const int64_t n_wg = (int64_t)batch * n_qt * c.hkv * group;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  if (n_wg == 0) return hipSuccess;
+  PrefillArgs a{c.k, c.v, c.ks, c.vs, c.table, q, cu_q, q_pos0, seq_lens, out,
+                c_scale, c.hkv, group, c.bs, c.mbps, n_qt, total_q, c.num_blocks, c.layout,
+                FastDiv::of(c.hkv * group), FastDiv::of(n_qt), FastDiv::of(group),
+                FastDiv::of(c.bs)};
   switch (c.mode) {
     case kK8V8: launch_prefill_mode<kK8V8>(c.d, a, (unsigned)n_wg, stream); break;
     case kK16V8: launch_prefill_mode<kK16V8>(c.d, a, (unsigned)n_wg, stream); break;
