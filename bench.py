@@ -77,7 +77,8 @@ ROW_BYTES = {"K8V8": lambda d: 2 * d + 8, "K16V8": lambda d: 3 * d + 4, "BF16": 
              "K8V16": lambda d: 3 * d + 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_k8v8_b16_t2048_traffic.json")
 KERNEL_SOURCES = ["fp8_kv_cache_append_amd/csrc/decode.hip",
-                  "fp8_kv_cache_append_amd/csrc/device.h"]
+                  "fp8_kv_cache_append_amd/csrc/device.h",
+                  "fp8_kv_cache_append_amd/csrc/launch.h"]
 
 
 def kernel_source_hash() -> str:
@@ -1113,6 +1114,9 @@ def main():
                     help="only the causal prefill of 2048 tokens (for profiling runs)")
     ap.add_argument("--ragged-only", action="store_true",
                     help="only the ragged batch-64 paged K8V8 decode (for profiling runs)")
+    ap.add_argument("--tokens", type=int, default=2048,
+                    help="cached tokens of the headline shape (2048; other lengths only "
+                         "for profiling runs with --no-extras)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has one, and the decode path "
@@ -1120,6 +1124,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0 or args.copies < 1:
         print("--steps >= 1, --warmup >= 0, --copies >= 1", file=sys.stderr)
+        sys.exit(2)
+    if args.tokens != 2048 and not args.no_extras:
+        print("--tokens other than 2048 needs --no-extras", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -1143,7 +1150,7 @@ def main():
         print(json.dumps({"prefill": bench_prefill()}), flush=True)
         return
 
-    w = synth.decode_b16_gqa8_d128(2048)
+    w = synth.decode_b16_gqa8_d128(args.tokens)
     head, hb = leg("headline K8V8", bench_decode, "K8V8", w, args.steps, args.warmup,
                    args.copies, replays=16)
     split_us = head["split_us"]
@@ -1207,7 +1214,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode_b16_hq16_hkv2_d128_t2048_k8v8_hbm_cold",
+        "config": {"workload": f"decode_b16_hq16_hkv2_d128_t{args.tokens}_k8v8_hbm_cold",
                    "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "head_dim": w.head_dim, "cached_tokens": int(w.lens[0]),
                    "kv_format": "e4m3 + fp32 scale per (token, KV head)",
