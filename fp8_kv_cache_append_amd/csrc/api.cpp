@@ -114,10 +114,17 @@ int plan(const fp8kv_cache* c, int32_t batch, int32_t max_seq_len, int32_t* chun
   // Splits of 256 keys (one 64-key tile per wave of a 4-wave work-group),
   // doubled (up to 1024) while the grid still gives every compute unit a
   // work-group: a wave then streams several tiles, half by half, and fewer
-  // splits make the merge cheaper.
+  // splits make the merge cheaper.  When 256-key splits leave compute units
+  // without a work-group, 128-key splits (half a tile per wave) double the
+  // work-groups, as long as the merge takes the splits in one batch (32).
   const int64_t pairs = (int64_t)batch * c->num_kv_heads;
   int64_t ch = 256;
-  while (ch < 1024 && pairs * ceil_div(max_seq_len, 2 * ch) >= fp8kv::kComputeUnits) ch *= 2;
+  if (pairs * ceil_div(max_seq_len, 256) < fp8kv::kComputeUnits &&
+      ceil_div(max_seq_len, 128) <= 32) {
+    ch = 128;
+  } else {
+    while (ch < 1024 && pairs * ceil_div(max_seq_len, 2 * ch) >= fp8kv::kComputeUnits) ch *= 2;
+  }
   *chunk = (int32_t)ch;
   *n_splits = max_seq_len > 0 ? (int32_t)ceil_div(max_seq_len, ch) : 0;
   return FP8KV_OK;

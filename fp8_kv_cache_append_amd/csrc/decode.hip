@@ -78,6 +78,7 @@ struct DecodeArgs {
 
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
 constexpr int kTile = 64;     // tokens per tile
+enum { kHalf = 0, kOne = 1, kMulti = 2 };  // keys per wave: half a tile, one, several
 constexpr int kMaxGroup = 16; // query heads per KV head (one MFMA column block)
 constexpr float kLazy = 8.0f; // log2 units the scores may exceed the reference by
 constexpr float kLazyP = 256.0f;  // 2^kLazy: the largest p = 2^(s - M) the reference allows
@@ -152,15 +153,16 @@ struct LaneOffsets {
 // scales and keys 0-31; 1 keys 32-63 only (the flags and scales are left as
 // they are).  A wave that streams several tiles issues the next tile's part
 // 0 once it has computed the current tile's first half (whose registers it
-// overwrites) and part 1 after the second half.
-template <int MODE, int D, int PART = 2>
+// overwrites) and part 1 after the second half.  NK: the keys the flags
+// cover (64, or 32 for a wave that attends half a tile: part 0 alone).
+template <int MODE, int D, int PART = 2, int NK = 64>
 __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs& a,
                                           const LaneOffsets& lo, int t0, int t_end, int tab,
                                           int e_base, int h, int lane, bool live) {
   using T = TileRegs<MODE, D>;
   int64_t row0[4];
   bool blk_ok[4];
-  bool all_ok = t0 + 64 <= t_end;
+  bool all_ok = t0 + NK <= t_end;
   const int64_t row_invalid = cache_row(a.layout, 0, 0, h, a.bs, a.hkv);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -168,7 +170,7 @@ __device__ __forceinline__ void load_tile(TileRegs<MODE, D>& r, const DecodeArgs
     const int eb = a.div_bs.div(tb);
     const int blk = __builtin_amdgcn_readlane(tab, min(eb - e_base, 63));
     blk_ok[kb] = (unsigned)blk < (unsigned)a.num_blocks;
-    all_ok = all_ok && blk_ok[kb];
+    if (kb < NK / 16) all_ok = all_ok && blk_ok[kb];
     // the sub-block's first row (its codes at row * D, its scales at row;
     // the next slot of the head is ss rows on)
     row0[kb] = blk_ok[kb] ? cache_row(a.layout, blk, tb - eb * a.bs, h, a.bs, a.hkv)
@@ -277,15 +279,17 @@ __device__ __forceinline__ int rotated_head(int pi, int b, const FastDiv& div_hk
 // numerical safety and kernel speed as separate gates": keep the fixed bias
 // exact, correct in score space).
 //
-// MULTI: the split holds more than one tile per wave (chunk > 4 tiles), so
-// the waves loop over their tiles.  Without it (chunk <= 4 tiles) each wave
-// computes at most one tile and there is no loop: a function of its own, so
-// that its register allocation is not shaped by the loop's.
+// SHAPE: kMulti, the split holds more than one tile per wave (chunk > 4
+// tiles), so the waves loop over their tiles; kOne, each wave computes at
+// most one tile and there is no loop (a function of its own, so that its
+// register allocation is not shaped by the loop's); kHalf, each wave
+// attends at most half a tile (32 keys; chunk <= 128), so that a short
+// context spreads over twice the work-groups and two waves share a SIMD.
 //
 // TB: the cache has a block table in memory; without one (contiguous cache)
 // the block ids are computed, a variant of its own so that no wait for a
 // table load sits in front of the first K/V loads.
-template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI, bool TB>
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE, bool TB>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
@@ -296,6 +300,9 @@ void decode_partial_kernel(DecodeArgs a) {
   constexpr int DPR = T::DPR;        // d values per V^T row group (MFMAs per PV chunk)
   constexpr bool kK8 = T::K8;
   constexpr bool kV8 = T::V8;
+  constexpr bool MULTI = SHAPE == kMulti;
+  constexpr bool HALF = SHAPE == kHalf;
+  constexpr int kTW = HALF ? kTile / 2 : kTile;  // keys a wave attends per tile
   // the first tile's loads go out before the sequence length is known
   constexpr bool kEarly = !TB && !MULTI;
 
@@ -443,8 +450,8 @@ void decode_partial_kernel(DecodeArgs a) {
   const int t_cap = min(a.mbps * a.bs, t_begin + a.chunk);
   T buf;
   if constexpr (kEarly) {
-    load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_cap, tab, e_base, h, lane,
-                       t_begin + wave * kTile < t_cap);
+    load_tile<MODE, D, HALF ? 0 : 2, kTW>(buf, a, lo, t_begin + wave * kTW, t_cap, tab, e_base,
+                                          h, lane, t_begin + wave * kTW < t_cap);
     // (the length, loaded before the tile, is used only from here on: the
     // compiler would otherwise move its wait in front of the tile's loads)
     asm volatile("" : "+v"(len));
@@ -480,7 +487,7 @@ void decode_partial_kernel(DecodeArgs a) {
   if constexpr (APPEND) {
     const int p = len - 1;
     if (len >= 1 && len <= a.mbps * a.bs && p >= t_begin && p < t_end &&
-        ((p - t_begin) / kTile) % kWaves == wave)
+        ((p - t_begin) / kTW) % kWaves == wave)
       pos_n = p;
   }
   pos_n = wave_uniform(pos_n);
@@ -833,10 +840,10 @@ void decode_partial_kernel(DecodeArgs a) {
   // stream.  Every load is issued unconditionally (a tile that does not exist
   // is issued empty, see load_tile), so the waits before each compute step
   // are exact.
-  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+  const int n_tiles = (t_end - t_begin + kTW - 1) / kTW;
   if constexpr (!kEarly)
-    load_tile<MODE, D>(buf, a, lo, t_begin + wave * kTile, t_end, tab, e_base, h, lane,
-                       wave < n_tiles);
+    load_tile<MODE, D, HALF ? 0 : 2, kTW>(buf, a, lo, t_begin + wave * kTW, t_end, tab, e_base,
+                                          h, lane, wave < n_tiles);
   // The first round trip's data, now that the tile loads are out: Q to LDS
   // (narrow QK: quantised first), the K bias product.
   if constexpr (!Q8) {
@@ -913,8 +920,8 @@ void decode_partial_kernel(DecodeArgs a) {
     qb_c = sum_over_groups(part) * a.c_scale;
   }
   if constexpr (kEarly) {  // narrow the early tile's flags to the length
-    const int t0 = t_begin + wave * kTile;
-    buf.full = buf.full && t0 + kTile <= t_end;
+    const int t0 = t_begin + wave * kTW;
+    buf.full = buf.full && t0 + kTW <= t_end;
     buf.tok_ok = buf.tok_ok && t0 + lane < t_end;
   }
   if (APPEND && pos_n >= 0) append_new();
@@ -932,7 +939,16 @@ void decode_partial_kernel(DecodeArgs a) {
   // 64 has blocks 0 and 1; the zero k-slots of blocks 2 and 3 take 2^0)
   if constexpr (Q8 && T::MX) q_exp_c = (c < G && g4 < D / 32) ? (int)s_qx[c][g4] : 127;
   if constexpr (!MULTI) {
-    if (wave < n_tiles) compute(buf, t_begin + wave * kTile);
+    if (wave < n_tiles) {
+      if constexpr (HALF) {  // keys 0-31 of the tile at t0: sub-blocks 0, 1, PV chunk 0
+        const int t0 = t_begin + wave * kTW;
+        compute_head(buf, t0);
+        const bool okb[4] = {buf.blk_ok[0], buf.blk_ok[1], buf.blk_ok[2], buf.blk_ok[3]};
+        attend(buf, t0, Half{}, 0, buf.full, okb);
+      } else {
+        compute(buf, t_begin + wave * kTile);
+      }
+    }
   } else if (wave < n_tiles) {
     const int m = (n_tiles - wave + kWaves - 1) / kWaves;  // tiles of this wave
     int tile = wave;
@@ -1102,32 +1118,34 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(FastDiv div_hkv, FastD
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
-template <int MODE, int D, bool APPEND, bool Q8, bool KB, bool MULTI>
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE>
 static void launch_split(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
   if (a.table)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, MULTI, true>), grid, block,
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, true>), grid, block,
                        0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, MULTI, false>), grid,
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, false>), grid,
                        block, 0, stream, a);
+}
+
+template <int MODE, int D, bool APPEND, bool Q8, bool KB>
+static void launch_split_shape(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if (a.chunk > kWaves * kTile)
+    launch_split<MODE, D, APPEND, Q8, KB, kMulti>(a, grid, block, stream);
+  else if (a.chunk > kWaves * kTile / 2)
+    launch_split<MODE, D, APPEND, Q8, KB, kOne>(a, grid, block, stream);
+  else
+    launch_split<MODE, D, APPEND, Q8, KB, kHalf>(a, grid, block, stream);
 }
 
 template <int MODE, bool APPEND, bool Q8, bool KB>
 static void launch_partial_d(const CacheView& c, const DecodeArgs& a, unsigned n_wg,
                              hipStream_t stream) {
-  const bool multi = a.chunk > kWaves * kTile;
   const dim3 grid(n_wg), block(64 * kWaves);
-  if (c.d == 128) {
-    if (multi)
-      launch_split<MODE, 128, APPEND, Q8, KB, true>(a, grid, block, stream);
-    else
-      launch_split<MODE, 128, APPEND, Q8, KB, false>(a, grid, block, stream);
-  } else {
-    if (multi)
-      launch_split<MODE, 64, APPEND, Q8, KB, true>(a, grid, block, stream);
-    else
-      launch_split<MODE, 64, APPEND, Q8, KB, false>(a, grid, block, stream);
-  }
+  if (c.d == 128)
+    launch_split_shape<MODE, 128, APPEND, Q8, KB>(a, grid, block, stream);
+  else
+    launch_split_shape<MODE, 64, APPEND, Q8, KB>(a, grid, block, stream);
 }
 
 template <int MODE, bool APPEND, bool Q8>

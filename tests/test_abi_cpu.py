@@ -133,13 +133,15 @@ def test_decode_plan():
     assert _plan(d, 64, 17, 32768)[0] == -4
     assert _plan(d, 64, 0, 32768)[0] == -1
     assert _plan(d, 64, 4, 32768 + 1)[0] == -1   # beyond the block table
-    assert _plan(d, 0, 4, 0) == (0, 256, 0)
+    assert _plan(d, 0, 4, 0) == (0, 128, 0)
     # contiguous B16 x 2 KV heads: the chunk doubles while every one of the
     # 256 compute units still gets a work-group
     d = _desc(num_blocks=16, block_size=8192, max_blocks_per_seq=1)
     assert _plan(d, 16, 8, 4096) == (0, 512, 8)      # 256 work-groups
     assert _plan(d, 16, 8, 8192) == (0, 1024, 8)     # 256 work-groups
-    assert _plan(d, 16, 8, 512) == (0, 256, 2)       # 64: no doubling
+    assert _plan(d, 16, 8, 512) == (0, 128, 4)       # 64 at 256: half-tile splits, 128
+    assert _plan(d, 16, 8, 2048) == (0, 256, 8)      # 256 work-groups at 256 keys
+    assert _plan(d, 16, 8, 4097) == (0, 512, 9)
     d16 = _desc(mode=1, num_blocks=16, block_size=8192, max_blocks_per_seq=1, k_scale=None)
     assert _plan(d16, 16, 8, 8192) == (0, 1024, 8)
     big = dict(num_blocks=24, block_size=16384, max_blocks_per_seq=1, num_seqs=24)

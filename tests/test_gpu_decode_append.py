@@ -183,3 +183,61 @@ def test_fused_append_invalid_block_is_not_written():
                                 [seqs[b][1][keep[b]] for b in range(2)], w.sm_scale,
                                 bounds=True)
     _gate(got, ref, lo, hi, "fused append, invalid block")
+
+
+def _split_step(cache, q_bits, lens, group, sm_scale, chunk, k_new=None, v_new=None):
+    """Split kernel with an explicit chunk (fused when k_new is given), then
+    the merge: the entry points the planner's choice dispatches to."""
+    lens = np.asarray(lens, np.int32)
+    b, hq, d = q_bits.shape
+    max_len = int(lens.max())
+    splits = -(-max_len // chunk)
+    hkv = cache.num_kv_heads
+    pacc = torch.full((b, hkv, splits, group, d), float("nan"), device=DEV)
+    pml = torch.full((b, hkv, splits, group, 2), float("nan"), device=DEV)
+    out = torch.full((b, hq, d), float("nan"), dtype=torch.float32, device=DEV)
+    dl = torch.from_numpy(lens).to(DEV)
+    if k_new is None:
+        binding.fp8kv_decode_partial(cache, q_tensor(q_bits), group, dl, max_len, sm_scale, chunk,
+                                     splits, pacc, pml)
+    else:
+        binding.fp8kv_decode_append_partial(
+            cache, torch.from_numpy(np.ascontiguousarray(k_new)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(v_new)).to(DEV), q_tensor(q_bits), group, dl,
+            max_len, sm_scale, chunk, splits, pacc, pml)
+    binding.fp8kv_decode_merge(b, hkv, group, d, splits, pacc, pml, out)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("chunk", [128, 256], ids=["half_tile", "one_tile"])
+@pytest.mark.parametrize("layout", ["token", "head"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "BF16", "K8V16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"hq{s[0]}_hkv{s[1]}_d{s[2]}_bs{s[4]}")
+def test_fused_append_each_split_shape(mode, shape, layout, chunk):
+    """Both single-pass split variants with the append fused in, whatever the
+    planner would pick for the shape: 128-key splits (each wave attends half
+    a 64-key tile) and 256-key splits (one tile per wave).  Bit-identical to
+    fp8kv_append followed by the plain split kernel with the same chunk, and
+    within the oracle gate."""
+    hq, hkv, d, lens, bs = shape
+    lens = np.array(lens, np.int32)
+    w = synth.Workload("t", len(lens), hq, hkv, d, lens, "outliers", block_size=bs,
+                       shuffle_blocks=bs > 0, seed=hq * 13 + d + bs + 5)
+    seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
+    q_bits = synth.q_bf16_bits(w.seed + 7, (w.batch, w.q_heads, w.head_dim))
+    fused, plain = make_cache(mode, w, layout=layout), make_cache(mode, w, layout=layout)
+    k_new = np.zeros((w.batch, w.kv_heads, w.head_dim), np.float32)
+    v_new = np.zeros_like(k_new)
+    for b, (k, v) in enumerate(seqs):
+        n = int(lens[b])
+        append_seq(fused, b, k[:n - 1], v[:n - 1])
+        append_seq(plain, b, k[:n], v[:n])
+        k_new[b], v_new[b] = k[n - 1], v[n - 1]
+    got = _split_step(fused, q_bits, lens, w.group, w.sm_scale, chunk, k_new, v_new)
+    want = _split_step(plain, q_bits, lens, w.group, w.sm_scale, chunk)
+    for x, y in zip(_cache_bytes(fused), _cache_bytes(plain)):
+        assert np.array_equal(x, y), (mode, chunk, "cache bytes differ")
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (mode, chunk, "output differs")
+    ref, lo, hi = oracle.decode(mode, q_bits, [s[0] for s in seqs], [s[1] for s in seqs],
+                                w.sm_scale, bounds=True)
+    _gate(got, ref, lo, hi, (mode, "fused append", chunk, shape, layout))
