@@ -94,8 +94,12 @@ template <int MODE, int D>
 struct PrefillShape {
   static constexpr bool K8 = k_is_e4m3(MODE);
   static constexpr bool V8 = v_is_e4m3(MODE);
-  static constexpr int LDK = D + 8;                          // LDS K row (bf16), padded
-  static constexpr int LDV = kKT + 8;                        // LDS V^T row (bf16), padded
+  // LDS rows: K unpadded, its 16-byte chunks permuted (k_chunk), V^T padded
+  // to kKT + 16 bf16 (160 bytes at kKT = 64).  Both make the QK and PV
+  // operand reads and the staging writes free of LDS bank conflicts.
+  static constexpr int LDK = D;
+  static constexpr int KSWZ = (D / 8 - 1) < 15 ? (D / 8 - 1) : 15;
+  static constexpr int LDV = kKT + 16;
   static constexpr int KBYTES = K8 ? D : 2 * D;              // bytes of one K row in HBM
   static constexpr int KW = KBYTES / 4 / 16;                 // 16-byte K loads per thread
   static constexpr int DG = D / 16;                          // d values per V staging thread
@@ -104,6 +108,19 @@ struct PrefillShape {
   static constexpr int NDB = D / 16;                         // PV column blocks of 16 d
   static constexpr int MF = 2 * kCB + 4 * kCB * NDB;         // merged floats per lane
 };
+
+// Place of 16-byte chunk j of K row r inside the row.  gfx950's LDS serves a
+// 16-byte access per lane in lane groups: a K operand read (16 lanes at 16
+// rows, one column) is conflict-free when those rows put the column in 16
+// different chunks, which j ^ (r % 16) does (a row padding of 16 bytes
+// leaves 4 extra cycles per read); a staging write (8 lanes: two rows, four
+// chunks 4 apart in each) when the eight land in different 16-byte slots of
+// 128 bytes, which the extra flip of bit 1 by bit 3 of j adds.  The map is a
+// permutation of each row's chunks.
+template <int KSWZ>
+__device__ __forceinline__ int k_chunk(int r, int j) {
+  return j ^ (r & KSWZ) ^ (((j >> 3) & 1) << 1);
+}
 
 // One staged 64-key tile.
 template <int MODE, int D>
@@ -331,9 +348,11 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     }
   };
   auto store_tile = [&](Tile& T, const StageRegs& R) {
-    // K: bf16 elements [spart * D/4, (spart+1) * D/4) of row gt / 4.  A key
-    // that does not exist keeps whatever row 0 holds: its score is masked.
-    __bf16* kd = &T.k[gt >> 2][spart * (D / 4)];
+    // K: 16-byte chunks [spart * D/32, (spart+1) * D/32) of row gt / 4, each
+    // at its k_chunk place.  A key that does not exist keeps whatever row 0
+    // holds: its score is masked.
+    u32x4_t* kd = reinterpret_cast<u32x4_t*>(&T.k[gt >> 2][0]);
+    constexpr int QCH = D / 32;  // chunks per quarter row
     if (S::K8) {
 #pragma unroll
       for (int i = 0; i < S::KW; ++i) {
@@ -342,12 +361,12 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
                       e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
         u32x4_t hi = {e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
                       e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
-        reinterpret_cast<u32x4_t*>(kd)[2 * i] = lo;
-        reinterpret_cast<u32x4_t*>(kd)[2 * i + 1] = hi;
+        kd[k_chunk<S::KSWZ>(gt >> 2, QCH * spart + 2 * i)] = lo;
+        kd[k_chunk<S::KSWZ>(gt >> 2, QCH * spart + 2 * i + 1)] = hi;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < S::KW; ++i) reinterpret_cast<u32x4_t*>(kd)[i] = R.kreg[i];
+      for (int i = 0; i < S::KW; ++i) kd[k_chunk<S::KSWZ>(gt >> 2, QCH * spart + i)] = R.kreg[i];
     }
     if (spart == 0) {
       T.ks[gt >> 2] = R.okk ? R.ksreg * a.c_scale : 0.0f;
@@ -440,11 +459,13 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
           for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
             for (int cb = 0; cb < kCB; ++cb) sacc[cb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const __bf16* krow = &T.k[16 * (2 * kp + hb) + c][0];
+            const u32x4_t* krow = reinterpret_cast<const u32x4_t*>(&T.k[16 * (2 * kp + hb) + c][0]);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-              const int d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1);
-              const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow + d0);
+              // d in [d0, d0 + 8), d0 = 64 * (kc >> 1) + 16 * g4 + 8 * (kc & 1):
+              // chunk d0 / 8 of row 16 * (2 * kp + hb) + c
+              const int ch = 8 * (kc >> 1) + 2 * g4 + (kc & 1);
+              const u32x4_t ka = krow[k_chunk<S::KSWZ>(c, ch)];
 #pragma unroll
               for (int cb = 0; cb < kCB; ++cb)
                 sacc[cb][hb] = mfma_16x16x32_bf16(ka, qb[cb][kc], sacc[cb][hb]);
