@@ -156,11 +156,22 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t r[4], uint32_t
   out[3] = byte_perm(p23h, p01h, 0x07060302u);
 }
 
-// TB: the cache has a block table in memory; without one (contiguous cache)
-// the block ids are computed, a variant of its own so that no wait for a
-// table load joins the paths of the loads.
-template <int MODE, int D, bool TB>
+// How a key's cache row is found:
+//  - kPTable: through the block table in memory;
+//  - kPComputed: no table (contiguous cache), block ids computed, so that no
+//    wait for a table load joins the paths of the loads;
+//  - kPLinear: no table and token-major rows, so key t of the sequence and
+//    KV head is row r0 + t * hkv; every K, V and scale load is then a 32-bit
+//    offset into a buffer resource over the sequence's rows up to the last
+//    key the query tile attends, and a key past it reads zeros (no row
+//    arithmetic in 64 bits, no selects for missing keys).  The host picks it
+//    when the whole cache's rows fit 31-bit byte offsets.
+enum { kPTable = 0, kPComputed = 1, kPLinear = 2 };
+
+template <int MODE, int D, int ADDR>
 __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a) {
+  constexpr bool TB = ADDR == kPTable;
+  constexpr bool LIN = ADDR == kPLinear;
   using S = PrefillShape<MODE, D>;
   using Tile = PrefillTile<MODE, D>;
   constexpr int KC = D / 32;
@@ -278,6 +289,24 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
   int cur_b = a.div_bs.div(cur_t);
   int cur_r = (cur_t - cur_b * a.bs) >> 4;
 
+  // kPLinear: buffer resources over the sequence's rows of KV head hk, from
+  // key 0 up to kv_end (and never past the end of the arrays); byte steps
+  // of one key
+  const int lin_step_k = a.hkv * S::KBYTES, lin_step_v = a.hkv * D * S::VE, lin_step_s = a.hkv * 4;
+  const int64_t lin_r0 = (int64_t)b * a.mbps * a.bs * a.hkv + hk;  // row of key 0
+  auto lin_rsrc = [&](const void* base, int64_t elem_bytes, int step) {
+    const int64_t rows = (int64_t)a.num_blocks * a.bs * a.hkv;       // rows in the cache
+    const int64_t want = (int64_t)kv_end * step;
+    const int64_t have = (rows - lin_r0) * elem_bytes;
+    const int64_t n = want < have ? want : have;
+    return buffer_rsrc(static_cast<const uint8_t*>(base) + lin_r0 * elem_bytes,
+                       n > 0 ? (uint32_t)n : 0u);
+  };
+  const __amdgpu_buffer_rsrc_t lin_k = lin_rsrc(a.k, S::KBYTES, lin_step_k);
+  const __amdgpu_buffer_rsrc_t lin_v = lin_rsrc(a.v, D * S::VE, lin_step_v);
+  const __amdgpu_buffer_rsrc_t lin_ks = lin_rsrc(a.ks, 4, lin_step_s);
+  const __amdgpu_buffer_rsrc_t lin_vs = lin_rsrc(a.vs, 4, lin_step_s);
+
   // A tile's block id (this lane's sub-block), its 16-key offset inside the
   // block and its first key, fetched ahead of the tile's loads.
   struct Pend {
@@ -308,6 +337,39 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
     uint32_t okv = 0;  // bit r: key 4*kq + r of the tile exists
   };
   auto load_tile = [&](StageRegs& R, const Pend& pd) {
+    if constexpr (LIN) {
+      // K row of key t_k (sub-block rw, from lane 4*rw), its scales, and this
+      // lane's four V rows (keys p_t + 4*(kq % 4) + r, r from the scalar
+      // offset); keys at or past kv_end read zeros
+      const int t_k = __builtin_amdgcn_readlane(pd.t, 4 * rw) + kin;
+      R.okk = t_k < kv_end;
+      const int ok_off = t_k * lin_step_k + spart * (S::KBYTES / 4);
+#pragma unroll
+      for (int i = 0; i < S::KW; ++i)
+        R.kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(lin_k, ok_off + 16 * i, 0, 0);
+      if (S::K8)
+        R.ksreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lin_ks, t_k * lin_step_s, 0, 0));
+      if (S::V8)
+        R.vsreg = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(lin_vs, t_k * lin_step_s, 0, 0));
+      R.okv = 0xfu;  // a missing key's V is already zero
+      const int ov_off = (pd.t + 4 * (kq & 3)) * lin_step_v + dq * (S::DG * S::VE);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int soff = r * lin_step_v;
+        if constexpr (S::VWORDS == 4) {
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(lin_v, ov_off, soff, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) R.vreg[r][e] = x[e];
+        } else if constexpr (S::VWORDS == 2) {
+          const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(lin_v, ov_off, soff, 0);
+          R.vreg[r][0] = x[0];
+          R.vreg[r][1] = x[1];
+        } else {
+          R.vreg[r][0] = __builtin_amdgcn_raw_buffer_load_b32(lin_v, ov_off, soff, 0);
+        }
+      }
+      return;
+    }
     const int p_id = pd.id, p_r = pd.r, p_t = pd.t;
     const bool sb_ok = (p_t < kv_end) && ((unsigned)p_id < (unsigned)a.num_blocks);
     // first row of this lane's V sub-block; its later slots follow every ss rows
@@ -652,11 +714,19 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
 
 template <int MODE, int D>
 static void launch_prefill_d(const PrefillArgs& a, unsigned n_wg, hipStream_t stream) {
+  using S = PrefillShape<MODE, D>;
+  // kPLinear: every byte offset into the K, V and scale arrays fits 31 bits
+  const int64_t rows = (int64_t)a.num_blocks * a.bs * a.hkv;
+  const int64_t row_bytes = S::KBYTES > D * S::VE ? S::KBYTES : D * S::VE;
+  const bool linear = !a.table && a.layout == kTokenMajor && rows * row_bytes < (int64_t(1) << 31);
   if (a.table)
-    hipLaunchKernelGGL((prefill_kernel<MODE, D, true>), dim3(n_wg), dim3(64 * kPWaves), 0, stream,
-                       a);
+    hipLaunchKernelGGL((prefill_kernel<MODE, D, kPTable>), dim3(n_wg), dim3(64 * kPWaves), 0,
+                       stream, a);
+  else if (linear)
+    hipLaunchKernelGGL((prefill_kernel<MODE, D, kPLinear>), dim3(n_wg), dim3(64 * kPWaves), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<MODE, D, false>), dim3(n_wg), dim3(64 * kPWaves), 0,
+    hipLaunchKernelGGL((prefill_kernel<MODE, D, kPComputed>), dim3(n_wg), dim3(64 * kPWaves), 0,
                        stream, a);
 }
 

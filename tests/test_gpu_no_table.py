@@ -78,26 +78,34 @@ def test_decode_append_without_table(mode, bs, capacity, layout):
     _gate(outs[1], ref, lo, hi, (mode, bs, "no table"))
 
 
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "K8V16", "BF16"])
 @pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("bs,capacity", LAYOUTS)
-def test_prefill_without_table(bs, capacity, layout):
+def test_prefill_without_table(bs, capacity, layout, mode):
+    # token-major rows without a table take the linear-offset path (keys read
+    # through buffer offsets, zeros past the last key); head-major rows the
+    # computed-block path; both must equal the table path bit for bit.  The
+    # second sequence's queries start at position 136: its first 136 keys are
+    # cached context, and its query tile ends inside a key tile.
     lens = np.array([640, 200], np.int32)
     w = synth.Workload("t", len(lens), 28, 4, 128, lens, "normal", block_size=bs,
                        prefill=True, seed=44)
-    cache_t, cache_n = _pair("K8V8", w, capacity, layout)
+    cache_t, cache_n = _pair(mode, w, capacity, layout)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
     for cache in (cache_t, cache_n):
         for b, (k, v) in enumerate(seqs):
             append_seq(cache, b, k, v)
-    n = int(lens.sum())
+    first = np.array([0, 136], np.int32)
+    nq = lens - first
+    n = int(nq.sum())
     q = q_tensor(synth.q_bf16_bits(w.seed, (n, w.q_heads, w.head_dim)))
-    cu = torch.tensor([0, int(lens[0]), n], dtype=torch.int32, device=DEV)
-    pos0 = torch.zeros(2, dtype=torch.int32, device=DEV)
+    cu = torch.tensor([0, int(nq[0]), n], dtype=torch.int32, device=DEV)
+    pos0 = torch.from_numpy(first).to(DEV)
     lens_t = torch.from_numpy(lens).to(DEV)
     outs = []
     for cache in (cache_t, cache_n):
         out = torch.full((n, w.q_heads, w.head_dim), float("nan"), device=DEV)
-        binding.fp8kv_prefill(cache, q, w.group, cu, pos0, lens_t, int(lens.max()), w.sm_scale,
+        binding.fp8kv_prefill(cache, q, w.group, cu, pos0, lens_t, int(nq.max()), w.sm_scale,
                               out)
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
