@@ -1114,6 +1114,8 @@ def main():
                     help="only the causal prefill of 2048 tokens (for profiling runs)")
     ap.add_argument("--ragged-only", action="store_true",
                     help="only the ragged batch-64 paged K8V8 decode (for profiling runs)")
+    ap.add_argument("--append-only", action="store_true",
+                    help="only the bulk append of 1 M rows (for profiling runs)")
     ap.add_argument("--tokens", type=int, default=2048,
                     help="cached tokens of the headline shape (2048; other lengths only "
                          "for profiling runs with --no-extras)")
@@ -1148,6 +1150,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill()}), flush=True)
+        return
+    if args.append_only:
+        print(json.dumps({"append_bulk": bench_append_bulk()}), flush=True)
         return
 
     w = synth.decode_b16_gqa8_d128(args.tokens)

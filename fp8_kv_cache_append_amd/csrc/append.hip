@@ -36,6 +36,8 @@ struct AppendArgs {
   int num_seqs;
   int num_blocks;
   int layout;
+  FastDiv div_hkv;  // by hkv: the token of a (token, head) pair
+  FastDiv div_bs;   // by bs: the block of a position
 };
 
 // Rows per thread: for a bulk append each thread handles R = 4 rows one
@@ -57,7 +59,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const uint32_t slots = gridDim.x * blockDim.x / kLanesPerRow;  // rows per sweep
   const uint32_t r0 = gtid / kLanesPerRow;
   const int sub = (int)(gtid % kLanesPerRow);
-  const uint32_t hkv = (uint32_t)a.hkv, bs = (uint32_t)a.bs;
 
   // Every row's state is uniform over its kLanesPerRow lanes, so the
   // butterfly below, run under a per-row condition, never reads a lane of
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    const uint32_t tok = pair[k] / hkv;
+    const uint32_t tok = (uint32_t)a.div_hkv.div((int)pair[k]);  // pair < 2^30
     seq[k] = a.seq_idx[tok];
     p[k] = a.pos[tok];
   }
@@ -86,16 +87,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     in[k] = in[k] && seq[k] >= 0 && seq[k] < a.num_seqs && p[k] >= 0 && p[k] < a.mbps * a.bs;
-    const int64_t ti = in[k] ? (int64_t)seq[k] * a.mbps + (uint32_t)p[k] / bs : 0;
+    const int64_t ti = in[k] ? (int64_t)seq[k] * a.mbps + a.div_bs.div(p[k]) : 0;
     blk[k] = a.table ? a.table[ti] : (int)ti;  // no table: contiguous
   }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     if (!in[k] || blk[k] < 0 || blk[k] >= a.num_blocks) continue;
     const int is_v = (int)((r0 + k * slots) & 1u);
-    const uint32_t h = pair[k] - (pair[k] / hkv) * hkv;
-    const uint32_t slot = (uint32_t)p[k] - ((uint32_t)p[k] / bs) * bs;
-    const int64_t row = cache_row(a.layout, blk[k], (int)slot, (int)h, a.bs, a.hkv);
+    const int h = a.div_hkv.mod((int)pair[k]);
+    const int slot = a.div_bs.mod(p[k]);  // 0 <= p < mbps * bs < 2^31
+    const int64_t row = cache_row(a.layout, blk[k], slot, h, a.bs, a.hkv);
     const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
     if (k_is_mx(MODE) && !is_v) {
       // block-scaled K: eight lanes hold a block of 32 values
@@ -142,7 +143,8 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
   const int64_t n_rows = 2 * (int64_t)n_tok * c.hkv;
   if (n_rows > INT32_MAX) return hipErrorInvalidValue;
   AppendArgs a{k_new, v_new, seq_idx, pos, c.table, c.k, c.v, c.ks, c.vs, c.kexp,
-               (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks, c.layout};
+               (int)n_rows, c.hkv, c.bs, c.mbps, c.num_seqs, c.num_blocks, c.layout,
+               FastDiv::of(c.hkv), FastDiv::of(c.bs)};
   switch (c.mode) {
     case kK8V8: return append_mode<kK8V8>(c, a, stream);
     case kK16V8: return append_mode<kK16V8>(c, a, stream);

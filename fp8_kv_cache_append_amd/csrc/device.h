@@ -96,16 +96,49 @@ __device__ __forceinline__ float row_amax(float4 x) {
   return m;
 }
 
+// x / b from y = RN(1 / b): q = RN(x y), the exact remainder r = x - b q (one
+// fma), then RN(q + r y).  With y the correctly rounded reciprocal this
+// correction step returns the correctly rounded quotient whenever nothing
+// underflows (Markstein's theorem on division by an fma-corrected
+// reciprocal); the sign is taken from x so that -0 stays -0.
+__host__ __device__ __forceinline__ float quotient_rn(float x, float b, float y) {
+  const float q = x * y;
+  const float r = __builtin_fmaf(-b, q, x);
+  return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+}
+
 // Four codes of the row with scale = amax / 448: the correctly rounded fp32
-// quotient x / scale (no reciprocal, no fast math), clamped to +-448 so that a
-// row whose scale is an fp32 subnormal saturates, then rounded to nearest
-// even onto OCP e4m3fn by v_cvt_pk_fp8_f32.  A zero scale gives zero codes.
+// quotient x / scale (no fast math), clamped to +-448 so that a row whose
+// scale is an fp32 subnormal saturates, then rounded to nearest even onto OCP
+// e4m3fn by v_cvt_pk_fp8_f32.  A zero scale gives zero codes.
+// For a scale in [2^-53, FLT_MAX] the quotients come from one correctly
+// rounded reciprocal per row and quotient_rn (three instructions each instead
+// of a full division).  A quotient of magnitude 2^-11 or more is then exactly
+// the correctly rounded one; below that quotient_rn may differ from it in the
+// last bits, but both are under 2^-10 with the sign of x, so both round to the
+// same signed zero code.  (Checked on the host against division for every
+// fp32 x with |x| <= amax at several scales, among them significands of all
+// ones and 2^-53; tests/test_quotient_cpu.py repeats the check on samples.)
+// Other scales take the division.
 __device__ __forceinline__ uint32_t e4m3_codes4(float4 x, float scale) {
   if (scale == 0.0f) return 0u;
-  const float y0 = fminf(fmaxf(x.x / scale, -kE4M3Max), kE4M3Max);
-  const float y1 = fminf(fmaxf(x.y / scale, -kE4M3Max), kE4M3Max);
-  const float y2 = fminf(fmaxf(x.z / scale, -kE4M3Max), kE4M3Max);
-  const float y3 = fminf(fmaxf(x.w / scale, -kE4M3Max), kE4M3Max);
+  float q0, q1, q2, q3;
+  if (scale >= 0x1p-53f && scale <= 0x1.fffffep127f) {
+    const float y = 1.0f / scale;  // correctly rounded
+    q0 = quotient_rn(x.x, scale, y);
+    q1 = quotient_rn(x.y, scale, y);
+    q2 = quotient_rn(x.z, scale, y);
+    q3 = quotient_rn(x.w, scale, y);
+  } else {
+    q0 = x.x / scale;
+    q1 = x.y / scale;
+    q2 = x.z / scale;
+    q3 = x.w / scale;
+  }
+  const float y0 = fminf(fmaxf(q0, -kE4M3Max), kE4M3Max);
+  const float y1 = fminf(fmaxf(q1, -kE4M3Max), kE4M3Max);
+  const float y2 = fminf(fmaxf(q2, -kE4M3Max), kE4M3Max);
+  const float y3 = fminf(fmaxf(q3, -kE4M3Max), kE4M3Max);
   uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
 }

@@ -78,17 +78,18 @@ def test_decode_append_without_table(mode, bs, capacity, layout):
     _gate(outs[1], ref, lo, hi, (mode, bs, "no table"))
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("mode", ["K8V8", "K16V8", "K8V16", "BF16"])
 @pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("bs,capacity", LAYOUTS)
-def test_prefill_without_table(bs, capacity, layout, mode):
+def test_prefill_without_table(bs, capacity, layout, mode, d):
     # token-major rows without a table take the linear-offset path (keys read
     # through buffer offsets, zeros past the last key); head-major rows the
     # computed-block path; both must equal the table path bit for bit.  The
     # second sequence's queries start at position 136: its first 136 keys are
     # cached context, and its query tile ends inside a key tile.
     lens = np.array([640, 200], np.int32)
-    w = synth.Workload("t", len(lens), 28, 4, 128, lens, "normal", block_size=bs,
+    w = synth.Workload("t", len(lens), 28, 4, d, lens, "normal", block_size=bs,
                        prefill=True, seed=44)
     cache_t, cache_n = _pair(mode, w, capacity, layout)
     seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
