@@ -715,8 +715,12 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(PrefillArgs a)
 template <int MODE, int D>
 static void launch_prefill_d(const PrefillArgs& a, unsigned n_wg, hipStream_t stream) {
   using S = PrefillShape<MODE, D>;
-  // kPLinear: every byte offset into the K, V and scale arrays fits 31 bits
-  const int64_t rows = (int64_t)a.num_blocks * a.bs * a.hkv;
+  // kPLinear: every byte offset into the K, V and scale arrays fits 31 bits,
+  // also for the keys the staging may address past a sequence's capacity
+  // (they read zeros): the first two tiles of each group are loaded whatever
+  // the length, so keys below 4 * kKT, later tiles only when they start
+  // below the length
+  const int64_t rows = (int64_t)a.num_blocks * a.bs * a.hkv + 4 * kKT * a.hkv;
   const int64_t row_bytes = S::KBYTES > D * S::VE ? S::KBYTES : D * S::VE;
   const bool linear = !a.table && a.layout == kTokenMajor && rows * row_bytes < (int64_t(1) << 31);
   if (a.table)
