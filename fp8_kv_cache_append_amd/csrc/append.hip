@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], e8m0_value((uint32_t)(e + 127)));
       if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
     } else if (quantise) {
-      const float scale = row_amax<kLanesPerRow>(x[k]) / kE4M3Max;  // correctly rounded
+      const float scale = storage_scale(row_amax<kLanesPerRow>(x[k]));  // RN(amax / 448)
       uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], scale);
       if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;

@@ -498,7 +498,7 @@ void decode_partial_kernel(DecodeArgs a) {
     const int blk = __builtin_amdgcn_readlane(tab, pb - e_base);
     const bool is_v = lane >= kLR;
     const bool quantise = is_v ? kV8 : kK8;
-    const float scale = row_amax<kLR>(xnew) / kE4M3Max;
+    const float scale = storage_scale(row_amax<kLR>(xnew));  // RN(amax / 448), as append
     const int sub = lane % kLR;
     if (lane == 0) {
       const int64_t row = (unsigned)blk < (unsigned)a.num_blocks

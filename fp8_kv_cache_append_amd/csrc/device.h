@@ -107,6 +107,16 @@ __host__ __device__ __forceinline__ float quotient_rn(float x, float b, float y)
   return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
 }
 
+// The storage rule's scale RN(amax / 448) from the constant RN(1 / 448) and
+// quotient_rn: exact for every fp32 amax in [2^-100, FLT_MAX] (checked for
+// all of them on the host; tests/test_quotient_cpu.py repeats it on a
+// stride); other values (zero, tiny, inf, NaN) divide.
+__host__ __device__ __forceinline__ float storage_scale(float amax) {
+  if (amax >= 0x1p-100f && amax <= 0x1.fffffep127f)
+    return quotient_rn(amax, kE4M3Max, 1.0f / kE4M3Max);
+  return amax / kE4M3Max;
+}
+
 // Four codes of the row with scale = amax / 448: the correctly rounded fp32
 // quotient x / scale (no fast math), clamped to +-448 so that a row whose
 // scale is an fp32 subnormal saturates, then rounded to nearest even onto OCP

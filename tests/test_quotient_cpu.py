@@ -14,7 +14,9 @@ amax / 448 across the range the kernel sends to this path ([2^-53, FLT_MAX]:
 powers of two, significands of all ones, random), at random x in
 [-amax, amax], at x whose quotient lies within a few ulps of every e4m3
 rounding midpoint and of the saturation bound 448, and at every fp32 x in a
-window of quotients around 1 and around 2^-11."""
+window of quotients around 1 and around 2^-11.  It also checks storage_scale,
+the scale RN(amax / 448) from the constant RN(1 / 448) and quotient_rn,
+against the division."""
 import os
 import subprocess
 
@@ -82,6 +84,21 @@ int main() {
       }
     }
   }
+  // storage_scale: RN(amax / 448) bit for bit, for every 13th fp32 amax from
+  // 2^-100 to FLT_MAX and every fp32 of two whole binades
+  long s_checked = 0, s_failed = 0;
+  auto check_scale = [&](float amax) {
+    ++s_checked;
+    if (u_of(fp8kv::storage_scale(amax)) != u_of(amax / 448.0f) && s_failed++ < 5)
+      std::printf("FAIL amax=%a\n", amax);
+  };
+  for (uint32_t u = u_of(0x1p-100f); u < 0x7f800000u; u += 13) check_scale(f_of(u));
+  for (uint32_t u = u_of(1.0f); u < u_of(4.0f); ++u) check_scale(f_of(u));
+  check_scale(0.0f);
+  check_scale(0x1p-149f);
+  check_scale(0x1.fffffep127f);
+  checked += s_checked;
+  failed += s_failed;
   std::printf("%ld %ld\n", checked, failed);
   return 0;
 }
