@@ -107,6 +107,17 @@ __host__ __device__ __forceinline__ float quotient_rn(float x, float b, float y)
   return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
 }
 
+// RN(1 / s) for s in [2^-53, 2^125]: the hardware reciprocal (within an ulp)
+// and one Newton step, e = 1 - s y0 (exact, one fma), y0 + e y0.  On gfx950
+// this is the correctly rounded reciprocal for every fp32 s in that range
+// (tests/test_gpu_reciprocal.py checks all 1.5 G of them on the device; from
+// 2^126 on, where 1 / s is subnormal, it is not).
+__device__ __forceinline__ float reciprocal_rn(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
 // The storage rule's scale RN(amax / 448) from the constant RN(1 / 448) and
 // quotient_rn: exact for every fp32 amax in [2^-100, FLT_MAX] (checked for
 // all of them on the host; tests/test_quotient_cpu.py repeats it on a
@@ -121,10 +132,11 @@ __host__ __device__ __forceinline__ float storage_scale(float amax) {
 // quotient x / scale (no fast math), clamped to +-448 so that a row whose
 // scale is an fp32 subnormal saturates, then rounded to nearest even onto OCP
 // e4m3fn by v_cvt_pk_fp8_f32.  A zero scale gives zero codes.
-// For a scale in [2^-53, FLT_MAX] the quotients come from one correctly
-// rounded reciprocal per row and quotient_rn (three instructions each instead
-// of a full division).  A quotient of magnitude 2^-11 or more is then exactly
-// the correctly rounded one; below that quotient_rn may differ from it in the
+// For a scale in [2^-53, 2^125] (every scale of a finite amax from
+// 448 * 2^-53 up: amax / 448 < 2^120) the quotients come from one correctly
+// rounded reciprocal per row (reciprocal_rn) and quotient_rn (three
+// instructions each instead of a full division).  A quotient of magnitude
+// 2^-11 or more is then exactly the correctly rounded one; below that quotient_rn may differ from it in the
 // last bits, but both are under 2^-10 with the sign of x, so both round to the
 // same signed zero code.  (Checked on the host against division for every
 // fp32 x with |x| <= amax at several scales, among them significands of all
@@ -133,8 +145,8 @@ __host__ __device__ __forceinline__ float storage_scale(float amax) {
 __device__ __forceinline__ uint32_t e4m3_codes4(float4 x, float scale) {
   if (scale == 0.0f) return 0u;
   float q0, q1, q2, q3;
-  if (scale >= 0x1p-53f && scale <= 0x1.fffffep127f) {
-    const float y = 1.0f / scale;  // correctly rounded
+  if (scale >= 0x1p-53f && scale <= 0x1p125f) {
+    const float y = reciprocal_rn(scale);  // RN(1 / scale)
     q0 = quotient_rn(x.x, scale, y);
     q1 = quotient_rn(x.y, scale, y);
     q2 = quotient_rn(x.z, scale, y);
