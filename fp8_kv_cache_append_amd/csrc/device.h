@@ -87,12 +87,33 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 // section "Storage"), for a row of D values held four per lane by D/4
 // consecutive, aligned lanes.
 //
-// row_amax: max |x| over the row (a butterfly inside the lane group; exact).
+// A lane move inside a 16-lane row by a DPP control word (gfx9 encoding:
+// quad permutation, row rotation, half-row mirror), every lane enabled.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// row_amax: max |x| over the row (exact).  The lane group is reduced by lane
+// moves that stay inside it: the two quad swaps (lane ^ 1, lane ^ 2), then
+// for 8 lanes the half-row mirror (the other quad), for 16 the rotations by 4
+// and 8 lanes (the other three quads), for 32 the 16-lane row swap as well.
 template <int LANES_PER_ROW>
 __device__ __forceinline__ float row_amax(float4 x) {
+  static_assert(LANES_PER_ROW == 8 || LANES_PER_ROW == 16 || LANES_PER_ROW == 32, "lane group");
   float m = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-#pragma unroll
-  for (int o = LANES_PER_ROW / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  m = fmaxf(m, dpp_move<0xB1>(m));  // quad_perm [1, 0, 3, 2]
+  m = fmaxf(m, dpp_move<0x4E>(m));  // quad_perm [2, 3, 0, 1]
+  if constexpr (LANES_PER_ROW == 8) {
+    m = fmaxf(m, dpp_move<0x141>(m));  // row_half_mirror
+  } else {
+    m = fmaxf(m, dpp_move<0x124>(m));  // row_ror 4
+    m = fmaxf(m, dpp_move<0x128>(m));  // row_ror 8
+  }
+  if constexpr (LANES_PER_ROW == 32) {
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  }
   return m;
 }
 
