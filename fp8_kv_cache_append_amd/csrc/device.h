@@ -90,31 +90,36 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 // A lane move inside a 16-lane row by a DPP control word (gfx9 encoding:
 // quad permutation, row rotation, half-row mirror), every lane enabled.
 template <int CTRL>
-__device__ __forceinline__ float dpp_move(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 
-// row_amax: max |x| over the row (exact).  The lane group is reduced by lane
-// moves that stay inside it: the two quad swaps (lane ^ 1, lane ^ 2), then
-// for 8 lanes the half-row mirror (the other quad), for 16 the rotations by 4
-// and 8 lanes (the other three quads), for 32 the 16-lane row swap as well.
+// row_amax: max |x| over the row (exact).  Each lane takes the maximum of its
+// four magnitudes; the lane group is then reduced by lane moves that stay
+// inside it: the two quad swaps (lane ^ 1, lane ^ 2), then for 8 lanes the
+// half-row mirror (the other quad), for 16 the rotations by 4 and 8 lanes
+// (the other three quads), for 32 the 16-lane row swap as well.  The
+// magnitudes are compared as their bit patterns: for finite non-negative
+// floats the unsigned order of the patterns is the order of the values, and
+// an integer maximum takes the lane move as its operand (one instruction a
+// step).
 template <int LANES_PER_ROW>
 __device__ __forceinline__ float row_amax(float4 x) {
   static_assert(LANES_PER_ROW == 8 || LANES_PER_ROW == 16 || LANES_PER_ROW == 32, "lane group");
-  float m = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
-  m = fmaxf(m, dpp_move<0xB1>(m));  // quad_perm [1, 0, 3, 2]
-  m = fmaxf(m, dpp_move<0x4E>(m));  // quad_perm [2, 3, 0, 1]
+  uint32_t m = __float_as_uint(fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+  m = max(m, dpp_move<0xB1>(m));  // quad_perm [1, 0, 3, 2]
+  m = max(m, dpp_move<0x4E>(m));  // quad_perm [2, 3, 0, 1]
   if constexpr (LANES_PER_ROW == 8) {
-    m = fmaxf(m, dpp_move<0x141>(m));  // row_half_mirror
+    m = max(m, dpp_move<0x141>(m));  // row_half_mirror
   } else {
-    m = fmaxf(m, dpp_move<0x124>(m));  // row_ror 4
-    m = fmaxf(m, dpp_move<0x128>(m));  // row_ror 8
+    m = max(m, dpp_move<0x124>(m));  // row_ror 4
+    m = max(m, dpp_move<0x128>(m));  // row_ror 8
   }
   if constexpr (LANES_PER_ROW == 32) {
-    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+    auto q = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    m = max((uint32_t)q[0], (uint32_t)q[1]);
   }
-  return m;
+  return __uint_as_float(m);
 }
 
 // x / b from y = RN(1 / b): q = RN(x y), the exact remainder r = x - b q (one
