@@ -49,16 +49,29 @@ struct AppendArgs {
 // the memory, sets the time, and it is better spread over more threads.
 constexpr int kBulkRowsPerThread = 4;
 constexpr int64_t kBulkThreads = 256 * 2048;  // threads the compute units hold at once
+constexpr int kAppendThreads = 256;           // threads per work-group
 
-template <int MODE, int D, int R>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+// ROW32: the cache has fewer than 2^31 rows (checked on the host), so a row
+// index is computed in 32 bits and its address is one multiply-add onto the
+// lane's base.
+template <int MODE, int D, int R, bool ROW32>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   constexpr int kLanesPerRow = D / 4;
   // Row indices fit in 32 bits (checked on the host), so the per-row
   // divisions by the head count and the block size are 32-bit.
-  const uint32_t gtid = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t slots = gridDim.x * blockDim.x / kLanesPerRow;  // rows per sweep
+  const uint32_t gtid = blockIdx.x * kAppendThreads + threadIdx.x;
+  // rows per sweep: even (a work-group holds 8 or 16 rows), so every row of
+  // a thread is a K row or every one a V row, as its first row is
+  const uint32_t slots = gridDim.x * (kAppendThreads / kLanesPerRow);
   const uint32_t r0 = gtid / kLanesPerRow;
   const int sub = (int)(gtid % kLanesPerRow);
+  const bool is_v = (r0 & 1u) != 0;
+  const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
+  constexpr int kMaxElem = 2;  // bytes per stored value: 1 (e4m3) or 2 (bf16)
+  const int elem = quantise ? 1 : kMaxElem;
+  // this lane's bytes of row 0 of the cache (its four values) and the scales
+  uint8_t* const lane_dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + 4 * sub * elem;
+  float* const scales = is_v ? a.vs : a.ks;
 
   // Every row's state is uniform over its kLanesPerRow lanes, so the
   // butterfly below, run under a per-row condition, never reads a lane of
@@ -73,7 +86,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     in[k] = row_id < (uint32_t)a.n_rows;
     const uint32_t rid = in[k] ? row_id : 0u;  // (a row that does not exist reads row 0)
     pair[k] = rid >> 1;
-    const float* src = ((rid & 1) ? a.v_new : a.k_new) + (uint64_t)pair[k] * D + 4 * sub;
+    const float* src = (is_v ? a.v_new : a.k_new) + (uint64_t)pair[k] * D + 4 * sub;
     x[k] = *reinterpret_cast<const float4*>(src);
   }
 #pragma unroll
@@ -93,41 +106,51 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     if (!in[k] || blk[k] < 0 || blk[k] >= a.num_blocks) continue;
-    const int is_v = (int)((r0 + k * slots) & 1u);
     const int h = a.div_hkv.mod((int)pair[k]);
     const int slot = a.div_bs.mod(p[k]);  // 0 <= p < mbps * bs < 2^31
-    const int64_t row = cache_row(a.layout, blk[k], slot, h, a.bs, a.hkv);
-    const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
+    int64_t row;
+    if constexpr (ROW32) {
+      const uint32_t b = (uint32_t)blk[k];
+      row = a.layout == kHeadMajor ? (b * a.hkv + h) * a.bs + slot : (b * a.bs + slot) * a.hkv + h;
+    } else {
+      row = cache_row(a.layout, blk[k], slot, h, a.bs, a.hkv);
+    }
+    uint8_t* dst = lane_dst + (uint64_t)row * (D * elem);
     if (k_is_mx(MODE) && !is_v) {
       // block-scaled K: eight lanes hold a block of 32 values
       const int e = mx_exponent(row_amax<8>(x[k]));
-      uint8_t* dst = static_cast<uint8_t*>(a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], e8m0_value((uint32_t)(e + 127)));
       if ((sub & 7) == 0) a.kexp[row * (D / 32) + sub / 8] = (uint8_t)(e + 127);
     } else if (quantise) {
       const float scale = storage_scale(row_amax<kLanesPerRow>(x[k]));  // RN(amax / 448)
-      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<uint32_t*>(dst) = e4m3_codes4(x[k], scale);
-      if (sub == 0) (is_v ? a.vs : a.ks)[row] = scale;
+      if (sub == 0) scales[row] = scale;
     } else {
-      uint16_t* dst = static_cast<uint16_t*>(is_v ? a.v : a.k) + row * D + 4 * sub;
       *reinterpret_cast<u32x2_t*>(dst) = bf16x4(x[k]);
     }
   }
 }
 
-template <int MODE, int R>
-static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
+template <int MODE, int R, bool ROW32>
+static hipError_t append_for_rows(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
   const int lanes = c.d / 4;
   const int64_t threads = ((int64_t)a.n_rows + R - 1) / R * lanes;
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (threads + kAppendThreads - 1) / kAppendThreads;
   // gtid and the row indices of the last sweep stay below 2^32
-  if (blocks * 256 > UINT32_MAX) return hipErrorInvalidValue;
+  if (blocks * kAppendThreads > UINT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(kAppendThreads);
   if (c.d == 128)
-    hipLaunchKernelGGL((append_kernel<MODE, 128, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<MODE, 128, R, ROW32>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((append_kernel<MODE, 64, R>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((append_kernel<MODE, 64, R, ROW32>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+template <int MODE, int R>
+static hipError_t append_for_d(const CacheView& c, const AppendArgs& a, hipStream_t stream) {
+  if ((int64_t)c.num_blocks * c.bs * c.hkv <= INT32_MAX)
+    return append_for_rows<MODE, R, true>(c, a, stream);
+  return append_for_rows<MODE, R, false>(c, a, stream);
 }
 
 template <int MODE>

@@ -172,21 +172,25 @@ __device__ __forceinline__ uint32_t e4m3_codes4(float4 x, float scale) {
   if (scale == 0.0f) return 0u;
   float q0, q1, q2, q3;
   if (scale >= 0x1p-53f && scale <= 0x1p125f) {
+    // quotient_rn without its sign step, which is taken after the clamp
+    // below: a nonzero quotient already has the sign of x, and the clamp
+    // is symmetric, so the codes are those of quotient_rn
     const float y = reciprocal_rn(scale);  // RN(1 / scale)
-    q0 = quotient_rn(x.x, scale, y);
-    q1 = quotient_rn(x.y, scale, y);
-    q2 = quotient_rn(x.z, scale, y);
-    q3 = quotient_rn(x.w, scale, y);
+    const float a0 = x.x * y, a1 = x.y * y, a2 = x.z * y, a3 = x.w * y;
+    q0 = __builtin_fmaf(__builtin_fmaf(-scale, a0, x.x), y, a0);
+    q1 = __builtin_fmaf(__builtin_fmaf(-scale, a1, x.y), y, a1);
+    q2 = __builtin_fmaf(__builtin_fmaf(-scale, a2, x.z), y, a2);
+    q3 = __builtin_fmaf(__builtin_fmaf(-scale, a3, x.w), y, a3);
   } else {
     q0 = x.x / scale;
     q1 = x.y / scale;
     q2 = x.z / scale;
     q3 = x.w / scale;
   }
-  const float y0 = fminf(fmaxf(q0, -kE4M3Max), kE4M3Max);
-  const float y1 = fminf(fmaxf(q1, -kE4M3Max), kE4M3Max);
-  const float y2 = fminf(fmaxf(q2, -kE4M3Max), kE4M3Max);
-  const float y3 = fminf(fmaxf(q3, -kE4M3Max), kE4M3Max);
+  const float y0 = __builtin_copysignf(__builtin_amdgcn_fmed3f(q0, -kE4M3Max, kE4M3Max), x.x);
+  const float y1 = __builtin_copysignf(__builtin_amdgcn_fmed3f(q1, -kE4M3Max, kE4M3Max), x.y);
+  const float y2 = __builtin_copysignf(__builtin_amdgcn_fmed3f(q2, -kE4M3Max, kE4M3Max), x.z);
+  const float y3 = __builtin_copysignf(__builtin_amdgcn_fmed3f(q3, -kE4M3Max, kE4M3Max), x.w);
   uint32_t codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)codes, true);
 }
