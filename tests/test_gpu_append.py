@@ -6,6 +6,7 @@ hand-derived fixtures, and an exhaustive sweep of every fp32 in [-448, 448]
 through the real append (rows whose amax is 448 have scale exactly 1, so the
 stored code is the plain e4m3 encoding of each value).
 """
+import ctypes
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -282,3 +283,41 @@ def test_append_near_midpoint_quotients(mode, n_tok):
     append_seq(cache, 0, k, v)
     torch.cuda.synchronize()
     _assert_rows_equal(read_rows(cache, 0, n_tok), _expect(mode, k, v), (mode, n_tok))
+
+
+def _cache_tensors(cache):
+    return [t.clone() for t in (cache.k, cache.v, cache.k_scale, cache.v_scale, cache.k_exp)
+            if t is not None]
+
+
+@pytest.mark.parametrize("layout", ["token", "head"])
+@pytest.mark.parametrize("mode", ["K8V8", "K16V8", "MXK8V8"])
+@pytest.mark.parametrize("n_tok", [40, 1100])   # one row per thread / the bulk path
+def test_append_64bit_row_indices(mode, layout, n_tok):
+    """A cache of 2^31 rows or more takes the kernel's 64-bit row arithmetic
+    (smaller ones a 32-bit row index).  The same rows are appended twice into
+    two copies of a small cache: once through its own descriptor, once through
+    a descriptor that declares 2^28 blocks (2^35 rows) while its block table
+    still names only blocks the copy holds, so every access stays inside the
+    allocation.  Both copies must hold the same bytes."""
+    hkv, d, bs = 8, 128, 16
+    lens = np.array([n_tok], np.int32)
+    w = synth.Workload("t", 1, hkv, hkv, d, lens, block_size=bs, shuffle_blocks=True, seed=21)
+    small, large = make_cache(mode, w, layout=layout), make_cache(mode, w, layout=layout)
+    assert torch.equal(small.block_table, large.block_table)
+    rng = np.random.default_rng(21)
+    k = torch.from_numpy(rng.standard_normal((n_tok, hkv, d)).astype(np.float32) * 3).cuda()
+    v = torch.from_numpy(rng.standard_normal((n_tok, hkv, d)).astype(np.float32)).cuda()
+    seq = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    pos = torch.from_numpy(rng.permutation(n_tok).astype(np.int32)).cuda()
+    binding.fp8kv_append(small, k, v, seq, pos)
+    desc = large.desc()
+    assert desc.num_blocks * bs * hkv < 2 ** 31
+    desc.num_blocks = 2 ** 28
+    st = binding.lib().fp8kv_append(ctypes.byref(desc), binding._ptr(k), binding._ptr(v),
+                                    binding._ptr(seq), binding._ptr(pos), n_tok, None)
+    assert st == 0, binding.lib().fp8kv_strerror(st)
+    torch.cuda.synchronize()
+    for a, b in zip(_cache_tensors(small), _cache_tensors(large)):
+        assert torch.equal(a, b), (mode, layout, n_tok)
+    assert torch.count_nonzero(small.k) > 0
