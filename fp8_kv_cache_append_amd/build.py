@@ -5,6 +5,10 @@ Each source is compiled to an object in parallel, then linked.  Flags:
   -O3, no fast-math         fp32 division stays correctly rounded (the append
                             codes are bit-exact with the definition)
   -packed-fp32-ops          packed fp32 VALU forms are disabled on the device
+  kernarg preload 16        a kernel whose leading arguments are scalars or
+                            pointers (the decode merge kernel) gets its first
+                            16 argument dwords in scalar registers at wave
+                            launch, without a load from the argument segment
 """
 from __future__ import annotations
 
@@ -24,7 +28,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Wall", "-Wno-unused-command-line-argument",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _compile(src: str, verbose: bool) -> str:

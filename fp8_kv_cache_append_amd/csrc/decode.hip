@@ -1031,13 +1031,19 @@ void decode_partial_kernel(DecodeArgs a) {
 // (MB = 4, 8 or 16, the smallest that takes a group's splits in one batch),
 // combined online with power-of-two weights; the groups then meet through
 // lane swaps, again with power-of-two weights.
+//
+// The arguments are pointers and scalars only (the divisors' multipliers and
+// shifts passed one by one), 13 dwords that the build preloads into scalar
+// registers at wave launch: the first loads, of the partials, go out without
+// a round trip for the arguments (a structure argument would be loaded from
+// memory).
 template <int D, int MB>
-__global__ __launch_bounds__(64) void decode_merge_kernel(FastDiv div_hkv, FastDiv div_group,
-                                                          int n_splits,
-                                                          const float* __restrict__ part_acc,
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part_acc,
                                                           const float* __restrict__ part_ml,
-                                                          float* __restrict__ out) {
-  const int hkv = div_hkv.d, group = div_group.d;
+                                                          float* __restrict__ out, int n_splits,
+                                                          uint32_t hkv_m, uint32_t hkv_l, int hkv,
+                                                          uint32_t g_m, uint32_t g_l, int group) {
+  const FastDiv div_hkv{hkv_m, hkv_l, hkv}, div_group{g_m, g_l, group};
   constexpr int L = D / 4;    // lanes per split group, four values each
   constexpr int NG = 64 / L;  // split groups of the wave
   // Work-group -> (pair, head).  As in the split kernel, when the pairs come
@@ -1216,15 +1222,16 @@ static void launch_merge_d(unsigned n_wg, int hkv, int group, int n_splits,
                            hipStream_t stream) {
   constexpr int NG = 64 / (D / 4);  // split groups per wave
   const int per_group = (n_splits + NG - 1) / NG;
+  const FastDiv fh = FastDiv::of(hkv), fg = FastDiv::of(group);
   if (per_group <= 4)
     hipLaunchKernelGGL((decode_merge_kernel<D, 4>), dim3(n_wg), dim3(64), 0, stream,
-                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
+                       part_acc, part_ml, out, n_splits, fh.m, fh.l, fh.d, fg.m, fg.l, fg.d);
   else if (per_group <= 8)
     hipLaunchKernelGGL((decode_merge_kernel<D, 8>), dim3(n_wg), dim3(64), 0, stream,
-                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
+                       part_acc, part_ml, out, n_splits, fh.m, fh.l, fh.d, fg.m, fg.l, fg.d);
   else
     hipLaunchKernelGGL((decode_merge_kernel<D, 16>), dim3(n_wg), dim3(64), 0, stream,
-                       FastDiv::of(hkv), FastDiv::of(group), n_splits, part_acc, part_ml, out);
+                       part_acc, part_ml, out, n_splits, fh.m, fh.l, fh.d, fg.m, fg.l, fg.d);
 }
 
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,
