@@ -73,9 +73,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   uint8_t* const lane_dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + 4 * sub * elem;
   float* const scales = is_v ? a.vs : a.ks;
 
-  // Every row's state is uniform over its kLanesPerRow lanes, so the
-  // butterfly below, run under a per-row condition, never reads a lane of
-  // another row or an inactive one.
+  // Every row's state is uniform over its kLanesPerRow lanes, so the lane
+  // moves of the row maximum, which stay inside a row's lane group and run
+  // under a per-row condition, never read a lane of another row or an
+  // inactive one.
   uint32_t pair[R];
   bool in[R];
   float4 x[R];
