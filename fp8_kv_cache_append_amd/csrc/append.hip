@@ -67,8 +67,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int sub = (int)(gtid % kLanesPerRow);
   const bool is_v = (r0 & 1u) != 0;
   const bool quantise = is_v ? v_is_e4m3(MODE) : k_is_e4m3(MODE);
-  constexpr int kMaxElem = 2;  // bytes per stored value: 1 (e4m3) or 2 (bf16)
-  const int elem = quantise ? 1 : kMaxElem;
+  const int elem = quantise ? 1 : 2;  // bytes per stored value: e4m3 or bf16
   // this lane's bytes of row 0 of the cache (its four values) and the scales
   uint8_t* const lane_dst = static_cast<uint8_t*>(is_v ? a.v : a.k) + 4 * sub * elem;
   float* const scales = is_v ? a.vs : a.ks;
