@@ -2,10 +2,12 @@
 K16V8 vs BF16, on one MI355X.
 
 Step: one decode step of batch 16, 16 query / 2 KV heads (GQA 8), head_dim
-128, 2048 keys per sequence (e4m3 K/V, N(0,1) with 2 % x10 outliers):
-  fp8kv_decode_append_partial: the split kernel, which also quantises and
-    stores each sequence's new token (position 2047) and attends it;
-  fp8kv_decode_merge: the merge kernel.
+128, 2048 keys per sequence (e4m3 K/V, N(0,1) with 2 % x10 outliers),
+through the library's entry point fp8kv_decode_append, which launches
+  the split kernel, which also quantises and stores each sequence's new
+    token (position 2047) and attends it (fp8kv_decode_append_partial);
+  the merge kernel (fp8kv_decode_merge), unless the plan has one split of
+    at most 256 keys, whose output the split kernel writes itself.
 The same step as three kernels (fp8kv_append, fp8kv_decode_partial,
 fp8kv_decode_merge) is timed too and reported as unfused_step_us, and the
 unfused control -- append, the whole cache dequantised to bf16 in HBM
@@ -345,9 +347,9 @@ class DecodeBench:
         self.kv_bytes = int(w.lens.sum()) * w.kv_heads * ROW_BYTES[mode](d)
         # narrow QK (Q quantised to e4m3 in the kernel): e4m3-K modes only
         self.narrow = mode in ("K8V8", "K8V16")
+        ws_bytes = binding.fp8kv_decode_workspace_bytes(base, w.batch, g, n)
+        self.ws = torch.empty(ws_bytes // 4 + 4, device=dev)
         if self.narrow:
-            ws_bytes = binding.fp8kv_decode_workspace_bytes(base, w.batch, g, n)
-            self.ws = torch.empty(ws_bytes // 4 + 4, device=dev)
             self.out_q8 = torch.empty_like(self.out)
         self.graph = None
         self.dq = None
@@ -369,15 +371,23 @@ class DecodeBench:
             self.lens, self.max_len, w.sm_scale, self.chunk, self.splits, self.pacc, self.pml)
 
     def step(self, i: int, ev=None):
-        """One decode step: append each sequence's new token (fused into the
-        split kernel), split partials, merge."""
+        """One decode step through fp8kv_decode_append: append each
+        sequence's new token (fused into the split kernel), split partials,
+        merge (none for a plan of one split).  With events (kernel_events):
+        the split and merge kernels through their own entry points, an event
+        pair around each."""
         b, w = self.binding, self.w
-        if ev: ev[0].record()
+        if ev is None:
+            b.fp8kv_decode_append(self.caches[i % len(self.caches)], self.k_new, self.v_new,
+                                  self.q, w.group, self.lens, self.max_len, w.sm_scale,
+                                  self.out, self.ws)
+            return
+        ev[0].record()
         self.split(i)
-        if ev: ev[1].record()
+        ev[1].record()
         b.fp8kv_decode_merge(w.batch, w.kv_heads, w.group, w.head_dim, self.splits,
                              self.pacc, self.pml, self.out)
-        if ev: ev[2].record()
+        ev[2].record()
 
     def step_q8(self, i: int):
         """The same step with narrow QK (fp8kv_decode_append_q8: the same two

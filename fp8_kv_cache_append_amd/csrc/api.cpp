@@ -197,7 +197,7 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
                         const uint16_t* q, int32_t gqa_group, const int32_t* seq_lens,
                         int32_t batch, int32_t max_seq_len, float sm_scale, int32_t chunk_tokens,
                         int32_t n_splits, float* part_acc, float* part_ml, bool q8,
-                        void* stream) {
+                        void* stream, float* out = nullptr) {
   int st = validate_decode_common(cache, gqa_group, batch, max_seq_len);
   if (st != FP8KV_OK) return st;
   if (q8 && (!fp8kv::k_is_e4m3(cache->mode) || cache->k_bias))
@@ -227,7 +227,7 @@ int decode_partial_impl(const fp8kv_cache* cache, const float* k_new, const floa
   if ((st = check_device()) != FP8KV_OK) return st;
   return launch_status(fp8kv::launch_decode_partial(
       view_of(cache), q, gqa_group, seq_lens, batch, log2_scale(sm_scale), chunk_tokens,
-      n_splits, part_acc, part_ml, k_new, v_new, q8, static_cast<hipStream_t>(stream)));
+      n_splits, part_acc, part_ml, k_new, v_new, out, q8, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -290,9 +290,14 @@ int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new
   if (!out || !aligned(out, 16)) return FP8KV_ERR_INVALID;
   if (splits > 0 && (!q || !seq_lens || !aligned(q, 16) || !aligned(seq_lens, 4)))
     return FP8KV_ERR_INVALID;
+  // A plan of one split (of at most 256 keys, bf16 QK, no K bias): the
+  // split kernel writes the output rows itself, since the merge of one split
+  // is a division by its row sum, and no merge kernel follows.
+  const bool direct = fp8kv::direct_output_ok(view_of(cache), q8, chunk, splits);
   st = decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
-                           sm_scale, chunk, splits, part_acc, part_ml, q8, stream);
-  if (st != FP8KV_OK) return st;
+                           sm_scale, chunk, splits, part_acc, part_ml, q8, stream,
+                           direct ? out : nullptr);
+  if (st != FP8KV_OK || direct) return st;
   return fp8kv_decode_merge(batch, cache->num_kv_heads, gqa_group, cache->head_dim, splits,
                             part_acc, part_ml, out, stream);
 }

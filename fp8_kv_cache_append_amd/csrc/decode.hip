@@ -74,6 +74,7 @@ struct DecodeArgs {
   FastDiv div_bs;      // by bs
   FastDiv div_splits;  // by n_splits
   FastDiv div_pairs;   // by the (sequence, KV head) pairs of the grid
+  float* out;          // a plan of one split: the output rows, written here (else null)
 };
 
 constexpr int kWaves = 4;     // waves per work-group; tiles are dealt round-robin
@@ -289,10 +290,17 @@ __device__ __forceinline__ int rotated_head(int pi, int b, const FastDiv& div_hk
 // TB: the cache has a block table in memory; without one (contiguous cache)
 // the block ids are computed, a variant of its own so that no wait for a
 // table load sits in front of the first K/V loads.
-template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE, bool TB>
+//
+// DIRECT: the plan has one split, so the work-group writes the pair's output
+// rows (a.out) as the merge kernel would and no merge kernel follows; an
+// instantiation of its own (at most one tile per wave, plain QK, no bias),
+// so that the other kernels carry none of its code.
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE, bool TB, bool DIRECT>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
+  static_assert(!DIRECT || (SHAPE != kMulti && !Q8 && !KB && !k_is_mx(MODE)),
+                "one-split output: single-pass shapes, plain QK");
   static_assert(!(Q8 && KB), "narrow QK takes no K bias");
   static_assert(!(k_is_mx(MODE) && (KB || APPEND)), "block-scaled K: no bias, no fused append");
   using T = TileRegs<MODE, D>;
@@ -462,7 +470,14 @@ void decode_partial_kernel(DecodeArgs a) {
   float* pacc = a.part_acc + ((int64_t)bh * a.n_splits + split) * G * D;
   float* pml = a.part_ml + ((int64_t)bh * a.n_splits + split) * G * 2;
   const bool empty = t_begin >= t_end;  // no key in this split
+  // DIRECT: the pair's output rows
+  float* const out_rows = DIRECT ? a.out + (int64_t)bh * G * D : nullptr;
   auto leave_empty = [&]() __attribute__((always_inline)) {
+    if constexpr (DIRECT) {  // no key: the rows are 0
+      for (int idx = 4 * threadIdx.x; idx < G * D; idx += 4 * blockDim.x)
+        *reinterpret_cast<f32x4_t*>(out_rows + idx) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
     for (int i = threadIdx.x; i < G; i += blockDim.x) {
       pml[2 * i] = -INFINITY;
       pml[2 * i + 1] = 0.0f;
@@ -989,24 +1004,14 @@ void decode_partial_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = 4 * threadIdx.x; idx < G * D; idx += 4 * blockDim.x) {
-    const int g = idx / D, d = idx % D;
+  // the waves' largest reference of head g and their row sum relative to it
+  auto ref_of = [&](int g) __attribute__((always_inline)) {
     float ms = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, s_m[w][g]);
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w][g];
-      if (mw == -INFINITY) continue;  // a wave without keys
-      sum += ldexpf(1.0f, (int)(mw - ms)) * *reinterpret_cast<const f32x4_t*>(&s_acc[w][g][d]);
-    }
-    *reinterpret_cast<f32x4_t*>(pacc + idx) = sum;
-  }
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    float ms = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, s_m[w][g]);
+    return ms;
+  };
+  auto sum_of = [&](int g, float ms) __attribute__((always_inline)) {
     float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -1015,6 +1020,34 @@ void decode_partial_kernel(DecodeArgs a) {
       const float lw = (s_l[w][0][g] + s_l[w][1][g]) + (s_l[w][2][g] + s_l[w][3][g]);
       lsum += ldexpf(lw, (int)(mw - ms));
     }
+    return lsum;
+  };
+  for (int idx = 4 * threadIdx.x; idx < G * D; idx += 4 * blockDim.x) {
+    const int g = idx / D, d = idx % D;
+    const float ms = ref_of(g);
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][g];
+      if (mw == -INFINITY) continue;  // a wave without keys
+      sum += ldexpf(1.0f, (int)(mw - ms)) * *reinterpret_cast<const f32x4_t*>(&s_acc[w][g][d]);
+    }
+    if constexpr (DIRECT) {
+      // the merge kernel's result for a single split: its weight is 1 and
+      // the other split groups add exact zeros, so it is (acc + 0) / l
+      // (which turns a -0 into +0), or 0 for a row without keys
+      const float l = sum_of(g, ms);
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+      if (l > 0.0f) o = (sum + 0.0f) / l;
+      *reinterpret_cast<f32x4_t*>(out_rows + idx) = o;
+    } else {
+      *reinterpret_cast<f32x4_t*>(pacc + idx) = sum;
+    }
+  }
+  if constexpr (DIRECT) return;
+  for (int g = threadIdx.x; g < G; g += blockDim.x) {
+    const float ms = ref_of(g);
+    const float lsum = sum_of(g, ms);
     pml[2 * g] = ms;
     pml[2 * g + 1] = lsum;
   }
@@ -1124,24 +1157,33 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   *reinterpret_cast<f32x4_t*>(out + ((int64_t)bh * group + g) * D + 4 * d4) = o;
 }
 
-template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE>
+template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE, bool DIRECT>
 static void launch_split(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
   if (a.table)
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, true>), grid, block,
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, true, DIRECT>),
+                       grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, false>), grid,
-                       block, 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<MODE, D, APPEND, Q8, KB, SHAPE, false, DIRECT>),
+                       grid, block, 0, stream, a);
 }
 
 template <int MODE, int D, bool APPEND, bool Q8, bool KB>
 static void launch_split_shape(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  if constexpr (!Q8 && !KB && !k_is_mx(MODE)) {
+    if (a.out) {  // one split of at most one tile per wave (direct_output_ok)
+      if (a.chunk > kWaves * kTile / 2)
+        launch_split<MODE, D, APPEND, Q8, KB, kOne, true>(a, grid, block, stream);
+      else
+        launch_split<MODE, D, APPEND, Q8, KB, kHalf, true>(a, grid, block, stream);
+      return;
+    }
+  }
   if (a.chunk > kWaves * kTile)
-    launch_split<MODE, D, APPEND, Q8, KB, kMulti>(a, grid, block, stream);
+    launch_split<MODE, D, APPEND, Q8, KB, kMulti, false>(a, grid, block, stream);
   else if (a.chunk > kWaves * kTile / 2)
-    launch_split<MODE, D, APPEND, Q8, KB, kOne>(a, grid, block, stream);
+    launch_split<MODE, D, APPEND, Q8, KB, kOne, false>(a, grid, block, stream);
   else
-    launch_split<MODE, D, APPEND, Q8, KB, kHalf>(a, grid, block, stream);
+    launch_split<MODE, D, APPEND, Q8, KB, kHalf, false>(a, grid, block, stream);
 }
 
 template <int MODE, bool APPEND, bool Q8, bool KB>
@@ -1198,7 +1240,8 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  const int32_t* seq_lens, int batch, float c_scale,
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
-                                 bool q8, hipStream_t stream) {
+                                 float* out, bool q8, hipStream_t stream) {
+  if (out && !direct_output_ok(c, q8, chunk, n_splits)) return hipErrorInvalidValue;
   const uint64_t rows = (uint64_t)c.num_blocks * c.bs * c.hkv;
   const uint64_t k_bytes = rows * c.d * (k_is_e4m3(c.mode) ? 1 : 2);
   const uint64_t v_bytes = rows * c.d * (v_is_e4m3(c.mode) ? 1 : 2);
@@ -1207,7 +1250,7 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                c.hkv,   group,     c.bs,    c.mbps,  chunk,    n_splits, c.num_blocks,
                c.layout, slot_stride(c.layout, c.hkv), k_bytes, v_bytes,
                FastDiv::of(c.hkv), FastDiv::of(c.bs), FastDiv::of(n_splits),
-               FastDiv::of(batch * c.hkv)};
+               FastDiv::of(batch * c.hkv), out};
   const unsigned n_wg = (unsigned)((int64_t)batch * c.hkv * n_splits);
   if (k_new)
     launch_partial_append<true>(c, a, n_wg, q8, stream);

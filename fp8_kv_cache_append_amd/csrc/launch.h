@@ -99,11 +99,19 @@ hipError_t launch_append(const CacheView& c, const float* k_new, const float* v_
 // [batch][hkv][D]) the kernel first appends each sequence's new token at
 // position seq_lens[b] - 1 (fused append); null pointers: plain decode.
 // q8: narrow QK (Q quantised to e4m3 in the kernel; e4m3 K modes only).
+// out (only where direct_output_ok): the output rows, written by the split
+// kernel as the merge kernel would write them; null: partials.
 hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int group,
                                  const int32_t* seq_lens, int batch, float c_scale,
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
-                                 bool q8, hipStream_t stream);
+                                 float* out, bool q8, hipStream_t stream);
+
+// A plan whose splits the split kernel can finish itself: one split of at
+// most one tile per wave (256 keys), bf16 QK, no K bias, per-row K scales.
+inline bool direct_output_ok(const CacheView& c, bool q8, int chunk, int n_splits) {
+  return n_splits == 1 && chunk <= 256 && !q8 && !c.kbias && !k_is_mx(c.mode);
+}
 
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,
                                const float* part_acc, const float* part_ml, float* out,
