@@ -290,10 +290,10 @@ int decode_impl(const fp8kv_cache* cache, const float* k_new, const float* v_new
   if (!out || !aligned(out, 16)) return FP8KV_ERR_INVALID;
   if (splits > 0 && (!q || !seq_lens || !aligned(q, 16) || !aligned(seq_lens, 4)))
     return FP8KV_ERR_INVALID;
-  // A plan of one split (of at most 256 keys, bf16 QK, no K bias): the
-  // split kernel writes the output rows itself, since the merge of one split
-  // is a division by its row sum, and no merge kernel follows.
-  const bool direct = fp8kv::direct_output_ok(view_of(cache), q8, chunk, splits);
+  // A plan of one split (of at most 256 keys, no K bias, per-row K scales):
+  // the split kernel writes the output rows itself, since the merge of one
+  // split is a division by its row sum, and no merge kernel follows.
+  const bool direct = fp8kv::direct_output_ok(view_of(cache), chunk, splits);
   st = decode_partial_impl(cache, k_new, v_new, q, gqa_group, seq_lens, batch, max_seq_len,
                            sm_scale, chunk, splits, part_acc, part_ml, q8, stream,
                            direct ? out : nullptr);

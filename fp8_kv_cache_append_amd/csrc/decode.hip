@@ -293,14 +293,14 @@ __device__ __forceinline__ int rotated_head(int pi, int b, const FastDiv& div_hk
 //
 // DIRECT: the plan has one split, so the work-group writes the pair's output
 // rows (a.out) as the merge kernel would and no merge kernel follows; an
-// instantiation of its own (at most one tile per wave, plain QK, no bias),
-// so that the other kernels carry none of its code.
+// instantiation of its own (at most one tile per wave, per-row K scales, no
+// bias), so that the other kernels carry none of its code.
 template <int MODE, int D, bool APPEND, bool Q8, bool KB, int SHAPE, bool TB, bool DIRECT>
 __global__ __launch_bounds__(64 * kWaves, split_wgs_per_cu(MODE, D))
 void decode_partial_kernel(DecodeArgs a) {
   static_assert(!Q8 || k_is_e4m3(MODE), "narrow QK needs e4m3 K codes");
-  static_assert(!DIRECT || (SHAPE != kMulti && !Q8 && !KB && !k_is_mx(MODE)),
-                "one-split output: single-pass shapes, plain QK");
+  static_assert(!DIRECT || (SHAPE != kMulti && !KB && !k_is_mx(MODE)),
+                "one-split output: single-pass shapes, per-row K scales, no bias");
   static_assert(!(Q8 && KB), "narrow QK takes no K bias");
   static_assert(!(k_is_mx(MODE) && (KB || APPEND)), "block-scaled K: no bias, no fused append");
   using T = TileRegs<MODE, D>;
@@ -1169,7 +1169,7 @@ static void launch_split(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t
 
 template <int MODE, int D, bool APPEND, bool Q8, bool KB>
 static void launch_split_shape(const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
-  if constexpr (!Q8 && !KB && !k_is_mx(MODE)) {
+  if constexpr (!KB && !k_is_mx(MODE)) {
     if (a.out) {  // one split of at most one tile per wave (direct_output_ok)
       if (a.chunk > kWaves * kTile / 2)
         launch_split<MODE, D, APPEND, Q8, KB, kOne, true>(a, grid, block, stream);
@@ -1241,7 +1241,7 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  int chunk, int n_splits, float* part_acc,
                                  float* part_ml, const float* k_new, const float* v_new,
                                  float* out, bool q8, hipStream_t stream) {
-  if (out && !direct_output_ok(c, q8, chunk, n_splits)) return hipErrorInvalidValue;
+  if (out && !direct_output_ok(c, chunk, n_splits)) return hipErrorInvalidValue;
   const uint64_t rows = (uint64_t)c.num_blocks * c.bs * c.hkv;
   const uint64_t k_bytes = rows * c.d * (k_is_e4m3(c.mode) ? 1 : 2);
   const uint64_t v_bytes = rows * c.d * (v_is_e4m3(c.mode) ? 1 : 2);

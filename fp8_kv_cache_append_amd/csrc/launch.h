@@ -108,9 +108,10 @@ hipError_t launch_decode_partial(const CacheView& c, const uint16_t* q, int grou
                                  float* out, bool q8, hipStream_t stream);
 
 // A plan whose splits the split kernel can finish itself: one split of at
-// most one tile per wave (256 keys), bf16 QK, no K bias, per-row K scales.
-inline bool direct_output_ok(const CacheView& c, bool q8, int chunk, int n_splits) {
-  return n_splits == 1 && chunk <= 256 && !q8 && !c.kbias && !k_is_mx(c.mode);
+// most one tile per wave (256 keys), no K bias, per-row K scales (bf16 or
+// narrow QK).
+inline bool direct_output_ok(const CacheView& c, int chunk, int n_splits) {
+  return n_splits == 1 && chunk <= 256 && !c.kbias && !k_is_mx(c.mode);
 }
 
 hipError_t launch_decode_merge(int batch, int hkv, int group, int d, int n_splits,

@@ -241,9 +241,9 @@ int fp8kv_decode_merge(int32_t batch, int32_t num_kv_heads, int32_t gqa_group,
 /*
  * Decode attention: fp8kv_decode_partial with the plan of fp8kv_decode_plan
  * (partials in `workspace`), then fp8kv_decode_merge.  A plan of one split
- * of at most 256 keys (bf16 QK, no K bias, per-row K scales) runs the split
- * kernel alone: it writes the output rows itself, bit-identical to the merge
- * of its one split.  One query token per sequence; seq_lens counts the keys
+ * of at most 256 keys (no K bias, per-row K scales; also for the narrow-QK
+ * entry points) runs the split kernel alone: it writes the output rows
+ * itself, bit-identical to the merge of its one split.  One query token per sequence; seq_lens counts the keys
  * it attends (the appended token included).
  * out: device fp32 [batch][num_kv_heads * gqa_group][head_dim].
  */

@@ -69,3 +69,40 @@ def test_single_split_matches_merge_kernel(case):
     ref, lo, hi = oracle.decode(mode, q_bits, [s[0][:n] for s, n in zip(seqs, lens)],
                                 [s[1][:n] for s, n in zip(seqs, lens)], w.sm_scale, bounds=True)
     _gate(got, ref, lo, hi, case)
+
+
+@pytest.mark.parametrize("mode", ["K8V8", "K8V16"])
+def test_single_split_narrow_qk(mode):
+    """Narrow QK (fp8kv_decode_q8) on plans of one split runs the split kernel
+    alone as well: its output meets the narrow-QK gate against the oracle's
+    narrow path, and the fused-append form (fp8kv_decode_append_q8) is
+    bit-identical to fp8kv_append followed by fp8kv_decode_q8."""
+    from test_gpu_decode_q8 import _narrow_gate, decode_q8
+    lens = np.array([77, 128, 5, 0], np.int32)
+    w = synth.Workload("one_split_q8", 4, 16, 2, 128, lens, "outliers", block_size=16,
+                       shuffle_blocks=True, seed=41)
+    fused, plain = make_cache(mode, w), make_cache(mode, w)
+    seqs = [synth.kv_sequence(w, b) for b in range(w.batch)]
+    k_new = np.zeros((w.batch, w.kv_heads, w.head_dim), np.float32)
+    v_new = np.zeros_like(k_new)
+    for b, (k, v) in enumerate(seqs):
+        n = int(lens[b])
+        if n:
+            append_seq(fused, b, k[:n - 1], v[:n - 1])
+            append_seq(plain, b, k[:n], v[:n])
+            k_new[b], v_new[b] = k[n - 1], v[n - 1]
+    chunk, splits = binding.fp8kv_decode_plan(plain, w.batch, w.group, int(lens.max()))
+    assert splits == 1, (chunk, splits)
+    q_bits = synth.q_bf16_bits(w.seed + 1, (w.batch, w.q_heads, w.head_dim))
+    want = decode_q8(plain, q_bits, lens, w.group, w.sm_scale)
+    ws = torch.empty(binding.fp8kv_decode_workspace_bytes(fused, w.batch, w.group,
+                                                          int(lens.max())) // 4 + 4, device=DEV)
+    got = torch.full((w.batch, w.q_heads, w.head_dim), float("nan"), device=DEV)
+    binding.fp8kv_decode_append_q8(fused, torch.from_numpy(k_new).to(DEV),
+                                   torch.from_numpy(v_new).to(DEV), q_tensor(q_bits), w.group,
+                                   torch.from_numpy(lens).to(DEV), int(lens.max()), w.sm_scale,
+                                   got, ws)
+    got = got.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), mode
+    _narrow_gate(want, mode, q_bits, [s[0][:n] for s, n in zip(seqs, lens)],
+                 [s[1][:n] for s, n in zip(seqs, lens)], w.sm_scale, ("one split q8", mode))
