@@ -259,8 +259,8 @@ int fp8kv_decode(const fp8kv_cache* cache, const uint16_t* q,
  * seq_lens[b] - 1 exactly as fp8kv_append stores it (same codes, scales and
  * bf16 bytes; not written if that position's block id is out of range), and
  * then attended with the rest of the sequence: the result equals
- * fp8kv_append followed by fp8kv_decode, in the two kernels of the split-KV
- * decode instead of three.  The slot is written by the work-group whose
+ * fp8kv_append followed by fp8kv_decode, in the kernels of the split-KV
+ * decode (two, or one for a plan of one split) instead of one more.  The slot is written by the work-group whose
  * split holds it, so it must not lie in keys that another sequence of the
  * same call attends (shared blocks must be full).
  *   k_new, v_new  device fp32 [batch][num_kv_heads][head_dim], 16-byte aligned
@@ -322,7 +322,7 @@ int fp8kv_decode_append_partial(const fp8kv_cache* cache, const float* k_new,
 /*
  * fp8kv_decode without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, serving loops or harnesses that
- * forbid allocation).  The same two kernels and the same plan as
+ * forbid allocation).  The same kernels and the same plan as
  * fp8kv_decode, so the output is bit-identical to fp8kv_decode's; the split
  * partials live in a device array the library owns instead of a caller
  * workspace: 64 MiB, one copy per GPU, loaded with the library's code
